@@ -1,0 +1,124 @@
+// kda_api.hip -- the C ABI of libkda (declared in include/kda.h): argument
+// validation on the host, workspace sizing, and kernel dispatch.  Nothing
+// here allocates device memory or synchronises, unless KDA_DEBUG_SYNC=1.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/kda.h"
+#include "kda_internal.hpp"
+
+namespace {
+
+bool debug_sync() {
+    static int flag = -1;
+    if (flag < 0) {
+        const char* e = getenv("KDA_DEBUG_SYNC");
+        flag = (e && e[0] == '1') ? 1 : 0;
+    }
+    return flag == 1;
+}
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+bool dim_ok(int d) { return d == 64 || d == 128; }
+
+kda_status finish(hipError_t err, void* stream) {
+    if (err != hipSuccess) return KDA_ERR_HIP;
+    if (debug_sync()) {
+        if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KDA_ERR_HIP;
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative or too large";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: unsupported d_k, d_v, chunk or dtype";
+        case KDA_ERR_ARG: return "KDA_ERR_ARG: invalid scalar argument";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not 16-byte aligned";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or execution error";
+    }
+    return "KDA_ERR_?: unknown status";
+}
+
+const char* kda_version(void) { return "libkda 0.1 gfx950"; }
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    return kda::chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                         float g_min, const float* s0, void* o, float* s_final, int B, int T, int H,
+                         int dk, int dv, int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (chunk != 64 || !dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (B > 65535 || H > 65535 || (long long)B * H * T > (1LL << 40)) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(s0) || !aligned16(o) || !aligned16(s_final) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t need = kda::chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16,
+                     workspace, stream};
+    return finish(kda::launch_chunk(a), stream);
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                              float g_min, float* state, void* o, int B, int H, int dk, int dv, kda_dtype dt,
+                              void* stream) {
+    if (B < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !z || !beta || !state || !o) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    kda::DecodeArgs a{q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
+    return finish(kda::launch_decode(a), stream);
+}
+
+size_t kda_out_gate_workspace_bytes(int B, int T, int H, int dv, int d_model, kda_dtype dt,
+                                    int with_projection) {
+    if (B < 0 || T < 0 || H < 0 || !dim_ok(dv)) return 0;
+    return kda::gate_workspace_bytes(B, T, H, dv, d_model, dt == KDA_BF16, with_projection != 0);
+}
+
+kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* w, void* y, int B, int T,
+                        int H, int dv, int d_model, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (B < 0 || T < 0 || H < 0 || d_model < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (w && (dt != KDA_BF16 || d_model % 16 != 0 || d_model == 0)) return KDA_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || !isfinite(eps)) return KDA_ERR_ARG;
+    const long long rows = (long long)B * T;
+    if (rows * H > (1LL << 40)) return KDA_ERR_SHAPE;
+    if (w && ((rows + 127) / 128 > 65535 || (long long)H * dv > (1 << 20))) return KDA_ERR_SHAPE;
+    if (rows == 0 || H == 0) return KDA_OK;
+    if (!o || !gate || !y) return KDA_ERR_NULL;
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(w) || !aligned16(y) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t need = kda::gate_workspace_bytes(B, T, H, dv, d_model, dt == KDA_BF16, w != nullptr);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    kda::GateArgs a{o, gate, eps, w, y, B, T, H, dv, d_model, dt == KDA_BF16, workspace, stream};
+    return finish(kda::launch_out_gate(a), stream);
+}
+
+}  // extern "C"

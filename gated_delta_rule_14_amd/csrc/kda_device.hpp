@@ -1,0 +1,102 @@
+// kda_device.hpp -- device-side building blocks shared by the libkda kernels
+// (gfx950 / CDNA4, wave64).
+//
+//  * element types: fp32 and bf16 (__bf16, converted round-to-nearest-even);
+//  * 16x16 MFMA tiles with fp32 accumulation: v_mfma_f32_16x16x32_bf16 for
+//    bf16 operands and v_mfma_f32_16x16x4_f32 for fp32 operands;
+//  * fragment loaders for operands stored "K-contiguous" (each row of the
+//    A operand and each column of the B operand is contiguous along the
+//    contraction index), which is how every LDS tile in libkda is laid out.
+//
+// Lane layout of a 16x16 tile on a 64-wide wavefront (lane l):
+//   A operand (16 x K):  row l%16, contraction indices [(l/16)*KPL, +KPL)
+//   B operand (K x 16):  col l%16, contraction indices [(l/16)*KPL, +KPL)
+//   C / D (16 x 16):     col l%16, rows 4*(l/16) + e, e = 0..3
+// where KPL is 8 for bf16 (K = 32 per instruction) and 1 for fp32 (K = 4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;   // 16-byte raw vector
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <class T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------- MFMA
+template <class CT> struct Mfma;
+
+template <> struct Mfma<bf16> {
+    static constexpr int KSTEP = 32;   // contraction length per instruction
+    static constexpr int KPL = 8;      // contraction elements per lane
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag from_floats(const float* v) {
+        frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (bf16)v[i];
+        return f;
+    }
+    static __device__ __forceinline__ void to_floats(frag f, float* v) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)f[i];
+    }
+};
+
+template <> struct Mfma<float> {
+    static constexpr int KSTEP = 4;
+    static constexpr int KPL = 1;
+    typedef float frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ frag from_floats(const float* v) { return v[0]; }
+    static __device__ __forceinline__ void to_floats(frag f, float* v) { v[0] = f; }
+};
+
+// Fragment of a K-contiguous tile: element (row0 + l%16, k0 + (l/16)*KPL + j).
+// `ld` is the row stride in elements; for bf16 the address must be 16-byte
+// aligned (ld and k0 multiples of 8).
+template <class CT>
+__device__ __forceinline__ typename Mfma<CT>::frag load_frag(const CT* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    const CT* p = base + (size_t)(row0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<CT>::KPL;
+    return *reinterpret_cast<const typename Mfma<CT>::frag*>(p);
+}
+
+// Same addressing, from an fp32 tile, converted to the operand type.
+template <class CT>
+__device__ __forceinline__ typename Mfma<CT>::frag load_frag_f32(const float* base, int ld, int row0, int k0) {
+    const int l = lane_id();
+    const float* p = base + (size_t)(row0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<CT>::KPL;
+    float v[Mfma<CT>::KPL];
+#pragma unroll
+    for (int j = 0; j < Mfma<CT>::KPL; ++j) v[j] = p[j];
+    return Mfma<CT>::from_floats(v);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row / column of accumulator element e held by this lane.
+__device__ __forceinline__ int acc_row(int e) { return 4 * (lane_id() >> 4) + e; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace kda

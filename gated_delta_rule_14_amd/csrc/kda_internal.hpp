@@ -1,0 +1,49 @@
+// kda_internal.hpp -- launcher interface between the host entry points
+// (kda_api.hip) and the kernel translation units.  Arguments have already
+// been validated when a launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v, *z, *beta;
+    float g_min;
+    float* state;
+    void* o;
+    int B, H, dk, dv;
+    bool bf16;
+    void* stream;
+};
+hipError_t launch_decode(const DecodeArgs& a);
+
+struct ChunkArgs {
+    const void *q, *k, *v, *z, *beta;
+    float g_min;
+    const float* s0;
+    void* o;
+    float* s_final;
+    int B, T, H, dk, dv;
+    bool bf16;
+    void* workspace;
+    void* stream;
+};
+size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
+hipError_t launch_chunk(const ChunkArgs& a);
+
+struct GateArgs {
+    const void *o, *gate;
+    float eps;
+    const void* w;
+    void* y;
+    int B, T, H, dv, d_model;
+    bool bf16;
+    void* workspace;
+    void* stream;
+};
+size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj);
+hipError_t launch_out_gate(const GateArgs& a);
+
+}  // namespace kda

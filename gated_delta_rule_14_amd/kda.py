@@ -1,0 +1,139 @@
+"""Python front end of libkda: argument marshalling only.
+
+Every step of the operator runs in the HIP kernels of libkda.so; torch is
+used for device memory (outputs, workspaces) and for the current HIP stream.
+Names follow the C ABI in include/kda.h:
+
+  chunk_fwd       -> kda_chunk_fwd        chunkwise prefill
+  recurrent_step  -> kda_recurrent_step   one decode token, state in place
+  out_gate        -> kda_out_gate         RMSNorm x sigmoid gate (+ projection)
+  layer           -> kda_chunk_fwd + kda_out_gate, returning the
+                     {"outputs", "final_state"} dictionary of the
+                     "KDA Recurrence" problem (final_state kept in fp32)
+"""
+import ctypes
+
+import torch
+
+from ._lib import KDA_BF16, KDA_F32, check, lib
+
+CHUNK = 64
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"libkda: unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"libkda: {name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"libkda: {name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"libkda: {name} must be contiguous")
+
+
+def chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return int(lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK,
+                                                   KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def chunk_fwd(q, k, v, z, beta, g_min, s0=None, *, o=None, s_final=None, workspace=None,
+              want_state=True):
+    """Chunkwise prefill. q, k, z: (B,T,H,dk); v: (B,T,H,dv); beta: (B,T,H);
+    s0: (B,H,dk,dv) fp32 or None.  Returns (o, s_final); s_final is fp32 and
+    None when want_state is False.  s_final may be passed as s0 (in place)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    need = lib().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK, _dt(q))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    check("kda_chunk_fwd", lib().kda_chunk_fwd(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(o), _p(s_final),
+        B, T, H, dk, dv, CHUNK, _dt(q), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev)))
+    return o, s_final
+
+
+def recurrent_step(q, k, v, z, beta, g_min, state, *, o=None):
+    """One decode token. q, k, z: (B,H,dk); v: (B,H,dv); beta: (B,H);
+    state: (B,H,dk,dv) fp32, updated in place.  Returns o (B,H,dv)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("state", state)):
+        _need(t, name, dev)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if state.dtype != torch.float32:
+        raise TypeError("libkda: state must be float32")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    check("kda_recurrent_step", lib().kda_recurrent_step(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(state), _p(o),
+        B, H, dk, dv, _dt(q), _stream(dev)))
+    return o
+
+
+def out_gate(o, gate, eps, w=None, *, y=None, workspace=None):
+    """RMSNorm over each head's dv values x sigmoid(gate), heads concatenated;
+    projected by w (d_model, H*dv) when given.  o, gate: (B,T,H,dv)."""
+    dev = o.device
+    _need(o, "o", dev)
+    _need(gate, "gate", dev)
+    B, T, H, dv = o.shape
+    d_model = 0
+    if w is not None:
+        _need(w, "w", dev)
+        d_model = w.shape[0]
+        if w.dtype != torch.bfloat16:
+            raise TypeError("libkda: projection w must be bfloat16")
+    if y is None:
+        width = d_model if w is not None else H * dv
+        y = torch.empty((B, T, width), dtype=o.dtype, device=dev)
+    need = lib().kda_out_gate_workspace_bytes(B, T, H, dv, d_model, _dt(o), int(w is not None))
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("kda_out_gate", lib().kda_out_gate(
+        _p(o), _p(gate), float(eps), _p(w), _p(y), B, T, H, dv, d_model, _dt(o),
+        _p(workspace), ws_bytes, _stream(dev)))
+    return y
+
+
+def layer(query, key, value, decay_logits, write_strength, output_gate_logits,
+          output_projection, initial_state, g_min, eps):
+    """The KDA layer of the "KDA Recurrence" problem: recurrence (chunkwise),
+    RMSNorm x sigmoid gate, head concat and projection.  Inputs are not
+    modified.  Returns {"outputs": (B,T,d_model), "final_state": (B,H,dk,dv) fp32}."""
+    s0 = initial_state
+    if s0 is not None and s0.dtype != torch.float32:
+        s0 = s0.float().contiguous()
+    o, s = chunk_fwd(query, key, value, decay_logits, write_strength, g_min, s0)
+    out = out_gate(o, output_gate_logits, eps, output_projection)
+    return {"outputs": out, "final_state": s}

@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of libkda, the Kimi Delta Attention (KDA) operator for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operator (Kimi Linear tech report, section 3, Eq. 1; also
+ * "Diagonal-Plus-Low-Rank Matrices and Kimi Delta Attention", section 2):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                          (read from the updated state)
+ *     alpha_t = exp(g_min * sigmoid(z_t)),  g_min < 0   ("KDA Recurrence")
+ *
+ * with one d_k x d_v state per (batch, head).  Three calls cover the path:
+ * chunkwise prefill, one decode token, and the output epilogue.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    and row-major in the layouts given below, and 16-byte aligned.  The
+ *    library never allocates or frees device memory; scratch space comes
+ *    from a caller-provided workspace whose size a query function returns.
+ *  - Inputs are never written (the one exception is the decode state,
+ *    which is the carry and is updated in place).
+ *  - Token tensors use one dtype (KDA_F32 or KDA_BF16) for q, k, v, z,
+ *    beta, the gate logits and the outputs o / y.  The recurrent state is
+ *    always fp32.
+ *  - Supported sizes: d_k, d_v in {64, 128}; chunk == 64; B, H >= 1;
+ *    T >= 0 (any T: the last chunk is masked).  Other sizes return
+ *    KDA_ERR_UNSUPPORTED.
+ *  - Arguments are checked on the host before anything is launched; a bad
+ *    argument returns a status and launches nothing.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL means the null stream) and the call
+ *    returns without waiting; a launch failure is reported as KDA_ERR_HIP.
+ *    Device-side faults surface at the caller's next synchronisation.
+ *    Setting the environment variable KDA_DEBUG_SYNC=1 makes every call
+ *    synchronise its stream and report execution errors as KDA_ERR_HIP.
+ *  - Not checked on the device: beta in [0, 1] and finite inputs (the
+ *    "KDA Recurrence" constraints).  g_min must be finite and < 0.
+ *  - The library keeps no state between calls and is re-entrant; calls on
+ *    different streams may run concurrently if their buffers are disjoint.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,         /* a required pointer is NULL                  */
+    KDA_ERR_SHAPE = 2,        /* a size is negative or overflows             */
+    KDA_ERR_UNSUPPORTED = 3,  /* d_k / d_v / chunk / dtype not supported     */
+    KDA_ERR_ARG = 4,          /* g_min not finite and negative, eps < 0 ...  */
+    KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */
+    KDA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned            */
+    KDA_ERR_HIP = 7           /* a HIP launch or execution error             */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_str(kda_status s);
+
+/* Library build identification (static string). */
+const char* kda_version(void);
+
+/*
+ * Chunkwise prefill.
+ *
+ * Computes o_t for t = 0..T-1 and the state after the last token, for every
+ * (batch, head), by the chunkwise expansion of Eq. 1 (tech report, section
+ * 3.1 and appendix B, Propositions 1-2 / Eqs. 16-19): per 64-token chunk,
+ * the decay-weighted key-key and query-key products, the unit-lower
+ * triangular solve that yields the WY/UT auxiliaries W and U, and the
+ * chunk-to-chunk state propagation.
+ *
+ *   q, k, z   (B, T, H, dk)  dtype dt   queries, keys, decay logits
+ *   v         (B, T, H, dv)  dtype dt   values
+ *   beta      (B, T, H)      dtype dt   write strengths
+ *   g_min                                lower log-decay bound, < 0
+ *   s0        (B, H, dk, dv) fp32       initial state, or NULL for zeros
+ *   o         (B, T, H, dv)  dtype dt   output (written)
+ *   s_final   (B, H, dk, dv) fp32       final state (written), or NULL to
+ *                                        skip; may equal s0 (in place)
+ *   workspace, workspace_bytes           device scratch of at least
+ *                                        kda_chunk_fwd_workspace_bytes()
+ * The result is deterministic: identical inputs give identical bits.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                     kda_dtype dt);
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                         const void* beta, float g_min, const float* s0, void* o,
+                         float* s_final, int B, int T, int H, int dk, int dv, int chunk,
+                         kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * One decode token for every (batch, head): the fused recurrent step.
+ *
+ * Order of the per-token step (agentlenshq blog on KDA, section on the
+ * fused recurrent decode kernel; "KDA Recurrence" readout rule): decay the
+ * state by alpha, predict p = S'^T k, residual r = beta (v - p), write
+ * S = S' + k r^T, read o = S^T q from the updated state.
+ *
+ *   q, k, z   (B, H, dk)  dtype dt
+ *   v         (B, H, dv)  dtype dt
+ *   beta      (B, H)      dtype dt
+ *   state     (B, H, dk, dv) fp32, read and updated IN PLACE
+ *   o         (B, H, dv)  dtype dt (written)
+ * The state is read once and written once per call.
+ */
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* z,
+                              const void* beta, float g_min, float* state, void* o,
+                              int B, int H, int dk, int dv, kda_dtype dt, void* stream);
+
+/*
+ * Output epilogue ("KDA Recurrence" problem statement and first worked
+ * example): per (batch, token, head), RMS normalisation over the d_v values
+ * with eps inside the square root and no learnable weight, multiplied by
+ * sigmoid(gate); heads concatenated to width H*d_v; then, if w is given,
+ * the projection out = y W^T with W of shape (d_model, H*d_v) and no bias.
+ *
+ *   o, gate   (B, T, H, dv)        dtype dt
+ *   eps                             >= 0
+ *   w         (d_model, H*dv) bf16, or NULL for no projection
+ *   y         (B, T, H*dv) dtype dt when w is NULL,
+ *             (B, T, d_model) dtype dt otherwise (written)
+ *   workspace kda_out_gate_workspace_bytes() bytes (0 when w is NULL)
+ * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.
+ */
+size_t kda_out_gate_workspace_bytes(int B, int T, int H, int dv, int d_model, kda_dtype dt,
+                                    int with_projection);
+kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* w, void* y,
+                        int B, int T, int H, int dv, int d_model, kda_dtype dt,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

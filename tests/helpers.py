@@ -1,0 +1,43 @@
+"""Shared helpers for the GPU parity tests: relative Frobenius errors and
+oracle runs on host copies of the exact bits the GPU consumed."""
+import numpy as np
+
+import kda_inputs as ki
+import oracle
+
+# Parity bars: fp32 token tensors 1e-5 on outputs and state; bf16 token
+# tensors with an fp32 state 2e-2 on outputs and 1e-2 on the final state.
+TOL = {"f32": (1e-5, 1e-5), "bf16": (2e-2, 1e-2)}
+
+
+def rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm((a - b).ravel()) / max(np.linalg.norm(b.ravel()), 1e-300))
+
+
+def host(t):
+    return ki.to_host_bits(t)
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def oracle_prefill(x, g_min=ki.G_MIN, heads=None, batches=None):
+    """Oracle on the host copy of prefill inputs x (dict of device tensors).
+    heads / batches select a subset (sampled outputs); returns (o, s)."""
+    sel_b = slice(None) if batches is None else batches
+    sel_h = slice(None) if heads is None else heads
+
+    def cut(t, lead_h_axis):
+        a = host(t)
+        a = a[sel_b]
+        idx = [slice(None)] * a.ndim
+        idx[lead_h_axis] = sel_h
+        return np.ascontiguousarray(a[tuple(idx)])
+
+    q, k, v, z = (cut(x[n], 2) for n in ("q", "k", "v", "z"))
+    beta = cut(x["beta"], 2)
+    s0 = cut(x["s0"], 1) if x.get("s0") is not None else None
+    return oracle.forward(q, k, v, z, beta, g_min, s0)

@@ -1,0 +1,129 @@
+"""The C ABI of libkda without a GPU: the library loads, exports every symbol
+include/kda.h declares, and rejects bad arguments on the host with the
+documented status codes before anything is launched.
+
+No call here reaches a kernel launch: every argument set is invalid, so
+the library returns from host-side validation (fake device addresses are
+never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_14_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, UNSUP, ARG, WS, ALIGN, HIP = range(8)
+F32, BF16 = 0, 1
+P = ctypes.c_void_p(0x100000)      # a fake, 16-byte aligned "device" address
+MIS = ctypes.c_void_p(0x100002)    # misaligned
+S = None                           # null stream
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libkda.so is not built; run __graft_entry__.build() first")
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = header_functions()
+    assert declared == set(_lib.SIGNATURES), declared ^ set(_lib.SIGNATURES)
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(handle, name), name
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.kda_status_str(code).decode()
+        assert s.startswith("KDA_")
+    assert lib.kda_status_str(99).decode().startswith("KDA_ERR_?")
+    assert b"gfx950" in lib.kda_version()
+
+
+def test_workspace_sizes(lib):
+    # bf16, d = 128: W, U, M, Q*e^G, (K*e^{G_C-G})^T in bf16 plus e^{G_C} fp32 per chunk
+    per = (64 * 128 * 4 + 64 * 64) * 2 + 128 * 4
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == 32 * 512 * per
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 65, 1, 128, 128, 64, BF16) == 2 * per
+    per32 = (64 * 64 * 4 + 64 * 64) * 4 + 64 * 4
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32) == 4 * per32
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, F32) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, F32) == 0
+    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2
+    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 0, BF16, 0) == 0
+
+
+def chunk(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, s0=None, o=P, sf=P, B=1, T=128, H=2,
+          dk=128, dv=128, chunk=64, dt=BF16, ws=None, ws_bytes=0):
+    return lib.kda_chunk_fwd(q, k, v, z, beta, g_min, s0, o, sf, B, T, H, dk, dv, chunk, dt, ws,
+                             ws_bytes, S)
+
+
+def test_chunk_fwd_rejects_bad_arguments(lib):
+    need = lib.kda_chunk_fwd_workspace_bytes(1, 128, 2, 128, 128, 64, BF16)
+    assert chunk(lib, q=None, ws=P, ws_bytes=need) == NULL
+    assert chunk(lib, o=None, ws=P, ws_bytes=need) == NULL
+    assert chunk(lib, dk=96) == UNSUP
+    assert chunk(lib, dv=256) == UNSUP
+    assert chunk(lib, chunk=32) == UNSUP
+    assert chunk(lib, dt=5) == UNSUP
+    assert chunk(lib, B=-1) == SHAPE
+    assert chunk(lib, T=-3) == SHAPE
+    assert chunk(lib, H=70000) == SHAPE
+    assert chunk(lib, g_min=0.0) == ARG
+    assert chunk(lib, g_min=1.0) == ARG
+    assert chunk(lib, g_min=float("nan")) == ARG
+    assert chunk(lib, g_min=float("-inf")) == ARG
+    assert chunk(lib, ws=None, ws_bytes=0) == WS
+    assert chunk(lib, ws=P, ws_bytes=need - 1) == WS
+    assert chunk(lib, k=MIS, ws=P, ws_bytes=need) == ALIGN
+    assert chunk(lib, s0=MIS, ws=P, ws_bytes=need) == ALIGN
+    assert chunk(lib, ws=MIS, ws_bytes=need) == ALIGN
+    # empty batch or heads: nothing to do, success without touching memory
+    assert chunk(lib, B=0) == OK
+    assert chunk(lib, H=0) == OK
+
+
+def step(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, state=P, o=P, B=4, H=2, dk=128, dv=128, dt=BF16):
+    return lib.kda_recurrent_step(q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt, S)
+
+
+def test_recurrent_step_rejects_bad_arguments(lib):
+    assert step(lib, state=None) == NULL
+    assert step(lib, beta=None) == NULL
+    assert step(lib, dk=32) == UNSUP
+    assert step(lib, dt=2) == UNSUP
+    assert step(lib, B=-2) == SHAPE
+    assert step(lib, g_min=0.5) == ARG
+    assert step(lib, state=MIS) == ALIGN
+    assert step(lib, B=0) == OK
+
+
+def gate(lib, o=P, g=P, eps=1e-6, w=None, y=P, B=2, T=8, H=4, dv=128, dm=0, dt=BF16, ws=None, wsb=0):
+    return lib.kda_out_gate(o, g, eps, w, y, B, T, H, dv, dm, dt, ws, wsb, S)
+
+
+def test_out_gate_rejects_bad_arguments(lib):
+    assert gate(lib, o=None) == NULL
+    assert gate(lib, dv=96) == UNSUP
+    assert gate(lib, eps=-1.0) == ARG
+    assert gate(lib, eps=float("nan")) == ARG
+    assert gate(lib, y=MIS) == ALIGN
+    assert gate(lib, w=P, dm=100, ws=P, wsb=1 << 30) == UNSUP       # d_model % 16
+    assert gate(lib, w=P, dm=64, dt=F32, ws=P, wsb=1 << 30) == UNSUP  # projection needs bf16
+    assert gate(lib, w=P, dm=64, ws=None) == WS
+    assert gate(lib, w=P, dm=64, ws=P, wsb=10) == WS
+    assert gate(lib, T=0) == OK
