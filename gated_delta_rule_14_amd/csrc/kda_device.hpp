@@ -97,6 +97,49 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ int acc_row(int e) { return 4 * (lane_id() >> 4) + e; }
 __device__ __forceinline__ int acc_col() { return lane_id() & 15; }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// v_rcp_f32 (1 ulp) instead of a correctly rounded IEEE division
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Four / eight consecutive elements, converted from / to fp32.  p must be
+// aligned to the access size (8 or 16 bytes for bf16, 16 or 32 for fp32).
+template <class CT> __device__ __forceinline__ void store4(CT* p, f32x4 v);
+template <> __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
+    *reinterpret_cast<f32x4*>(p) = v;
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, f32x4 v) {
+    bf16x4 b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x4*>(p) = b;
+}
+template <class CT> __device__ __forceinline__ f32x4 load4(const CT* p);
+template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
+    return *reinterpret_cast<const f32x4*>(p);
+}
+template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+// Raw (unconverted) four-element vectors, for register prefetch: converting
+// at load time would make the load's consumer wait for it.
+template <class CT> struct Raw4;
+template <> struct Raw4<float> { typedef f32x4 type; };
+template <> struct Raw4<bf16> { typedef bf16x4 type; };
+template <class CT> __device__ __forceinline__ typename Raw4<CT>::type load_raw4(const CT* p) {
+    return *reinterpret_cast<const typename Raw4<CT>::type*>(p);
+}
+__device__ __forceinline__ f32x4 widen4(f32x4 v) { return v; }
+__device__ __forceinline__ f32x4 widen4(bf16x4 b) { return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]}; }
+
+template <class CT> __device__ __forceinline__ void store8(CT* p, const float* v) {
+    store4<CT>(p, f32x4{v[0], v[1], v[2], v[3]});
+    store4<CT>(p + 4, f32x4{v[4], v[5], v[6], v[7]});
+}
+template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float* v) {
+    bf16x8 b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = b;
+}
 
 }  // namespace kda
