@@ -70,14 +70,20 @@ struct Ws {
 
 // ---------------------------------------------------------------------------
 // Intra-chunk work of one (b, h, chunk): 256 threads.
+//
+// Decay exponents are kept in log2 units (G2 = G * log2 e) so that every
+// factor is one v_exp_f32.  In phases 1-2 a thread owns two adjacent key
+// channels over RP consecutive rows, so global and LDS accesses are packed
+// pairs and the row scan runs in registers.
 // ---------------------------------------------------------------------------
 template <class E, int DK, int DV>
 struct Intra {
     typedef typename Compute<E>::type CT;
-    static constexpr int NPART = 256 / DK;   // threads per key channel
-    static constexpr int RP = C / NPART;     // rows per thread (16 or 32)
-    static constexpr int NPV = 256 / DV;
-    static constexpr int RPV = C / NPV;
+    static constexpr int CP = DK / 2;        // column pairs
+    static constexpr int NPART = 256 / CP;   // row parts (4 or 8)
+    static constexpr int RP = C / NPART;     // rows per thread (16 or 8)
+    static constexpr int CPV = DV / 2;
+    static constexpr int RPV = C / (256 / CPV);
     static constexpr int LDK = DK + 8;       // K-contiguous tile stride (CT)
     static constexpr int LC = C + 8;         // token-contiguous tile stride (CT)
     static constexpr int LA = C + 4;         // fp32 64x64 tile strides
@@ -88,11 +94,11 @@ struct Intra {
     static constexpr size_t R1 = align16(cmax(3 * TILE, OFF_RV + (size_t)DV * LC * sizeof(CT)));
     static constexpr size_t OFF_RT = R1;     // R_K^T [DK][LC]
     static constexpr size_t OFF_DSC = OFF_RT + align16((size_t)DK * LC * sizeof(CT));
-    static constexpr size_t OFF_GM = OFF_DSC + 6 * DK * 4;
-    static constexpr size_t OFF_CAR = OFF_GM + 5 * DK * 4;
-    static constexpr size_t OFF_BET = OFF_CAR + NPART * DK * 4;
+    static constexpr size_t OFF_CAR = OFF_DSC;    // scan carries, dead before dsc is written
+    static constexpr size_t OFF_GM = OFF_DSC + (NPART > 6 ? NPART : 6) * DK * 4;
+    static constexpr size_t OFF_BET = OFF_GM + 5 * DK * 4;
     static constexpr size_t LDS = OFF_BET + C * 4;
-    static_assert(RP % 16 == 0 && RPV % 8 == 0, "intra tiling");
+    static_assert(RP % 8 == 0 && RPV % 8 == 0 && 16 % RP == 0, "intra tiling");
 };
 
 // Block pairs (R, I), I <= R, of A and M handled by each of the 4 waves.
@@ -100,6 +106,9 @@ __constant__ int kPairs[4][3][2] = {{{0, 0}, {1, 0}, {3, 3}},
                                     {{1, 1}, {2, 0}, {3, 2}},
                                     {{2, 1}, {2, 2}, {3, 1}},
                                     {{3, 0}, {-1, -1}, {-1, -1}}};
+
+template <class E> __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+template <> __device__ __forceinline__ float dexp2<float>(float x) { return exp2f(x); }
 
 template <class E, int DK, int DV>
 __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __restrict__ k,
@@ -111,6 +120,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     typedef Mfma<CT> MF;
     typedef Ws<CT, DK, DV> WL;
     constexpr int LDK = L::LDK, LC = L::LC, LA = L::LA, LT = L::LT, RP = L::RP, RPV = L::RPV;
+    constexpr float LOG2E = 1.4426950408889634f;
 
     CT* KL = reinterpret_cast<CT*>(smem);             // [C][LDK] k * e^{G_r - G_m(R)}
     CT* QL = KL + C * LDK;                              // [C][LDK] q * e^{G_r - G_m(R)}
@@ -121,7 +131,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     CT* RT = reinterpret_cast<CT*>(smem + L::OFF_RT);   // [DK][LC] R_K^T = (beta k e^G)^T
     CT* RV = reinterpret_cast<CT*>(smem + L::OFF_RV);   // [DV][LC] R_V^T = (beta v)^T (after phase 3)
     float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{G_m(R) - G_m(I)}
-    float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);     // [5][DK] G_m(R), G_C
+    float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);     // [5][DK] G2_m(R), G2_C
     float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);   // [NPART][DK]
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);   // [C]
 
@@ -133,92 +143,119 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     float* gEGC = reinterpret_cast<float*>(reinterpret_cast<CT*>(blk) + WL::END);
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int last = valid - 1;
+    // chunk-base pointers (uniform) and 32-bit per-row offsets
+    const E* zb = z + row0 * DK;
+    const E* kb = k + row0 * DK;
+    const E* qb = q + row0 * DK;
+    const E* vb = v + row0 * DV;
+    const int rsk = H * DK, rsv = H * DV;
 
-    // ---- phase 1: gate and chunk-local scan, one key channel per thread group
+    // ---- phase 1: loads, gate, chunk-local scan of the log2 decay
     if (tid < C) bet[tid] = tid < valid ? to_f32(beta[row0 + (size_t)tid * H]) : 0.f;
-    const int c = tid % DK, part = tid / DK, r0 = part * RP;
-    const int cv = tid % DV, rv0 = (tid / DV) * RPV;
-    // All global loads first, at clamped (always valid) rows and without any
-    // branch, so they are in flight together; rows past the end of the
-    // sequence are then zeroed arithmetically.
-    E zr[RP], kr[RP], qr[RP], vr[RPV];
+    const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+    const int cv0 = 2 * (tid % L::CPV), rv0 = (tid / L::CPV) * RPV;
+    typename Pair<E>::type zr[RP], kr[RP], qr[RP], vr[RPV];
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
-        const size_t off = (row0 + (size_t)min(r0 + i, valid - 1) * H) * DK + c;
-        zr[i] = z[off];
-        kr[i] = k[off];
-        qr[i] = q[off];
+        const int off = min(r0 + i, last) * rsk + c0;      // clamped: always in bounds
+        zr[i] = load2<E>(zb + off);
+        kr[i] = load2<E>(kb + off);
+        qr[i] = load2<E>(qb + off);
     }
 #pragma unroll
-    for (int i = 0; i < RPV; ++i) vr[i] = v[(row0 + (size_t)min(rv0 + i, valid - 1) * H) * DV + cv];
-    float G[RP], kv[RP], qv[RP], vv[RPV];
+    for (int i = 0; i < RPV; ++i) vr[i] = load2<E>(vb + min(rv0 + i, last) * rsv + cv0);
+
+    const float kg2 = g_min * LOG2E;
+    float G[RP][2], kv[RP][2], qv[RP][2];
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
-        const float msk = r0 + i < valid ? 1.f : 0.f;
-        G[i] = msk * (g_min * dsigmoid<E>(to_f32(zr[i])));
-        kv[i] = msk * to_f32(kr[i]);
-        qv[i] = msk * to_f32(qr[i]);
+        const bool ok = r0 + i < valid;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float g2 = kg2 * __builtin_amdgcn_rcpf(1.0f + dexp2<E>(-LOG2E * to_f32(zr[i][j])));
+            G[i][j] = ok ? g2 : 0.f;
+            kv[i][j] = ok ? to_f32(kr[i][j]) : 0.f;
+            qv[i][j] = ok ? to_f32(qr[i][j]) : 0.f;
+        }
+        s0 += G[i][0];
+        s1 += G[i][1];
+        G[i][0] = s0;
+        G[i][1] = s1;
     }
-#pragma unroll
-    for (int i = 0; i < RPV; ++i) vv[i] = to_f32(vr[i]);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < RP; ++i) { s += G[i]; G[i] = s; }
-    car[part * DK + c] = s;
+    car[part * DK + c0] = s0;
+    car[part * DK + c0 + 1] = s1;
     __syncthreads();
-    float carry = 0.f, gC = 0.f;
+    float cr[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < L::NPART; ++p) {
-        const float t = car[p * DK + c];
-        if (p < part) carry += t;
-        gC += t;     // same summation order as carry + s of the last part
-    }
+    for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float t = car[p * DK + c0 + j];
+            if (p < part) cr[j] += t;
+            gC[j] += t;     // same summation order as the carry plus the last part's sum
+        }
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
-        G[i] += carry;
-        if ((i & 15) == 7) gm[((r0 + i) >> 4) * DK + c] = G[i];
+        G[i][0] += cr[0];
+        G[i][1] += cr[1];
+        if (((r0 + i) & 15) == 7) {
+            gm[((r0 + i) >> 4) * DK + c0] = G[i][0];
+            gm[((r0 + i) >> 4) * DK + c0 + 1] = G[i][1];
+        }
     }
     if (part == 0) {
-        gm[4 * DK + c] = gC;
-        gEGC[c] = dexp<E>(gC);
+        gm[4 * DK + c0] = gC[0];
+        gm[4 * DK + c0 + 1] = gC[1];
+        gEGC[c0] = dexp2<E>(gC[0]);
+        gEGC[c0 + 1] = dexp2<E>(gC[1]);
     }
     __syncthreads();
 
-    // ---- phase 2: decay-scaled operands
+    // ---- phase 2: decay-scaled operands (the thread's rows lie in one block R)
     {
-        constexpr int NB = RP / 16;
-        float gmR[NB], eGm[NB], eCGm[NB];
+        const int R = r0 >> 4;
+        float gmR[2], eGm[2], eCGm[2];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            gmR[j] = gm[((r0 >> 4) + j) * DK + c];
-            eGm[j] = dexp<E>(gmR[j]);
-            eCGm[j] = dexp<E>(gC - gmR[j]);
+        for (int j = 0; j < 2; ++j) {
+            gmR[j] = gm[R * DK + c0 + j];
+            eGm[j] = dexp2<E>(gmR[j]);
+            eCGm[j] = dexp2<E>(gC[j] - gmR[j]);
         }
-        float rk[RP], kg[RP];
+        float rk[2][RP], kg[2][RP];
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
-            const int r = r0 + i, j = i >> 4;
-            const float el = G[i] - gmR[j];
-            const float left = dexp<E>(el), right = dexp<E>(-el);
-            const float kL = kv[i] * left, qL = qv[i] * left, kR = kv[i] * right;
-            KL[r * LDK + c] = from_f32<CT>(kL);
-            QL[r * LDK + c] = from_f32<CT>(qL);
-            KR[r * LDK + c] = from_f32<CT>(kR);
-            gQG[r * DK + c] = from_f32<CT>(qL * eGm[j]);
-            rk[i] = bet[r] * kL * eGm[j];
-            kg[i] = kR * eCGm[j];
+            const int r = r0 + i;
+            float kl[2], ql[2], kR[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float el = G[i][j] - gmR[j];
+                const float left = dexp2<E>(el), right = dexp2<E>(-el);
+                kl[j] = kv[i][j] * left;
+                ql[j] = qv[i][j] * left;
+                kR[j] = kv[i][j] * right;
+                rk[j][i] = bet[r] * kl[j] * eGm[j];
+                kg[j][i] = kR[j] * eCGm[j];
+            }
+            store2<CT>(KL + r * LDK + c0, kl[0], kl[1]);
+            store2<CT>(QL + r * LDK + c0, ql[0], ql[1]);
+            store2<CT>(KR + r * LDK + c0, kR[0], kR[1]);
+            store2<CT>(gQG + r * DK + c0, ql[0] * eGm[0], ql[1] * eGm[1]);
         }
 #pragma unroll
-        for (int i = 0; i < RP; i += 8) {
-            store8<CT>(RT + c * LC + r0 + i, &rk[i]);
-            store8<CT>(gKGT + c * C + r0 + i, &kg[i]);
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < RP; i += 8) {
+                store8<CT>(RT + (c0 + j) * LC + r0 + i, &rk[j][i]);
+                store8<CT>(gKGT + (c0 + j) * C + r0 + i, &kg[j][i]);
+            }
     }
     for (int idx = tid; idx < 6 * DK; idx += 256) {
         const int p = idx / DK, cc = idx % DK;
         const int R = p < 1 ? 1 : (p < 3 ? 2 : 3);
         const int I = p - R * (R - 1) / 2;
-        dsc[idx] = dexp<E>(gm[R * DK + cc] - gm[I * DK + cc]);
+        dsc[idx] = dexp2<E>(gm[R * DK + cc] - gm[I * DK + cc]);
     }
     __syncthreads();
 
@@ -232,14 +269,15 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
         if (R < 0) break;
         f32x4 accA = zero4(), accM = zero4();
         const float* dv = dsc + (R * (R - 1) / 2 + I) * DK;
+#pragma unroll
         for (int kk = 0; kk < DK; kk += MF::KSTEP) {
             typename MF::frag ak = load_frag<CT>(KR, LDK, I * SUB, kk);
             if (I < R) {
                 float t[MF::KPL];
                 MF::to_floats(ak, t);
-                const int c0 = kk + (l >> 4) * MF::KPL;
+                const int cc = kk + (l >> 4) * MF::KPL;
 #pragma unroll
-                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] *= dv[c0 + jj];
+                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] *= dv[cc + jj];
                 ak = MF::from_floats(t);
             }
             accA = MF::mma(ak, load_frag<CT>(KL, LDK, R * SUB, kk), accA);
@@ -272,51 +310,72 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
         *reinterpret_cast<f32x4*>(As + (R * SUB + (l & 15)) * LA + I * SUB + 4 * (l >> 4)) =
             f32x4{av[j][0], av[j][1], av[j][2], av[j][3]};
     }
+    {
+        float t0[RPV], t1[RPV];
 #pragma unroll
-    for (int i = 0; i < RPV; ++i) vv[i] *= bet[rv0 + i];   // bet is 0 past the end
+        for (int i = 0; i < RPV; ++i) {
+            const float bb = bet[rv0 + i];      // 0 past the end of the sequence
+            t0[i] = bb * to_f32(vr[i][0]);
+            t1[i] = bb * to_f32(vr[i][1]);
+        }
 #pragma unroll
-    for (int i = 0; i < RPV; i += 8) store8<CT>(RV + cv * LC + rv0 + i, &vv[i]);
+        for (int i = 0; i < RPV; i += 8) {
+            store8<CT>(RV + cv0 * LC + rv0 + i, &t0[i]);
+            store8<CT>(RV + (cv0 + 1) * LC + rv0 + i, &t1[i]);
+        }
+    }
     __syncthreads();
 
     // ---- phase 4: T = (I + A)^{-1}, blocked forward substitution
-    // 4a: diagonal blocks; wave w inverts I + A_ww column by column (lane = column).
-    if (l < SUB) {
-        const int base = w * SUB;
+    // 4a: the four unit-lower diagonal blocks I + A_bb, inverted by wave 0,
+    //     lane = (block l/16, column l%16), by substitution down the column.
+    if (w == 0) {
+        const int base = (l >> 4) * SUB, col = l & 15;
         float x[SUB];
 #pragma unroll
         for (int r = 0; r < SUB; ++r) {
-            float acc = (r == l) ? 1.f : 0.f;
+            float acc = (r == col) ? 1.f : 0.f;
 #pragma unroll
             for (int i = 0; i < r; ++i) acc -= As[(base + r) * LA + base + i] * x[i];
             x[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < SUB; ++r) Ts[(base + r) * LT + base + l] = x[r];
+        for (int r = 0; r < SUB; ++r) Ts[(base + r) * LT + base + col] = x[r];
     } else {
-        // the other lanes clear the blocks right of the diagonal block
-        const int ncols = C - (w + 1) * SUB;
-        for (int i = l - SUB; i < SUB * ncols; i += 64 - SUB)
-            Ts[(w * SUB + i / ncols) * LT + (w + 1) * SUB + i % ncols] = 0.f;
+        // waves 1..3 clear the strictly upper blocks (row block R, column block > R)
+        for (int i = tid - 64; i < 6 * SUB * SUB; i += 192) {
+            const int p = i / (SUB * SUB), e = i % (SUB * SUB);
+            const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+            const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+            Ts[(R * SUB + e / SUB) * LT + I * SUB + e % SUB] = 0.f;
+        }
     }
     __syncthreads();
-    // 4b: off-diagonal blocks, one block row at a time:
-    //     T_RI = -T_RR * sum_{J=I}^{R-1} A_RJ T_JI
+    // 4b: off-diagonal blocks on fp32 MFMA, one block row R at a time; wave I
+    //     computes T_RI = -T_RR * sum_{J=I}^{R-1} A_RJ T_JI.
     for (int R = 1; R < 4; ++R) {
-        const int rl = tid >> 4, il = tid & 15;
-        for (int I = 0; I < R; ++I) {
-            float acc = 0.f;
+        if (w < R) {
+            const int I = w;
+            f32x4 x = zero4();
             for (int J = I; J < R; ++J)
 #pragma unroll
-                for (int t = 0; t < SUB; ++t)
-                    acc += As[(R * SUB + rl) * LA + J * SUB + t] * Ts[(J * SUB + t) * LT + I * SUB + il];
-            Xs[(I * SUB + rl) * SUB + il] = acc;
-        }
-        __syncthreads();
-        for (int I = 0; I < R; ++I) {
-            float acc = 0.f;
+                for (int kk = 0; kk < SUB; kk += 4) {
+                    const float a = As[(R * SUB + (l & 15)) * LA + J * SUB + kk + (l >> 4)];
+                    const float b = Ts[(J * SUB + kk + (l >> 4)) * LT + I * SUB + (l & 15)];
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+                }
+            float* xs = Xs + I * SUB * SUB;
 #pragma unroll
-            for (int t = 0; t < SUB; ++t) acc -= Ts[(R * SUB + rl) * LT + R * SUB + t] * Xs[(I * SUB + t) * SUB + il];
-            Ts[(R * SUB + rl) * LT + I * SUB + il] = acc;
+            for (int e = 0; e < 4; ++e) xs[(4 * (l >> 4) + e) * SUB + (l & 15)] = x[e];
+            f32x4 y = zero4();
+#pragma unroll
+            for (int kk = 0; kk < SUB; kk += 4) {
+                const float a = Ts[(R * SUB + (l & 15)) * LT + R * SUB + kk + (l >> 4)];
+                const float b = xs[(kk + (l >> 4)) * SUB + (l & 15)];
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, y, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ts[(R * SUB + 4 * (l >> 4) + e) * LT + I * SUB + (l & 15)] = -y[e];
         }
         __syncthreads();
     }
@@ -412,15 +471,80 @@ struct Inter {
     }
 };
 
+// One chunk of the recurrence for one wave: consumes the operands in `cur`
+// (chunk n) and starts the loads of chunk min(n + 2, NC - 1) into `fill`.
+// The prefetch is unconditional: under a branch the wait-count insertion
+// would assume the no-load path and stall on it.
+template <class E, int DK, int DV, int TV>
+__device__ __forceinline__ void chain_step(typename Inter<E, DK, DV, TV>::Regs& cur,
+                                           typename Inter<E, DK, DV, TV>::Regs& fill, int n, int NC, int T,
+                                           int H, int b, int h, int col0, const unsigned char* chain,
+                                           E* __restrict__ o, f32x4 (&accS)[DK / 64][TV / 16],
+                                           typename Compute<E>::type* Sb0, typename Compute<E>::type* Sb1,
+                                           typename Compute<E>::type* Vn) {
+    typedef Inter<E, DK, DV, TV> L;
+    typedef typename L::CT CT;
+    typedef typename L::MF MF;
+    typedef Ws<CT, DK, DV> WL;
+    constexpr int LDK = L::LDK, LC = L::LC, RB = L::RB, NT = L::NT, KS = L::KS;
+    const int l = lane_id(), w = wave_id();
+    CT* sb = (n & 1) ? Sb1 : Sb0;
+    CT* sbn = (n & 1) ? Sb0 : Sb1;
+    L::load(fill, chain + (size_t)min(n + 2, NC - 1) * WL::BYTES, w, l, col0);
+
+    // V_new = U - W S (rows 16w.. x TV) and O^T = S^T (Q e^G)^T (TV x rows 16w..)
+    f32x4 accP[NT], accO[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) { accP[ct] = zero4(); accO[ct] = zero4(); }
+#pragma unroll
+    for (int kk = 0; kk < L::NKD; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const typename MF::frag fs = load_frag<CT>(sb, LDK, ct * 16, kk * KS);
+            accP[ct] = MF::mma(cur.w[kk], fs, accP[ct]);
+            accO[ct] = MF::mma(fs, cur.qg[kk], accO[ct]);
+        }
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+        store4<CT>(Vn + (ct * 16 + (l & 15)) * LC + w * 16 + 4 * (l >> 4), widen4(cur.u[ct]) - accP[ct]);
+    __syncthreads();
+
+    // O^T += V_new^T M^T ;  S <- Diag(e^{G_C}) S + (K e^{G_C-G})^T V_new
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) accS[rb][ct] *= cur.eg[rb];
+#pragma unroll
+    for (int kk = 0; kk < L::NKC; ++kk)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const typename MF::frag fv = load_frag<CT>(Vn, LC, ct * 16, kk * KS);
+            accO[ct] = MF::mma(fv, cur.m[kk], accO[ct]);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) accS[rb][ct] = MF::mma(cur.kg[rb][kk], fv, accS[rb][ct]);
+        }
+    const int t = n * C + w * 16 + (l & 15);
+    if (t < T) {
+        E* orow = o + (((size_t)b * T + t) * H + h) * DV + col0;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) store4<E>(orow + ct * 16 + 4 * (l >> 4), accO[ct]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+            store4<CT>(sbn + (ct * 16 + (l & 15)) * LDK + w * (DK / 4) + rb * 16 + 4 * (l >> 4), accS[rb][ct]);
+    __syncthreads();
+}
+
 template <class E, int DK, int DV, int TV>
 __global__ __launch_bounds__(256) void chunk_inter_kernel(
     E* __restrict__ o, const float* __restrict__ s0, float* __restrict__ s_final, int T, int H,
     int NC, const unsigned char* __restrict__ ws) {
     typedef Inter<E, DK, DV, TV> L;
     typedef typename L::CT CT;
-    typedef typename L::MF MF;
     typedef Ws<CT, DK, DV> WL;
-    constexpr int LDK = L::LDK, LC = L::LC, RB = L::RB, NT = L::NT, KS = L::KS;
+    constexpr int LDK = L::LDK, RB = L::RB, NT = L::NT;
 
     extern __shared__ __align__(16) unsigned char smem[];
     CT* Sb0 = reinterpret_cast<CT*>(smem);                          // [TV][LDK] S^T, ping
@@ -453,62 +577,19 @@ __global__ __launch_bounds__(256) void chunk_inter_kernel(
             store4<CT>(Sb0 + col * LDK + row, accS[rb][ct]);
         }
 
-    typename L::Regs cur, nxt;
-    L::load(cur, chain, w, l, col0);
+    // three operand sets in flight: chunk n is consumed while n+1 and n+2 load
+    typename L::Regs r0, r1, r2;
+    L::load(r0, chain, w, l, col0);
+    L::load(r1, chain + (size_t)min(1, NC - 1) * WL::BYTES, w, l, col0);
     __syncthreads();
-
-    for (int n = 0; n < NC; ++n) {
-        CT* sb = (n & 1) ? Sb1 : Sb0;
-        CT* sbn = (n & 1) ? Sb0 : Sb1;
-        // Unconditional (clamped) prefetch of the next chunk: under a branch the
-        // wait-count insertion would assume the no-load path and stall on it.
-        L::load(nxt, chain + (size_t)min(n + 1, NC - 1) * WL::BYTES, w, l, col0);
-
-        // V_new = U - W S (rows 16w.. x TV) and O^T = S^T (Q e^G)^T (TV x rows 16w..)
-        f32x4 accP[NT], accO[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct) { accP[ct] = zero4(); accO[ct] = zero4(); }
-#pragma unroll
-        for (int kk = 0; kk < L::NKD; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const typename MF::frag fs = load_frag<CT>(sb, LDK, ct * 16, kk * KS);
-                accP[ct] = MF::mma(cur.w[kk], fs, accP[ct]);
-                accO[ct] = MF::mma(fs, cur.qg[kk], accO[ct]);
-            }
-#pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-            store4<CT>(Vn + (ct * 16 + (l & 15)) * LC + w * 16 + 4 * (l >> 4), widen4(cur.u[ct]) - accP[ct]);
-        __syncthreads();
-
-        // O^T += V_new^T M^T ;  S <- Diag(e^{G_C}) S + (K e^{G_C-G})^T V_new
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) accS[rb][ct] *= cur.eg[rb];
-#pragma unroll
-        for (int kk = 0; kk < L::NKC; ++kk)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const typename MF::frag fv = load_frag<CT>(Vn, LC, ct * 16, kk * KS);
-                accO[ct] = MF::mma(fv, cur.m[kk], accO[ct]);
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb) accS[rb][ct] = MF::mma(cur.kg[rb][kk], fv, accS[rb][ct]);
-            }
-        const int t = n * C + w * 16 + (l & 15);
-        if (t < T) {
-            E* orow = o + (((size_t)b * T + t) * H + h) * DV + col0;
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct) store4<E>(orow + ct * 16 + 4 * (l >> 4), accO[ct]);
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int ct = 0; ct < NT; ++ct)
-                store4<CT>(sbn + (ct * 16 + (l & 15)) * LDK + w * (DK / 4) + rb * 16 + 4 * (l >> 4), accS[rb][ct]);
-        __syncthreads();
-        cur = nxt;
+    int n = 0;
+    for (; n + 3 <= NC; n += 3) {
+        chain_step<E, DK, DV, TV>(r0, r2, n, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+        chain_step<E, DK, DV, TV>(r1, r0, n + 1, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+        chain_step<E, DK, DV, TV>(r2, r1, n + 2, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
     }
+    if (n < NC) chain_step<E, DK, DV, TV>(r0, r2, n, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+    if (n + 1 < NC) chain_step<E, DK, DV, TV>(r1, r0, n + 1, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
 
     if (s_final) {
 #pragma unroll
@@ -521,6 +602,7 @@ __global__ __launch_bounds__(256) void chunk_inter_kernel(
                 for (int e = 0; e < 4; ++e) s_final[(bh * DK + row + e) * DV + col0 + col] = accS[rb][ct][e];
             }
     }
+    (void)LDK;
 }
 
 // State pass-through for T == 0: s_final = s0 (or zeros).

@@ -25,6 +25,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;   // 16-byte raw vector
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -35,7 +36,9 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Wave index, made provably wave-uniform so that it lives in an SGPR: table
+// lookups become scalar loads and branches on it become scalar branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---------------------------------------------------------------- MFMA
 template <class CT> struct Mfma;
@@ -120,6 +123,20 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
     const bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
     return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
+// Two consecutive elements of type E, loaded / stored as one access.
+template <class E> struct Pair;
+template <> struct Pair<float> { typedef f32x2 type; };
+template <> struct Pair<bf16> { typedef bf16x2 type; };
+template <class E> __device__ __forceinline__ typename Pair<E>::type load2(const E* p) {
+    return *reinterpret_cast<const typename Pair<E>::type*>(p);
+}
+template <class E> __device__ __forceinline__ void store2(E* p, float a, float b) {
+    typename Pair<E>::type v;
+    v[0] = from_f32<E>(a);
+    v[1] = from_f32<E>(b);
+    *reinterpret_cast<typename Pair<E>::type*>(p) = v;
+}
+
 // Raw (unconverted) four-element vectors, for register prefetch: converting
 // at load time would make the load's consumer wait for it.
 template <class CT> struct Raw4;
