@@ -423,12 +423,27 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Inter-chunk recurrence of one (b, h, value-column tile): 256 threads.
+// Chunk-to-chunk recurrence over a range of chunks of one chain (b, h) and
+// one tile of TV state columns: 256 threads.
+//
+//   CM_EXPAND    X starts from the given state; V_new = U - W X; outputs
+//                O = (Q e^G) X + M V_new are written; X is the state S.
+//   CM_COMPOSE_R X starts from 0 with the same inputs and no outputs: the
+//                range's input term R, S_end = P S_start + R.
+//   CM_COMPOSE_P X (d_k x d_k) starts from I with no inputs (V_new = -W X):
+//                the range's transition P = prod_n (Diag(e^{G_C}) - K~^T W).
+// The fp32 X tile lives in MFMA accumulators; each wave loads its operands
+// for the next chunk straight from the workspace into registers while the
+// current chunk is computed; only X^T and V_new^T go through LDS.
 // ---------------------------------------------------------------------------
-template <class E, int DK, int DV, int TV>
-struct Inter {
+enum { CM_EXPAND = 0, CM_COMPOSE_R = 1, CM_COMPOSE_P = 2 };
+
+template <class E, int DK, int DV, int NCOL, int TV, int MODE>
+struct Chain {
     typedef typename Compute<E>::type CT;
     typedef Mfma<CT> MF;
+    static constexpr bool OUT = MODE == CM_EXPAND;
+    static constexpr bool HASU = MODE != CM_COMPOSE_P;
     static constexpr int KS = MF::KSTEP;
     static constexpr int NKD = DK / KS;     // k-steps over d_k
     static constexpr int NKC = C / KS;      // k-steps over the chunk's tokens
@@ -437,12 +452,13 @@ struct Inter {
     static constexpr int LDK = DK + 8, LC = C + 8;
     static constexpr size_t SB_BYTES = (size_t)TV * LDK * sizeof(CT);
     static constexpr size_t LDS = 2 * SB_BYTES + (size_t)TV * LC * sizeof(CT);
+    static_assert(NCOL % TV == 0 && TV % 16 == 0, "chain tiling");
 
     // One chunk's operands as held by one wave (rows 16w.. of W, Q*e^G, M;
     // state rows w*DK/4.. of (K*e^{G_C-G})^T; V_new init; e^{G_C}).
     struct Regs {
-        typename MF::frag w[NKD], qg[NKD], m[NKC], kg[RB][NKC];
-        typename Raw4<CT>::type u[NT];
+        typename MF::frag w[NKD], qg[OUT ? NKD : 1], m[OUT ? NKC : 1], kg[RB][NKC];
+        typename Raw4<CT>::type u[HASU ? NT : 1];
         f32x4 eg[RB];
     };
 
@@ -452,18 +468,20 @@ struct Inter {
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk) {
             r.w[kk] = load_frag<CT>(base + WL::W, DK, w * 16, kk * KS);
-            r.qg[kk] = load_frag<CT>(base + WL::QG, DK, w * 16, kk * KS);
+            if constexpr (OUT) r.qg[kk] = load_frag<CT>(base + WL::QG, DK, w * 16, kk * KS);
         }
 #pragma unroll
         for (int kk = 0; kk < NKC; ++kk) {
-            r.m[kk] = load_frag<CT>(base + WL::M, C, w * 16, kk * KS);
+            if constexpr (OUT) r.m[kk] = load_frag<CT>(base + WL::M, C, w * 16, kk * KS);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 r.kg[rb][kk] = load_frag<CT>(base + WL::KGT, C, w * (DK / 4) + rb * 16, kk * KS);
         }
+        if constexpr (HASU) {
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct)
-            r.u[ct] = load_raw4<CT>(base + WL::UT + (size_t)(col0 + ct * 16 + (l & 15)) * C + w * 16 + 4 * (l >> 4));
+            for (int ct = 0; ct < NT; ++ct)
+                r.u[ct] = load_raw4<CT>(base + WL::UT + (size_t)(col0 + ct * 16 + (l & 15)) * C + w * 16 + 4 * (l >> 4));
+        }
         const float* eg = reinterpret_cast<const float*>(base + WL::END);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -472,17 +490,17 @@ struct Inter {
 };
 
 // One chunk of the recurrence for one wave: consumes the operands in `cur`
-// (chunk n) and starts the loads of chunk min(n + 2, NC - 1) into `fill`.
-// The prefetch is unconditional: under a branch the wait-count insertion
-// would assume the no-load path and stall on it.
-template <class E, int DK, int DV, int TV>
-__device__ __forceinline__ void chain_step(typename Inter<E, DK, DV, TV>::Regs& cur,
-                                           typename Inter<E, DK, DV, TV>::Regs& fill, int n, int NC, int T,
-                                           int H, int b, int h, int col0, const unsigned char* chain,
-                                           E* __restrict__ o, f32x4 (&accS)[DK / 64][TV / 16],
-                                           typename Compute<E>::type* Sb0, typename Compute<E>::type* Sb1,
-                                           typename Compute<E>::type* Vn) {
-    typedef Inter<E, DK, DV, TV> L;
+// (chunk n) and starts the loads of chunk nfill into `fill`.  The prefetch
+// is unconditional (the caller clamps nfill): under a branch the wait-count
+// insertion would assume the no-load path and stall on it.
+template <class E, int DK, int DV, int NCOL, int TV, int MODE>
+__device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, MODE>::Regs& cur,
+                                           typename Chain<E, DK, DV, NCOL, TV, MODE>::Regs& fill, int n,
+                                           int nfill, int T, int H, int b, int h, int col0,
+                                           const unsigned char* chain, E* __restrict__ o,
+                                           f32x4 (&accS)[DK / 64][TV / 16], typename Compute<E>::type* Sb0,
+                                           typename Compute<E>::type* Sb1, typename Compute<E>::type* Vn) {
+    typedef Chain<E, DK, DV, NCOL, TV, MODE> L;
     typedef typename L::CT CT;
     typedef typename L::MF MF;
     typedef Ws<CT, DK, DV> WL;
@@ -490,26 +508,33 @@ __device__ __forceinline__ void chain_step(typename Inter<E, DK, DV, TV>::Regs& 
     const int l = lane_id(), w = wave_id();
     CT* sb = (n & 1) ? Sb1 : Sb0;
     CT* sbn = (n & 1) ? Sb0 : Sb1;
-    L::load(fill, chain + (size_t)min(n + 2, NC - 1) * WL::BYTES, w, l, col0);
+    L::load(fill, chain + (size_t)nfill * WL::BYTES, w, l, col0);
 
-    // V_new = U - W S (rows 16w.. x TV) and O^T = S^T (Q e^G)^T (TV x rows 16w..)
-    f32x4 accP[NT], accO[NT];
+    // V_new = U - W X (rows 16w.. x TV) and O^T = X^T (Q e^G)^T (TV x rows 16w..)
+    f32x4 accP[NT], accO[L::OUT ? NT : 1];
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct) { accP[ct] = zero4(); accO[ct] = zero4(); }
+    for (int ct = 0; ct < NT; ++ct) accP[ct] = zero4();
+    if constexpr (L::OUT) {
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) accO[ct] = zero4();
+    }
 #pragma unroll
     for (int kk = 0; kk < L::NKD; ++kk)
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const typename MF::frag fs = load_frag<CT>(sb, LDK, ct * 16, kk * KS);
             accP[ct] = MF::mma(cur.w[kk], fs, accP[ct]);
-            accO[ct] = MF::mma(fs, cur.qg[kk], accO[ct]);
+            if constexpr (L::OUT) accO[ct] = MF::mma(fs, cur.qg[kk], accO[ct]);
         }
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-        store4<CT>(Vn + (ct * 16 + (l & 15)) * LC + w * 16 + 4 * (l >> 4), widen4(cur.u[ct]) - accP[ct]);
+    for (int ct = 0; ct < NT; ++ct) {
+        f32x4 vn = -accP[ct];
+        if constexpr (L::HASU) vn += widen4(cur.u[ct]);
+        store4<CT>(Vn + (ct * 16 + (l & 15)) * LC + w * 16 + 4 * (l >> 4), vn);
+    }
     __syncthreads();
 
-    // O^T += V_new^T M^T ;  S <- Diag(e^{G_C}) S + (K e^{G_C-G})^T V_new
+    // O^T += V_new^T M^T ;  X <- Diag(e^{G_C}) X + (K e^{G_C-G})^T V_new
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -519,15 +544,17 @@ __device__ __forceinline__ void chain_step(typename Inter<E, DK, DV, TV>::Regs& 
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const typename MF::frag fv = load_frag<CT>(Vn, LC, ct * 16, kk * KS);
-            accO[ct] = MF::mma(fv, cur.m[kk], accO[ct]);
+            if constexpr (L::OUT) accO[ct] = MF::mma(fv, cur.m[kk], accO[ct]);
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) accS[rb][ct] = MF::mma(cur.kg[rb][kk], fv, accS[rb][ct]);
         }
-    const int t = n * C + w * 16 + (l & 15);
-    if (t < T) {
-        E* orow = o + (((size_t)b * T + t) * H + h) * DV + col0;
+    if constexpr (L::OUT) {
+        const int t = n * C + w * 16 + (l & 15);
+        if (t < T) {
+            E* orow = o + (((size_t)b * T + t) * H + h) * DV + col0;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) store4<E>(orow + ct * 16 + 4 * (l >> 4), accO[ct]);
+            for (int ct = 0; ct < NT; ++ct) store4<E>(orow + ct * 16 + 4 * (l >> 4), accO[ct]);
+        }
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -537,34 +564,130 @@ __device__ __forceinline__ void chain_step(typename Inter<E, DK, DV, TV>::Regs& 
     __syncthreads();
 }
 
-template <class E, int DK, int DV, int TV>
-__global__ __launch_bounds__(256) void chunk_inter_kernel(
-    E* __restrict__ o, const float* __restrict__ s0, float* __restrict__ s_final, int T, int H,
-    int NC, const unsigned char* __restrict__ ws) {
-    typedef Inter<E, DK, DV, TV> L;
-    typedef typename L::CT CT;
+// Grid: 1-D over (tile, segment, chain), tile index major.  Workgroups are
+// dealt round-robin to the 8 XCDs, so when B*H*nseg is a multiple of 8 all
+// column tiles of one (segment, chain) run on one XCD and share its
+// workspace through the same L2.  Segment s covers chunks [sL, min(sL+L, NC)).
+//   xin : CM_EXPAND entry states [nseg][B*H][DK][NCOL] (NULL = zeros)
+//   xout: CM_EXPAND final state [B*H][DK][NCOL] when nseg == 1 (NULL = skip);
+//         CM_COMPOSE_* the range results [nseg][B*H][DK][NCOL]
+template <class E, int DK, int DV, int NCOL, int TV, int MODE>
+__global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const float* __restrict__ xin,
+                                                    float* __restrict__ xout, int T, int H, int NC, int L,
+                                                    int nchain, const unsigned char* __restrict__ ws) {
+    typedef Chain<E, DK, DV, NCOL, TV, MODE> LC_;
+    typedef typename LC_::CT CT;
     typedef Ws<CT, DK, DV> WL;
-    constexpr int LDK = L::LDK, RB = L::RB, NT = L::NT;
+    constexpr int LDK = LC_::LDK, RB = LC_::RB, NT = LC_::NT;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    CT* Sb0 = reinterpret_cast<CT*>(smem);                          // [TV][LDK] S^T, ping
-    CT* Sb1 = reinterpret_cast<CT*>(smem + L::SB_BYTES);            // pong
-    CT* Vn = reinterpret_cast<CT*>(smem + 2 * L::SB_BYTES);         // [TV][LC] V_new^T
+    CT* Sb0 = reinterpret_cast<CT*>(smem);                            // [TV][LDK] X^T, ping
+    CT* Sb1 = reinterpret_cast<CT*>(smem + LC_::SB_BYTES);            // pong
+    CT* Vn = reinterpret_cast<CT*>(smem + 2 * LC_::SB_BYTES);         // [TV][LC] V_new^T
 
-    // 1-D grid of (tile, chain) with the tile index major: workgroups are
-    // dealt round-robin to the 8 XCDs, so when the number of chains B*H is a
-    // multiple of 8 all value tiles of a chain run on one XCD and read the
-    // chain's workspace through the same L2.
-    const int nchain = gridDim.x / (DV / TV);
-    const int tile = blockIdx.x / nchain;
-    const size_t bh = blockIdx.x % nchain;
+    const int per_tile = gridDim.x / (NCOL / TV);
+    const int tile = blockIdx.x / per_tile;
+    const int rem = blockIdx.x % per_tile;
+    const int seg = rem / nchain;
+    const size_t bh = rem % nchain;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int l = lane_id(), w = wave_id();
     const int col0 = tile * TV;
+    const int n0 = seg * L, n1 = min(NC, n0 + L);
     const unsigned char* chain = ws + bh * NC * WL::BYTES;
+    const size_t xrow = ((size_t)seg * nchain + bh) * DK;    // row 0 of this (segment, chain) block
 
-    // state rows of this lane: w*DK/4 + rb*16 + 4*(l/16) + e ; column ct*16 + l%16
+    // X rows of this lane: w*DK/4 + rb*16 + 4*(l/16) + e ; column col0 + ct*16 + l%16
     f32x4 accS[RB][NT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+            const int col = col0 + ct * 16 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float x = 0.f;
+                if constexpr (MODE == CM_EXPAND) x = xin ? xin[(xrow + row + e) * NCOL + col] : 0.f;
+                if constexpr (MODE == CM_COMPOSE_P) x = (row + e == col) ? 1.f : 0.f;
+                accS[rb][ct][e] = x;
+            }
+            store4<CT>(Sb0 + (ct * 16 + (l & 15)) * LDK + row, accS[rb][ct]);
+        }
+
+    // two operand sets: chunk n is consumed while chunk n+1 loads
+    typename LC_::Regs r0, r1;
+    LC_::load(r0, chain + (size_t)n0 * WL::BYTES, w, l, col0);
+    __syncthreads();
+    int n = n0;
+    for (; n + 2 <= n1; n += 2) {
+        chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n + 1, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+        chain_step<E, DK, DV, NCOL, TV, MODE>(r1, r0, n + 1, min(n + 2, n1 - 1), T, H, b, h, col0, chain, o, accS,
+                                              Sb0, Sb1, Vn);
+    }
+    if (n < n1) chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+
+    if (xout) {
+        const size_t orow = MODE == CM_EXPAND ? bh * DK : xrow;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+                const int col = col0 + ct * 16 + (l & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xout[(orow + row + e) * NCOL + col] = accS[rb][ct][e];
+            }
+    }
+    (void)LDK;
+}
+
+// ---------------------------------------------------------------------------
+// Scan over segments for one chain and one tile of TV value columns:
+//   Sent[j] = S_j,  S_{j+1} = P_j S_j + R_j,  s_final = S_nseg,
+// in fp32 on v_mfma_f32_16x16x4_f32.  The contraction index is visited in
+// blocks of 16 as k = 16 kb + 4 g + t (g = lane group, t = sub-step), so each
+// lane reads four consecutive entries of a P row (one 16-byte load) and of
+// an S^T row in LDS.
+// ---------------------------------------------------------------------------
+template <int DK, int TV>
+struct ScanRegs {
+    struct T {
+        f32x4 pa[DK / 64][DK / 16];
+        float rr[DK / 64][TV / 16][4];
+    };
+};
+
+template <int DK, int DV, int TV>
+__device__ __forceinline__ void scan_fetch(typename ScanRegs<DK, TV>::T& r, const float* __restrict__ P,
+                                           const float* __restrict__ R, int j, int nchain, size_t bh, int col0,
+                                           int w, int l) {
+    constexpr int RB = DK / 64, NT = TV / 16;
+    const size_t blk = ((size_t)j * nchain + bh) * DK;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+            r.pa[rb][kb] = *reinterpret_cast<const f32x4*>(P + (blk + w * (DK / 4) + rb * 16 + (l & 15)) * DK +
+                                                            kb * 16 + 4 * (l >> 4));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                r.rr[rb][ct][e] = R[(blk + w * (DK / 4) + rb * 16 + 4 * (l >> 4) + e) * DV + col0 + ct * 16 + (l & 15)];
+    }
+}
+
+// One segment of the scan: Sent[j] = S; S <- P_j S + R_j (operands in `cur`),
+// while segment jn's operands load into `nxt`.
+template <int DK, int DV, int TV>
+__device__ __forceinline__ void scan_step(f32x4 (&acc)[DK / 64][TV / 16], typename ScanRegs<DK, TV>::T& cur,
+                                          typename ScanRegs<DK, TV>::T& nxt, const float* __restrict__ P,
+                                          const float* __restrict__ R, float* __restrict__ Sent, float* St, int j,
+                                          int jn, int nchain, size_t bh, int col0, int w, int l) {
+    constexpr int RB = DK / 64, NT = TV / 16, LS = DK + 4;
+    scan_fetch<DK, DV, TV>(nxt, P, R, jn, nchain, bh, col0, w, l);
+    const size_t blk = ((size_t)j * nchain + bh) * DK;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -572,37 +695,71 @@ __global__ __launch_bounds__(256) void chunk_inter_kernel(
             const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
             const int col = ct * 16 + (l & 15);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                accS[rb][ct][e] = s0 ? s0[(bh * DK + row + e) * DV + col0 + col] : 0.f;
-            store4<CT>(Sb0 + col * LDK + row, accS[rb][ct]);
+            for (int e = 0; e < 4; ++e) Sent[(blk + row + e) * DV + col0 + col] = acc[rb][ct][e];
+            *reinterpret_cast<f32x4*>(St + col * LS + row) = acc[rb][ct];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[rb][ct][e] = cur.rr[rb][ct][e];   // accumulate onto R_j
         }
-
-    // three operand sets in flight: chunk n is consumed while n+1 and n+2 load
-    typename L::Regs r0, r1, r2;
-    L::load(r0, chain, w, l, col0);
-    L::load(r1, chain + (size_t)min(1, NC - 1) * WL::BYTES, w, l, col0);
     __syncthreads();
-    int n = 0;
-    for (; n + 3 <= NC; n += 3) {
-        chain_step<E, DK, DV, TV>(r0, r2, n, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
-        chain_step<E, DK, DV, TV>(r1, r0, n + 1, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
-        chain_step<E, DK, DV, TV>(r2, r1, n + 2, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+#pragma unroll
+    for (int kb = 0; kb < DK / 16; ++kb) {
+        f32x4 sv[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+            sv[ct] = *reinterpret_cast<const f32x4*>(St + (ct * 16 + (l & 15)) * LS + kb * 16 + 4 * (l >> 4));
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct)
+                    acc[rb][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(cur.pa[rb][kb][t], sv[ct][t], acc[rb][ct], 0, 0, 0);
     }
-    if (n < NC) chain_step<E, DK, DV, TV>(r0, r2, n, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
-    if (n + 1 < NC) chain_step<E, DK, DV, TV>(r1, r0, n + 1, NC, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+    __syncthreads();
+}
 
+template <int DK, int DV, int TV>
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ P, const float* __restrict__ R,
+                                                       const float* __restrict__ s0, float* __restrict__ Sent,
+                                                       float* __restrict__ s_final, int nseg, int nchain) {
+    constexpr int RB = DK / 64, NT = TV / 16, LS = DK + 4;
+    __shared__ __align__(16) float St[TV * LS];     // S^T tile
+    const int tile = blockIdx.x / nchain;
+    const size_t bh = blockIdx.x % nchain;
+    const int l = lane_id(), w = wave_id();
+    const int col0 = tile * TV;
+
+    f32x4 acc[RB][NT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4) + e;
+                acc[rb][ct][e] = s0 ? s0[(bh * DK + row) * DV + col0 + ct * 16 + (l & 15)] : 0.f;
+            }
+    // P_j rows of this wave and the R_j tile, prefetched one segment ahead in
+    // two register sets (a / b, explicitly unrolled: no dynamic indexing)
+    typename ScanRegs<DK, TV>::T ra, rb_;
+    scan_fetch<DK, DV, TV>(ra, P, R, 0, nchain, bh, col0, w, l);
+    int j = 0;
+    for (; j + 2 <= nseg; j += 2) {
+        scan_step<DK, DV, TV>(acc, ra, rb_, P, R, Sent, St, j, j + 1, nchain, bh, col0, w, l);
+        scan_step<DK, DV, TV>(acc, rb_, ra, P, R, Sent, St, j + 1, min(j + 2, nseg - 1), nchain, bh, col0, w, l);
+    }
+    if (j < nseg) scan_step<DK, DV, TV>(acc, ra, rb_, P, R, Sent, St, j, j, nchain, bh, col0, w, l);
     if (s_final) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
-                const int col = ct * 16 + (l & 15);
+            for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s_final[(bh * DK + row + e) * DV + col0 + col] = accS[rb][ct][e];
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4) + e;
+                    s_final[(bh * DK + row) * DV + col0 + ct * 16 + (l & 15)] = acc[rb][ct][e];
+                }
     }
-    (void)LDK;
 }
 
 // State pass-through for T == 0: s_final = s0 (or zeros).
@@ -612,27 +769,90 @@ __global__ void state_copy_kernel(const float* __restrict__ s0, float* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Sequences of at least 2*SEG_L chunks use two levels (compose / scan /
+// expand over segments of SEG_L chunks); shorter ones one chain per tile.
+constexpr int SEG_L = 16;
+
+struct Layout {
+    size_t chunks, p_off, r_off, e_off, total;
+    int nseg;
+};
+
+template <class CT, int DK, int DV>
+static Layout layout_t(int B, int T, int H) {
+    Layout lo{};
+    const size_t NC = ((size_t)T + C - 1) / C;
+    const size_t nchain = (size_t)B * H;
+    lo.chunks = nchain * NC * Ws<CT, DK, DV>::BYTES;
+    lo.nseg = NC >= 2 * SEG_L ? (int)((NC + SEG_L - 1) / SEG_L) : 1;
+    lo.p_off = lo.r_off = lo.e_off = lo.total = lo.chunks;
+    if (lo.nseg > 1) {
+        lo.r_off = lo.p_off + (size_t)lo.nseg * nchain * DK * DK * 4;
+        lo.e_off = lo.r_off + (size_t)lo.nseg * nchain * DK * DV * 4;
+        lo.total = lo.e_off + (size_t)lo.nseg * nchain * DK * DV * 4;
+    }
+    return lo;
+}
+
+template <class K>
+static hipError_t set_lds(K kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <class E, int DK, int DV>
 static hipError_t launch_chunk_t(const ChunkArgs& a) {
     typedef typename Compute<E>::type CT;
-    constexpr int TV = sizeof(CT) == 2 ? 32 : 16;
+    constexpr bool BF = sizeof(CT) == 2;
+    constexpr int TVS = BF ? 32 : 16;          // single level: more chains on the chip
+    constexpr int TVV = BF ? DV : 16;          // two level: one read of the operands per chunk
+    constexpr int TVK = BF ? DK : 16;
     const int NC = (a.T + C - 1) / C;
+    const int nchain = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     typedef Intra<E, DK, DV> LI;
-    typedef Inter<E, DK, DV, TV> LX;
     static_assert(LI::LDS <= 160 * 1024, "intra LDS budget");
-    static_assert(LX::LDS <= 64 * 1024, "inter LDS budget");
-    hipError_t err = hipFuncSetAttribute((const void*)chunk_intra_kernel<E, DK, DV>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS);
-    if (err != hipSuccess) return err;
+    const Layout lo = layout_t<CT, DK, DV>(a.B, a.T, a.H);
     unsigned char* ws = (unsigned char*)a.workspace;
+    hipError_t err = set_lds(chunk_intra_kernel<E, DK, DV>, LI::LDS);
+    if (err != hipSuccess) return err;
     hipLaunchKernelGGL((chunk_intra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(256), LI::LDS, st,
                        (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta,
                        a.g_min, a.T, a.H, NC, ws);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((chunk_inter_kernel<E, DK, DV, TV>), dim3((DV / TV) * a.H * a.B), dim3(256), LX::LDS, st,
-                       (E*)a.o, a.s0, a.s_final, a.T, a.H, NC, (const unsigned char*)ws);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+
+    if (lo.nseg == 1) {
+        typedef Chain<E, DK, DV, DV, TVS, CM_EXPAND> LX;
+        if ((err = set_lds(chain_kernel<E, DK, DV, DV, TVS, CM_EXPAND>, LX::LDS)) != hipSuccess) return err;
+        hipLaunchKernelGGL((chain_kernel<E, DK, DV, DV, TVS, CM_EXPAND>), dim3((DV / TVS) * nchain), dim3(256),
+                           LX::LDS, st, (E*)a.o, a.s0, a.s_final, a.T, a.H, NC, NC, nchain,
+                           (const unsigned char*)ws);
+        return hipGetLastError();
+    }
+    float* Pb = reinterpret_cast<float*>(ws + lo.p_off);
+    float* Rb = reinterpret_cast<float*>(ws + lo.r_off);
+    float* Eb = reinterpret_cast<float*>(ws + lo.e_off);
+    const int nseg = lo.nseg;
+    typedef Chain<E, DK, DV, DV, TVV, CM_COMPOSE_R> LR;
+    typedef Chain<E, DK, DV, DK, TVK, CM_COMPOSE_P> LP;
+    typedef Chain<E, DK, DV, DV, TVV, CM_EXPAND> LE;
+    if ((err = set_lds(chain_kernel<E, DK, DV, DV, TVV, CM_COMPOSE_R>, LR::LDS)) != hipSuccess) return err;
+    if ((err = set_lds(chain_kernel<E, DK, DV, DK, TVK, CM_COMPOSE_P>, LP::LDS)) != hipSuccess) return err;
+    if ((err = set_lds(chain_kernel<E, DK, DV, DV, TVV, CM_EXPAND>, LE::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((chain_kernel<E, DK, DV, DK, TVK, CM_COMPOSE_P>), dim3((DK / TVK) * nseg * nchain), dim3(256),
+                       LP::LDS, st, (E*)nullptr, (const float*)nullptr, Pb, a.T, a.H, NC, SEG_L, nchain,
+                       (const unsigned char*)ws);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((chain_kernel<E, DK, DV, DV, TVV, CM_COMPOSE_R>), dim3((DV / TVV) * nseg * nchain), dim3(256),
+                       LR::LDS, st, (E*)nullptr, (const float*)nullptr, Rb, a.T, a.H, NC, SEG_L, nchain,
+                       (const unsigned char*)ws);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, 32>), dim3((DV / 32) * nchain), dim3(256), 0, st, Pb, Rb, a.s0, Eb,
+                       a.s_final, nseg, nchain);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((chain_kernel<E, DK, DV, DV, TVV, CM_EXPAND>), dim3((DV / TVV) * nseg * nchain), dim3(256),
+                       LE::LDS, st, (E*)a.o, (const float*)Eb, (float*)nullptr, a.T, a.H, NC, SEG_L, nchain,
+                       (const unsigned char*)ws);
     return hipGetLastError();
 }
 
@@ -644,19 +864,16 @@ static hipError_t launch_chunk_e(const ChunkArgs& a) {
     return launch_chunk_t<E, 64, 64>(a);
 }
 
-template <class E>
-static size_t ws_bytes_e(int dk, int dv) {
-    typedef typename Compute<E>::type CT;
-    if (dk == 128 && dv == 128) return Ws<CT, 128, 128>::BYTES;
-    if (dk == 128 && dv == 64) return Ws<CT, 128, 64>::BYTES;
-    if (dk == 64 && dv == 128) return Ws<CT, 64, 128>::BYTES;
-    return Ws<CT, 64, 64>::BYTES;
+template <class CT>
+static size_t ws_bytes_t(int B, int T, int H, int dk, int dv) {
+    if (dk == 128 && dv == 128) return layout_t<CT, 128, 128>(B, T, H).total;
+    if (dk == 128 && dv == 64) return layout_t<CT, 128, 64>(B, T, H).total;
+    if (dk == 64 && dv == 128) return layout_t<CT, 64, 128>(B, T, H).total;
+    return layout_t<CT, 64, 64>(B, T, H).total;
 }
 
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16) {
-    const size_t NC = ((size_t)T + C - 1) / C;
-    const size_t per = bf16 ? ws_bytes_e<kda::bf16>(dk, dv) : ws_bytes_e<float>(dk, dv);
-    return (size_t)B * H * NC * per;
+    return bf16 ? ws_bytes_t<kda::bf16>(B, T, H, dk, dv) : ws_bytes_t<float>(B, T, H, dk, dv);
 }
 
 hipError_t launch_chunk(const ChunkArgs& a) {

@@ -11,7 +11,8 @@
 //   o     = S^T q = S'^T q + (k . q) r
 // which is Eq. 1 of the tech report rearranged exactly.
 //
-// Work mapping: one 256-thread workgroup per (b, h).  Thread t owns four
+// Work mapping: one workgroup per (b, h) (512 threads for d_k = d_v = 128,
+// 256 otherwise).  Thread t owns four
 // consecutive value columns (a float4) of DK / NRG rows, the rows of one
 // thread being NRG apart so that a wavefront's loads cover whole adjacent
 // rows (fully coalesced 16-byte accesses).  The state is read once into
@@ -21,17 +22,23 @@
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
+// Threads per (b, h) for d_k = d_v = 128: 512 keeps 32 state values per
+// thread, which leaves room for more resident waves than 256 threads do.
+#ifndef KDA_DECODE_THREADS
+#define KDA_DECODE_THREADS 512
+#endif
+
 namespace kda {
 
-template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+template <class E, int DK, int DV, int NTH>
+__global__ __launch_bounds__(NTH) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const E* __restrict__ beta, float g_min,
     float* __restrict__ state, E* __restrict__ o) {
     constexpr int NQ = DV / 4;       // column quads
-    constexpr int NRG = 256 / NQ;    // row groups
+    constexpr int NRG = NTH / NQ;    // row groups
     constexpr int R = DK / NRG;      // rows per thread
-    static_assert(NQ * NRG == 256 && R * NRG == DK, "bad decode tiling");
+    static_assert(NQ * NRG == NTH && R * NRG == DK, "bad decode tiling");
 
     __shared__ float red_p[NRG][DV];
     __shared__ float red_q[NRG][DV];
@@ -101,7 +108,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
 template <class E, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(256), 0,
+    constexpr int NTH = (DK == 128 && DV == 128) ? KDA_DECODE_THREADS : 256;
+    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH>), dim3(a.B * a.H), dim3(NTH), 0,
                        (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
                        (const E*)a.z, (const E*)a.beta, a.g_min, a.state, (E*)a.o);
     return hipGetLastError();

@@ -56,7 +56,12 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     # bf16, d = 128: W, U, M, Q*e^G, (K*e^{G_C-G})^T in bf16 plus e^{G_C} fp32 per chunk
     per = (64 * 128 * 4 + 64 * 64) * 2 + 128 * 4
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == 32 * 512 * per
+    # 32768 tokens = 512 chunks: two levels over 32 segments of 16 chunks, which adds the
+    # per-segment transition P (d_k x d_k), input term R and entry state (d_k x d_v), fp32
+    seg = 32 * 32 * (128 * 128 + 2 * 128 * 128) * 4
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == 32 * 512 * per + seg
+    # below 32 chunks a single level: no segment buffers
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 31 * per
     assert lib.kda_chunk_fwd_workspace_bytes(1, 65, 1, 128, 128, 64, BF16) == 2 * per
     per32 = (64 * 64 * 4 + 64 * 64) * 4 + 64 * 4
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32) == 4 * per32

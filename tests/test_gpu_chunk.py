@@ -127,6 +127,54 @@ def test_prefill_then_decode_handoff():
     assert rel(f64(st), f64(s)) < 1e-5
 
 
+# ------------------------------------------------------------------ two levels
+# From 32 chunks on, the prefill composes per-segment transitions (16 chunks
+# each), scans them, and expands outputs from the segment entry states.
+@pytest.mark.parametrize("T", [2048, 2113, 3007])
+@pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
+def test_two_level_ragged(T, dtype, tag):
+    x = ki.prefill_inputs(1, T, 2, 128, 128, dtype, seed=T, device=DEV, s0_var=0.01)
+    check(x, tag, label=f"two-level T={T}")
+
+
+@pytest.mark.parametrize("z_mean", [-6.0, -8.0])
+@pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
+def test_two_level_long_memory(z_mean, dtype, tag):
+    """Slow decay across 60 chunks / 4 segments: the segment transitions and
+    the scan carry most of the outputs."""
+    x = ki.prefill_inputs(2, 3840, 2, 128, 128, dtype, seed=31, device=DEV, z_mean=z_mean, s0_var=0.01)
+    check(x, tag, label=f"two-level z~N({z_mean},1)")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+@pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
+def test_two_level_widths(dk, dv, dtype, tag):
+    x = ki.prefill_inputs(1, 2100, 3, dk, dv, dtype, seed=dk + dv, device=DEV, s0_var=0.01, z_mean=-5.0)
+    check(x, tag, label=f"two-level dk={dk} dv={dv}")
+
+
+def test_two_level_no_decay_and_no_initial_state():
+    x = ki.prefill_inputs(1, 2200, 2, 64, 64, torch.float32, seed=33, device=DEV)
+    x["z"] = torch.full_like(x["z"], -1e4)
+    x["s0"] = None
+    check(x, "f32", label="two-level alpha=1, S0=None")
+
+
+def test_two_level_split_resume():
+    """The two-level path and the single-level path give the same state:
+    fwd(T) equals fwd(T2; S0 = fwd(T1)) with T1 single level."""
+    x = ki.prefill_inputs(1, 2560, 2, 128, 128, torch.float32, seed=34, device=DEV, s0_var=0.01, z_mean=-4.0)
+    o, s = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
+    t1 = 512
+    a = {n: x[n][:, :t1].contiguous() for n in ("q", "k", "v", "z", "beta")}
+    r = {n: x[n][:, t1:].contiguous() for n in ("q", "k", "v", "z", "beta")}
+    oa, sa = kda.chunk_fwd(a["q"], a["k"], a["v"], a["z"], a["beta"], ki.G_MIN, x["s0"])
+    ob, sb = kda.chunk_fwd(r["q"], r["k"], r["v"], r["z"], r["beta"], ki.G_MIN, sa)
+    torch.cuda.synchronize()
+    assert rel(f64(torch.cat([oa, ob], 1)), f64(o)) < 1e-5
+    assert rel(f64(sb), f64(s)) < 1e-5
+
+
 # ------------------------------------------------------------------ full sizes
 def test_prefill_32k_full_size_sampled():
     """B=1, T=32768, H=32, d=128, bf16, S0 ~ N(0, 0.01): the prefill workload
