@@ -11,8 +11,15 @@ are generated on the GPU before timing and stay resident in HBM.
 Also measured in the same run:
   * decode: kda_recurrent_step over B=256 sequences, H=32, d=128, fp32 state,
     1024 successive tokens (inputs for all steps pre-generated in HBM);
-  * cpu_baseline: the fp64 oracle on the host cores over a bounded sample of
-    the prefill workload (a few heads over the full 32k tokens).
+  * epilogue: RMSNorm x gate + projection of the training-shape workload
+    (8 x 8192 tokens, 4096 -> 2304), against the bf16 MFMA peak;
+  * cpu_baseline: the fp64 oracle on the host cores over the prefill
+    workload (all heads over the full 32k tokens).
+
+Counter support: --copy-only runs a 1 GiB device copy for counter
+calibration; --pmc-summary turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into
+profiles/prefill_32k_traffic.json, which later runs report as `traffic`
+while the kernel sources are unchanged.
 
 Prints one JSON line.
 """
@@ -26,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+import glob
+import hashlib
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
@@ -33,6 +43,15 @@ PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 2      # q, k, z, v in; b
 PREFILL_FLOP_PER_TOKEN_HEAD = 163840                           # chunk form, d = 128, C = 64
 DECODE_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 DECODE_FLOP_PER_HEAD_STEP = 114688
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_32k_traffic.json")
+CSRC = os.path.join(ROOT, "gated_delta_rule_14_amd", "csrc")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -44,6 +63,12 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=32)
+    p.add_argument("--no-epilogue", action="store_true")
+    p.add_argument("--copy-only", action="store_true",
+                   help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE runs of the prefill and of --copy-only "
+                        "into profiles/prefill_32k_traffic.json")
     return p.parse_args()
 
 
@@ -104,8 +129,111 @@ def bench_decode(torch, kda, ki, nsteps):
         "workload": "decode_256", "B": B, "H": H, "dk": dk, "dv": dv, "steps": nsteps,
         "value": B * nsteps / total, "unit": "tokens/s", "us_per_step": per * 1e6,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
+                     "algorithmic_bytes": bytes_step, "kernel": "decode_step_kernel"},
     }
+
+
+def bench_epilogue(torch, kda, ki, steps=5):
+    """RMSNorm x gate + projection of the training-shape workload:
+    (8, 8192, 32, 128) -> (8, 8192, 2304) bf16; the projection is the only
+    MFMA-bound part of the path."""
+    cfg = ki.WORKLOADS["train_8x8k"]
+    B, T, H, dv, dm = cfg["B"], cfg["T"], cfg["H"], cfg["dv"], cfg["d_model"]
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    o = (torch.randn((B, T, H, dv), generator=g, device=dev) * 0.3).to(torch.bfloat16)
+    gate = ki.gate_logits((B, T, H), dv, torch.bfloat16, 5, dev)
+    w = ki.projection(dm, H * dv, 5, dev)
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B * T * H * dv * 2, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        kda.out_gate(o, gate, ki.EPS, w, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        kda.out_gate(o, gate, ki.EPS, w, y=y, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    per = a.elapsed_time(b) * 1e-3 / steps
+    flop = 2.0 * B * T * H * dv * dm
+    tf = flop / per / 1e12
+    return {"workload": "train_8x8k epilogue", "M": B * T, "K": H * dv, "N": dm, "us_per_call": round(per * 1e6, 1),
+            "value": round(B * T / per, 1), "unit": "tokens/s",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "gate_kernel + proj_gemm_kernel (projection FLOP only)"}}
+
+
+def copy_only(torch):
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": src.numel(), "calls": 3}), flush=True)
+
+
+def _pmc_per_dispatch(path, counter):
+    import csv
+    import collections
+    acc = collections.defaultdict(float)
+    n = collections.Counter()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = r["Kernel_Name"]
+        acc[k] += float(r["Counter_Value"])
+        n[(k, r["Dispatch_Id"])] += 1
+    disp = collections.Counter(k for (k, _) in n)
+    return {k: acc[k] / disp[k] for k in acc}
+
+
+def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the prefill kernels,
+    scaled by what the same counters read for a 1 GiB device copy."""
+    f = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    wr = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    cf = _pmc_per_dispatch(cfetch_csv, "FETCH_SIZE")
+    cw = _pmc_per_dispatch(cwrite_csv, "WRITE_SIZE")
+    copy_k = max(cf, key=cf.get)
+    true_kib = (1 << 30) / 1024.0
+    sf, sw = true_kib / cf[copy_k], true_kib / cw[max(cw, key=cw.get)]
+    kernels = {}
+    for k in sorted(set(f) | set(wr)):
+        if "kda" not in k:
+            continue
+        kernels[k] = {"fetch_kib": round(f.get(k, 0.0), 1), "write_kib": round(wr.get(k, 0.0), 1),
+                      "hbm_bytes": round((f.get(k, 0.0) * sf + wr.get(k, 0.0) * sw) * 1024)}
+    out = {"source_hash": kernel_source_hash(), "copy_fetch_scale": round(sf, 4), "copy_write_scale": round(sw, 4),
+           "copy_kernel": copy_k, "kernels": kernels,
+           "prefill_hbm_bytes_per_call": sum(v["hbm_bytes"] for k, v in kernels.items()
+                                             if "chunk_intra" in k or "chain_kernel" in k or "seg_scan" in k),
+           "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --no-cpu --steps 2 "
+                      "--warmup 1 --decode-steps 8 --no-epilogue; same with --copy-only for the scale factors"}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def measured_traffic(which):
+    """HBM bytes per prefill call ("prefill") or per decode step ("decode")
+    from the committed counter summary, or None when the kernels have changed
+    since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    if which == "prefill":
+        return t.get("prefill_hbm_bytes_per_call")
+    for k, v in t.get("kernels", {}).items():
+        if "decode_step_kernel" in k:
+            return v["hbm_bytes"]
+    return None
 
 
 def cpu_baseline(torch, ki, nheads):
@@ -130,6 +258,9 @@ def cpu_baseline(torch, ki, nheads):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the operator shards over (batch, head) chains with no communication; see the design notes)",
@@ -142,6 +273,9 @@ def main():
     from gated_delta_rule_14_amd import _lib
 
     _lib.lib()
+    if args.copy_only:
+        copy_only(torch)
+        return
     r = bench_prefill(torch, kda, ki, args.steps, args.warmup)
     tok_s = r["tokens"] / r["mean"]
     gbs = r["bytes"] / r["mean"] / 1e9
@@ -161,12 +295,16 @@ def main():
         "config": {"workload": "prefill_32k", "B": r["B"], "T": r["T"], "H": r["H"], "dk": r["dk"],
                    "dv": r["dv"], "chunk": 64, "state": "fp32", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "kda_chunk_fwd (intra + inter launches)",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
+                     "algorithmic_bytes": r["bytes"],
+                     "kernel": "kda_chunk_fwd: chunk_intra_kernel + chain_kernel (compose P, compose R, expand) "
+                               "+ seg_scan_kernel",
                      "mfma_frac": round(r["flop"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_decode:
         line["decode"] = bench_decode(torch, kda, ki, args.decode_steps)
+    if not args.no_epilogue:
+        line["epilogue"] = bench_epilogue(torch, kda, ki)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(torch, ki, args.cpu_heads)
     print(json.dumps(line), flush=True)

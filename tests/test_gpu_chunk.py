@@ -189,3 +189,30 @@ def test_train_8x8k_full_size_sampled():
     x = ki.workload_inputs("train_8x8k", seed=2, device=DEV)
     o, s = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
     check(x, "bf16", heads=[5, 27], batches=[3, 7], o=o, s=s, label="train_8x8k")
+
+
+def test_long_1m_full_size_sampled():
+    """B=1, T=1,048,576, H=32, d=128, bf16, z ~ N(2,1), S0 = 0, then the
+    RMSNorm x gate epilogue: the long-context workload at full size (16,384
+    chunks, 1,024 segments, all heads launched); the oracle runs one sampled
+    head over all tokens, and the epilogue on sampled rows."""
+    import oracle
+    from helpers import host
+    x = ki.workload_inputs("long_1m", seed=4, device=DEV)
+    o, s = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
+    y = kda.out_gate(o, x["gate"], ki.EPS)
+    torch.cuda.synchronize()
+    h = 13
+    hsel = [h]
+    ro, rs = oracle_prefill({n: x[n] for n in ("q", "k", "v", "z", "beta", "s0")}, heads=hsel)
+    eo, es = rel(f64(o[:, :, hsel]), ro), rel(f64(s[:, hsel]), rs)
+    print(f"chunk long_1m (head {h}): o {eo:.2e} state {es:.2e}")
+    assert eo < 2e-2 and es < 1e-2
+    rng = np.random.default_rng(2)
+    rows = np.sort(rng.choice(x["q"].shape[1], 256, replace=False))
+    oh = np.ascontiguousarray(host(o)[:, rows])
+    gh = np.ascontiguousarray(host(x["gate"])[:, rows])
+    ry = oracle.out_gate(oh, gh, ki.EPS)
+    ey = rel(f64(y)[:, rows], ry)
+    print(f"long_1m epilogue (256 rows): {ey:.2e}")
+    assert ey < 2e-2

@@ -78,3 +78,26 @@ def test_train_8x8k_epilogue_projection_sampled_rows():
     e = rel(f64(y).reshape(B * T, dm)[rows], ref)
     print(f"train_8x8k epilogue + projection (64 rows): {e:.2e}")
     assert e < 2e-2
+
+
+def test_train_8x8k_layer_sampled():
+    """The training-shape layer end to end (chunkwise prefill, then the
+    gate + projection to d_model = 2304): the oracle runs the recurrence for
+    one sampled batch row (all 32 heads, all 8192 tokens) and the epilogue
+    and projection on 32 sampled tokens of it."""
+    x = ki.workload_inputs("train_8x8k", seed=6, device=DEV)
+    res = kda.layer(x["q"], x["k"], x["v"], x["z"], x["beta"], x["gate"], x["w"], x["s0"], ki.G_MIN, ki.EPS)
+    torch.cuda.synchronize()
+    B, T, H, dv = x["v"].shape
+    b = 5
+    rng = np.random.default_rng(3)
+    ts = np.sort(rng.choice(T, 32, replace=False))
+    # oracle recurrence for batch b, all heads (needed for the projected rows), then epilogue on sampled tokens
+    cut = {n: np.ascontiguousarray(host(x[n])[b:b + 1]) for n in ("q", "k", "v", "z", "beta")}
+    ro, rs = oracle.forward(cut["q"], cut["k"], cut["v"], cut["z"], cut["beta"], ki.G_MIN, None)
+    gh = np.ascontiguousarray(host(x["gate"])[b:b + 1, ts])
+    ref = oracle.out_gate(np.ascontiguousarray(ro[:, ts]), gh, ki.EPS, host(x["w"]))
+    e_out = rel(f64(res["outputs"])[b:b + 1, ts], ref)
+    e_s = rel(f64(res["final_state"])[b:b + 1], rs)
+    print(f"train_8x8k layer (batch {b}, 32 rows): outputs {e_out:.2e} final_state {e_s:.2e}")
+    assert e_out < 2e-2 and e_s < 1e-2
