@@ -873,7 +873,24 @@ static size_t ws_bytes_t(int B, int T, int H, int dk, int dv) {
 }
 
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16) {
-    return bf16 ? ws_bytes_t<kda::bf16>(B, T, H, dk, dv) : ws_bytes_t<float>(B, T, H, dk, dv);
+    return bf16 ? seg_workspace_bytes(B, T, H, dk, dv) : ws_bytes_t<float>(B, T, H, dk, dv);
+}
+
+template <int DK, int DV>
+static hipError_t launch_scan_t(const float* P, const float* R, const float* s0, float* Sent, float* s_final,
+                                int nseg, int nchain, hipStream_t st) {
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, 32>), dim3((DV / 32) * nchain), dim3(256), 0, st, P, R, s0, Sent,
+                       s_final, nseg, nchain);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_scan(const float* P, const float* R, const float* s0, float* Sent, float* s_final, int nseg,
+                           int nchain, int dk, int dv, void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (dk == 128 && dv == 128) return launch_scan_t<128, 128>(P, R, s0, Sent, s_final, nseg, nchain, st);
+    if (dk == 128 && dv == 64) return launch_scan_t<128, 64>(P, R, s0, Sent, s_final, nseg, nchain, st);
+    if (dk == 64 && dv == 128) return launch_scan_t<64, 128>(P, R, s0, Sent, s_final, nseg, nchain, st);
+    return launch_scan_t<64, 64>(P, R, s0, Sent, s_final, nseg, nchain, st);
 }
 
 hipError_t launch_chunk(const ChunkArgs& a) {
@@ -884,7 +901,7 @@ hipError_t launch_chunk(const ChunkArgs& a) {
                            dim3(256), 0, (hipStream_t)a.stream, a.s0, a.s_final, n);
         return hipGetLastError();
     }
-    return a.bf16 ? launch_chunk_e<kda::bf16>(a) : launch_chunk_e<float>(a);
+    return a.bf16 ? launch_chunk_seg(a) : launch_chunk_e<float>(a);
 }
 
 }  // namespace kda

@@ -32,6 +32,12 @@ struct ChunkArgs {
 };
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
 hipError_t launch_chunk(const ChunkArgs& a);
+// bf16 tokens: fused segment kernels (seg.hip); fp32 tokens: per-chunk
+// workspace kernels (chunk.hip).  Both use the segment scan of chunk.hip.
+size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_chunk_seg(const ChunkArgs& a);
+hipError_t launch_seg_scan(const float* P, const float* R, const float* s0, float* Sent, float* s_final, int nseg,
+                           int nchain, int dk, int dv, void* stream);
 
 struct GateArgs {
     const void *o, *gate;

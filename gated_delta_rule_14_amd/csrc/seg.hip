@@ -1,0 +1,772 @@
+// seg.hip -- kda_chunk_fwd on bf16 tokens: fused segment kernels.
+//
+// Same chunk form as the fp32 path (Kimi Linear tech report, section 3.1 and
+// appendix B, Propositions 1-2, Eqs. 16-19; beta_r scales the whole
+// right-hand side of Eqs. 17 and 19):
+//   V_new = U - W S,  O = (Q e^G) S + M V_new,  S' = Diag(e^{G_C}) S + (K e^{G_C-G})^T V_new.
+// Here the per-chunk products (W, U, M, Q e^G, K e^{G_C-G}, e^{G_C}) never
+// leave the chip: one workgroup of 512 threads walks a segment of chunks of
+// one (b, h) chain, computes each chunk's products into LDS from the raw
+// tokens, and advances a d_k x N fp32 state held in MFMA accumulators.
+//
+//  * EXPAND  the state starts from the given entry state; the outputs O are
+//            written; the state is S.
+//  * COMPOSE the state is [P | R] (d_k x (d_k + d_v)) starting from [I | 0]:
+//            the segment's affine map S_end = P S_start + R, with
+//            P = prod_n (Diag(e^{G_C}) - K~_n^T W_n) and R the state reached
+//            from S_start = 0.  A scan over segments then gives every
+//            segment's entry state, and EXPAND runs all segments in parallel.
+//
+// State in registers.  Each chain wave owns 16-column tiles of the state.  A
+// 16x16x32 bf16 MFMA reads operand B as (column l%16, contraction indices
+// 8(l/16)..+7) and leaves its result as (column l%16, rows 4(l/16)+e).  Two
+// vertically adjacent accumulator tiles therefore hold, in each lane, exactly
+// the eight values of a B fragment, up to an order of the contraction index
+// inside each 32-block.  That order is fixed once (pcol below), and every
+// LDS operand that is contracted against accumulator-held data (W, Q e^G and
+// M against the state or V_new; (K e^{G_C-G})^T against V_new) is stored with
+// its contraction columns in the same order.  So V_new = U - W S, the outputs
+// and the state update read only the shared per-chunk operands from LDS; the
+// state and V_new never leave the registers of the wave that owns them.
+//
+// Overflow handling of the decay factors is that of the fp32 path: A and M
+// per 16x16 block pair with reference rows m(R) = 16R + 7, decay exponents in
+// log2 units so that every factor is one v_exp_f32.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace segk {
+
+constexpr int C = 64;       // chunk length
+constexpr int SUB = 16;     // block size of A, M and the triangular solve
+constexpr int NTH = 512;    // threads per workgroup (8 waves)
+constexpr float LOG2E = 1.4426950408889634f;
+enum { COMPOSE = 0, EXPAND = 1 };
+
+constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
+
+// Storage position of contraction index x: inside each block of 32,
+// x = 16 h + 4 g + j is stored at 8 g + 4 h + j, so lane group g of a
+// fragment load (8 consecutive stored elements) gets rows 4g..4g+3 of two
+// vertically adjacent 16-row accumulator tiles.
+__host__ __device__ constexpr int pcol(int x) {
+    return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
+}
+
+// LDS layout (byte offsets) of one workgroup.
+template <int DK, int DV, int MODE>
+struct Lay {
+    static constexpr bool EXP = MODE == EXPAND;
+    static constexpr int CP = DK / 2;            // key-channel pairs
+    static constexpr int NPART = NTH / CP;       // row parts (8 or 16)
+    static constexpr int RP = C / NPART;         // rows per thread (8 or 4)
+    static constexpr int CPV = DV / 2;
+    static constexpr int RPV = C / (NTH / CPV);
+    static constexpr int LDK = DK + 8;           // (C x DK) bf16 tiles
+    static constexpr int LC = C + 8;             // (d x C) bf16 tiles
+    static constexpr int LU = C + 4;             // U^T (DV x C) bf16
+    static constexpr int LB = SUB + 8;           // 16x16 bf16 operand blocks
+    static constexpr int BS = SUB * SUB + 16;    // fp32 diagonal block stride (words)
+    static constexpr size_t TILE = (size_t)C * LDK * 2;
+    static constexpr size_t UTB = (size_t)DV * LU * 2;
+    static constexpr size_t OFF_KL = 0;                                    // KL, then -W [C][LDK] pcol
+    static constexpr size_t OFF_KR = TILE;                                 // KR, then U^T [DV][LU]
+    static constexpr size_t OFF_QL = OFF_KR + a16(mx(TILE, UTB));          // QL (EXPAND)
+    static constexpr size_t OFF_RT = OFF_QL + (EXP ? TILE : 0);            // (beta k e^G)^T [DK][LC]
+    static constexpr size_t OFF_RV = OFF_RT + a16((size_t)DK * LC * 2);    // (beta v)^T [DV][LC]
+    static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
+    static constexpr size_t OFF_QG = OFF_KGT + a16((size_t)DK * LC * 2);   // q e^G [C][LDK] pcol
+    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol
+    static constexpr size_t OFF_AS = OFF_M + (EXP ? a16((size_t)C * LC * 2) : 0);   // diag A blocks fp32
+    static constexpr size_t OFF_AB = OFF_AS + (size_t)4 * BS * 4;          // -A off-diag blocks bf16
+    static constexpr size_t OFF_DB = OFF_AB + a16((size_t)6 * SUB * LB * 2);   // (I+A_RR)^{-1} bf16
+    static constexpr size_t OFF_EGC = OFF_DB + a16((size_t)4 * SUB * LB * 2);
+    static constexpr size_t OFF_DSC = OFF_EGC + (size_t)DK * 4;            // [6][DK] block factors
+    static constexpr size_t OFF_CAR = OFF_DSC + 6 * (size_t)DK * 4;        // [NPART][DK] part sums
+    static constexpr size_t OFF_BET = OFF_CAR + (size_t)NPART * DK * 4;
+    static constexpr size_t LDS = OFF_BET + C * 4;
+    static_assert(RP % 4 == 0 && RPV % 4 == 0 && 16 % RP == 0, "intra tiling");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// One chunk's raw tokens, as this thread loads them (register prefetch).
+template <int DK, int DV, int MODE>
+struct In {
+    typedef Lay<DK, DV, MODE> L;
+    bf16x2 z[L::RP], k[L::RP], q[L::EXP ? L::RP : 1], v[L::RPV];
+    bf16 beta;
+};
+
+// Loads are unconditional at clamped rows (always in bounds): a load under a
+// branch makes the wait-count insertion assume the no-load path.
+template <int DK, int DV, int MODE>
+__device__ __forceinline__ void fetch_zkq(In<DK, DV, MODE>& r, const bf16* __restrict__ q,
+                                          const bf16* __restrict__ k, const bf16* __restrict__ z,
+                                          const bf16* __restrict__ beta, size_t row0, int valid, int H) {
+    typedef Lay<DK, DV, MODE> L;
+    const int tid = threadIdx.x;
+    const int c0 = 2 * (tid % L::CP), r0 = (tid / L::CP) * L::RP;
+    const int last = valid - 1, rs = H * DK;
+    const bf16* zb = z + row0 * DK;
+    const bf16* kb = k + row0 * DK;
+    const bf16* qb = q + row0 * DK;
+#pragma unroll
+    for (int i = 0; i < L::RP; ++i) {
+        const int off = min(r0 + i, last) * rs + c0;
+        r.z[i] = load2<bf16>(zb + off);
+        r.k[i] = load2<bf16>(kb + off);
+        if constexpr (L::EXP) r.q[i] = load2<bf16>(qb + off);
+    }
+    r.beta = beta[row0 + (size_t)min(tid & (C - 1), last) * H];
+}
+
+template <int DK, int DV, int MODE>
+__device__ __forceinline__ void fetch_v(In<DK, DV, MODE>& r, const bf16* __restrict__ v, size_t row0, int valid,
+                                        int H) {
+    typedef Lay<DK, DV, MODE> L;
+    const int tid = threadIdx.x;
+    const int cv0 = 2 * (tid % L::CPV), rv0 = (tid / L::CPV) * L::RPV;
+    const bf16* vb = v + row0 * DV;
+#pragma unroll
+    for (int i = 0; i < L::RPV; ++i) r.v[i] = load2<bf16>(vb + min(rv0 + i, valid - 1) * (H * DV) + cv0);
+}
+
+// Block pairs (R, I), I <= R, of A and M per wave: the diagonal pairs (no
+// cross-block factor) two to a wave.
+__constant__ int kSegPairs[8][2][2] = {{{0, 0}, {3, 3}}, {{1, 1}, {2, 2}}, {{1, 0}, {-1, -1}}, {{2, 0}, {-1, -1}},
+                                       {{2, 1}, {-1, -1}}, {{3, 0}, {-1, -1}}, {{3, 1}, {-1, -1}}, {{3, 2}, {-1, -1}}};
+
+__device__ __forceinline__ void store4p(bf16* p, float a, float b, float c, float d) {
+    store4<bf16>(p, f32x4{a, b, c, d});
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+// 16x16x16 bf16 MFMA: A (row l%16, k 4(l/16)..+3), B (col l%16, same k), C as usual
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                     0, 0);
+}
+__device__ __forceinline__ bf16x4 to_bf4(f32x4 v) {
+    return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+
+// Phase 1 arithmetic on the thread's RP rows of channels c0, c0+1: the gate in
+// log2 units and its chunk-local running sum; rows at or past `valid` (only
+// in a ragged last chunk) act as identity tokens (g = 0, k = q = 0).
+template <bool FULL, int RP, bool EXP>
+__device__ __forceinline__ void gate_scan(const bf16x2 (&zr)[RP], const bf16x2 (&kr)[RP],
+                                          const bf16x2 (&qr)[EXP ? RP : 1], float kg2, int r0, int valid,
+                                          float (&G)[RP][2], float (&kv)[RP][2], float (&qv)[EXP ? RP : 1][2]) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        const bool ok = FULL || r0 + i < valid;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float g2 = kg2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)zr[i][j]));
+            G[i][j] = ok ? g2 : 0.f;
+            kv[i][j] = ok ? (float)kr[i][j] : 0.f;
+            if constexpr (EXP) qv[i][j] = ok ? (float)qr[i][j] : 0.f;
+        }
+        s0 += G[i][0];
+        s1 += G[i][1];
+        G[i][0] = s0;
+        G[i][1] = s1;
+    }
+}
+
+__device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (bf16)a[i];
+        r[i + 4] = (bf16)b[i];
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// One chunk of the recurrence for one chain wave owning NTW state column
+// tiles.  Rows of the state in this lane: 16 rt + 4 (l/16) + e; columns
+// col0 + 16 ct + l%16.  With hasu false the value input is zero (the P part
+// of COMPOSE).  EXPAND writes the chunk's outputs o[token][ocol0 + ...].
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int MODE, int NTW>
+__device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu, int ucol0, const unsigned char* smem,
+                                           bf16* __restrict__ orow0, int valid, size_t ostride) {
+    typedef Lay<DK, DV, MODE> L;
+    typedef Mfma<bf16> MF;
+    constexpr int NKD = DK / 32;
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    const bf16* UT = reinterpret_cast<const bf16*>(smem + L::OFF_KR);
+    const bf16* KGT = reinterpret_cast<const bf16*>(smem + L::OFF_KGT);
+    const bf16* Wn = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
+    const bf16* QG = reinterpret_cast<const bf16*>(smem + L::OFF_QG);
+    const bf16* Ms = reinterpret_cast<const bf16*>(smem + L::OFF_M);
+    const float* egc = reinterpret_cast<const float*>(smem + L::OFF_EGC);
+
+    // V_new = U - W S (rows 16 yt + 4g + e) and, for EXPAND, the S part of
+    // O^T = S^T (Q e^G)^T + V_new^T M^T; one 32-row block of S at a time.
+    // Operand fragments are loaded one block ahead of their MFMAs.
+    f32x4 y[4][NTW];
+#pragma unroll
+    for (int yt = 0; yt < 4; ++yt)
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct)
+            y[yt][ct] = hasu ? load4<bf16>(UT + (ucol0 + ct * 16 + c) * L::LU + yt * 16 + 4 * g) : zero4();
+    f32x4 ov[L::EXP ? 4 : 1][NTW];
+    if constexpr (L::EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) ov[ot][ct] = zero4();
+    }
+    MF::frag wf[2][4], qf[2][L::EXP ? 4 : 1];
+#pragma unroll
+    for (int yt = 0; yt < 4; ++yt) wf[0][yt] = load_frag<bf16>(Wn, L::LDK, yt * 16, 0);
+    if constexpr (L::EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) qf[0][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKD; ++kb) {
+        const int cur = kb & 1, nxt = cur ^ 1;
+        if (kb + 1 < NKD) {
+#pragma unroll
+            for (int yt = 0; yt < 4; ++yt) wf[nxt][yt] = load_frag<bf16>(Wn, L::LDK, yt * 16, (kb + 1) * 32);
+            if constexpr (L::EXP) {
+#pragma unroll
+                for (int ot = 0; ot < 4; ++ot) qf[nxt][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, (kb + 1) * 32);
+            }
+        }
+        bf16x8 xb[NTW];
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) xb[ct] = pack8(xs[2 * kb][ct], xs[2 * kb + 1][ct]);
+#pragma unroll
+        for (int yt = 0; yt < 4; ++yt)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) y[yt][ct] = MF::mma(wf[cur][yt], xb[ct], y[yt][ct]);
+        if constexpr (L::EXP) {
+#pragma unroll
+            for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+                for (int ct = 0; ct < NTW; ++ct) ov[ot][ct] = MF::mma(xb[ct], qf[cur][ot], ov[ot][ct]);
+        }
+    }
+    // next operands: the first K~^T row block and e^{G_C} (and M for EXPAND)
+    MF::frag kf[2][2];
+    f32x4 dv[2];
+    kf[0][0] = load_frag<bf16>(KGT, L::LC, 0, 0);
+    kf[0][1] = load_frag<bf16>(KGT, L::LC, 0, 32);
+    dv[0] = *reinterpret_cast<const f32x4*>(egc + 4 * g);
+    MF::frag mf[L::EXP ? 4 : 1][2];
+    if constexpr (L::EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+            mf[ot][0] = load_frag<bf16>(Ms, L::LC, ot * 16, 0);
+            mf[ot][1] = load_frag<bf16>(Ms, L::LC, ot * 16, 32);
+        }
+    }
+    bf16x8 yb[2][NTW];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) yb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
+
+    if constexpr (L::EXP) {
+        // lane holds O[16 ot + c][col0 + 16 ct + 4g + e]
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) {
+                ov[ot][ct] = MF::mma(yb[0][ct], mf[ot][0], ov[ot][ct]);
+                ov[ot][ct] = MF::mma(yb[1][ct], mf[ot][1], ov[ot][ct]);
+            }
+            if (ot * 16 + c < valid) {
+                bf16* orow = orow0 + (size_t)(ot * 16 + c) * ostride + 4 * g;
+#pragma unroll
+                for (int ct = 0; ct < NTW; ++ct) store4<bf16>(orow + ct * 16, ov[ot][ct]);
+            }
+        }
+    }
+
+    // S <- Diag(e^{G_C}) S + K~^T V_new
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt) {
+        const int cur = rt & 1, nxt = cur ^ 1;
+        if (rt + 1 < DK / 16) {
+            kf[nxt][0] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 0);
+            kf[nxt][1] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 32);
+            dv[nxt] = *reinterpret_cast<const f32x4*>(egc + (rt + 1) * 16 + 4 * g);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) {
+            xs[rt][ct] *= dv[cur];
+            xs[rt][ct] = MF::mma(kf[cur][0], yb[0][ct], xs[rt][ct]);
+            xs[rt][ct] = MF::mma(kf[cur][1], yb[1][ct], xs[rt][ct]);
+        }
+    }
+}
+
+// Chain waves and tiles per wave.  EXPAND: the DV/16 value tiles; COMPOSE:
+// the DK/16 tiles of P followed by the DV/16 tiles of R (a wave's tiles are
+// all P or all R since DK/16 is even).
+template <int DK, int DV, int MODE>
+struct Tiles {
+    static constexpr int N = MODE == EXPAND ? DV / 16 : (DK + DV) / 16;
+    static constexpr int NTW = N > 8 ? 2 : 1;
+    static constexpr int NWAVES = (N + NTW - 1) / NTW;
+    static_assert(NWAVES <= 8, "chain waves");
+};
+
+// Right-looking substitution steps for columns I0..I1-1 of a 16x16
+// strictly lower block stored transposed (at[i * 16 + r] = A_ri):
+// x_r -= A_ri x_i for r > i.
+template <int I0, int I1>
+__device__ __forceinline__ void inv_batch(const float* at, float (&x)[SUB]) {
+    f32x4 av[I1 - I0][4];
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int r4 = (i + 1) / 4; r4 < 4; ++r4) av[i - I0][r4] = *reinterpret_cast<const f32x4*>(at + i * SUB + 4 * r4);
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int r4 = (i + 1) / 4; r4 < 4; ++r4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (4 * r4 + e > i) x[4 * r4 + e] -= av[i - I0][r4][e] * x[i];
+}
+
+// ---------------------------------------------------------------------------
+// The chunk's own products, from its tokens in `in`, into LDS.  On return
+// (after a barrier) LDS holds -W, U^T, K~^T, e^{G_C} and, for EXPAND, Q e^G
+// and M.  `in` is refilled with chunk `nx` once its values are consumed.
+//
+//  1  gate, chunk-local running sum of the log2 decay per channel; carries
+//     between row parts through LDS                                  | barrier
+//  2  block reference values G_m(R) from the carries; the decay-scaled
+//     operands k e^{G_r - G_m(R)}, k e^{G_m(R) - G_r}, q e^{G_r - G_m(R)},
+//     (beta k e^G)^T, (beta v)^T, (k e^{G_C - G})^T, q e^G and the
+//     cross-block factors e^{G_m(R) - G_m(I)}                        | barrier
+//  3  A (and M) per 16x16 block pair on MFMA                         | barrier
+//  4a the four diagonal blocks (I + A_RR)^{-1} by substitution      | barrier
+//  4b (I + A) [W | U] = [R_K | R_V] by block forward substitution,
+//     X_R = (I + A_RR)^{-1} (B_R - sum_{J<R} A_RJ X_J); every wave owns
+//     columns of the right-hand side, so the rounds need no barrier  | barrier
+// ---------------------------------------------------------------------------
+template <int DK, int DV, int MODE>
+__device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_min, unsigned char* smem,
+                                      const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                      const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                      const bf16* __restrict__ beta, size_t nx_row0, int nx_valid, int H) {
+    typedef Lay<DK, DV, MODE> L;
+    typedef Mfma<bf16> MF;
+    constexpr bool EXP = L::EXP;
+    constexpr int LDK = L::LDK, LC = L::LC, RP = L::RP, RPV = L::RPV, LB = L::LB, BS = L::BS;
+
+    bf16* KL = reinterpret_cast<bf16*>(smem + L::OFF_KL);   // [C][LDK] k e^{G_r - G_m(R)}
+    bf16* KR = reinterpret_cast<bf16*>(smem + L::OFF_KR);   // [C][LDK] k e^{G_m(R) - G_r}
+    bf16* QL = reinterpret_cast<bf16*>(smem + L::OFF_QL);   // [C][LDK] q e^{G_r - G_m(R)}
+    bf16* Wn = reinterpret_cast<bf16*>(smem + L::OFF_KL);   // [C][LDK] -W, pcol   (phase 4b on)
+    bf16* UT = reinterpret_cast<bf16*>(smem + L::OFF_KR);   // [DV][LU] U^T        (phase 4b on)
+    bf16* RT = reinterpret_cast<bf16*>(smem + L::OFF_RT);   // [DK][LC]
+    bf16* RV = reinterpret_cast<bf16*>(smem + L::OFF_RV);   // [DV][LC]
+    bf16* KGT = reinterpret_cast<bf16*>(smem + L::OFF_KGT); // [DK][LC] pcol
+    bf16* QG = reinterpret_cast<bf16*>(smem + L::OFF_QG);   // [C][LDK] pcol
+    bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);    // [C][LC] pcol
+    float* As = reinterpret_cast<float*>(smem + L::OFF_AS); // [4][BS] diagonal blocks, row stride 16
+    bf16* Ab = reinterpret_cast<bf16*>(smem + L::OFF_AB);   // [6][16][LB] -A_RJ
+    bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);   // [4][16][LB] (I + A_RR)^{-1}
+    float* egc = reinterpret_cast<float*>(smem + L::OFF_EGC);
+    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{G_m(R) - G_m(I)}
+    float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);   // [NPART][DK]
+    float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);   // [C]
+
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+    const int cv0 = 2 * (tid % L::CPV), rv0 = (tid / L::CPV) * RPV;
+
+    // ---- phase 1
+    if (tid < C) bet[tid] = tid < valid ? (float)in.beta : 0.f;
+    const float kg2 = g_min * LOG2E;
+    float G[RP][2], kv[RP][2], qv[EXP ? RP : 1][2];
+    if (valid == C)
+        gate_scan<true, RP, EXP>(in.z, in.k, in.q, kg2, r0, valid, G, kv, qv);
+    else
+        gate_scan<false, RP, EXP>(in.z, in.k, in.q, kg2, r0, valid, G, kv, qv);
+    fetch_zkq<DK, DV, MODE>(in, q, k, z, beta, nx_row0, nx_valid, H);
+    car[part * DK + c0] = G[RP - 1][0];
+    car[part * DK + c0 + 1] = G[RP - 1][1];
+    __syncthreads();
+
+    // ---- phase 2
+    {
+        // carry into this part, block reference values G_m(R') (row 16R'+7
+        // closes part (16R'+8)/RP - 1) and the chunk total G_C
+        float cr[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f}, gm[4][2];
+#pragma unroll
+        for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float t = car[p * DK + c0 + j];
+                if (p < part) cr[j] += t;
+                gC[j] += t;
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+                    if (p == (16 * R + 8) / RP - 1) gm[R][j] = gC[j];
+            }
+        const int R = r0 >> 4;
+        float gmR[2], eGm[2], eCGm[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            gmR[j] = R == 0 ? gm[0][j] : R == 1 ? gm[1][j] : R == 2 ? gm[2][j] : gm[3][j];
+            eGm[j] = __builtin_amdgcn_exp2f(gmR[j]);
+            eCGm[j] = __builtin_amdgcn_exp2f(gC[j] - gmR[j]);
+        }
+        if (part == 0) {
+            egc[c0] = __builtin_amdgcn_exp2f(gC[0]);
+            egc[c0 + 1] = __builtin_amdgcn_exp2f(gC[1]);
+        }
+        if (part < 6) {
+            // pair index p = R'(R'-1)/2 + I', I' < R'
+            const int Rp = part < 1 ? 1 : (part < 3 ? 2 : 3);
+            const int Ip = part - Rp * (Rp - 1) / 2;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float a = gm[0][j], b = gm[0][j];
+#pragma unroll
+                for (int t = 1; t < 4; ++t) {
+                    if (Rp == t) a = gm[t][j];
+                    if (Ip == t) b = gm[t][j];
+                }
+                dsc[part * DK + c0 + j] = __builtin_amdgcn_exp2f(a - b);
+            }
+        }
+        float rk[2][RP], kg[2][RP];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+            float kl[2], kR[2], ql[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float el = G[i][j] + cr[j] - gmR[j];
+                const float left = __builtin_amdgcn_exp2f(el), right = __builtin_amdgcn_exp2f(-el);
+                kl[j] = kv[i][j] * left;
+                kR[j] = kv[i][j] * right;
+                if constexpr (EXP) ql[j] = qv[i][j] * left;
+                rk[j][i] = kl[j] * eGm[j];
+                kg[j][i] = kR[j] * eCGm[j];
+            }
+            store2<bf16>(KL + r * LDK + c0, kl[0], kl[1]);
+            store2<bf16>(KR + r * LDK + c0, kR[0], kR[1]);
+            if constexpr (EXP) {
+                store2<bf16>(QL + r * LDK + c0, ql[0], ql[1]);
+                store2<bf16>(QG + r * LDK + pcol(c0), ql[0] * eGm[0], ql[1] * eGm[1]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < RP; i += 4) {
+                store4p(RT + (c0 + j) * LC + r0 + i, rk[j][i], rk[j][i + 1], rk[j][i + 2], rk[j][i + 3]);
+                store4p(KGT + (c0 + j) * LC + pcol(r0 + i), kg[j][i], kg[j][i + 1], kg[j][i + 2], kg[j][i + 3]);
+            }
+        // V^T as loaded (rows past the end are multiplied by beta = 0 through
+        // the beta-scaled diagonal inverses, so their values do not matter)
+#pragma unroll
+        for (int i = 0; i < RPV; i += 4)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                *reinterpret_cast<bf16x4*>(RV + (cv0 + j) * LC + rv0 + i) =
+                    bf16x4{in.v[i][j], in.v[i + 1][j], in.v[i + 2][j], in.v[i + 3][j]};
+        fetch_v<DK, DV, MODE>(in, v, nx_row0, nx_valid, H);
+    }
+    __syncthreads();
+
+    // ---- phase 3: A (and M) per 16x16 block pair, computed transposed so each
+    //      lane holds four consecutive key indices i of one row r
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int R = kSegPairs[w][j][0], I = kSegPairs[w][j][1];
+        if (R < 0) break;
+        f32x4 accA = zero4(), accM = zero4();
+        const float* dv = dsc + (R * (R - 1) / 2 + I) * DK;
+#pragma unroll
+        for (int kk = 0; kk < DK; kk += MF::KSTEP) {
+            MF::frag ak = load_frag<bf16>(KR, LDK, I * SUB, kk);
+            if (I < R) {
+                float t[MF::KPL];
+                MF::to_floats(ak, t);
+                const int cc = kk + (l >> 4) * MF::KPL;
+#pragma unroll
+                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] *= dv[cc + jj];
+                ak = MF::from_floats(t);
+            }
+            accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
+            if constexpr (EXP) accM = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM);
+        }
+        const int rr = l & 15, r = R * SUB + rr;
+        const int ii = 4 * (l >> 4), i0 = I * SUB + ii;
+        if (I == R) {
+            // beta_r A_ri, strictly lower, stored transposed: As[R][i][r]
+            const float br = bet[r];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) As[R * BS + (ii + e) * SUB + rr] = (ii + e < rr) ? br * accA[e] : 0.f;
+        } else {
+            // -A~_RI without the row factor beta_r (it is folded into the inverses)
+            store4p(Ab + ((R * (R - 1) / 2 + I) * SUB + rr) * LB + ii, -accA[0], -accA[1], -accA[2], -accA[3]);
+        }
+        if constexpr (EXP) {
+            float mv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mv[e] = (i0 + e <= r) ? accM[e] : 0.f;
+            store4p(Ms + r * LC + pcol(i0), mv[0], mv[1], mv[2], mv[3]);
+        }
+    }
+    if constexpr (EXP) {
+        // strictly upper blocks of M are zero: waves 2..7 one block each
+        if (w >= 2) {
+            const int p = w - 2;
+            const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+            const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+            store4p(Ms + (R * SUB + (l & 15)) * LC + pcol(I * SUB + 4 * (l >> 4)), 0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    // ---- phase 4a: waves 0 and 1 invert the two diagonal blocks they have
+    //      just formed, D'_b = (I + beta_b A~_bb)^{-1} diag(beta_b), lane =
+    //      (block, column), by right-looking substitution down the column
+    if (w < 2) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's As stores
+        const int b = kSegPairs[w][(l >> 4) & 1][0], col = l & 15;
+        const float* at = As + b * BS;       // at[i * 16 + r] = beta_r A~_ri
+        float x[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) x[r] = (r == col) ? 1.f : 0.f;
+        // columns of A in three batches; a batch's 4-row pieces below the
+        // diagonal are all loaded before they are used
+        inv_batch<0, 3>(at, x);
+        inv_batch<3, 7>(at, x);
+        inv_batch<7, 15>(at, x);
+        if (l < 32) {
+            const float bc = bet[b * SUB + col];
+            bf16* d = Db + b * SUB * LB + col;
+#pragma unroll
+            for (int r = 0; r < SUB; ++r) d[r * LB] = (bf16)(x[r] * bc);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 4b: block substitution on 16-column tiles of [R_K | R_V]
+    //      (tile t < DK/16: W columns 16t..; else U columns), tiles w, w+8
+    //      advanced together
+    {
+        constexpr int NTT = (DK + DV) / 16;
+        constexpr int NS = NTT > 8 ? 2 : 1;
+        const int g = l >> 4, c = l & 15;
+        bf16x4 ab[6], db[4];
+#pragma unroll
+        for (int p = 0; p < 6; ++p) ab[p] = *reinterpret_cast<const bf16x4*>(Ab + (p * SUB + c) * LB + 4 * g);
+#pragma unroll
+        for (int R = 0; R < 4; ++R) db[R] = *reinterpret_cast<const bf16x4*>(Db + (R * SUB + c) * LB + 4 * g);
+        bool act[NS], isw[NS];
+        int col[NS];
+        f32x4 rhs[NS][4];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int t = min(w + 8 * s, NTT - 1);
+            act[s] = w + 8 * s < NTT;
+            isw[s] = t < DK / 16;
+            col[s] = isw[s] ? 16 * t + c : 16 * (t - DK / 16) + c;
+            const bf16* src = (isw[s] ? RT : RV) + col[s] * LC + 4 * g;
+#pragma unroll
+            for (int R = 0; R < 4; ++R) rhs[s][R] = load4<bf16>(src + R * SUB);
+        }
+        bf16x4 xb[NS][4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                f32x4 acc = rhs[s][R];
+#pragma unroll
+                for (int J = 0; J < R; ++J) acc = mma16(ab[R * (R - 1) / 2 + J], xb[s][J], acc);
+                const f32x4 x = mma16(db[R], to_bf4(acc), zero4());
+                xb[s][R] = to_bf4(x);
+                if (act[s]) {
+                    if (isw[s]) {
+                        // -W[16R + 4g + e][col], contraction index col stored at pcol(col)
+                        bf16* wp = Wn + (R * SUB + 4 * g) * LDK + pcol(col[s]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) wp[e * LDK] = (bf16)(-x[e]);
+                    } else {
+                        store4<bf16>(UT + col[s] * L::LU + R * SUB + 4 * g, x);
+                    }
+                }
+            }
+    }
+    __syncthreads();
+}
+
+// Grid: one workgroup per (segment, chain), chain index fastest.  Segment s
+// covers chunks [s L, min(s L + L, NC)).
+//   EXPAND : xin  entry states [nseg][B*H][DK][DV] (NULL = zeros);
+//            xo0  final state [B*H][DK][DV] (NULL = skip; used when nseg == 1).
+//   COMPOSE: xo0  P [nseg][B*H][DK][DK],  xo1  R [nseg][B*H][DK][DV].
+template <int DK, int DV, int MODE>
+__global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                  const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                  const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
+                                                  int L, int nchain, const float* __restrict__ xin,
+                                                  float* __restrict__ xo0, float* __restrict__ xo1,
+                                                  bf16* __restrict__ o) {
+    typedef Tiles<DK, DV, MODE> TL;
+    constexpr int NTW = TL::NTW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int seg = blockIdx.x / nchain;
+    const size_t bh = blockIdx.x % nchain;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int l = lane_id(), w = wave_id();
+    const int n0 = seg * L, n1 = min(NC, n0 + L);
+    const int t0w = w * NTW;                    // first tile of this wave
+    const bool chain_wave = w < TL::NWAVES;
+    const bool ptile = MODE == COMPOSE && t0w < DK / 16;
+    const int col0 = 16 * t0w - (MODE == COMPOSE && !ptile ? DK : 0);   // first column in P, R or S
+    const int NX = (MODE == COMPOSE && ptile) ? DK : DV;                // columns of this wave's matrix
+
+    f32x4 xs[DK / 16][NTW];
+    const size_t xblk = ((size_t)seg * nchain + bh) * DK;
+#pragma unroll
+    for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = rt * 16 + 4 * (l >> 4) + e, col = col0 + ct * 16 + (l & 15);
+                float x = 0.f;
+                if constexpr (MODE == EXPAND) x = (xin && chain_wave) ? xin[(xblk + row) * DV + col] : 0.f;
+                if constexpr (MODE == COMPOSE) x = (ptile && row == col) ? 1.f : 0.f;
+                xs[rt][ct][e] = x;
+            }
+
+    In<DK, DV, MODE> in;
+    {
+        const size_t row0 = ((size_t)b * T + (size_t)n0 * C) * H + h;
+        const int valid = min(C, T - n0 * C);
+        fetch_zkq<DK, DV, MODE>(in, q, k, z, beta, row0, valid, H);
+        fetch_v<DK, DV, MODE>(in, v, row0, valid, H);
+    }
+    const size_t ostride = (size_t)H * DV;
+    const bool hasu = MODE == EXPAND || !ptile;
+    auto orow = [&](int n) { return o + (((size_t)b * T + (size_t)n * C) * H + h) * DV + col0; };
+    for (int n = n0; n < n1; ++n) {
+        const int valid = min(C, T - n * C);
+        const int nn = min(n + 1, n1 - 1);      // prefetch target, clamped (unconditional)
+        intra<DK, DV, MODE>(in, valid, g_min, smem, q, k, v, z, beta, ((size_t)b * T + (size_t)nn * C) * H + h,
+                            min(C, T - nn * C), H);
+        // the next chunk's phase 1 writes neither the chain operands nor
+        // anything the chain reads: no barrier after the chain step
+        if (chain_wave) chain_step<DK, DV, MODE, NTW>(xs, hasu, col0, smem, orow(n), valid, ostride);
+    }
+
+    float* xo = MODE == COMPOSE ? (ptile ? xo0 : xo1) : xo0;
+    if (chain_wave && xo) {
+        const size_t ob = MODE == COMPOSE ? xblk : bh * DK;
+#pragma unroll
+        for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = rt * 16 + 4 * (l >> 4) + e, col = col0 + ct * 16 + (l & 15);
+                    xo[(ob + row) * NX + col] = xs[rt][ct][e];
+                }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.  Segments: one per chain (a single EXPAND pass from s0) when
+// there are enough chains to fill the chip; otherwise about 1024 segments in
+// all, of at least MIN_L chunks.
+constexpr int MIN_L = 8;
+constexpr int TARGET_WG = 1024;
+constexpr int FILL_CHAINS = 256;
+
+struct Plan {
+    int nseg, L;
+    size_t p_off, r_off, e_off, total;
+};
+
+static Plan plan(int B, int T, int H, int DK, int DV) {
+    Plan p{};
+    const int NC = (T + C - 1) / C;
+    const long nchain = (long)B * H;
+    int nseg = 1;
+    if (nchain < FILL_CHAINS && NC >= 2 * MIN_L) {
+        const long want = (TARGET_WG + nchain - 1) / nchain;
+        nseg = (int)(want < NC / MIN_L ? want : NC / MIN_L);
+        if (nseg < 1) nseg = 1;
+    }
+    p.L = (NC + nseg - 1) / nseg;
+    p.nseg = nseg > 1 ? (NC + p.L - 1) / p.L : 1;
+    p.p_off = p.r_off = p.e_off = p.total = 0;
+    if (p.nseg > 1) {
+        p.r_off = (size_t)p.nseg * nchain * DK * DK * 4;
+        p.e_off = p.r_off + (size_t)p.nseg * nchain * DK * DV * 4;
+        p.total = p.e_off + (size_t)p.nseg * nchain * DK * DV * 4;
+    }
+    return p;
+}
+
+template <class K>
+static hipError_t set_lds(K kernel, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int DK, int DV>
+static hipError_t launch_t(const ChunkArgs& a) {
+    const int NC = (a.T + C - 1) / C;
+    const int nchain = a.B * a.H;
+    hipStream_t st = (hipStream_t)a.stream;
+    const Plan p = plan(a.B, a.T, a.H, DK, DV);
+    const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v, *z = (const bf16*)a.z,
+               *beta = (const bf16*)a.beta;
+    typedef Lay<DK, DV, EXPAND> LE;
+    typedef Lay<DK, DV, COMPOSE> LCm;
+    hipError_t err;
+    if ((err = set_lds(seg_kernel<DK, DV, EXPAND>, LE::LDS)) != hipSuccess) return err;
+    if (p.nseg == 1) {
+        hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(nchain), dim3(NTH), LE::LDS, st, q, k, v, z, beta,
+                           a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o);
+        return hipGetLastError();
+    }
+    unsigned char* ws = (unsigned char*)a.workspace;
+    float* Pb = reinterpret_cast<float*>(ws + p.p_off);
+    float* Rb = reinterpret_cast<float*>(ws + p.r_off);
+    float* Eb = reinterpret_cast<float*>(ws + p.e_off);
+    if ((err = set_lds(seg_kernel<DK, DV, COMPOSE>, LCm::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((seg_kernel<DK, DV, COMPOSE>), dim3(p.nseg * nchain), dim3(NTH), LCm::LDS, st, q, k, v, z,
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream)) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(p.nseg * nchain), dim3(NTH), LE::LDS, st, q, k, v, z,
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr,
+                       (bf16*)a.o);
+    return hipGetLastError();
+}
+
+}  // namespace segk
+
+size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) { return segk::plan(B, T, H, dk, dv).total; }
+
+hipError_t launch_chunk_seg(const ChunkArgs& a) {
+    if (a.dk == 128 && a.dv == 128) return segk::launch_t<128, 128>(a);
+    if (a.dk == 128 && a.dv == 64) return segk::launch_t<128, 64>(a);
+    if (a.dk == 64 && a.dv == 128) return segk::launch_t<64, 128>(a);
+    return segk::launch_t<64, 64>(a);
+}
+
+}  // namespace kda

@@ -85,7 +85,14 @@ const char* kda_version(void);
  *                                        skip; may equal s0 (in place)
  *   workspace, workspace_bytes           device scratch of at least
  *                                        kda_chunk_fwd_workspace_bytes()
+ *                                        bytes; may be NULL when that is 0
  * The result is deterministic: identical inputs give identical bits.
+ *
+ * Workspace: bf16 sequences split into segments when there are fewer than
+ * 256 (batch, head) chains (the per-segment transition P, input term R and
+ * entry state, fp32); a single segment needs no workspace.  fp32 sequences
+ * also stage the per-chunk products (W, U^T, M, q e^G, (k e^{G_C-G})^T,
+ * e^{G_C}).
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                      kda_dtype dt);

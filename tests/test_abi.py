@@ -54,17 +54,24 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # bf16, d = 128: W, U, M, Q*e^G, (K*e^{G_C-G})^T in bf16 plus e^{G_C} fp32 per chunk
-    per = (64 * 128 * 4 + 64 * 64) * 2 + 128 * 4
-    # 32768 tokens = 512 chunks: two levels over 32 segments of 16 chunks, which adds the
-    # per-segment transition P (d_k x d_k), input term R and entry state (d_k x d_v), fp32
+    # bf16: 32 chains of 512 chunks -> 32 segments of 16 chunks each; per
+    # segment and chain the transition P (d_k x d_k), the input term R and
+    # the entry state (d_k x d_v), fp32
     seg = 32 * 32 * (128 * 128 + 2 * 128 * 128) * 4
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == 32 * 512 * per + seg
-    # below 32 chunks a single level: no segment buffers
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 31 * per
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 65, 1, 128, 128, 64, BF16) == 2 * per
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == seg
+    # one chain of 31 chunks: 3 segments of at least 8 chunks
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 3 * 3 * 128 * 128 * 4
+    # below 16 chunks, or with 256 chains or more, a single segment: no workspace
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 15 * 64, 1, 128, 128, 64, BF16) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, BF16) == 0
+    # 4 chains of 64 chunks: 8 segments of 8 chunks
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 4096, 4, 64, 64, 64, BF16) == 8 * 4 * (64 * 64 + 2 * 64 * 64) * 4
+    # fp32: per-chunk W, U^T, M, Q*e^G, (K*e^{G_C-G})^T plus e^{G_C}
     per32 = (64 * 64 * 4 + 64 * 64) * 4 + 64 * 4
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32) == 4 * per32
+    per = (64 * 128 * 4 + 64 * 64) * 4 + 128 * 4
+    seg32 = 32 * 32 * (128 * 128 + 2 * 128 * 128) * 4
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, F32) == 32 * 512 * per + seg32
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, F32) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, F32) == 0
     assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2
@@ -78,7 +85,9 @@ def chunk(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, s0=None, o=P, sf=P, B=1, 
 
 
 def test_chunk_fwd_rejects_bad_arguments(lib):
-    need = lib.kda_chunk_fwd_workspace_bytes(1, 128, 2, 128, 128, 64, BF16)
+    # fp32 always stages per-chunk products, so these shapes need a workspace
+    need = lib.kda_chunk_fwd_workspace_bytes(1, 128, 2, 128, 128, 64, F32)
+    assert need > 0
     assert chunk(lib, q=None, ws=P, ws_bytes=need) == NULL
     assert chunk(lib, o=None, ws=P, ws_bytes=need) == NULL
     assert chunk(lib, dk=96) == UNSUP
@@ -92,8 +101,13 @@ def test_chunk_fwd_rejects_bad_arguments(lib):
     assert chunk(lib, g_min=1.0) == ARG
     assert chunk(lib, g_min=float("nan")) == ARG
     assert chunk(lib, g_min=float("-inf")) == ARG
-    assert chunk(lib, ws=None, ws_bytes=0) == WS
-    assert chunk(lib, ws=P, ws_bytes=need - 1) == WS
+    assert chunk(lib, ws=None, ws_bytes=0, dt=F32) == WS
+    assert chunk(lib, ws=P, ws_bytes=need - 1, dt=F32) == WS
+    # bf16 with few chains over a long sequence: segment buffers are needed
+    need_bf = lib.kda_chunk_fwd_workspace_bytes(1, 4096, 2, 128, 128, 64, BF16)
+    assert need_bf > 0
+    assert chunk(lib, T=4096, ws=None, ws_bytes=0) == WS
+    assert chunk(lib, T=4096, ws=P, ws_bytes=need_bf - 1) == WS
     assert chunk(lib, k=MIS, ws=P, ws_bytes=need) == ALIGN
     assert chunk(lib, s0=MIS, ws=P, ws_bytes=need) == ALIGN
     assert chunk(lib, ws=MIS, ws_bytes=need) == ALIGN
