@@ -879,7 +879,7 @@ size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16) {
 template <int DK, int DV>
 static hipError_t launch_scan_t(const float* P, const float* R, const float* s0, float* Sent, float* s_final,
                                 int nseg, int nchain, hipStream_t st) {
-    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, 32>), dim3((DV / 32) * nchain), dim3(256), 0, st, P, R, s0, Sent,
+    hipLaunchKernelGGL((seg_scan_kernel<DK, DV, 16>), dim3((DV / 16) * nchain), dim3(256), 0, st, P, R, s0, Sent,
                        s_final, nseg, nchain);
     return hipGetLastError();
 }

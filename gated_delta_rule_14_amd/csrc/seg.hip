@@ -386,7 +386,10 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);   // [C]
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
-    const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+    __builtin_assume(w >= 0 && w < NTH / 64);
+    // row part of this thread: one per wave when a wave spans all key channels
+    const int part = L::CP == 64 ? w : tid / L::CP;
+    const int c0 = 2 * (tid % L::CP), r0 = part * RP;
     const int cv0 = 2 * (tid % L::CPV), rv0 = (tid / L::CPV) * RPV;
 
     // ---- phase 1
@@ -628,6 +631,7 @@ __global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, co
     const size_t bh = blockIdx.x % nchain;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int l = lane_id(), w = wave_id();
+    __builtin_assume(w >= 0 && w < NTH / 64);
     const int n0 = seg * L, n1 = min(NC, n0 + L);
     const int t0w = w * NTW;                    // first tile of this wave
     const bool chain_wave = w < TL::NWAVES;
@@ -686,11 +690,131 @@ __global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, co
 }
 
 // ---------------------------------------------------------------------------
+// Scan over segments for one chain and 16 state columns:
+//   Sent[j] = S_j,  S_{j+1} = P_j S_j + R_j,  s_final = S_nseg.
+// The products run on bf16 MFMA with both operands split into a high and a
+// low bf16 part (x = hi + lo, |lo| <= 2^-9 |x|) and the three significant
+// cross products accumulated in fp32, which keeps about 16 significant bits
+// of P and S.  Wave w owns state rows 32w..32w+31; P_j's rows for the next
+// segment are prefetched while the current one is applied.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        hi[i] = (bf16)a[i];
+        hi[i + 4] = (bf16)b[i];
+        lo[i] = (bf16)(a[i] - (float)hi[i]);
+        lo[i + 4] = (bf16)(b[i] - (float)hi[i + 4]);
+    }
+}
+
+template <int DK, int DV>
+struct ScanIn {
+    f32x4 p[2][DK / 32][2];   // P rows (32w + 16 rb + l%16), columns 32 kb + 8 (l/16) .. +7
+    float r[2][4];            // R rows 32w + 16 rb + 4 (l/16) + e, column col0 + l%16
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void scan_load(ScanIn<DK, DV>& in, const float* __restrict__ P, const float* __restrict__ R,
+                                          int j, int nchain, size_t bh, int col0, int w, int l) {
+    const size_t blk = ((size_t)j * nchain + bh) * DK;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float* prow = P + (blk + 32 * w + 16 * rb + (l & 15)) * DK + 8 * (l >> 4);
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            in.p[rb][kb][0] = *reinterpret_cast<const f32x4*>(prow + 32 * kb);
+            in.p[rb][kb][1] = *reinterpret_cast<const f32x4*>(prow + 32 * kb + 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            in.r[rb][e] = R[(blk + 32 * w + 16 * rb + 4 * (l >> 4) + e) * DV + col0 + (l & 15)];
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void scan_apply(f32x4 (&acc)[2], const ScanIn<DK, DV>& in, float* __restrict__ Sent,
+                                           float* St, int j, int nchain, size_t bh, int col0, int w, int l) {
+    constexpr int LS = DK + 4;
+    typedef Mfma<bf16> MF;
+    const size_t blk = ((size_t)j * nchain + bh) * DK;
+    const int c = l & 15, g = l >> 4;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = 32 * w + 16 * rb + 4 * g;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Sent[(blk + row + e) * DV + col0 + c] = acc[rb][e];
+        *reinterpret_cast<f32x4*>(St + c * LS + row) = acc[rb];
+    }
+    __syncthreads();
+    f32x4 nacc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) nacc[rb] = f32x4{in.r[rb][0], in.r[rb][1], in.r[rb][2], in.r[rb][3]};
+#pragma unroll
+    for (int kb = 0; kb < DK / 32; ++kb) {
+        bf16x8 shi, slo;
+        split8(*reinterpret_cast<const f32x4*>(St + c * LS + 32 * kb + 8 * g),
+               *reinterpret_cast<const f32x4*>(St + c * LS + 32 * kb + 8 * g + 4), shi, slo);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            bf16x8 phi, plo;
+            split8(in.p[rb][kb][0], in.p[rb][kb][1], phi, plo);
+            nacc[rb] = MF::mma(phi, shi, nacc[rb]);
+            nacc[rb] = MF::mma(plo, shi, nacc[rb]);
+            nacc[rb] = MF::mma(phi, slo, nacc[rb]);
+        }
+    }
+    acc[0] = nacc[0];
+    acc[1] = nacc[1];
+    __syncthreads();
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void scan_x3_kernel(const float* __restrict__ P, const float* __restrict__ R,
+                                                      const float* __restrict__ s0, float* __restrict__ Sent,
+                                                      float* __restrict__ s_final, int nseg, int nchain) {
+    static_assert(DK == 128, "four waves of 32 state rows");
+    constexpr int LS = DK + 4;
+    __shared__ __align__(16) float St[16 * LS];
+    const int tile = blockIdx.x / nchain;
+    const size_t bh = blockIdx.x % nchain;
+    const int l = lane_id(), w = wave_id();
+    const int col0 = tile * 16;
+    f32x4 acc[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 32 * w + 16 * rb + 4 * (l >> 4) + e;
+            acc[rb][e] = s0 ? s0[(bh * DK + row) * DV + col0 + (l & 15)] : 0.f;
+        }
+    ScanIn<DK, DV> a, b;
+    scan_load<DK, DV>(a, P, R, 0, nchain, bh, col0, w, l);
+    int j = 0;
+    for (; j + 2 <= nseg; j += 2) {
+        scan_load<DK, DV>(b, P, R, j + 1, nchain, bh, col0, w, l);
+        scan_apply<DK, DV>(acc, a, Sent, St, j, nchain, bh, col0, w, l);
+        scan_load<DK, DV>(a, P, R, min(j + 2, nseg - 1), nchain, bh, col0, w, l);
+        scan_apply<DK, DV>(acc, b, Sent, St, j + 1, nchain, bh, col0, w, l);
+    }
+    if (j < nseg) scan_apply<DK, DV>(acc, a, Sent, St, j, nchain, bh, col0, w, l);
+    if (s_final) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 32 * w + 16 * rb + 4 * (l >> 4) + e;
+                s_final[(bh * DK + row) * DV + col0 + (l & 15)] = acc[rb][e];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.  Segments: one per chain (a single EXPAND pass from s0) when
 // there are enough chains to fill the chip; otherwise about 1024 segments in
 // all, of at least MIN_L chunks.
 constexpr int MIN_L = 8;
-constexpr int TARGET_WG = 1024;
+constexpr int TARGET_WG = 256;
 constexpr int FILL_CHAINS = 256;
 
 struct Plan {
@@ -750,8 +874,14 @@ static hipError_t launch_t(const ChunkArgs& a) {
     hipLaunchKernelGGL((seg_kernel<DK, DV, COMPOSE>), dim3(p.nseg * nchain), dim3(NTH), LCm::LDS, st, q, k, v, z,
                        beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if ((err = launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream)) != hipSuccess)
-        return err;
+    if constexpr (DK == 128) {
+        hipLaunchKernelGGL((scan_x3_kernel<DK, DV>), dim3((DV / 16) * nchain), dim3(256), 0, st, (const float*)Pb,
+                           (const float*)Rb, a.s0, Eb, a.s_final, p.nseg, nchain);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    } else {
+        if ((err = launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream)) != hipSuccess)
+            return err;
+    }
     hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(p.nseg * nchain), dim3(NTH), LE::LDS, st, q, k, v, z,
                        beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr,
                        (bf16*)a.o);

@@ -54,10 +54,11 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # bf16: 32 chains of 512 chunks -> 32 segments of 16 chunks each; per
-    # segment and chain the transition P (d_k x d_k), the input term R and
-    # the entry state (d_k x d_v), fp32
-    seg = 32 * 32 * (128 * 128 + 2 * 128 * 128) * 4
+    # bf16: 32 chains of 512 chunks -> 8 segments of 64 chunks each (256
+    # segments in all, one per compute unit); per segment and chain the
+    # transition P (d_k x d_k), the input term R and the entry state
+    # (d_k x d_v), fp32
+    seg = 8 * 32 * (128 * 128 + 2 * 128 * 128) * 4
     assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == seg
     # one chain of 31 chunks: 3 segments of at least 8 chunks
     assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 3 * 3 * 128 * 128 * 4

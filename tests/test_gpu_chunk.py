@@ -128,8 +128,9 @@ def test_prefill_then_decode_handoff():
 
 
 # ------------------------------------------------------------------ two levels
-# From 32 chunks on, the prefill composes per-segment transitions (16 chunks
-# each), scans them, and expands outputs from the segment entry states.
+# With few chains and enough chunks the prefill splits each sequence into
+# segments (bf16: at least 8 chunks each; fp32: 16), composes each segment's
+# transition, scans them, and expands outputs from the segment entry states.
 @pytest.mark.parametrize("T", [2048, 2113, 3007])
 @pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
 def test_two_level_ragged(T, dtype, tag):
@@ -140,8 +141,8 @@ def test_two_level_ragged(T, dtype, tag):
 @pytest.mark.parametrize("z_mean", [-6.0, -8.0])
 @pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
 def test_two_level_long_memory(z_mean, dtype, tag):
-    """Slow decay across 60 chunks / 4 segments: the segment transitions and
-    the scan carry most of the outputs."""
+    """Slow decay across 60 chunks split into segments: the segment
+    transitions and the scan carry most of the outputs."""
     x = ki.prefill_inputs(2, 3840, 2, 128, 128, dtype, seed=31, device=DEV, z_mean=z_mean, s0_var=0.01)
     check(x, tag, label=f"two-level z~N({z_mean},1)")
 
@@ -194,7 +195,7 @@ def test_train_8x8k_full_size_sampled():
 def test_long_1m_full_size_sampled():
     """B=1, T=1,048,576, H=32, d=128, bf16, z ~ N(2,1), S0 = 0, then the
     RMSNorm x gate epilogue: the long-context workload at full size (16,384
-    chunks, 1,024 segments, all heads launched); the oracle runs one sampled
+    chunks per head in 8 segments, all heads launched); the oracle runs one sampled
     head over all tokens, and the epilogue on sampled rows."""
     import oracle
     from helpers import host
