@@ -8,11 +8,21 @@
 //
 //  * gate_kernel: one row of d_v values per 1..2 dozen lanes, 16-byte loads,
 //    shuffle reduction of the sum of squares; HBM-bound elementwise work.
+//  * the projection out (M x N) = y (M x K) . W (N x K)^T is a plain bf16
+//    GEMM with fp32 accumulation: it runs on hipBLASLt (one library handle per
+//    device, one heuristic query per shape, both cached), with a library
+//    workspace appended to the y buffer.  When the library offers no
+//    algorithm for a shape, proj_gemm_kernel below computes it.
 //  * proj_gemm_kernel: out (M x N) = y (M x K) . W (N x K)^T in bf16 with
 //    fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Both operands are
 //    K-contiguous, which is the native operand layout of the MFMA, so tiles
 //    go global -> registers -> LDS without any transpose.  128x128 block
 //    tile, 64-deep K stages, double-buffered LDS, 4 waves of 64x64.
+#include <hipblaslt/hipblaslt.h>
+
+#include <mutex>
+#include <vector>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -157,11 +167,77 @@ static hipError_t launch_gate(const void* o, const void* gate, float eps, void* 
     return hipGetLastError();
 }
 
+// Library workspace for the projection GEMM, after the y buffer.
+constexpr size_t LT_WS = (size_t)32 << 20;
+
+static size_t y_bytes(int B, int T, int H, int dv) { return ((size_t)B * T * H * dv * 2 + 255) / 256 * 256; }
+
 size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj) {
     (void)d_model; (void)bf16;
     if (!proj) return 0;
-    return (size_t)B * T * H * dv * 2;   // gated activations y, bf16
+    return y_bytes(B, T, H, dv) + LT_WS;   // gated activations y (bf16), then the GEMM's workspace
 }
+
+namespace {
+// One hipBLASLt handle per device and the chosen algorithm per (device, M,
+// N, K), created on first use.  Column-major view: out^T (N x M) =
+// W (stored K x N, transposed) . y^T (stored K x M).
+struct LtPlan {
+    int dev, M, N, K;
+    bool ok;
+    hipblasLtMatmulDesc_t op;
+    hipblasLtMatrixLayout_t a, b, c;
+    hipblasLtMatmulAlgo_t algo;
+    size_t ws;
+};
+struct LtState {
+    std::mutex mu;
+    hipblasLtHandle_t handle[64] = {};
+    std::vector<LtPlan> plans;
+};
+LtState& lt_state() {
+    static LtState s;
+    return s;
+}
+
+const LtPlan* lt_plan(int dev, int M, int N, int K) {
+    LtState& s = lt_state();
+    std::lock_guard<std::mutex> lock(s.mu);
+    for (const LtPlan& p : s.plans)
+        if (p.dev == dev && p.M == M && p.N == N && p.K == K) return p.ok ? &p : nullptr;
+    LtPlan p{dev, M, N, K, false, nullptr, nullptr, nullptr, nullptr, {}, 0};
+    if (dev < 0 || dev >= 64) return nullptr;
+    if (!s.handle[dev] && hipblasLtCreate(&s.handle[dev]) != HIPBLAS_STATUS_SUCCESS) s.handle[dev] = nullptr;
+    hipblasLtHandle_t h = s.handle[dev];
+    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    const uint64_t wsmax = LT_WS;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    hipblasLtMatmulHeuristicResult_t res{};
+    int count = 0;
+    bool ok = h && hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.c, HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax,
+                                                    sizeof(wsmax)) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.a, p.b, p.c, p.c, pref, 1, &res, &count) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              count > 0 && res.workspaceSize <= LT_WS;
+    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+    if (ok) {
+        p.algo = res.algo;
+        p.ws = res.workspaceSize;
+    }
+    p.ok = ok;
+    s.plans.push_back(p);
+    return ok ? &s.plans.back() : nullptr;
+}
+}  // namespace
 
 hipError_t launch_out_gate(const GateArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
@@ -174,6 +250,16 @@ hipError_t launch_out_gate(const GateArgs& a) {
     if (err != hipSuccess) return err;
     const int M = a.B * a.T, N = a.d_model, K = a.H * a.dv;
     if (M == 0) return hipSuccess;
+    int dev = 0;
+    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
+    if (const LtPlan* p = lt_plan(dev, M, N, K)) {
+        const float one = 1.f, zero = 0.f;
+        void* lws = (unsigned char*)a.workspace + y_bytes(a.B, a.T, a.H, a.dv);
+        const hipblasStatus_t r =
+            hipblasLtMatmul(lt_state().handle[dev], p->op, &one, a.w, p->a, a.workspace, p->b, &zero, a.y, p->c, a.y,
+                            p->c, &p->algo, lws, p->ws, st);
+        return r == HIPBLAS_STATUS_SUCCESS ? hipGetLastError() : hipErrorLaunchFailure;
+    }
     dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM);
     hipLaunchKernelGGL(proj_gemm_kernel, grid, dim3(256), 0, st, (const bf16*)a.workspace,
                        (const bf16*)a.w, (bf16*)a.y, M, N, K);

@@ -100,6 +100,12 @@ def recurrent_step(q, k, v, z, beta, g_min, state, *, o=None):
     return o
 
 
+def out_gate_workspace_bytes(B, T, H, dv, d_model, dtype, with_projection):
+    return int(lib().kda_out_gate_workspace_bytes(B, T, H, dv, d_model,
+                                                  KDA_BF16 if dtype == torch.bfloat16 else KDA_F32,
+                                                  int(bool(with_projection))))
+
+
 def out_gate(o, gate, eps, w=None, *, y=None, workspace=None):
     """RMSNorm over each head's dv values x sigmoid(gate), heads concatenated;
     projected by w (d_model, H*dv) when given.  o, gate: (B,T,H,dv)."""

@@ -133,8 +133,11 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  *   w         (d_model, H*dv) bf16, or NULL for no projection
  *   y         (B, T, H*dv) dtype dt when w is NULL,
  *             (B, T, d_model) dtype dt otherwise (written)
- *   workspace kda_out_gate_workspace_bytes() bytes (0 when w is NULL)
- * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.
+ *   workspace kda_out_gate_workspace_bytes() bytes (0 when w is NULL): the
+ *             gated activations y and the projection GEMM's scratch
+ * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.  The
+ * projection runs on hipBLASLt (bf16 inputs, fp32 accumulation); a shape the
+ * library has no algorithm for runs on libkda's own GEMM kernel.
  */
 size_t kda_out_gate_workspace_bytes(int B, int T, int H, int dv, int d_model, kda_dtype dt,
                                     int with_projection);

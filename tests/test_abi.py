@@ -75,7 +75,8 @@ def test_workspace_sizes(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, F32) == 32 * 512 * per + seg32
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, F32) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, F32) == 0
-    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2
+    # gated activations y (bf16), then 32 MiB for the projection GEMM's library workspace
+    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2 + (32 << 20)
     assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 0, BF16, 0) == 0
 
 
