@@ -23,11 +23,13 @@
 // vertically adjacent accumulator tiles therefore hold, in each lane, exactly
 // the eight values of a B fragment, up to an order of the contraction index
 // inside each 32-block.  That order is fixed once (pcol below), and every
-// LDS operand that is contracted against accumulator-held data (W, Q e^G and
-// M against the state or V_new; (K e^{G_C-G})^T against V_new) is stored with
-// its contraction columns in the same order.  So V_new = U - W S, the outputs
-// and the state update read only the shared per-chunk operands from LDS; the
-// state and V_new never leave the registers of the wave that owns them.
+// LDS operand that is contracted against accumulator-held data (K e^G and
+// Q e^G against the state; T' against Z; M against V_new; (K e^{G_C-G})^T
+// against V_new) is stored with its contraction columns in the same order.
+// So Z = V - K e^G S, V_new = T' Z (which is U - W S, with
+// T' = (I + A)^{-1} diag(beta)), the outputs and the state update read only
+// the shared per-chunk operands from LDS; the state, Z and V_new never
+// leave the registers of the wave that owns them.
 //
 // Overflow handling of the decay factors is that of the fp32 path: A and M
 // per 16x16 block pair with reference rows m(R) = 16R + 7, decay exponents in
@@ -66,16 +68,14 @@ struct Lay {
     static constexpr int RPV = C / (NTH / CPV);
     static constexpr int LDK = DK + 8;           // (C x DK) bf16 tiles
     static constexpr int LC = C + 8;             // (d x C) bf16 tiles
-    static constexpr int LU = C + 4;             // U^T (DV x C) bf16
     static constexpr int LB = SUB + 8;           // 16x16 bf16 operand blocks
     static constexpr int BS = SUB * SUB + 16;    // fp32 diagonal block stride (words)
     static constexpr size_t TILE = (size_t)C * LDK * 2;
-    static constexpr size_t UTB = (size_t)DV * LU * 2;
-    static constexpr size_t OFF_KL = 0;                                    // KL, then -W [C][LDK] pcol
-    static constexpr size_t OFF_KR = TILE;                                 // KR, then U^T [DV][LU]
-    static constexpr size_t OFF_QL = OFF_KR + a16(mx(TILE, UTB));          // QL (EXPAND)
-    static constexpr size_t OFF_RT = OFF_QL + (EXP ? TILE : 0);            // (beta k e^G)^T [DK][LC]
-    static constexpr size_t OFF_RV = OFF_RT + a16((size_t)DK * LC * 2);    // (beta v)^T [DV][LC]
+    static constexpr size_t OFF_KL = 0;                                    // KL, then T' [C][LC] pcol
+    static constexpr size_t OFF_KR = TILE;                                 // KR
+    static constexpr size_t OFF_QL = OFF_KR + TILE;                        // QL (EXPAND)
+    static constexpr size_t OFF_KG = OFF_QL + (EXP ? TILE : 0);            // -k e^G [C][LDK] pcol
+    static constexpr size_t OFF_RV = OFF_KG + TILE;                        // v^T [DV][LC]
     static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
     static constexpr size_t OFF_QG = OFF_KGT + a16((size_t)DK * LC * 2);   // q e^G [C][LDK] pcol
     static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol
@@ -200,14 +200,15 @@ __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu,
     typedef Mfma<bf16> MF;
     constexpr int NKD = DK / 32;
     const int l = lane_id(), g = l >> 4, c = l & 15;
-    const bf16* UT = reinterpret_cast<const bf16*>(smem + L::OFF_KR);
+    const bf16* VT = reinterpret_cast<const bf16*>(smem + L::OFF_RV);
+    const bf16* Tp = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
     const bf16* KGT = reinterpret_cast<const bf16*>(smem + L::OFF_KGT);
-    const bf16* Wn = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
+    const bf16* KGn = reinterpret_cast<const bf16*>(smem + L::OFF_KG);
     const bf16* QG = reinterpret_cast<const bf16*>(smem + L::OFF_QG);
     const bf16* Ms = reinterpret_cast<const bf16*>(smem + L::OFF_M);
     const float* egc = reinterpret_cast<const float*>(smem + L::OFF_EGC);
 
-    // V_new = U - W S (rows 16 yt + 4g + e) and, for EXPAND, the S part of
+    // Z = V - (K e^G) S (rows 16 yt + 4g + e) and, for EXPAND, the S part of
     // O^T = S^T (Q e^G)^T + V_new^T M^T; one 32-row block of S at a time.
     // Operand fragments are loaded one block ahead of their MFMAs.
     f32x4 y[4][NTW];
@@ -215,7 +216,7 @@ __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu,
     for (int yt = 0; yt < 4; ++yt)
 #pragma unroll
         for (int ct = 0; ct < NTW; ++ct)
-            y[yt][ct] = hasu ? load4<bf16>(UT + (ucol0 + ct * 16 + c) * L::LU + yt * 16 + 4 * g) : zero4();
+            y[yt][ct] = hasu ? load4<bf16>(VT + (ucol0 + ct * 16 + c) * L::LC + yt * 16 + 4 * g) : zero4();
     f32x4 ov[L::EXP ? 4 : 1][NTW];
     if constexpr (L::EXP) {
 #pragma unroll
@@ -225,7 +226,7 @@ __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu,
     }
     MF::frag wf[2][4], qf[2][L::EXP ? 4 : 1];
 #pragma unroll
-    for (int yt = 0; yt < 4; ++yt) wf[0][yt] = load_frag<bf16>(Wn, L::LDK, yt * 16, 0);
+    for (int yt = 0; yt < 4; ++yt) wf[0][yt] = load_frag<bf16>(KGn, L::LDK, yt * 16, 0);
     if constexpr (L::EXP) {
 #pragma unroll
         for (int ot = 0; ot < 4; ++ot) qf[0][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, 0);
@@ -235,7 +236,7 @@ __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu,
         const int cur = kb & 1, nxt = cur ^ 1;
         if (kb + 1 < NKD) {
 #pragma unroll
-            for (int yt = 0; yt < 4; ++yt) wf[nxt][yt] = load_frag<bf16>(Wn, L::LDK, yt * 16, (kb + 1) * 32);
+            for (int yt = 0; yt < 4; ++yt) wf[nxt][yt] = load_frag<bf16>(KGn, L::LDK, yt * 16, (kb + 1) * 32);
             if constexpr (L::EXP) {
 #pragma unroll
                 for (int ot = 0; ot < 4; ++ot) qf[nxt][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, (kb + 1) * 32);
@@ -269,7 +270,25 @@ __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu,
             mf[ot][1] = load_frag<bf16>(Ms, L::LC, ot * 16, 32);
         }
     }
+    // V_new = T' Z with T' = (I + A)^{-1} diag(beta)
     bf16x8 yb[2][NTW];
+    {
+        bf16x8 zb[2][NTW];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) zb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
+#pragma unroll
+        for (int yt = 0; yt < 4; ++yt) {
+            const MF::frag t0 = load_frag<bf16>(Tp, L::LC, yt * 16, 0);
+            const MF::frag t1 = load_frag<bf16>(Tp, L::LC, yt * 16, 32);
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) {
+                y[yt][ct] = MF::mma(t0, zb[0][ct], zero4());
+                y[yt][ct] = MF::mma(t1, zb[1][ct], y[yt][ct]);
+            }
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -342,20 +361,20 @@ __device__ __forceinline__ void inv_batch(const float* at, float (&x)[SUB]) {
 
 // ---------------------------------------------------------------------------
 // The chunk's own products, from its tokens in `in`, into LDS.  On return
-// (after a barrier) LDS holds -W, U^T, K~^T, e^{G_C} and, for EXPAND, Q e^G
-// and M.  `in` is refilled with chunk `nx` once its values are consumed.
+// (after a barrier) LDS holds T' = (I + A)^{-1} diag(beta), -K e^G, V^T,
+// K~^T, e^{G_C} and, for EXPAND, Q e^G and M.  `in` is refilled with chunk
+// `nx` once its values are consumed.
 //
 //  1  gate, chunk-local running sum of the log2 decay per channel; carries
 //     between row parts through LDS                                  | barrier
 //  2  block reference values G_m(R) from the carries; the decay-scaled
 //     operands k e^{G_r - G_m(R)}, k e^{G_m(R) - G_r}, q e^{G_r - G_m(R)},
-//     (beta k e^G)^T, (beta v)^T, (k e^{G_C - G})^T, q e^G and the
-//     cross-block factors e^{G_m(R) - G_m(I)}                        | barrier
-//  3  A (and M) per 16x16 block pair on MFMA                         | barrier
-//  4a the four diagonal blocks (I + A_RR)^{-1} by substitution      | barrier
-//  4b (I + A) [W | U] = [R_K | R_V] by block forward substitution,
-//     X_R = (I + A_RR)^{-1} (B_R - sum_{J<R} A_RJ X_J); every wave owns
-//     columns of the right-hand side, so the rounds need no barrier  | barrier
+//     -k e^G, v^T, (k e^{G_C - G})^T, q e^G and the cross-block factors
+//     e^{G_m(R) - G_m(I)}                                            | barrier
+//  3  A (and M) per 16x16 block pair on MFMA; the waves holding the
+//     diagonal blocks invert them, beta folded in: D'_R             | barrier
+//  4  T' by block forward substitution on the identity's columns; the
+//     chain then forms V_new = T' (V - K e^G S), which is U - W S    | barrier
 // ---------------------------------------------------------------------------
 template <int DK, int DV, int MODE>
 __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_min, unsigned char* smem,
@@ -370,9 +389,8 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
     bf16* KL = reinterpret_cast<bf16*>(smem + L::OFF_KL);   // [C][LDK] k e^{G_r - G_m(R)}
     bf16* KR = reinterpret_cast<bf16*>(smem + L::OFF_KR);   // [C][LDK] k e^{G_m(R) - G_r}
     bf16* QL = reinterpret_cast<bf16*>(smem + L::OFF_QL);   // [C][LDK] q e^{G_r - G_m(R)}
-    bf16* Wn = reinterpret_cast<bf16*>(smem + L::OFF_KL);   // [C][LDK] -W, pcol   (phase 4b on)
-    bf16* UT = reinterpret_cast<bf16*>(smem + L::OFF_KR);   // [DV][LU] U^T        (phase 4b on)
-    bf16* RT = reinterpret_cast<bf16*>(smem + L::OFF_RT);   // [DK][LC]
+    bf16* Tp = reinterpret_cast<bf16*>(smem + L::OFF_KL);   // [C][LC] T' = (I+A)^{-1} diag(beta), pcol (phase 4 on)
+    bf16* KGn = reinterpret_cast<bf16*>(smem + L::OFF_KG);  // [C][LDK] -k e^G, pcol
     bf16* RV = reinterpret_cast<bf16*>(smem + L::OFF_RV);   // [DV][LC]
     bf16* KGT = reinterpret_cast<bf16*>(smem + L::OFF_KGT); // [DK][LC] pcol
     bf16* QG = reinterpret_cast<bf16*>(smem + L::OFF_QG);   // [C][LDK] pcol
@@ -448,7 +466,7 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
                 dsc[part * DK + c0 + j] = __builtin_amdgcn_exp2f(a - b);
             }
         }
-        float rk[2][RP], kg[2][RP];
+        float kg[2][RP];
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
             const int r = r0 + i;
@@ -460,11 +478,11 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
                 kl[j] = kv[i][j] * left;
                 kR[j] = kv[i][j] * right;
                 if constexpr (EXP) ql[j] = qv[i][j] * left;
-                rk[j][i] = kl[j] * eGm[j];
                 kg[j][i] = kR[j] * eCGm[j];
             }
             store2<bf16>(KL + r * LDK + c0, kl[0], kl[1]);
             store2<bf16>(KR + r * LDK + c0, kR[0], kR[1]);
+            store2<bf16>(KGn + r * LDK + pcol(c0), -kl[0] * eGm[0], -kl[1] * eGm[1]);
             if constexpr (EXP) {
                 store2<bf16>(QL + r * LDK + c0, ql[0], ql[1]);
                 store2<bf16>(QG + r * LDK + pcol(c0), ql[0] * eGm[0], ql[1] * eGm[1]);
@@ -474,7 +492,6 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < RP; i += 4) {
-                store4p(RT + (c0 + j) * LC + r0 + i, rk[j][i], rk[j][i + 1], rk[j][i + 2], rk[j][i + 3]);
                 store4p(KGT + (c0 + j) * LC + pcol(r0 + i), kg[j][i], kg[j][i + 1], kg[j][i + 2], kg[j][i + 3]);
             }
         // V^T as loaded (rows past the end are multiplied by beta = 0 through
@@ -562,52 +579,36 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
     }
     __syncthreads();
 
-    // ---- phase 4b: block substitution on 16-column tiles of [R_K | R_V]
-    //      (tile t < DK/16: W columns 16t..; else U columns), tiles w, w+8
-    //      advanced together
-    {
-        constexpr int NTT = (DK + DV) / 16;
-        constexpr int NS = NTT > 8 ? 2 : 1;
+    // ---- phase 4: T' = (I + A)^{-1} diag(beta) by block forward substitution
+    //      on the columns of the identity.  Wave w < 4 owns column block w:
+    //      X_R = D'_R (E_R - sum_{J<R} A~_RJ X_J) with E the identity, so
+    //      X_R = 0 above the diagonal and X_w = D'_w.
+    if (w < 4) {
         const int g = l >> 4, c = l & 15;
         bf16x4 ab[6], db[4];
 #pragma unroll
         for (int p = 0; p < 6; ++p) ab[p] = *reinterpret_cast<const bf16x4*>(Ab + (p * SUB + c) * LB + 4 * g);
 #pragma unroll
         for (int R = 0; R < 4; ++R) db[R] = *reinterpret_cast<const bf16x4*>(Db + (R * SUB + c) * LB + 4 * g);
-        bool act[NS], isw[NS];
-        int col[NS];
-        f32x4 rhs[NS][4];
+        f32x4 eye;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int t = min(w + 8 * s, NTT - 1);
-            act[s] = w + 8 * s < NTT;
-            isw[s] = t < DK / 16;
-            col[s] = isw[s] ? 16 * t + c : 16 * (t - DK / 16) + c;
-            const bf16* src = (isw[s] ? RT : RV) + col[s] * LC + 4 * g;
+        for (int e = 0; e < 4; ++e) eye[e] = (4 * g + e == c) ? 1.f : 0.f;
+        bf16x4 xb[4];
+        bf16* tcol = Tp + 4 * g * LC + pcol(16 * w + c);
 #pragma unroll
-            for (int R = 0; R < 4; ++R) rhs[s][R] = load4<bf16>(src + R * SUB);
-        }
-        bf16x4 xb[NS][4];
+        for (int R = 0; R < 4; ++R) {
+            f32x4 x = zero4();
+            if (R >= w) {
+                f32x4 acc = (R == w) ? eye : zero4();
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                f32x4 acc = rhs[s][R];
-#pragma unroll
-                for (int J = 0; J < R; ++J) acc = mma16(ab[R * (R - 1) / 2 + J], xb[s][J], acc);
-                const f32x4 x = mma16(db[R], to_bf4(acc), zero4());
-                xb[s][R] = to_bf4(x);
-                if (act[s]) {
-                    if (isw[s]) {
-                        // -W[16R + 4g + e][col], contraction index col stored at pcol(col)
-                        bf16* wp = Wn + (R * SUB + 4 * g) * LDK + pcol(col[s]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) wp[e * LDK] = (bf16)(-x[e]);
-                    } else {
-                        store4<bf16>(UT + col[s] * L::LU + R * SUB + 4 * g, x);
-                    }
-                }
+                for (int J = 0; J < R; ++J)
+                    if (J >= w) acc = mma16(ab[R * (R - 1) / 2 + J], xb[J], acc);
+                x = mma16(db[R], to_bf4(acc), zero4());
             }
+            xb[R] = to_bf4(x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tcol[(R * SUB + e) * LC] = xb[R][e];
+        }
     }
     __syncthreads();
 }
