@@ -107,17 +107,18 @@ __device__ __forceinline__ void fetch_zkq(In<DK, DV, MODE>& r, const bf16* __res
                                           const bf16* __restrict__ beta, size_t row0, int valid, int H) {
     typedef Lay<DK, DV, MODE> L;
     const int tid = threadIdx.x;
-    const int c0 = 2 * (tid % L::CP), r0 = (tid / L::CP) * L::RP;
+    const int c0 = 2 * (tid % L::CP), r0 = (L::CP == 64 ? wave_id() : tid / L::CP) * L::RP;
     const int last = valid - 1, rs = H * DK;
     const bf16* zb = z + row0 * DK;
     const bf16* kb = k + row0 * DK;
     const bf16* qb = q + row0 * DK;
 #pragma unroll
     for (int i = 0; i < L::RP; ++i) {
-        const int off = min(r0 + i, last) * rs + c0;
-        r.z[i] = load2<bf16>(zb + off);
-        r.k[i] = load2<bf16>(kb + off);
-        if constexpr (L::EXP) r.q[i] = load2<bf16>(qb + off);
+        // row pointer (wave-uniform when a wave spans all channels) + lane offset
+        const size_t ro = (size_t)min(r0 + i, last) * rs;
+        r.z[i] = load2<bf16>(zb + ro + c0);
+        r.k[i] = load2<bf16>(kb + ro + c0);
+        if constexpr (L::EXP) r.q[i] = load2<bf16>(qb + ro + c0);
     }
     r.beta = beta[row0 + (size_t)min(tid & (C - 1), last) * H];
 }
@@ -127,10 +128,10 @@ __device__ __forceinline__ void fetch_v(In<DK, DV, MODE>& r, const bf16* __restr
                                         int H) {
     typedef Lay<DK, DV, MODE> L;
     const int tid = threadIdx.x;
-    const int cv0 = 2 * (tid % L::CPV), rv0 = (tid / L::CPV) * L::RPV;
+    const int cv0 = 2 * (tid % L::CPV), rv0 = (L::CPV == 64 ? wave_id() : tid / L::CPV) * L::RPV;
     const bf16* vb = v + row0 * DV;
 #pragma unroll
-    for (int i = 0; i < L::RPV; ++i) r.v[i] = load2<bf16>(vb + min(rv0 + i, valid - 1) * (H * DV) + cv0);
+    for (int i = 0; i < L::RPV; ++i) r.v[i] = load2<bf16>(vb + (size_t)min(rv0 + i, valid - 1) * (H * DV) + cv0);
 }
 
 // Block pairs (R, I), I <= R, of A and M per wave: the diagonal pairs (no
@@ -467,13 +468,14 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
             }
         }
         float kg[2][RP];
+        const float off[2] = {cr[0] - gmR[0], cr[1] - gmR[1]};   // row r: G2_r - G2_m(R) = G[i] + off
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
             const int r = r0 + i;
             float kl[2], kR[2], ql[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const float el = G[i][j] + cr[j] - gmR[j];
+                const float el = G[i][j] + off[j];
                 const float left = __builtin_amdgcn_exp2f(el), right = __builtin_amdgcn_exp2f(-el);
                 kl[j] = kv[i][j] * left;
                 kR[j] = kv[i][j] * right;
