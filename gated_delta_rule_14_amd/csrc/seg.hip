@@ -34,6 +34,8 @@
 // Overflow handling of the decay factors is that of the fp32 path: A and M
 // per 16x16 block pair with reference rows m(R) = 16R + 7, decay exponents in
 // log2 units so that every factor is one v_exp_f32.
+#include <stdlib.h>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -72,6 +74,7 @@ struct Lay {
     static constexpr int BS = SUB * SUB + 16;    // fp32 diagonal block stride (words)
     static constexpr size_t TILE = (size_t)C * LDK * 2;
     static constexpr size_t OFF_KL = 0;                                    // KL, then T' [C][LC] pcol
+    static constexpr size_t OFF_TP = OFF_KL;
     static constexpr size_t OFF_KR = TILE;                                 // KR
     static constexpr size_t OFF_QL = OFF_KR + TILE;                        // QL (EXPAND)
     static constexpr size_t OFF_KG = OFF_QL + (EXP ? TILE : 0);            // -k e^G [C][LDK] pcol
@@ -194,15 +197,14 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
 // col0 + 16 ct + l%16.  With hasu false the value input is zero (the P part
 // of COMPOSE).  EXPAND writes the chunk's outputs o[token][ocol0 + ...].
 // ---------------------------------------------------------------------------
-template <int DK, int DV, int MODE, int NTW>
+template <int DK, int DV, int MODE, int NTW, class L = Lay<DK, DV, MODE>>
 __device__ __forceinline__ void chain_step(f32x4 (&xs)[DK / 16][NTW], bool hasu, int ucol0, const unsigned char* smem,
                                            bf16* __restrict__ orow0, int valid, size_t ostride) {
-    typedef Lay<DK, DV, MODE> L;
     typedef Mfma<bf16> MF;
     constexpr int NKD = DK / 32;
     const int l = lane_id(), g = l >> 4, c = l & 15;
     const bf16* VT = reinterpret_cast<const bf16*>(smem + L::OFF_RV);
-    const bf16* Tp = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
+    const bf16* Tp = reinterpret_cast<const bf16*>(smem + L::OFF_TP);
     const bf16* KGT = reinterpret_cast<const bf16*>(smem + L::OFF_KGT);
     const bf16* KGn = reinterpret_cast<const bf16*>(smem + L::OFF_KG);
     const bf16* QG = reinterpret_cast<const bf16*>(smem + L::OFF_QG);
@@ -693,6 +695,539 @@ __global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, co
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined fused kernel for d_k = d_v = 128.  Waves 0-3 own the state and
+// run the recurrence step of chunk m-1 while waves 4-7 compute the gate,
+// the decay-scaled operands and the inverted diagonal blocks of chunk m, so
+// that the MFMA-bound step and the VALU-bound gate overlap on every SIMD.
+// Gate wave 4 + R handles rows 16R..16R+15 of a chunk over all key channels.
+// The block reference row 16R+7 lies in its own rows, so the factors
+// e^{+-(G_r - G_m(R))}, the diagonal block A_RR (and M_RR) and its inverse
+// need nothing from the other waves; block sums and references are
+// exchanged through LDS at the first barrier.
+//
+// Iteration i, chunk m = n0 + i:
+//  S1  waves 4-7: gate, block-local running sums, k e^{G-G_m}, k e^{G_m-G},
+//                 q e^{G-G_m}; block sums and references; A_RR (and M_RR)
+//                 on MFMA, then D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R)
+//      waves 0-3: recurrence step of chunk m-1 (reads only its operands:
+//                 T', -k e^G, v^T, K~^T, e^{G_C}, q e^G, M)             | barrier
+//  S2  waves 4-7: absolute references from the block sums; -k e^G, q e^G,
+//                 (k e^{G_C-G})^T, e^{G_C}, v^T (and M_RR)
+//      waves 0-3: the six off-diagonal block pairs of A (and M) with their
+//                 cross-block factors e^{G_m(R) - G_m(I)}                 | barrier
+//  S3  waves 4-7: T' column blocks                                        | barrier
+// State tiles: EXPAND, wave w owns columns 32w..32w+31 of S; COMPOSE, waves
+// 0-1 own 64 columns of P and waves 2-3 64 columns of R, advanced 32 columns
+// at a time.
+// ---------------------------------------------------------------------------
+template <int MODE>
+struct PLay {
+    static constexpr int DK = 128, DV = 128;
+    static constexpr bool EXP = MODE == EXPAND;
+    static constexpr int LDK = DK + 8, LC = C + 8, LB = SUB + 8, BS = SUB * SUB + 16;
+    static constexpr size_t TILE = (size_t)C * LDK * 2;
+    static constexpr size_t OFF_TP = 0;                                    // T' [C][LC] pcol
+    static constexpr size_t OFF_KL = a16((size_t)C * LC * 2);              // [C][LDK] k e^{G_r - G_m(R)}
+    static constexpr size_t OFF_KR = OFF_KL + TILE;                        // [C][LDK] k e^{G_m(R) - G_r}
+    static constexpr size_t OFF_QL = OFF_KR + TILE;                        // [C][LDK] q e^{G_r - G_m(R)} (EXPAND)
+    static constexpr size_t OFF_KG = OFF_QL + (EXP ? TILE : 0);            // -k e^G [C][LDK] pcol
+    static constexpr size_t OFF_RV = OFF_KG + TILE;                        // v^T [DV][LC]
+    static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
+    static constexpr size_t OFF_QG = OFF_KGT + a16((size_t)DK * LC * 2);   // q e^G [C][LDK] pcol (EXPAND)
+    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol (EXPAND)
+    static constexpr size_t OFF_AS = OFF_M + (EXP ? a16((size_t)C * LC * 2) : 0);   // [4][BS] beta A~_RR^T
+    static constexpr size_t OFF_AB = OFF_AS + (size_t)4 * BS * 4;          // [6][16][LB] -A~_RI
+    static constexpr size_t OFF_DB = OFF_AB + a16((size_t)6 * SUB * LB * 2);   // [4][16][LB] D'_R
+    static constexpr size_t OFF_EGC = OFF_DB + a16((size_t)4 * SUB * LB * 2);
+    static constexpr size_t OFF_DSC = OFF_EGC + (size_t)DK * 4;            // [6][DK] e^{G_m(R) - G_m(I)}
+    static constexpr size_t OFF_TOT = OFF_DSC + 6 * (size_t)DK * 4;        // [4][DK] block sums of the gate
+    static constexpr size_t OFF_MLOC = OFF_TOT + 4 * (size_t)DK * 4;       // [4][DK] G_m(R) - G_{16R-1}
+    static constexpr size_t OFF_BET = OFF_MLOC + 4 * (size_t)DK * 4;
+    static constexpr size_t LDS = OFF_BET + C * 4;
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// One chunk's tokens as a gate wave loads them: rows 16R + i, channels 2l,
+// 2l+1 (v likewise); beta of row l.
+template <bool EXP>
+struct PIn {
+    bf16x2 z[SUB], k[SUB], q[EXP ? SUB : 1];
+    bf16 beta;
+};
+// v of rows 16R + i, channels 2l, 2l+1, as the wave that writes v^T loads it:
+// the state waves for EXPAND (fewer live registers in the gate waves, which
+// hold q), the gate waves for COMPOSE (whose state waves hold P and R).
+struct PV {
+    bf16x2 v[SUB];
+};
+
+// Stand-in token for positions past the end of a ragged last chunk: z = -inf
+// gives a zero gate (alpha = 1) and k = q = 0 a token that neither writes nor
+// reads, so it acts as the identity (beta is set to 0 as well).
+__device__ const unsigned short kPadZ[128] = {0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80};
+__device__ const unsigned short kPadKQ[128] = {0};
+
+template <bool EXP>
+__device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                           const bf16* __restrict__ z, const bf16* __restrict__ beta, size_t row0,
+                                           int valid, int H, int R) {
+    const int l = lane_id(), c0 = 2 * l, last = valid - 1;
+    const size_t rs = (size_t)H * 128;
+    const bf16* zb = z + row0 * 128 + c0;
+    const bf16* kb = k + row0 * 128 + c0;
+    const bf16* qb = q + row0 * 128 + c0;
+    const bf16* pz = reinterpret_cast<const bf16*>(kPadZ) + c0;
+    const bf16* pkq = reinterpret_cast<const bf16*>(kPadKQ) + c0;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        // wave-uniform choice of the row: a real token or the stand-in
+        const bool ok = SUB * R + i <= last;
+        const size_t ro = (size_t)(SUB * R + i) * rs;
+        r.z[i] = load2<bf16>(ok ? zb + ro : pz);
+        r.k[i] = load2<bf16>(ok ? kb + ro : pkq);
+        if constexpr (EXP) r.q[i] = load2<bf16>(ok ? qb + ro : pkq);
+    }
+    r.beta = beta[row0 + (size_t)min(l, last) * H];
+}
+
+__device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size_t row0, int valid, int H, int R) {
+    const int l = lane_id(), last = valid - 1;
+    const size_t rs = (size_t)H * 128;
+    const bf16* vb = v + row0 * 128 + 2 * l;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) r.v[i] = load2<bf16>(vb + (size_t)min(SUB * R + i, last) * rs);
+}
+
+// S1 of gate wave R (rows past the end arrive as identity tokens).  On
+// return kl, kr, ql hold the block's decay-scaled k and q (fp32).
+template <int MODE>
+__device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, int valid, float kg2,
+                                          unsigned char* smem, float (&kl)[SUB][2], float (&kr)[SUB][2],
+                                          float (&ql)[MODE == EXPAND ? SUB : 1][2]) {
+    typedef PLay<MODE> L;
+    constexpr bool EXP = L::EXP;
+    constexpr int LDK = L::LDK;
+    const int l = lane_id(), c0 = 2 * l;
+    bf16* KL = reinterpret_cast<bf16*>(smem + L::OFF_KL);
+    bf16* KR = reinterpret_cast<bf16*>(smem + L::OFF_KR);
+    bf16* QL = reinterpret_cast<bf16*>(smem + L::OFF_QL);
+    float* tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
+    float* mloc = reinterpret_cast<float*>(smem + L::OFF_MLOC);
+    float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
+
+    float G[SUB][2];
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            G[i][j] = kg2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][j]));
+        s0 += G[i][0];
+        s1 += G[i][1];
+        G[i][0] = s0;
+        G[i][1] = s1;
+    }
+    const float m0 = G[7][0], m1 = G[7][1];
+    *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{s0, s1};
+    *reinterpret_cast<float2*>(mloc + R * 128 + c0) = float2{m0, m1};
+    if ((l >> 4) == R) bet[l] = l < valid ? (float)in.beta : 0.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const int r = SUB * R + i;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float el = G[i][j] - (j ? m1 : m0);
+            const float left = __builtin_amdgcn_exp2f(el), right = __builtin_amdgcn_exp2f(-el);
+            const float kv = (float)in.k[i][j];
+            kl[i][j] = kv * left;
+            kr[i][j] = kv * right;
+            if constexpr (EXP) ql[i][j] = (float)in.q[i][j] * left;
+        }
+        store2<bf16>(KL + r * LDK + c0, kl[i][0], kl[i][1]);
+        store2<bf16>(KR + r * LDK + c0, kr[i][0], kr[i][1]);
+        if constexpr (EXP) store2<bf16>(QL + r * LDK + c0, ql[i][0], ql[i][1]);
+    }
+}
+
+// S2 of gate wave R, after pipe_abs: A_RR (and M_RR) from the block's own
+// rows of KL, KR, QL, then D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R).
+template <int MODE>
+__device__ __forceinline__ void pipe_diag(int R, unsigned char* smem) {
+    typedef PLay<MODE> L;
+    typedef Mfma<bf16> MF;
+    constexpr bool EXP = L::EXP;
+    constexpr int LDK = L::LDK, LC = L::LC, LB = L::LB, BS = L::BS;
+    int l = lane_id();
+    asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
+    const bf16* KL = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
+    const bf16* KR = reinterpret_cast<const bf16*>(smem + L::OFF_KR);
+    const bf16* QL = reinterpret_cast<const bf16*>(smem + L::OFF_QL);
+    bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);
+    float* As = reinterpret_cast<float*>(smem + L::OFF_AS);
+    bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);
+    const float* bet = reinterpret_cast<const float*>(smem + L::OFF_BET);
+    // A_RR (and M_RR) transposed: lane holds row r = 16R + l%16, key indices
+    // i = 16R + 4(l/16) + e
+    f32x4 accA = zero4(), accM = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 128; kk += MF::KSTEP) {
+        const MF::frag ak = load_frag<bf16>(KR, LDK, R * SUB, kk);
+        accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
+        if constexpr (EXP) accM = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM);
+    }
+    const int rr = l & 15, ii = 4 * (l >> 4);
+    {
+        const float br = bet[R * SUB + rr];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[R * BS + (ii + e) * SUB + rr] = (ii + e < rr) ? br * accA[e] : 0.f;
+        if constexpr (EXP) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) accM[e] = (ii + e <= rr) ? accM[e] : 0.f;
+            store4p(Ms + (R * SUB + rr) * LC + pcol(R * SUB + ii), accM[0], accM[1], accM[2], accM[3]);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's As stores
+
+    // D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R): lane = column, right-looking
+    // substitution down the column (lanes 16.. repeat lanes 0..15)
+    const int col = l & 15;
+    const float* at = As + R * BS;   // at[i * 16 + r] = beta_r A~_ri
+    float x[SUB];
+#pragma unroll
+    for (int r = 0; r < SUB; ++r) x[r] = (r == col) ? 1.f : 0.f;
+    inv_batch<0, 3>(at, x);
+    inv_batch<3, 7>(at, x);
+    inv_batch<7, 11>(at, x);
+    inv_batch<11, 15>(at, x);
+    if (l < 16) {
+        const float bc = bet[R * SUB + col];
+        bf16* d = Db + R * SUB * LB + col;
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) d[r * LB] = (bf16)(x[r] * bc);
+    }
+}
+
+
+// S2 of gate wave R: absolute block references from the block sums, then the
+// chain operands of block R.
+// v^T of rows 16R..16R+15 as loaded (rows past the end meet beta = 0 in the solve).
+template <int MODE>
+__device__ __forceinline__ void pipe_vt(const PV& pv, int R, unsigned char* smem) {
+    typedef PLay<MODE> L;
+    constexpr int LC = L::LC;
+    const int c0 = 2 * lane_id();
+    bf16* RV = reinterpret_cast<bf16*>(smem + L::OFF_RV);
+#pragma unroll
+    for (int i = 0; i < SUB; i += 4)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<bf16x4*>(RV + (c0 + j) * LC + SUB * R + i) =
+                bf16x4{pv.v[i][j], pv.v[i + 1][j], pv.v[i + 2][j], pv.v[i + 3][j]};
+}
+
+template <int MODE>
+__device__ __forceinline__ void pipe_abs(int R, unsigned char* smem,
+                                         const float (&kl)[SUB][2], const float (&kr)[SUB][2],
+                                         const float (&ql)[MODE == EXPAND ? SUB : 1][2]) {
+    typedef PLay<MODE> L;
+    constexpr bool EXP = L::EXP;
+    constexpr int LDK = L::LDK, LC = L::LC;
+    const int l = lane_id(), c0 = 2 * l;
+    bf16* KGn = reinterpret_cast<bf16*>(smem + L::OFF_KG);
+    bf16* QG = reinterpret_cast<bf16*>(smem + L::OFF_QG);
+    bf16* KGT = reinterpret_cast<bf16*>(smem + L::OFF_KGT);
+    float* egc = reinterpret_cast<float*>(smem + L::OFF_EGC);
+    const float* tot = reinterpret_cast<const float*>(smem + L::OFF_TOT);
+    const float* mloc = reinterpret_cast<const float*>(smem + L::OFF_MLOC);
+
+    float gR[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};   // G before block R; G_C
+#pragma unroll
+    for (int B = 0; B < 4; ++B) {
+        const float2 t = *reinterpret_cast<const float2*>(tot + B * 128 + c0);
+        if (B < R) {
+            gR[0] += t.x;
+            gR[1] += t.y;
+        }
+        gC[0] += t.x;
+        gC[1] += t.y;
+    }
+    const float2 ml = *reinterpret_cast<const float2*>(mloc + R * 128 + c0);
+    const float mR[2] = {gR[0] + ml.x, gR[1] + ml.y};
+    float eGm[2], eCGm[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        eGm[j] = __builtin_amdgcn_exp2f(mR[j]);
+        eCGm[j] = __builtin_amdgcn_exp2f(gC[j] - mR[j]);
+    }
+    if (R == 0) *reinterpret_cast<float2*>(egc + c0) = float2{__builtin_amdgcn_exp2f(gC[0]),
+                                                              __builtin_amdgcn_exp2f(gC[1])};
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const int r = SUB * R + i;
+        store2<bf16>(KGn + r * LDK + pcol(c0), -kl[i][0] * eGm[0], -kl[i][1] * eGm[1]);
+        if constexpr (EXP) store2<bf16>(QG + r * LDK + pcol(c0), ql[i][0] * eGm[0], ql[i][1] * eGm[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < SUB; i += 4)
+            store4p(KGT + (c0 + j) * LC + pcol(SUB * R + i), kr[i][j] * eCGm[j], kr[i + 1][j] * eCGm[j],
+                    kr[i + 2][j] * eCGm[j], kr[i + 3][j] * eCGm[j]);
+}
+
+// Off-diagonal block pairs (R, I), I < R, per state wave: two each for waves
+// 0-1, one each for waves 2-3.
+__constant__ int kPipePairs[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 0}, {3, 1}}, {{2, 1}, {-1, -1}}, {{3, 2}, {-1, -1}}};
+
+// S2 of a state wave: the cross-block factors e^{G_m(R) - G_m(I)} of its NP
+// pairs into LDS (read back by the same wave only), then -A~_RI (without the
+// row factor beta_r, which the inverses carry) and M_RI, the NP pairs
+// interleaved in one pass over the key channels.
+template <int MODE, int NP>
+__device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
+    typedef PLay<MODE> L;
+    typedef Mfma<bf16> MF;
+    constexpr bool EXP = L::EXP;
+    constexpr int LDK = L::LDK, LC = L::LC, LB = L::LB, DK = L::DK;
+    int l = lane_id();
+    asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
+    const bf16* KL = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
+    const bf16* KR = reinterpret_cast<const bf16*>(smem + L::OFF_KR);
+    const bf16* QL = reinterpret_cast<const bf16*>(smem + L::OFF_QL);
+    bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);
+    bf16* Ab = reinterpret_cast<bf16*>(smem + L::OFF_AB);
+    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);
+    const float* tot = reinterpret_cast<const float*>(smem + L::OFF_TOT);
+    const float* mloc = reinterpret_cast<const float*>(smem + L::OFF_MLOC);
+    const int c0 = 2 * l;
+    int Rp[NP], Ip[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        Rp[j] = kPipePairs[w][j][0];
+        Ip[j] = kPipePairs[w][j][1];
+        const int R = Rp[j], I = Ip[j];
+        // G_m(R) - G_m(I) = (block sums I..R-1) + mloc_R - mloc_I
+        const float2 mr = *reinterpret_cast<const float2*>(mloc + R * 128 + c0);
+        const float2 mi = *reinterpret_cast<const float2*>(mloc + I * 128 + c0);
+        float d0 = mr.x - mi.x, d1 = mr.y - mi.y;
+#pragma unroll
+        for (int B = 0; B < 3; ++B)
+            if (B >= I && B < R) {
+                const float2 t = *reinterpret_cast<const float2*>(tot + B * 128 + c0);
+                d0 += t.x;
+                d1 += t.y;
+            }
+        *reinterpret_cast<float2*>(dsc + (R * (R - 1) / 2 + I) * DK + c0) =
+            float2{__builtin_amdgcn_exp2f(d0), __builtin_amdgcn_exp2f(d1)};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's dsc rows
+    f32x4 accA[NP], accM[NP];
+#pragma unroll
+    for (int j = 0; j < NP; ++j) accA[j] = accM[j] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < DK; kk += MF::KSTEP) {
+        const int cc = kk + (l >> 4) * MF::KPL;
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            const int R = Rp[j], I = Ip[j];
+            const float* dv = dsc + (R * (R - 1) / 2 + I) * DK + cc;
+            MF::frag ak = load_frag<bf16>(KR, LDK, I * SUB, kk);
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(dv), d1 = *reinterpret_cast<const f32x4*>(dv + 4);
+            float t[MF::KPL];
+            MF::to_floats(ak, t);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                t[jj] *= d0[jj];
+                t[jj + 4] *= d1[jj];
+            }
+            ak = MF::from_floats(t);
+            accA[j] = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA[j]);
+            if constexpr (EXP) accM[j] = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM[j]);
+        }
+    }
+    const int rr = l & 15, ii = 4 * (l >> 4);
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int R = Rp[j], I = Ip[j];
+        store4p(Ab + ((R * (R - 1) / 2 + I) * SUB + rr) * LB + ii, -accA[j][0], -accA[j][1], -accA[j][2],
+                -accA[j][3]);
+        if constexpr (EXP)
+            store4p(Ms + (R * SUB + rr) * LC + pcol(I * SUB + ii), accM[j][0], accM[j][1], accM[j][2], accM[j][3]);
+    }
+}
+
+// S3: column block wT of T' = (I + A)^{-1} diag(beta) by block forward
+// substitution on the identity's columns: X_R = D'_R (E_R - sum_{J<R} A~_RJ X_J).
+template <int MODE>
+__device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
+    typedef PLay<MODE> L;
+    constexpr int LC = L::LC, LB = L::LB;
+    int l = lane_id();
+    asm volatile("" : "+v"(l));
+    const int g = l >> 4, c = l & 15;
+    const bf16* Ab = reinterpret_cast<const bf16*>(smem + L::OFF_AB);
+    const bf16* Db = reinterpret_cast<const bf16*>(smem + L::OFF_DB);
+    bf16* Tp = reinterpret_cast<bf16*>(smem + L::OFF_TP);
+    bf16x4 ab[6], db[4];
+#pragma unroll
+    for (int p = 0; p < 6; ++p) ab[p] = *reinterpret_cast<const bf16x4*>(Ab + (p * SUB + c) * LB + 4 * g);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) db[R] = *reinterpret_cast<const bf16x4*>(Db + (R * SUB + c) * LB + 4 * g);
+    f32x4 eye;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) eye[e] = (4 * g + e == c) ? 1.f : 0.f;
+    bf16x4 xb[4];
+    bf16* tcol = Tp + 4 * g * LC + pcol(16 * wT + c);
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        f32x4 x = zero4();
+        if (R >= wT) {
+            f32x4 acc = (R == wT) ? eye : zero4();
+#pragma unroll
+            for (int J = 0; J < R; ++J)
+                if (J >= wT) acc = mma16(ab[R * (R - 1) / 2 + J], xb[J], acc);
+            x = mma16(db[R], to_bf4(acc), zero4());
+        }
+        xb[R] = to_bf4(x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tcol[(R * SUB + e) * LC] = xb[R][e];
+    }
+}
+
+// Same grid and arguments as seg_kernel.
+template <int MODE>
+__global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                   const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                   const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
+                                                   int L, int nchain, const float* __restrict__ xin,
+                                                   float* __restrict__ xo0, float* __restrict__ xo1,
+                                                   bf16* __restrict__ o) {
+    typedef PLay<MODE> LY;
+    constexpr int DK = 128, DV = 128;
+    constexpr bool EXP = MODE == EXPAND;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int seg = blockIdx.x / nchain;
+    const size_t bh = blockIdx.x % nchain;
+    const int b = (int)(bh / H), h = (int)(bh % H);
+    const int l = lane_id(), w = wave_id();
+    __builtin_assume(w >= 0 && w < NTH / 64);
+    const int n0 = seg * L, n1 = min(NC, n0 + L), nL = n1 - n0;
+    auto row_of = [&](int n) { return ((size_t)b * T + (size_t)n * C) * H + h; };
+
+    if constexpr (EXP) {
+        // strictly upper blocks of M stay zero
+        if (w >= 2) {
+            const int p = w - 2;
+            const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+            const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+            store4p(reinterpret_cast<bf16*>(smem + LY::OFF_M) + (R * SUB + (l & 15)) * LY::LC +
+                        pcol(I * SUB + 4 * (l >> 4)),
+                    0.f, 0.f, 0.f, 0.f);
+        }
+    }
+
+    if (w < 4) {
+        // ---------------- state waves
+        constexpr int NH = EXP ? 1 : 2;          // 32-column halves per wave
+        const bool ptile = !EXP && w < 2;
+        const bool hasu = EXP || !ptile;
+        const int NX = ptile ? DK : DV;
+        const int cbase = EXP ? 32 * w : 64 * (w & 1);
+        const size_t xblk = ((size_t)seg * nchain + bh) * DK;
+        f32x4 xs[NH][DK / 16][2];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+            for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = rt * 16 + 4 * (l >> 4) + e, col = cbase + 32 * hh + ct * 16 + (l & 15);
+                        float x = 0.f;
+                        if constexpr (EXP) x = xin ? xin[(xblk + row) * DV + col] : 0.f;
+                        else x = (ptile && row == col) ? 1.f : 0.f;
+                        xs[hh][rt][ct][e] = x;
+                    }
+        const size_t ostride = (size_t)H * DV;
+        PV pv;
+        if constexpr (EXP) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
+        for (int i = 0; i <= nL; ++i) {
+            if (i > 0) {
+                const int m = n0 + i - 1;
+                const int valid = min(C, T - m * C);
+#pragma unroll
+                for (int hh = 0; hh < NH; ++hh) {
+                    const int col0 = cbase + 32 * hh;
+                    chain_step<DK, DV, MODE, 2, LY>(xs[hh], hasu, col0, smem, o + row_of(m) * DV + col0, valid,
+                                                    ostride);
+                    __builtin_amdgcn_sched_barrier(0);   // one half's working set at a time
+                }
+            }
+            if (i == nL) break;
+            __syncthreads();   // S1 | S2
+            if constexpr (EXP) {
+                pipe_vt<MODE>(pv, w, smem);
+                const int mn = min(n0 + i + 1, n1 - 1);
+                pfetch_v(pv, v, row_of(mn), min(C, T - mn * C), H, w);
+            }
+            if (w < 2)
+                pipe_pairs<MODE, 2>(w, smem);
+            else
+                pipe_pairs<MODE, 1>(w, smem);
+            __syncthreads();   // S2 | S3
+            __syncthreads();   // S3 | next S1
+        }
+        float* xo = EXP ? xo0 : (ptile ? xo0 : xo1);
+        if (xo) {
+            const size_t ob = EXP ? bh * DK : xblk;
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+                for (int rt = 0; rt < DK / 16; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int row = rt * 16 + 4 * (l >> 4) + e;
+                            const int col = cbase + 32 * hh + ct * 16 + (l & 15);
+                            xo[(ob + row) * NX + col] = xs[hh][rt][ct][e];
+                        }
+        }
+    } else {
+        // ---------------- gate waves: block R of each chunk
+        const int R = w - 4;
+        const float kg2 = g_min * LOG2E;
+        PIn<EXP> in;
+        PV pv;
+        {
+            const int valid = min(C, T - n0 * C);
+            pfetch_zkq<EXP>(in, q, k, z, beta, row_of(n0), valid, H, R);
+            if constexpr (!EXP) pfetch_v(pv, v, row_of(n0), valid, H, R);
+        }
+        float kl[SUB][2], kr[SUB][2], ql[EXP ? SUB : 1][2];
+        for (int i = 0; i < nL; ++i) {
+            const int m = n0 + i;
+            const int valid = min(C, T - m * C);
+            const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
+            const int valid_n = min(C, T - mn * C);
+            pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
+            pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
+            __syncthreads();   // S1 | S2
+            pipe_abs<MODE>(R, smem, kl, kr, ql);
+            if constexpr (!EXP) {
+                pipe_vt<MODE>(pv, R, smem);
+                pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+            }
+            pipe_diag<MODE>(R, smem);
+            __syncthreads();   // S2 | S3
+            pipe_tsolve<MODE>(R, smem);
+            __syncthreads();   // S3 | next S1
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Scan over segments for one chain and 16 state columns:
 //   Sent[j] = S_j,  S_{j+1} = P_j S_j + R_j,  s_final = S_nseg.
 // The products run on bf16 MFMA with both operands split into a high and a
@@ -852,6 +1387,30 @@ static hipError_t set_lds(K kernel, size_t bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
+// The pipelined kernels serve d_k = d_v = 128 unless KDA_PIPELINE=0 (the
+// plain fused kernels then run, for comparison).
+static bool use_pipe() {
+    static const bool on = [] {
+        const char* e = getenv("KDA_PIPELINE");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
+
+template <int DK, int DV, int MODE>
+static void* fused_kernel() {
+    if constexpr (DK == 128 && DV == 128)
+        if (use_pipe()) return (void*)pipe_kernel<MODE>;
+    return (void*)seg_kernel<DK, DV, MODE>;
+}
+
+template <int DK, int DV, int MODE>
+static size_t fused_lds() {
+    if constexpr (DK == 128 && DV == 128)
+        if (use_pipe()) return PLay<MODE>::LDS;
+    return Lay<DK, DV, MODE>::LDS;
+}
+
 template <int DK, int DV>
 static hipError_t launch_t(const ChunkArgs& a) {
     const int NC = (a.T + C - 1) / C;
@@ -860,22 +1419,25 @@ static hipError_t launch_t(const ChunkArgs& a) {
     const Plan p = plan(a.B, a.T, a.H, DK, DV);
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v, *z = (const bf16*)a.z,
                *beta = (const bf16*)a.beta;
-    typedef Lay<DK, DV, EXPAND> LE;
-    typedef Lay<DK, DV, COMPOSE> LCm;
+    typedef void (*KFn)(const bf16*, const bf16*, const bf16*, const bf16*, const bf16*, float, int, int, int, int,
+                        int, const float*, float*, float*, bf16*);
+    const KFn kexp = (KFn)fused_kernel<DK, DV, EXPAND>();
+    const KFn kcmp = (KFn)fused_kernel<DK, DV, COMPOSE>();
+    const size_t lexp = fused_lds<DK, DV, EXPAND>(), lcmp = fused_lds<DK, DV, COMPOSE>();
     hipError_t err;
-    if ((err = set_lds(seg_kernel<DK, DV, EXPAND>, LE::LDS)) != hipSuccess) return err;
+    if ((err = set_lds(kexp, lexp)) != hipSuccess) return err;
     if (p.nseg == 1) {
-        hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(nchain), dim3(NTH), LE::LDS, st, q, k, v, z, beta,
-                           a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o);
+        hipLaunchKernelGGL(kexp, dim3(nchain), dim3(NTH), lexp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC, NC,
+                           nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o);
         return hipGetLastError();
     }
     unsigned char* ws = (unsigned char*)a.workspace;
     float* Pb = reinterpret_cast<float*>(ws + p.p_off);
     float* Rb = reinterpret_cast<float*>(ws + p.r_off);
     float* Eb = reinterpret_cast<float*>(ws + p.e_off);
-    if ((err = set_lds(seg_kernel<DK, DV, COMPOSE>, LCm::LDS)) != hipSuccess) return err;
-    hipLaunchKernelGGL((seg_kernel<DK, DV, COMPOSE>), dim3(p.nseg * nchain), dim3(NTH), LCm::LDS, st, q, k, v, z,
-                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
+    if ((err = set_lds(kcmp, lcmp)) != hipSuccess) return err;
+    hipLaunchKernelGGL(kcmp, dim3(p.nseg * nchain), dim3(NTH), lcmp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC,
+                       p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if constexpr (DK == 128) {
         hipLaunchKernelGGL((scan_x3_kernel<DK, DV>), dim3((DV / 16) * nchain), dim3(256), 0, st, (const float*)Pb,
@@ -885,9 +1447,8 @@ static hipError_t launch_t(const ChunkArgs& a) {
         if ((err = launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream)) != hipSuccess)
             return err;
     }
-    hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(p.nseg * nchain), dim3(NTH), LE::LDS, st, q, k, v, z,
-                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr,
-                       (bf16*)a.o);
+    hipLaunchKernelGGL(kexp, dim3(p.nseg * nchain), dim3(NTH), lexp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC,
+                       p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr, (bf16*)a.o);
     return hipGetLastError();
 }
 
