@@ -761,44 +761,45 @@ struct PV {
     bf16x2 v[SUB];
 };
 
-// Stand-in token for positions past the end of a ragged last chunk: z = -inf
-// gives a zero gate (alpha = 1) and k = q = 0 a token that neither writes nor
-// reads, so it acts as the identity (beta is set to 0 as well).
-__device__ const unsigned short kPadZ[128] = {0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80, 0xFF80};
-__device__ const unsigned short kPadKQ[128] = {0};
-
 template <bool EXP>
 __device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
                                            const bf16* __restrict__ z, const bf16* __restrict__ beta, size_t row0,
                                            int valid, int H, int R) {
-    const int l = lane_id(), c0 = 2 * l, last = valid - 1;
-    const size_t rs = (size_t)H * 128;
-    const bf16* zb = z + row0 * 128 + c0;
-    const bf16* kb = k + row0 * 128 + c0;
-    const bf16* qb = q + row0 * 128 + c0;
-    const bf16* pz = reinterpret_cast<const bf16*>(kPadZ) + c0;
-    const bf16* pkq = reinterpret_cast<const bf16*>(kPadKQ) + c0;
+    const int l = lane_id(), last = valid - 1;
+    const unsigned c0 = 2u * (unsigned)l;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-        // wave-uniform choice of the row: a real token or the stand-in
-        const bool ok = SUB * R + i <= last;
-        const size_t ro = (size_t)(SUB * R + i) * rs;
-        r.z[i] = load2<bf16>(ok ? zb + ro : pz);
-        r.k[i] = load2<bf16>(ok ? kb + ro : pkq);
-        if constexpr (EXP) r.q[i] = load2<bf16>(ok ? qb + ro : pkq);
+        // row clamped to the last token (rows past it are masked at use)
+        const size_t ro = (row0 + (size_t)min(SUB * R + i, last) * H) * 128;
+        r.z[i] = load2<bf16>(z + ro + c0);
+        r.k[i] = load2<bf16>(k + ro + c0);
+        if constexpr (EXP) r.q[i] = load2<bf16>(q + ro + c0);
     }
     r.beta = beta[row0 + (size_t)min(l, last) * H];
 }
 
-__device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size_t row0, int valid, int H, int R) {
-    const int l = lane_id(), last = valid - 1;
-    const size_t rs = (size_t)H * 128;
-    const bf16* vb = v + row0 * 128 + 2 * l;
+// Rows at or past `valid` of a ragged last chunk become identity tokens:
+// z = -inf (a zero gate, alpha = 1) and k = q = 0 (no write, no read); beta
+// is set to 0 where it is stored.
+template <bool EXP>
+__device__ __forceinline__ void pmask(PIn<EXP>& r, int valid, int R) {
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) r.v[i] = load2<bf16>(vb + (size_t)min(SUB * R + i, last) * rs);
+    for (int i = 0; i < SUB; ++i) {
+        const unsigned keep = SUB * R + i < valid ? 0xffffffffu : 0u;
+        r.z[i] = __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, r.z[i]) & keep) | (0xff80ff80u & ~keep));
+        r.k[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.k[i]) & keep);
+        if constexpr (EXP) r.q[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.q[i]) & keep);
+    }
 }
 
-// S1 of gate wave R (rows past the end arrive as identity tokens).  On
+__device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size_t row0, int valid, int H, int R) {
+    const unsigned c0 = 2u * (unsigned)lane_id();
+    const int last = valid - 1;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) r.v[i] = load2<bf16>(v + (row0 + (size_t)min(SUB * R + i, last) * H) * 128 + c0);
+}
+
+// S1 of gate wave R (rows past the end have been made identity tokens).  On
 // return kl, kr, ql hold the block's decay-scaled k and q (fp32).
 template <int MODE>
 __device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, int valid, float kg2,
@@ -815,20 +816,19 @@ __device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, 
     float* mloc = reinterpret_cast<float*>(smem + L::OFF_MLOC);
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
 
-    float G[SUB][2];
+    // S[i] = running sum of sigmoid(z) over the block's rows; the log2 decay
+    // is G = kg2 S, folded into the exponents below
+    float S[SUB][2];
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            G[i][j] = kg2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][j]));
-        s0 += G[i][0];
-        s1 += G[i][1];
-        G[i][0] = s0;
-        G[i][1] = s1;
+        s0 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][0]));
+        s1 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][1]));
+        S[i][0] = s0;
+        S[i][1] = s1;
     }
-    const float m0 = G[7][0], m1 = G[7][1];
-    *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{s0, s1};
+    const float m0 = kg2 * S[7][0], m1 = kg2 * S[7][1];
+    *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{kg2 * s0, kg2 * s1};
     *reinterpret_cast<float2*>(mloc + R * 128 + c0) = float2{m0, m1};
     if ((l >> 4) == R) bet[l] = l < valid ? (float)in.beta : 0.f;
 #pragma unroll
@@ -836,7 +836,7 @@ __device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, 
         const int r = SUB * R + i;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float el = G[i][j] - (j ? m1 : m0);
+            const float el = __builtin_fmaf(kg2, S[i][j], -(j ? m1 : m0));   // G_r - G_m(R)
             const float left = __builtin_amdgcn_exp2f(el), right = __builtin_amdgcn_exp2f(-el);
             const float kv = (float)in.k[i][j];
             kl[i][j] = kv * left;
@@ -1211,6 +1211,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             const int valid = min(C, T - m * C);
             const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
             const int valid_n = min(C, T - mn * C);
+            if (valid < C) pmask<EXP>(in, valid, R);
             pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
             pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
             __syncthreads();   // S1 | S2
