@@ -211,8 +211,8 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
     out = {"source_hash": kernel_source_hash(), "copy_fetch_scale": round(sf, 4), "copy_write_scale": round(sw, 4),
            "copy_kernel": copy_k, "kernels": kernels,
            "prefill_hbm_bytes_per_call": sum(v["hbm_bytes"] for k, v in kernels.items()
-                                             if "seg_kernel" in k or "scan_x3" in k or "seg_scan" in k or "chunk_intra" in k
-                                             or "chain_kernel" in k),
+                                             if "pipe_kernel" in k or "seg_kernel" in k or "scan_x3" in k
+                                             or "seg_scan" in k or "chunk_intra" in k or "chain_kernel" in k),
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --no-cpu --steps 2 "
                       "--warmup 1 --decode-steps 8 --no-epilogue; same with --copy-only for the scale factors"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -299,7 +299,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
                      "algorithmic_bytes": r["bytes"],
-                     "kernel": "kda_chunk_fwd: seg_kernel (compose) + seg_scan_kernel + seg_kernel (expand)",
+                     "kernel": "kda_chunk_fwd: pipe_kernel (compose) + scan_x3_kernel + pipe_kernel (expand)",
                      "mfma_frac": round(r["flop"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_decode:

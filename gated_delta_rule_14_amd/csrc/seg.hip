@@ -732,20 +732,159 @@ struct PLay {
     static constexpr size_t OFF_QL = OFF_KR + TILE;                        // [C][LDK] q e^{G_r - G_m(R)} (EXPAND)
     static constexpr size_t OFF_KG = OFF_QL + (EXP ? TILE : 0);            // -k e^G [C][LDK] pcol
     static constexpr size_t OFF_RV = OFF_KG + TILE;                        // v^T [DV][LC]
+    // K~^T and e^{G_C}: COMPOSE keeps two buffers (by chunk parity), so that
+    // chunk m-1's state update can run while chunk m's are written
+    static constexpr int NKB = EXP ? 1 : 2;
+    static constexpr size_t KGT_SZ = a16((size_t)DK * LC * 2);
     static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
-    static constexpr size_t OFF_QG = OFF_KGT + a16((size_t)DK * LC * 2);   // q e^G [C][LDK] pcol (EXPAND)
+    static constexpr size_t OFF_QG = OFF_KGT + NKB * KGT_SZ;               // q e^G [C][LDK] pcol (EXPAND)
     static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol (EXPAND)
     static constexpr size_t OFF_AS = OFF_M + (EXP ? a16((size_t)C * LC * 2) : 0);   // [4][BS] beta A~_RR^T
     static constexpr size_t OFF_AB = OFF_AS + (size_t)4 * BS * 4;          // [6][16][LB] -A~_RI
     static constexpr size_t OFF_DB = OFF_AB + a16((size_t)6 * SUB * LB * 2);   // [4][16][LB] D'_R
     static constexpr size_t OFF_EGC = OFF_DB + a16((size_t)4 * SUB * LB * 2);
-    static constexpr size_t OFF_DSC = OFF_EGC + (size_t)DK * 4;            // [6][DK] e^{G_m(R) - G_m(I)}
+    static constexpr size_t OFF_DSC = OFF_EGC + NKB * (size_t)DK * 4;      // [6][DK] e^{G_m(R) - G_m(I)}
     static constexpr size_t OFF_TOT = OFF_DSC + 6 * (size_t)DK * 4;        // [4][DK] block sums of the gate
     static constexpr size_t OFF_MLOC = OFF_TOT + 4 * (size_t)DK * 4;       // [4][DK] G_m(R) - G_{16R-1}
     static constexpr size_t OFF_BET = OFF_MLOC + 4 * (size_t)DK * 4;
     static constexpr size_t LDS = OFF_BET + C * 4;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// Recurrence step of the pipelined kernel, first part: V_new = T' Z with
+// Z = V - (K e^G) S, left in yb as bf16 B fragments, and for EXPAND the
+// outputs O = (Q e^G) S + M V_new.  Same register layouts as chain_step.
+template <int MODE, int NTW, class L>
+__device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[2][NTW], bool hasu, int ucol0,
+                                        const unsigned char* smem, bf16* __restrict__ orow0, int valid,
+                                        size_t ostride) {
+    typedef Mfma<bf16> MF;
+    constexpr bool EXP = MODE == EXPAND;
+    const int l = lane_id(), g = l >> 4, c = l & 15;
+    const bf16* VT = reinterpret_cast<const bf16*>(smem + L::OFF_RV);
+    const bf16* Tp = reinterpret_cast<const bf16*>(smem + L::OFF_TP);
+    const bf16* KGn = reinterpret_cast<const bf16*>(smem + L::OFF_KG);
+    const bf16* QG = reinterpret_cast<const bf16*>(smem + L::OFF_QG);
+    const bf16* Ms = reinterpret_cast<const bf16*>(smem + L::OFF_M);
+    f32x4 y[4][NTW];
+#pragma unroll
+    for (int yt = 0; yt < 4; ++yt)
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct)
+            y[yt][ct] = hasu ? load4<bf16>(VT + (ucol0 + ct * 16 + c) * L::LC + yt * 16 + 4 * g) : zero4();
+    f32x4 ov[EXP ? 4 : 1][NTW];
+    if constexpr (EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) ov[ot][ct] = zero4();
+    }
+    MF::frag wf[2][4], qf[2][EXP ? 4 : 1];
+#pragma unroll
+    for (int yt = 0; yt < 4; ++yt) wf[0][yt] = load_frag<bf16>(KGn, L::LDK, yt * 16, 0);
+    if constexpr (EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) qf[0][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int cur = kb & 1, nxt = cur ^ 1;
+        if (kb + 1 < 4) {
+#pragma unroll
+            for (int yt = 0; yt < 4; ++yt) wf[nxt][yt] = load_frag<bf16>(KGn, L::LDK, yt * 16, (kb + 1) * 32);
+            if constexpr (EXP) {
+#pragma unroll
+                for (int ot = 0; ot < 4; ++ot) qf[nxt][ot] = load_frag<bf16>(QG, L::LDK, ot * 16, (kb + 1) * 32);
+            }
+        }
+        bf16x8 xb[NTW];
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) xb[ct] = pack8(xs[2 * kb][ct], xs[2 * kb + 1][ct]);
+#pragma unroll
+        for (int yt = 0; yt < 4; ++yt)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) y[yt][ct] = MF::mma(wf[cur][yt], xb[ct], y[yt][ct]);
+        if constexpr (EXP) {
+#pragma unroll
+            for (int ot = 0; ot < 4; ++ot)
+#pragma unroll
+                for (int ct = 0; ct < NTW; ++ct) ov[ot][ct] = MF::mma(xb[ct], qf[cur][ot], ov[ot][ct]);
+        }
+    }
+    MF::frag mf[EXP ? 4 : 1][2];
+    if constexpr (EXP) {
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+            mf[ot][0] = load_frag<bf16>(Ms, L::LC, ot * 16, 0);
+            mf[ot][1] = load_frag<bf16>(Ms, L::LC, ot * 16, 32);
+        }
+    }
+    {
+        bf16x8 zb[2][NTW];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) zb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
+#pragma unroll
+        for (int yt = 0; yt < 4; ++yt) {
+            const MF::frag t0 = load_frag<bf16>(Tp, L::LC, yt * 16, 0);
+            const MF::frag t1 = load_frag<bf16>(Tp, L::LC, yt * 16, 32);
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) {
+                y[yt][ct] = MF::mma(t0, zb[0][ct], zero4());
+                y[yt][ct] = MF::mma(t1, zb[1][ct], y[yt][ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) yb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
+    if constexpr (EXP) {
+        // lane holds O[16 ot + c][col0 + 16 ct + 4g + e]
+#pragma unroll
+        for (int ot = 0; ot < 4; ++ot) {
+#pragma unroll
+            for (int ct = 0; ct < NTW; ++ct) {
+                ov[ot][ct] = MF::mma(yb[0][ct], mf[ot][0], ov[ot][ct]);
+                ov[ot][ct] = MF::mma(yb[1][ct], mf[ot][1], ov[ot][ct]);
+            }
+            if (ot * 16 + c < valid) {
+                bf16* orow = orow0 + (size_t)(ot * 16 + c) * ostride + 4 * g;
+#pragma unroll
+                for (int ct = 0; ct < NTW; ++ct) store4<bf16>(orow + ct * 16, ov[ot][ct]);
+            }
+        }
+    }
+}
+
+// Second part: S <- Diag(e^{G_C}) S + K~^T V_new.
+template <int NTW, class L>
+__device__ __forceinline__ void chain_b(f32x4 (&xs)[8][NTW], const bf16x8 (&yb)[2][NTW], const bf16* KGT,
+                                        const float* egc) {
+    typedef Mfma<bf16> MF;
+    const int g = lane_id() >> 4;
+    MF::frag kf[2][2];
+    f32x4 dv[2];
+    kf[0][0] = load_frag<bf16>(KGT, L::LC, 0, 0);
+    kf[0][1] = load_frag<bf16>(KGT, L::LC, 0, 32);
+    dv[0] = *reinterpret_cast<const f32x4*>(egc + 4 * g);
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+        const int cur = rt & 1, nxt = cur ^ 1;
+        if (rt + 1 < 8) {
+            kf[nxt][0] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 0);
+            kf[nxt][1] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 32);
+            dv[nxt] = *reinterpret_cast<const f32x4*>(egc + (rt + 1) * 16 + 4 * g);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NTW; ++ct) {
+            xs[rt][ct] *= dv[cur];
+            xs[rt][ct] = MF::mma(kf[cur][0], yb[0][ct], xs[rt][ct]);
+            xs[rt][ct] = MF::mma(kf[cur][1], yb[1][ct], xs[rt][ct]);
+        }
+    }
+}
 
 // One chunk's tokens as a gate wave loads them: rows 16R + i, channels 2l,
 // 2l+1 (v likewise); beta of row l.
@@ -766,14 +905,18 @@ __device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__
                                            const bf16* __restrict__ z, const bf16* __restrict__ beta, size_t row0,
                                            int valid, int H, int R) {
     const int l = lane_id(), last = valid - 1;
-    const unsigned c0 = 2u * (unsigned)l;
+    // wave-uniform chunk bases and 32-bit byte offsets (row, clamped to the
+    // last token, then the lane's two channels): scalar-base addressing
+    const char* zb = reinterpret_cast<const char*>(z + row0 * 128);
+    const char* kb = reinterpret_cast<const char*>(k + row0 * 128);
+    const char* qb = reinterpret_cast<const char*>(q + row0 * 128);
+    const unsigned lo = 4u * (unsigned)l, rstride = (unsigned)H * 256u;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
-        // row clamped to the last token (rows past it are masked at use)
-        const size_t ro = (row0 + (size_t)min(SUB * R + i, last) * H) * 128;
-        r.z[i] = load2<bf16>(z + ro + c0);
-        r.k[i] = load2<bf16>(k + ro + c0);
-        if constexpr (EXP) r.q[i] = load2<bf16>(q + ro + c0);
+        const unsigned off = (unsigned)min(SUB * R + i, last) * rstride + lo;
+        r.z[i] = *reinterpret_cast<const bf16x2*>(zb + off);
+        r.k[i] = *reinterpret_cast<const bf16x2*>(kb + off);
+        if constexpr (EXP) r.q[i] = *reinterpret_cast<const bf16x2*>(qb + off);
     }
     r.beta = beta[row0 + (size_t)min(l, last) * H];
 }
@@ -793,10 +936,12 @@ __device__ __forceinline__ void pmask(PIn<EXP>& r, int valid, int R) {
 }
 
 __device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size_t row0, int valid, int H, int R) {
-    const unsigned c0 = 2u * (unsigned)lane_id();
     const int last = valid - 1;
+    const char* vb = reinterpret_cast<const char*>(v + row0 * 128);
+    const unsigned lo = 4u * (unsigned)lane_id(), rstride = (unsigned)H * 256u;
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) r.v[i] = load2<bf16>(v + (row0 + (size_t)min(SUB * R + i, last) * H) * 128 + c0);
+    for (int i = 0; i < SUB; ++i)
+        r.v[i] = *reinterpret_cast<const bf16x2*>(vb + (unsigned)min(SUB * R + i, last) * rstride + lo);
 }
 
 // S1 of gate wave R (rows past the end have been made identity tokens).  On
@@ -849,32 +994,40 @@ __device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, 
     }
 }
 
-// S2 of gate wave R, after pipe_abs: A_RR (and M_RR) from the block's own
-// rows of KL, KR, QL, then D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R).
+// S2 of gate wave R: A_RR (and M_RR) from the block's own rows of KL, KR,
+// QL, transposed: lane holds row r = 16R + l%16, key indices 16R + 4(l/16) + e.
+// Issued first, so that pipe_abs runs while the products are in flight.
 template <int MODE>
-__device__ __forceinline__ void pipe_diag(int R, unsigned char* smem) {
+__device__ __forceinline__ void pipe_diag_mma(int R, const unsigned char* smem, f32x4& accA, f32x4& accM) {
     typedef PLay<MODE> L;
     typedef Mfma<bf16> MF;
-    constexpr bool EXP = L::EXP;
-    constexpr int LDK = L::LDK, LC = L::LC, LB = L::LB, BS = L::BS;
-    int l = lane_id();
-    asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
+    constexpr int LDK = L::LDK;
     const bf16* KL = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
     const bf16* KR = reinterpret_cast<const bf16*>(smem + L::OFF_KR);
     const bf16* QL = reinterpret_cast<const bf16*>(smem + L::OFF_QL);
-    bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);
-    float* As = reinterpret_cast<float*>(smem + L::OFF_AS);
-    bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);
-    const float* bet = reinterpret_cast<const float*>(smem + L::OFF_BET);
-    // A_RR (and M_RR) transposed: lane holds row r = 16R + l%16, key indices
-    // i = 16R + 4(l/16) + e
-    f32x4 accA = zero4(), accM = zero4();
+    accA = zero4();
+    accM = zero4();
 #pragma unroll
     for (int kk = 0; kk < 128; kk += MF::KSTEP) {
         const MF::frag ak = load_frag<bf16>(KR, LDK, R * SUB, kk);
         accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
-        if constexpr (EXP) accM = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM);
+        if constexpr (L::EXP) accM = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM);
     }
+}
+
+// Then beta_r A~_RR (strictly lower) and M_RR into LDS, and
+// D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R).
+template <int MODE>
+__device__ __forceinline__ void pipe_diag_inv(int R, unsigned char* smem, const f32x4& accA, f32x4 accM) {
+    typedef PLay<MODE> L;
+    constexpr bool EXP = L::EXP;
+    constexpr int LC = L::LC, LB = L::LB, BS = L::BS;
+    int l = lane_id();
+    asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
+    bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);
+    float* As = reinterpret_cast<float*>(smem + L::OFF_AS);
+    bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);
+    const float* bet = reinterpret_cast<const float*>(smem + L::OFF_BET);
     const int rr = l & 15, ii = 4 * (l >> 4);
     {
         const float br = bet[R * SUB + rr];
@@ -888,8 +1041,8 @@ __device__ __forceinline__ void pipe_diag(int R, unsigned char* smem) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's As stores
 
-    // D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R): lane = column, right-looking
-    // substitution down the column (lanes 16.. repeat lanes 0..15)
+    // lane = column, right-looking substitution down the column (lanes 16..
+    // repeat lanes 0..15)
     const int col = l & 15;
     const float* at = As + R * BS;   // at[i * 16 + r] = beta_r A~_ri
     float x[SUB];
@@ -906,7 +1059,6 @@ __device__ __forceinline__ void pipe_diag(int R, unsigned char* smem) {
         for (int r = 0; r < SUB; ++r) d[r * LB] = (bf16)(x[r] * bc);
     }
 }
-
 
 // S2 of gate wave R: absolute block references from the block sums, then the
 // chain operands of block R.
@@ -928,15 +1080,15 @@ __device__ __forceinline__ void pipe_vt(const PV& pv, int R, unsigned char* smem
 template <int MODE>
 __device__ __forceinline__ void pipe_abs(int R, unsigned char* smem,
                                          const float (&kl)[SUB][2], const float (&kr)[SUB][2],
-                                         const float (&ql)[MODE == EXPAND ? SUB : 1][2]) {
+                                         const float (&ql)[MODE == EXPAND ? SUB : 1][2], int buf) {
     typedef PLay<MODE> L;
     constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK, LC = L::LC;
     const int l = lane_id(), c0 = 2 * l;
     bf16* KGn = reinterpret_cast<bf16*>(smem + L::OFF_KG);
     bf16* QG = reinterpret_cast<bf16*>(smem + L::OFF_QG);
-    bf16* KGT = reinterpret_cast<bf16*>(smem + L::OFF_KGT);
-    float* egc = reinterpret_cast<float*>(smem + L::OFF_EGC);
+    bf16* KGT = reinterpret_cast<bf16*>(smem + L::OFF_KGT + buf * L::KGT_SZ);
+    float* egc = reinterpret_cast<float*>(smem + L::OFF_EGC + buf * 128 * 4);
     const float* tot = reinterpret_cast<const float*>(smem + L::OFF_TOT);
     const float* mloc = reinterpret_cast<const float*>(smem + L::OFF_MLOC);
 
@@ -1152,23 +1304,32 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         const size_t ostride = (size_t)H * DV;
         PV pv;
         if constexpr (EXP) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
-        for (int i = 0; i <= nL; ++i) {
-            if (i > 0) {
-                const int m = n0 + i - 1;
-                const int valid = min(C, T - m * C);
+        bf16x8 yb[NH][2][2];
+        // state update of chunk n from V_new in yb (COMPOSE defers it to S2)
+        auto update = [&](int n) {
+            const int bufn = LY::NKB == 2 ? (n & 1) : 0;
+            const bf16* KGT = reinterpret_cast<const bf16*>(smem + LY::OFF_KGT + bufn * LY::KGT_SZ);
+            const float* egc = reinterpret_cast<const float*>(smem + LY::OFF_EGC + bufn * 128 * 4);
 #pragma unroll
-                for (int hh = 0; hh < NH; ++hh) {
-                    const int col0 = cbase + 32 * hh;
-                    chain_step<DK, DV, MODE, 2, LY>(xs[hh], hasu, col0, smem, o + row_of(m) * DV + col0, valid,
-                                                    ostride);
-                    __builtin_amdgcn_sched_barrier(0);   // one half's working set at a time
-                }
+            for (int hh = 0; hh < NH; ++hh) {
+                chain_b<2, LY>(xs[hh], yb[hh], KGT, egc);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (i == nL) break;
-            __syncthreads();   // S1 | S2
+        };
+        auto chain = [&](int m) {
+            const int valid = min(C, T - m * C);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+                const int col0 = cbase + 32 * hh;
+                chain_a<MODE, 2, LY>(xs[hh], yb[hh], hasu, col0, smem, o + row_of(m) * DV + col0, valid, ostride);
+                __builtin_amdgcn_sched_barrier(0);   // one half's working set at a time
+            }
+        };
+        // S2 and S3 of chunk n (the state waves' share)
+        auto s2s3 = [&](int n) {
             if constexpr (EXP) {
                 pipe_vt<MODE>(pv, w, smem);
-                const int mn = min(n0 + i + 1, n1 - 1);
+                const int mn = min(n + 1, n1 - 1);
                 pfetch_v(pv, v, row_of(mn), min(C, T - mn * C), H, w);
             }
             if (w < 2)
@@ -1177,7 +1338,24 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 1>(w, smem);
             __syncthreads();   // S2 | S3
             __syncthreads();   // S3 | next S1
+        };
+        // iteration 0 has no step to run; iterations 1.. run the step of the
+        // previous chunk in S1 (COMPOSE: its state update in S2)
+        __syncthreads();   // S1 | S2
+        s2s3(n0);
+        for (int i = 1; i < nL; ++i) {
+            const int m = n0 + i;
+            chain(m - 1);
+            if constexpr (EXP) update(m - 1);
+            __syncthreads();   // S1 | S2
+            if constexpr (!EXP) {
+                update(m - 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            s2s3(m);
         }
+        chain(n1 - 1);
+        update(n1 - 1);
         float* xo = EXP ? xo0 : (ptile ? xo0 : xo1);
         if (xo) {
             const size_t ob = EXP ? bh * DK : xblk;
@@ -1215,12 +1393,18 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
             pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
             __syncthreads();   // S1 | S2
-            pipe_abs<MODE>(R, smem, kl, kr, ql);
-            if constexpr (!EXP) {
+            f32x4 accA, accM;
+            if constexpr (EXP) {
+                // products in flight while the operands are written
+                pipe_diag_mma<MODE>(R, smem, accA, accM);
+                pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
+            } else {
+                pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
                 pipe_vt<MODE>(pv, R, smem);
-                pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+                pipe_diag_mma<MODE>(R, smem, accA, accM);
             }
-            pipe_diag<MODE>(R, smem);
+            pipe_diag_inv<MODE>(R, smem, accA, accM);
+            if constexpr (!EXP) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
             __syncthreads();   // S2 | S3
             pipe_tsolve<MODE>(R, smem);
             __syncthreads();   // S3 | next S1
