@@ -48,9 +48,15 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_14_amd", "csrc")
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank lines removed, so
+    that the stored counters stay attached to the code they were taken on."""
+    import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

@@ -34,6 +34,12 @@
 // Overflow handling of the decay factors is that of the fp32 path: A and M
 // per 16x16 block pair with reference rows m(R) = 16R + 7, decay exponents in
 // log2 units so that every factor is one v_exp_f32.
+//
+// Two kernels walk the segments.  pipe_kernel (d_k = d_v = 128) splits the
+// waves into state waves, which advance the state, and gate waves, which
+// prepare the next chunk, so that the MFMA-bound step and the VALU-bound gate
+// run side by side on every SIMD.  seg_kernel (every width) runs all phases
+// on all waves one after the other; it serves d_k or d_v = 64.
 #include <stdlib.h>
 
 #include "kda_device.hpp"
