@@ -52,7 +52,7 @@ constexpr int C = 64;       // chunk length
 constexpr int SUB = 16;     // block size of A, M and the triangular solve
 constexpr int NTH = 512;    // threads per workgroup (8 waves)
 constexpr float LOG2E = 1.4426950408889634f;
-enum { COMPOSE = 0, EXPAND = 1 };
+enum { COMPOSE = 0, EXPAND = 1, EXPAND_LITE = 2 };
 
 constexpr size_t a16(size_t x) { return (x + 15) / 16 * 16; }
 constexpr size_t mx(size_t a, size_t b) { return a > b ? a : b; }
@@ -729,33 +729,48 @@ __global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, co
 template <int MODE>
 struct PLay {
     static constexpr int DK = 128, DV = 128;
-    static constexpr bool EXP = MODE == EXPAND;
+    static constexpr bool EXP = MODE != COMPOSE;      // outputs O (and so q, M)
+    static constexpr bool LITE = MODE == EXPAND_LITE; // T' read from the compose pass
+    static constexpr bool SOLVE = !LITE;              // A, its inverses and T' formed here
     static constexpr int LDK = DK + 8, LC = C + 8, LB = SUB + 8, BS = SUB * SUB + 16;
     static constexpr size_t TILE = (size_t)C * LDK * 2;
+    static constexpr size_t CC = a16((size_t)C * LC * 2);                 // one C x C bf16 operand
     static constexpr size_t OFF_TP = 0;                                    // T' [C][LC] pcol
-    static constexpr size_t OFF_KL = a16((size_t)C * LC * 2);              // [C][LDK] k e^{G_r - G_m(R)}
+    static constexpr size_t OFF_KL = CC;                                   // [C][LDK] k e^{G_r - G_m(R)}
     static constexpr size_t OFF_KR = OFF_KL + TILE;                        // [C][LDK] k e^{G_m(R) - G_r}
-    static constexpr size_t OFF_QL = OFF_KR + TILE;                        // [C][LDK] q e^{G_r - G_m(R)} (EXPAND)
+    static constexpr size_t OFF_QL = OFF_KR + TILE;                        // [C][LDK] q e^{G_r - G_m(R)} (outputs)
     static constexpr size_t OFF_KG = OFF_QL + (EXP ? TILE : 0);            // -k e^G [C][LDK] pcol
     static constexpr size_t OFF_RV = OFF_KG + TILE;                        // v^T [DV][LC]
     // K~^T and e^{G_C}: COMPOSE keeps two buffers (by chunk parity), so that
     // chunk m-1's state update can run while chunk m's are written
-    static constexpr int NKB = EXP ? 1 : 2;
+    static constexpr int NKB = MODE == COMPOSE ? 2 : 1;
     static constexpr size_t KGT_SZ = a16((size_t)DK * LC * 2);
     static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
-    static constexpr size_t OFF_QG = OFF_KGT + NKB * KGT_SZ;               // q e^G [C][LDK] pcol (EXPAND)
-    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol (EXPAND)
-    static constexpr size_t OFF_AS = OFF_M + (EXP ? a16((size_t)C * LC * 2) : 0);   // [4][BS] beta A~_RR^T
-    static constexpr size_t OFF_AB = OFF_AS + (size_t)4 * BS * 4;          // [6][16][LB] -A~_RI
-    static constexpr size_t OFF_DB = OFF_AB + a16((size_t)6 * SUB * LB * 2);   // [4][16][LB] D'_R
-    static constexpr size_t OFF_EGC = OFF_DB + a16((size_t)4 * SUB * LB * 2);
+    static constexpr size_t OFF_QG = OFF_KGT + NKB * KGT_SZ;               // q e^G [C][LDK] pcol (outputs)
+    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol (outputs)
+    static constexpr size_t OFF_AS = OFF_M + (EXP ? CC : 0);               // [4][BS] beta A~_RR^T
+    static constexpr size_t OFF_AB = OFF_AS + (SOLVE ? (size_t)4 * BS * 4 : 0);             // [6][16][LB] -A~_RI
+    static constexpr size_t OFF_DB = OFF_AB + (SOLVE ? a16((size_t)6 * SUB * LB * 2) : 0);  // [4][16][LB] D'_R
+    static constexpr size_t OFF_EGC = OFF_DB + (SOLVE ? a16((size_t)4 * SUB * LB * 2) : 0);
     static constexpr size_t OFF_DSC = OFF_EGC + NKB * (size_t)DK * 4;      // [6][DK] e^{G_m(R) - G_m(I)}
-    static constexpr size_t OFF_TOT = OFF_DSC + 6 * (size_t)DK * 4;        // [4][DK] block sums of the gate
+    static constexpr size_t OFF_TOT = OFF_DSC + 6 * (size_t)DK * 4;        // [4][DK] block sums
     static constexpr size_t OFF_MLOC = OFF_TOT + 4 * (size_t)DK * 4;       // [4][DK] G_m(R) - G_{16R-1}
     static constexpr size_t OFF_BET = OFF_MLOC + 4 * (size_t)DK * 4;
     static constexpr size_t LDS = OFF_BET + C * 4;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// Per-chunk T' handed from the compose pass to the expand pass: per (chain,
+// chunk) one 64 x 64 bf16 matrix, rows of 64 in the LDS column order (pcol),
+// 8 KB.
+constexpr size_t TM_ELEMS = (size_t)C * C;
+
+// Piece p (16 bytes) of a chunk's T': row p / 8, eighth p % 8 of the row; its
+// place in LDS (padded rows of LC).
+template <class L>
+__device__ __forceinline__ f32x4* tp_lds(unsigned char* smem, int p) {
+    return reinterpret_cast<f32x4*>(smem + L::OFF_TP + (size_t)(p >> 3) * L::LC * 2 + (p & 7) * 16);
+}
 
 // Recurrence step of the pipelined kernel, first part: V_new = T' Z with
 // Z = V - (K e^G) S, left in yb as bf16 B fragments, and for EXPAND the
@@ -765,7 +780,7 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
                                         const unsigned char* smem, bf16* __restrict__ orow0, int valid,
                                         size_t ostride) {
     typedef Mfma<bf16> MF;
-    constexpr bool EXP = MODE == EXPAND;
+    constexpr bool EXP = L::EXP;
     const int l = lane_id(), g = l >> 4, c = l & 15;
     const bf16* VT = reinterpret_cast<const bf16*>(smem + L::OFF_RV);
     const bf16* Tp = reinterpret_cast<const bf16*>(smem + L::OFF_TP);
@@ -894,9 +909,9 @@ __device__ __forceinline__ void chain_b(f32x4 (&xs)[8][NTW], const bf16x8 (&yb)[
 
 // One chunk's tokens as a gate wave loads them: rows 16R + i, channels 2l,
 // 2l+1 (v likewise); beta of row l.
-template <bool EXP>
+template <bool HASQ>
 struct PIn {
-    bf16x2 z[SUB], k[SUB], q[EXP ? SUB : 1];
+    bf16x2 z[SUB], k[SUB], q[HASQ ? SUB : 1];
     bf16 beta;
 };
 // v of rows 16R + i, channels 2l, 2l+1, as the wave that writes v^T loads it:
@@ -906,8 +921,8 @@ struct PV {
     bf16x2 v[SUB];
 };
 
-template <bool EXP>
-__device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
+template <bool HASQ>
+__device__ __forceinline__ void pfetch_zkq(PIn<HASQ>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
                                            const bf16* __restrict__ z, const bf16* __restrict__ beta, size_t row0,
                                            int valid, int H, int R) {
     const int l = lane_id(), last = valid - 1;
@@ -922,7 +937,7 @@ __device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__
         const unsigned off = (unsigned)min(SUB * R + i, last) * rstride + lo;
         r.z[i] = *reinterpret_cast<const bf16x2*>(zb + off);
         r.k[i] = *reinterpret_cast<const bf16x2*>(kb + off);
-        if constexpr (EXP) r.q[i] = *reinterpret_cast<const bf16x2*>(qb + off);
+        if constexpr (HASQ) r.q[i] = *reinterpret_cast<const bf16x2*>(qb + off);
     }
     r.beta = beta[row0 + (size_t)min(l, last) * H];
 }
@@ -930,14 +945,14 @@ __device__ __forceinline__ void pfetch_zkq(PIn<EXP>& r, const bf16* __restrict__
 // Rows at or past `valid` of a ragged last chunk become identity tokens:
 // z = -inf (a zero gate, alpha = 1) and k = q = 0 (no write, no read); beta
 // is set to 0 where it is stored.
-template <bool EXP>
-__device__ __forceinline__ void pmask(PIn<EXP>& r, int valid, int R) {
+template <bool HASQ>
+__device__ __forceinline__ void pmask(PIn<HASQ>& r, int valid, int R) {
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
         const unsigned keep = SUB * R + i < valid ? 0xffffffffu : 0u;
         r.z[i] = __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, r.z[i]) & keep) | (0xff80ff80u & ~keep));
         r.k[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.k[i]) & keep);
-        if constexpr (EXP) r.q[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.q[i]) & keep);
+        if constexpr (HASQ) r.q[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.q[i]) & keep);
     }
 }
 
@@ -953,9 +968,9 @@ __device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size
 // S1 of gate wave R (rows past the end have been made identity tokens).  On
 // return kl, kr, ql hold the block's decay-scaled k and q (fp32).
 template <int MODE>
-__device__ __forceinline__ void pipe_gate(const PIn<MODE == EXPAND>& in, int R, int valid, float kg2,
+__device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
                                           unsigned char* smem, float (&kl)[SUB][2], float (&kr)[SUB][2],
-                                          float (&ql)[MODE == EXPAND ? SUB : 1][2]) {
+                                          float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
     typedef PLay<MODE> L;
     constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK;
@@ -1016,7 +1031,7 @@ __device__ __forceinline__ void pipe_diag_mma(int R, const unsigned char* smem, 
 #pragma unroll
     for (int kk = 0; kk < 128; kk += MF::KSTEP) {
         const MF::frag ak = load_frag<bf16>(KR, LDK, R * SUB, kk);
-        accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
+        if constexpr (L::SOLVE) accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
         if constexpr (L::EXP) accM = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM);
     }
 }
@@ -1026,7 +1041,6 @@ __device__ __forceinline__ void pipe_diag_mma(int R, const unsigned char* smem, 
 template <int MODE>
 __device__ __forceinline__ void pipe_diag_inv(int R, unsigned char* smem, const f32x4& accA, f32x4 accM) {
     typedef PLay<MODE> L;
-    constexpr bool EXP = L::EXP;
     constexpr int LC = L::LC, LB = L::LB, BS = L::BS;
     int l = lane_id();
     asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
@@ -1035,34 +1049,34 @@ __device__ __forceinline__ void pipe_diag_inv(int R, unsigned char* smem, const 
     bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);
     const float* bet = reinterpret_cast<const float*>(smem + L::OFF_BET);
     const int rr = l & 15, ii = 4 * (l >> 4);
-    {
+    if constexpr (L::EXP) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accM[e] = (ii + e <= rr) ? accM[e] : 0.f;
+        store4p(Ms + (R * SUB + rr) * LC + pcol(R * SUB + ii), accM[0], accM[1], accM[2], accM[3]);
+    }
+    if constexpr (L::SOLVE) {
         const float br = bet[R * SUB + rr];
 #pragma unroll
         for (int e = 0; e < 4; ++e) As[R * BS + (ii + e) * SUB + rr] = (ii + e < rr) ? br * accA[e] : 0.f;
-        if constexpr (EXP) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) accM[e] = (ii + e <= rr) ? accM[e] : 0.f;
-            store4p(Ms + (R * SUB + rr) * LC + pcol(R * SUB + ii), accM[0], accM[1], accM[2], accM[3]);
-        }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's As stores
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's As stores
 
-    // lane = column, right-looking substitution down the column (lanes 16..
-    // repeat lanes 0..15)
-    const int col = l & 15;
-    const float* at = As + R * BS;   // at[i * 16 + r] = beta_r A~_ri
-    float x[SUB];
+        // lane = column, right-looking substitution down the column (lanes
+        // 16.. repeat lanes 0..15)
+        const int col = l & 15;
+        const float* at = As + R * BS;   // at[i * 16 + r] = beta_r A~_ri
+        float x[SUB];
 #pragma unroll
-    for (int r = 0; r < SUB; ++r) x[r] = (r == col) ? 1.f : 0.f;
-    inv_batch<0, 3>(at, x);
-    inv_batch<3, 7>(at, x);
-    inv_batch<7, 11>(at, x);
-    inv_batch<11, 15>(at, x);
-    if (l < 16) {
-        const float bc = bet[R * SUB + col];
-        bf16* d = Db + R * SUB * LB + col;
+        for (int r = 0; r < SUB; ++r) x[r] = (r == col) ? 1.f : 0.f;
+        inv_batch<0, 3>(at, x);
+        inv_batch<3, 7>(at, x);
+        inv_batch<7, 11>(at, x);
+        inv_batch<11, 15>(at, x);
+        if (l < 16) {
+            const float bc = bet[R * SUB + col];
+            bf16* d = Db + R * SUB * LB + col;
 #pragma unroll
-        for (int r = 0; r < SUB; ++r) d[r * LB] = (bf16)(x[r] * bc);
+            for (int r = 0; r < SUB; ++r) d[r * LB] = (bf16)(x[r] * bc);
+        }
     }
 }
 
@@ -1086,7 +1100,7 @@ __device__ __forceinline__ void pipe_vt(const PV& pv, int R, unsigned char* smem
 template <int MODE>
 __device__ __forceinline__ void pipe_abs(int R, unsigned char* smem,
                                          const float (&kl)[SUB][2], const float (&kr)[SUB][2],
-                                         const float (&ql)[MODE == EXPAND ? SUB : 1][2], int buf) {
+                                         const float (&ql)[MODE != COMPOSE ? SUB : 1][2], int buf) {
     typedef PLay<MODE> L;
     constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK, LC = L::LC;
@@ -1199,17 +1213,18 @@ __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
                 t[jj + 4] *= d1[jj];
             }
             ak = MF::from_floats(t);
-            accA[j] = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA[j]);
-            if constexpr (EXP) accM[j] = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM[j]);
+            if constexpr (L::SOLVE) accA[j] = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA[j]);
+            if constexpr (L::EXP) accM[j] = MF::mma(ak, load_frag<bf16>(QL, LDK, R * SUB, kk), accM[j]);
         }
     }
     const int rr = l & 15, ii = 4 * (l >> 4);
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
         const int R = Rp[j], I = Ip[j];
-        store4p(Ab + ((R * (R - 1) / 2 + I) * SUB + rr) * LB + ii, -accA[j][0], -accA[j][1], -accA[j][2],
-                -accA[j][3]);
-        if constexpr (EXP)
+        if constexpr (L::SOLVE)
+            store4p(Ab + ((R * (R - 1) / 2 + I) * SUB + rr) * LB + ii, -accA[j][0], -accA[j][1], -accA[j][2],
+                    -accA[j][3]);
+        if constexpr (L::EXP)
             store4p(Ms + (R * SUB + rr) * LC + pcol(I * SUB + ii), accM[j][0], accM[j][1], accM[j][2], accM[j][3]);
     }
 }
@@ -1252,17 +1267,19 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
     }
 }
 
-// Same grid and arguments as seg_kernel.
+// Same grid and arguments as seg_kernel, plus tm: the per-chunk T'
+// ([chain][chunk] x TM_ELEMS bf16) that COMPOSE writes and EXPAND_LITE reads
+// (unused by EXPAND, which forms it itself).
 template <int MODE>
 __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const bf16* __restrict__ z,
                                                    const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
                                                    int L, int nchain, const float* __restrict__ xin,
                                                    float* __restrict__ xo0, float* __restrict__ xo1,
-                                                   bf16* __restrict__ o) {
+                                                   bf16* __restrict__ o, bf16* __restrict__ tm) {
     typedef PLay<MODE> LY;
     constexpr int DK = 128, DV = 128;
-    constexpr bool EXP = MODE == EXPAND;
+    constexpr bool EXP = LY::EXP, LITE = LY::LITE;
     extern __shared__ __align__(16) unsigned char smem[];
     const int seg = blockIdx.x / nchain;
     const size_t bh = blockIdx.x % nchain;
@@ -1270,7 +1287,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
     const int l = lane_id(), w = wave_id();
     __builtin_assume(w >= 0 && w < NTH / 64);
     const int n0 = seg * L, n1 = min(NC, n0 + L), nL = n1 - n0;
-    auto row_of = [&](int n) { return ((size_t)b * T + (size_t)n * C) * H + h; };
+    auto row_of = [&](int n) __attribute__((always_inline)) { return ((size_t)b * T + (size_t)n * C) * H + h; };
+    auto tm_of = [&](int n) __attribute__((always_inline)) { return tm + (bh * NC + n) * TM_ELEMS; };
 
     if constexpr (EXP) {
         // strictly upper blocks of M stay zero
@@ -1312,7 +1330,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         if constexpr (EXP) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
         bf16x8 yb[NH][2][2];
         // state update of chunk n from V_new in yb (COMPOSE defers it to S2)
-        auto update = [&](int n) {
+        auto update = [&](int n) __attribute__((always_inline)) {
             const int bufn = LY::NKB == 2 ? (n & 1) : 0;
             const bf16* KGT = reinterpret_cast<const bf16*>(smem + LY::OFF_KGT + bufn * LY::KGT_SZ);
             const float* egc = reinterpret_cast<const float*>(smem + LY::OFF_EGC + bufn * 128 * 4);
@@ -1322,7 +1340,14 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        auto chain = [&](int m) {
+        auto chain = [&](int m) __attribute__((always_inline)) {
+            // COMPOSE hands the chunk's T' (complete since the last barrier)
+            // to the expand pass
+            if constexpr (MODE == COMPOSE) {
+                f32x4* g = reinterpret_cast<f32x4*>(tm_of(m));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) g[threadIdx.x + 256 * j] = *tp_lds<LY>(smem, threadIdx.x + 256 * j);
+            }
             const int valid = min(C, T - m * C);
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
@@ -1331,8 +1356,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 __builtin_amdgcn_sched_barrier(0);   // one half's working set at a time
             }
         };
-        // S2 and S3 of chunk n (the state waves' share)
-        auto s2s3 = [&](int n) {
+        // the state waves' share of the steps after S1 for chunk n
+        auto rest = [&](int n) __attribute__((always_inline)) {
             if constexpr (EXP) {
                 pipe_vt<MODE>(pv, w, smem);
                 const int mn = min(n + 1, n1 - 1);
@@ -1342,13 +1367,13 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 2>(w, smem);
             else
                 pipe_pairs<MODE, 1>(w, smem);
-            __syncthreads();   // S2 | S3
-            __syncthreads();   // S3 | next S1
+            if constexpr (!LITE) __syncthreads();   // S2 | S3
+            __syncthreads();   // S3 (S2 for EXPAND_LITE) | next S1
         };
         // iteration 0 has no step to run; iterations 1.. run the step of the
         // previous chunk in S1 (COMPOSE: its state update in S2)
         __syncthreads();   // S1 | S2
-        s2s3(n0);
+        rest(n0);
         for (int i = 1; i < nL; ++i) {
             const int m = n0 + i;
             chain(m - 1);
@@ -1358,7 +1383,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 update(m - 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            s2s3(m);
+            rest(m);
         }
         chain(n1 - 1);
         update(n1 - 1);
@@ -1398,6 +1423,14 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             if (valid < C) pmask<EXP>(in, valid, R);
             pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
             pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
+            // EXPAND_LITE: this chunk's T' from the compose pass, into
+            // registers now and into LDS after the barrier
+            f32x4 tpr[2];
+            if constexpr (LITE) {
+                const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(m));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) tpr[j] = tg[(threadIdx.x - 256) + 256 * j];
+            }
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
             if constexpr (EXP) {
@@ -1411,9 +1444,14 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             }
             pipe_diag_inv<MODE>(R, smem, accA, accM);
             if constexpr (!EXP) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
-            __syncthreads();   // S2 | S3
-            pipe_tsolve<MODE>(R, smem);
-            __syncthreads();   // S3 | next S1
+            if constexpr (LITE) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
+            } else {
+                __syncthreads();   // S2 | S3
+                pipe_tsolve<MODE>(R, smem);
+            }
+            __syncthreads();   // S3 (S2 for EXPAND_LITE) | next S1
         }
     }
 }
@@ -1548,8 +1586,18 @@ constexpr int FILL_CHAINS = 256;
 
 struct Plan {
     int nseg, L;
-    size_t p_off, r_off, e_off, total;
+    size_t p_off, r_off, e_off, tm_off, total;
 };
+
+// The pipelined kernels serve d_k = d_v = 128 unless KDA_PIPELINE=0 (the
+// single-role fused kernels then run, for comparison).
+static bool use_pipe() {
+    static const bool on = [] {
+        const char* e = getenv("KDA_PIPELINE");
+        return !(e && e[0] == '0');
+    }();
+    return on;
+}
 
 static Plan plan(int B, int T, int H, int DK, int DV) {
     Plan p{};
@@ -1563,11 +1611,14 @@ static Plan plan(int B, int T, int H, int DK, int DV) {
     }
     p.L = (NC + nseg - 1) / nseg;
     p.nseg = nseg > 1 ? (NC + p.L - 1) / p.L : 1;
-    p.p_off = p.r_off = p.e_off = p.total = 0;
+    p.p_off = p.r_off = p.e_off = p.tm_off = p.total = 0;
     if (p.nseg > 1) {
         p.r_off = (size_t)p.nseg * nchain * DK * DK * 4;
         p.e_off = p.r_off + (size_t)p.nseg * nchain * DK * DV * 4;
-        p.total = p.e_off + (size_t)p.nseg * nchain * DK * DV * 4;
+        p.tm_off = p.e_off + (size_t)p.nseg * nchain * DK * DV * 4;
+        p.total = p.tm_off;
+        // the pipelined path hands every chunk's T' from compose to expand
+        if (DK == 128 && DV == 128 && use_pipe()) p.total += (size_t)nchain * NC * TM_ELEMS * 2;
     }
     return p;
 }
@@ -1578,68 +1629,82 @@ static hipError_t set_lds(K kernel, size_t bytes) {
     return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-// The pipelined kernels serve d_k = d_v = 128 unless KDA_PIPELINE=0 (the
-// plain fused kernels then run, for comparison).
-static bool use_pipe() {
-    static const bool on = [] {
-        const char* e = getenv("KDA_PIPELINE");
-        return !(e && e[0] == '0');
-    }();
-    return on;
-}
-
-template <int DK, int DV, int MODE>
-static void* fused_kernel() {
-    if constexpr (DK == 128 && DV == 128)
-        if (use_pipe()) return (void*)pipe_kernel<MODE>;
-    return (void*)seg_kernel<DK, DV, MODE>;
-}
-
-template <int DK, int DV, int MODE>
-static size_t fused_lds() {
-    if constexpr (DK == 128 && DV == 128)
-        if (use_pipe()) return PLay<MODE>::LDS;
-    return Lay<DK, DV, MODE>::LDS;
-}
-
 template <int DK, int DV>
-static hipError_t launch_t(const ChunkArgs& a) {
+static hipError_t launch_scan(const ChunkArgs& a, const Plan& p, float* Pb, float* Rb, float* Eb) {
+    const int nchain = a.B * a.H;
+    if constexpr (DK == 128) {
+        hipLaunchKernelGGL((scan_x3_kernel<DK, DV>), dim3((DV / 16) * nchain), dim3(256), 0, (hipStream_t)a.stream,
+                           (const float*)Pb, (const float*)Rb, a.s0, Eb, a.s_final, p.nseg, nchain);
+        return hipGetLastError();
+    } else {
+        return launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream);
+    }
+}
+
+// d_k = d_v = 128: compose (writing every chunk's T'), scan, and the light
+// expand; one full expand pass when one segment per chain suffices.
+static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
-    const Plan p = plan(a.B, a.T, a.H, DK, DV);
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v, *z = (const bf16*)a.z,
                *beta = (const bf16*)a.beta;
-    typedef void (*KFn)(const bf16*, const bf16*, const bf16*, const bf16*, const bf16*, float, int, int, int, int,
-                        int, const float*, float*, float*, bf16*);
-    const KFn kexp = (KFn)fused_kernel<DK, DV, EXPAND>();
-    const KFn kcmp = (KFn)fused_kernel<DK, DV, COMPOSE>();
-    const size_t lexp = fused_lds<DK, DV, EXPAND>(), lcmp = fused_lds<DK, DV, COMPOSE>();
     hipError_t err;
-    if ((err = set_lds(kexp, lexp)) != hipSuccess) return err;
     if (p.nseg == 1) {
-        hipLaunchKernelGGL(kexp, dim3(nchain), dim3(NTH), lexp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC, NC,
-                           nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o);
+        if ((err = set_lds(pipe_kernel<EXPAND>, PLay<EXPAND>::LDS)) != hipSuccess) return err;
+        hipLaunchKernelGGL(pipe_kernel<EXPAND>, dim3(nchain), dim3(NTH), PLay<EXPAND>::LDS, st, q, k, v, z, beta,
+                           a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o,
+                           (bf16*)nullptr);
         return hipGetLastError();
     }
     unsigned char* ws = (unsigned char*)a.workspace;
     float* Pb = reinterpret_cast<float*>(ws + p.p_off);
     float* Rb = reinterpret_cast<float*>(ws + p.r_off);
     float* Eb = reinterpret_cast<float*>(ws + p.e_off);
-    if ((err = set_lds(kcmp, lcmp)) != hipSuccess) return err;
-    hipLaunchKernelGGL(kcmp, dim3(p.nseg * nchain), dim3(NTH), lcmp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC,
-                       p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
+    bf16* TM = reinterpret_cast<bf16*>(ws + p.tm_off);
+    if ((err = set_lds(pipe_kernel<COMPOSE>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL(pipe_kernel<COMPOSE>, dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr, TM);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if constexpr (DK == 128) {
-        hipLaunchKernelGGL((scan_x3_kernel<DK, DV>), dim3((DV / 16) * nchain), dim3(256), 0, st, (const float*)Pb,
-                           (const float*)Rb, a.s0, Eb, a.s_final, p.nseg, nchain);
-        if ((err = hipGetLastError()) != hipSuccess) return err;
-    } else {
-        if ((err = launch_seg_scan(Pb, Rb, a.s0, Eb, a.s_final, p.nseg, nchain, DK, DV, a.stream)) != hipSuccess)
-            return err;
+    if ((err = launch_scan<128, 128>(a, p, Pb, Rb, Eb)) != hipSuccess) return err;
+    if ((err = set_lds(pipe_kernel<EXPAND_LITE>, PLay<EXPAND_LITE>::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL(pipe_kernel<EXPAND_LITE>, dim3(p.nseg * nchain), dim3(NTH), PLay<EXPAND_LITE>::LDS, st, q, k,
+                       v, z, beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr,
+                       (float*)nullptr, (bf16*)a.o, TM);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_t(const ChunkArgs& a) {
+    const Plan p = plan(a.B, a.T, a.H, DK, DV);
+    if constexpr (DK == 128 && DV == 128)
+        if (use_pipe()) return launch_pipe(a, p);
+    const int NC = (a.T + C - 1) / C;
+    const int nchain = a.B * a.H;
+    hipStream_t st = (hipStream_t)a.stream;
+    const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v, *z = (const bf16*)a.z,
+               *beta = (const bf16*)a.beta;
+    typedef Lay<DK, DV, EXPAND> LE;
+    typedef Lay<DK, DV, COMPOSE> LCm;
+    hipError_t err;
+    if ((err = set_lds(seg_kernel<DK, DV, EXPAND>, LE::LDS)) != hipSuccess) return err;
+    if (p.nseg == 1) {
+        hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(nchain), dim3(NTH), LE::LDS, st, q, k, v, z, beta,
+                           a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL(kexp, dim3(p.nseg * nchain), dim3(NTH), lexp, st, q, k, v, z, beta, a.g_min, a.T, a.H, NC,
-                       p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr, (bf16*)a.o);
+    unsigned char* ws = (unsigned char*)a.workspace;
+    float* Pb = reinterpret_cast<float*>(ws + p.p_off);
+    float* Rb = reinterpret_cast<float*>(ws + p.r_off);
+    float* Eb = reinterpret_cast<float*>(ws + p.e_off);
+    if ((err = set_lds(seg_kernel<DK, DV, COMPOSE>, LCm::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((seg_kernel<DK, DV, COMPOSE>), dim3(p.nseg * nchain), dim3(NTH), LCm::LDS, st, q, k, v, z,
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_scan<DK, DV>(a, p, Pb, Rb, Eb)) != hipSuccess) return err;
+    hipLaunchKernelGGL((seg_kernel<DK, DV, EXPAND>), dim3(p.nseg * nchain), dim3(NTH), LE::LDS, st, q, k, v, z,
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr, (float*)nullptr,
+                       (bf16*)a.o);
     return hipGetLastError();
 }
 
