@@ -1280,6 +1280,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
     typedef PLay<MODE> LY;
     constexpr int DK = 128, DV = 128;
     constexpr bool EXP = LY::EXP, LITE = LY::LITE;
+    // v^T is written by the state waves in EXPAND, by the gate waves otherwise
+    constexpr bool VSTATE = MODE == EXPAND;
     extern __shared__ __align__(16) unsigned char smem[];
     const int seg = blockIdx.x / nchain;
     const size_t bh = blockIdx.x % nchain;
@@ -1327,7 +1329,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                     }
         const size_t ostride = (size_t)H * DV;
         PV pv;
-        if constexpr (EXP) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
+        if constexpr (VSTATE) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
         bf16x8 yb[NH][2][2];
         // state update of chunk n from V_new in yb (COMPOSE defers it to S2)
         auto update = [&](int n) __attribute__((always_inline)) {
@@ -1358,7 +1360,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         };
         // the state waves' share of the steps after S1 for chunk n
         auto rest = [&](int n) __attribute__((always_inline)) {
-            if constexpr (EXP) {
+            if constexpr (VSTATE) {
                 pipe_vt<MODE>(pv, w, smem);
                 const int mn = min(n + 1, n1 - 1);
                 pfetch_v(pv, v, row_of(mn), min(C, T - mn * C), H, w);
@@ -1412,7 +1414,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         {
             const int valid = min(C, T - n0 * C);
             pfetch_zkq<EXP>(in, q, k, z, beta, row_of(n0), valid, H, R);
-            if constexpr (!EXP) pfetch_v(pv, v, row_of(n0), valid, H, R);
+            if constexpr (!VSTATE) pfetch_v(pv, v, row_of(n0), valid, H, R);
         }
         float kl[SUB][2], kr[SUB][2], ql[EXP ? SUB : 1][2];
         for (int i = 0; i < nL; ++i) {
@@ -1437,13 +1439,14 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 // products in flight while the operands are written
                 pipe_diag_mma<MODE>(R, smem, accA, accM);
                 pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
+                if constexpr (!VSTATE) pipe_vt<MODE>(pv, R, smem);
             } else {
                 pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
                 pipe_vt<MODE>(pv, R, smem);
                 pipe_diag_mma<MODE>(R, smem, accA, accM);
             }
             pipe_diag_inv<MODE>(R, smem, accA, accM);
-            if constexpr (!EXP) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+            if constexpr (!VSTATE) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
             if constexpr (LITE) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
