@@ -942,6 +942,34 @@ __device__ __forceinline__ void pfetch_zkq(PIn<HASQ>& r, const bf16* __restrict_
     r.beta = beta[row0 + (size_t)min(l, last) * H];
 }
 
+// The same loads in two parts: z alone, then k, q and beta.
+template <bool HASQ>
+__device__ __forceinline__ void pfetch_z(PIn<HASQ>& r, const bf16* __restrict__ z, size_t row0, int valid, int H,
+                                         int R) {
+    const int last = valid - 1;
+    const char* zb = reinterpret_cast<const char*>(z + row0 * 128);
+    const unsigned lo = 4u * (unsigned)lane_id(), rstride = (unsigned)H * 256u;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i)
+        r.z[i] = *reinterpret_cast<const bf16x2*>(zb + (unsigned)min(SUB * R + i, last) * rstride + lo);
+}
+
+template <bool HASQ>
+__device__ __forceinline__ void pfetch_kq(PIn<HASQ>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                          const bf16* __restrict__ beta, size_t row0, int valid, int H, int R) {
+    const int l = lane_id(), last = valid - 1;
+    const char* kb = reinterpret_cast<const char*>(k + row0 * 128);
+    const char* qb = reinterpret_cast<const char*>(q + row0 * 128);
+    const unsigned lo = 4u * (unsigned)l, rstride = (unsigned)H * 256u;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const unsigned off = (unsigned)min(SUB * R + i, last) * rstride + lo;
+        r.k[i] = *reinterpret_cast<const bf16x2*>(kb + off);
+        if constexpr (HASQ) r.q[i] = *reinterpret_cast<const bf16x2*>(qb + off);
+    }
+    r.beta = beta[row0 + (size_t)min(l, last) * H];
+}
+
 // Rows at or past `valid` of a ragged last chunk become identity tokens:
 // z = -inf (a zero gate, alpha = 1) and k = q = 0 (no write, no read); beta
 // is set to 0 where it is stored.
@@ -965,12 +993,27 @@ __device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size
         r.v[i] = *reinterpret_cast<const bf16x2*>(vb + (unsigned)min(SUB * R + i, last) * rstride + lo);
 }
 
-// S1 of gate wave R (rows past the end have been made identity tokens).  On
-// return kl, kr, ql hold the block's decay-scaled k and q (fp32).
+// S[i] = running sum of sigmoid(z) over the block's rows (registers only);
+// the log2 decay is G = kg2 S.
+template <bool HASQ>
+__device__ __forceinline__ void gate_sums(const PIn<HASQ>& in, float (&S)[SUB][2]) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        s0 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][0]));
+        s1 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][1]));
+        S[i][0] = s0;
+        S[i][1] = s1;
+    }
+}
+
+// The rest of S1: block sums and references, beta, the block-local factors
+// e^{+-(G_r - G_m(R))} and the operands k e^{G-G_m} (not needed without the
+// solve), k e^{G_m-G}, q e^{G-G_m}.
 template <int MODE>
-__device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
-                                          unsigned char* smem, float (&kl)[SUB][2], float (&kr)[SUB][2],
-                                          float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
+__device__ __forceinline__ void gate_rest(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
+                                          unsigned char* smem, const float (&S)[SUB][2], float (&kl)[SUB][2],
+                                          float (&kr)[SUB][2], float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
     typedef PLay<MODE> L;
     constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK;
@@ -981,20 +1024,8 @@ __device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R,
     float* tot = reinterpret_cast<float*>(smem + L::OFF_TOT);
     float* mloc = reinterpret_cast<float*>(smem + L::OFF_MLOC);
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
-
-    // S[i] = running sum of sigmoid(z) over the block's rows; the log2 decay
-    // is G = kg2 S, folded into the exponents below
-    float S[SUB][2];
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < SUB; ++i) {
-        s0 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][0]));
-        s1 += __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[i][1]));
-        S[i][0] = s0;
-        S[i][1] = s1;
-    }
     const float m0 = kg2 * S[7][0], m1 = kg2 * S[7][1];
-    *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{kg2 * s0, kg2 * s1};
+    *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{kg2 * S[SUB - 1][0], kg2 * S[SUB - 1][1]};
     *reinterpret_cast<float2*>(mloc + R * 128 + c0) = float2{m0, m1};
     if ((l >> 4) == R) bet[l] = l < valid ? (float)in.beta : 0.f;
 #pragma unroll
@@ -1009,10 +1040,21 @@ __device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R,
             kr[i][j] = kv * right;
             if constexpr (EXP) ql[i][j] = (float)in.q[i][j] * left;
         }
-        store2<bf16>(KL + r * LDK + c0, kl[i][0], kl[i][1]);
+        if constexpr (L::SOLVE) store2<bf16>(KL + r * LDK + c0, kl[i][0], kl[i][1]);
         store2<bf16>(KR + r * LDK + c0, kr[i][0], kr[i][1]);
         if constexpr (EXP) store2<bf16>(QL + r * LDK + c0, ql[i][0], ql[i][1]);
     }
+}
+
+// S1 of gate wave R (rows past the end have been made identity tokens).  On
+// return kl, kr, ql hold the block's decay-scaled k and q (fp32).
+template <int MODE>
+__device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
+                                          unsigned char* smem, float (&kl)[SUB][2], float (&kr)[SUB][2],
+                                          float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
+    float S[SUB][2];
+    gate_sums<MODE != COMPOSE>(in, S);
+    gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
 }
 
 // S2 of gate wave R: A_RR (and M_RR) from the block's own rows of KL, KR,
@@ -1331,7 +1373,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         PV pv;
         if constexpr (VSTATE) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
         bf16x8 yb[NH][2][2];
-        // state update of chunk n from V_new in yb (COMPOSE defers it to S2)
+        // state update of chunk n from V_new in yb (COMPOSE defers it to S3)
         auto update = [&](int n) __attribute__((always_inline)) {
             const int bufn = LY::NKB == 2 ? (n & 1) : 0;
             const bf16* KGT = reinterpret_cast<const bf16*>(smem + LY::OFF_KGT + bufn * LY::KGT_SZ);
@@ -1359,7 +1401,9 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             }
         };
         // the state waves' share of the steps after S1 for chunk n
-        auto rest = [&](int n) __attribute__((always_inline)) {
+        // (COMPOSE: the previous chunk's state update in S3, while the gate
+        // waves solve for T')
+        auto rest = [&](int n, bool upd) __attribute__((always_inline)) {
             if constexpr (VSTATE) {
                 pipe_vt<MODE>(pv, w, smem);
                 const int mn = min(n + 1, n1 - 1);
@@ -1369,23 +1413,23 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 2>(w, smem);
             else
                 pipe_pairs<MODE, 1>(w, smem);
-            if constexpr (!LITE) __syncthreads();   // S2 | S3
+            if constexpr (!LITE) {
+                __syncthreads();   // S2 | S3
+                if constexpr (!EXP)
+                    if (upd) update(n - 1);
+            }
             __syncthreads();   // S3 (S2 for EXPAND_LITE) | next S1
         };
         // iteration 0 has no step to run; iterations 1.. run the step of the
-        // previous chunk in S1 (COMPOSE: its state update in S2)
+        // previous chunk in S1 (COMPOSE: its state update in S3)
         __syncthreads();   // S1 | S2
-        rest(n0);
+        rest(n0, false);
         for (int i = 1; i < nL; ++i) {
             const int m = n0 + i;
             chain(m - 1);
             if constexpr (EXP) update(m - 1);
             __syncthreads();   // S1 | S2
-            if constexpr (!EXP) {
-                update(m - 1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            rest(m);
+            rest(m, true);
         }
         chain(n1 - 1);
         update(n1 - 1);
@@ -1404,6 +1448,51 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                             const int col = cbase + 32 * hh + ct * 16 + (l & 15);
                             xo[(ob + row) * NX + col] = xs[hh][rt][ct][e];
                         }
+        }
+    } else if constexpr (LITE) {
+        // ---------------- gate waves, EXPAND_LITE: block R of each chunk.
+        // The next chunk's running sums of sigmoid(z) are formed in S2, where
+        // the state waves' M pairs leave room, and kept in registers.
+        const int R = w - 4;
+        const float kg2 = g_min * LOG2E;
+        PIn<true> in;
+        PV pv;
+        float S[SUB][2];
+        {
+            const int valid = min(C, T - n0 * C);
+            pfetch_zkq<true>(in, q, k, z, beta, row_of(n0), valid, H, R);
+            pfetch_v(pv, v, row_of(n0), valid, H, R);
+            if (valid < C) pmask<true>(in, valid, R);
+            gate_sums<true>(in, S);
+        }
+        float kl[SUB][2], kr[SUB][2], ql[SUB][2];
+        for (int i = 0; i < nL; ++i) {
+            const int m = n0 + i;
+            const int valid = min(C, T - m * C);
+            const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
+            const int valid_n = min(C, T - mn * C);
+            pfetch_z<true>(in, z, row_of(mn), valid_n, H, R);   // this chunk's z is consumed
+            gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
+            pfetch_kq<true>(in, q, k, beta, row_of(mn), valid_n, H, R);
+            // this chunk's T' from the compose pass, into LDS after the barrier
+            f32x4 tpr[2];
+            {
+                const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(m));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) tpr[j] = tg[(threadIdx.x - 256) + 256 * j];
+            }
+            __syncthreads();   // S1 | S2
+            f32x4 accA, accM;
+            pipe_diag_mma<MODE>(R, smem, accA, accM);
+            pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
+            pipe_vt<MODE>(pv, R, smem);
+            pipe_diag_inv<MODE>(R, smem, accA, accM);
+            pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
+            if (valid_n < C) pmask<true>(in, valid_n, R);
+            gate_sums<true>(in, S);
+            __syncthreads();   // S2 | next S1
         }
     } else {
         // ---------------- gate waves: block R of each chunk
