@@ -703,28 +703,37 @@ __global__ __launch_bounds__(NTH) void seg_kernel(const bf16* __restrict__ q, co
 // ---------------------------------------------------------------------------
 // Pipelined fused kernel for d_k = d_v = 128.  Waves 0-3 own the state and
 // run the recurrence step of chunk m-1 while waves 4-7 compute the gate,
-// the decay-scaled operands and the inverted diagonal blocks of chunk m, so
-// that the MFMA-bound step and the VALU-bound gate overlap on every SIMD.
-// Gate wave 4 + R handles rows 16R..16R+15 of a chunk over all key channels.
-// The block reference row 16R+7 lies in its own rows, so the factors
-// e^{+-(G_r - G_m(R))}, the diagonal block A_RR (and M_RR) and its inverse
-// need nothing from the other waves; block sums and references are
-// exchanged through LDS at the first barrier.
+// the decay-scaled operands and the solve of chunk m, so that the MFMA-bound
+// step and the VALU-bound gate overlap on every SIMD.  Gate wave 4 + R
+// handles rows 16R..16R+15 of a chunk over all key channels.  The block
+// reference row 16R+7 lies in its own rows, so the factors
+// e^{+-(G_r - G_m(R))}, the diagonal blocks A_RR, M_RR and the inverse of
+// I + beta_R A~_RR need nothing from the other waves; block sums and
+// references are exchanged through LDS at the first barrier.
 //
-// Iteration i, chunk m = n0 + i:
-//  S1  waves 4-7: gate, block-local running sums, k e^{G-G_m}, k e^{G_m-G},
-//                 q e^{G-G_m}; block sums and references; A_RR (and M_RR)
-//                 on MFMA, then D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R)
-//      waves 0-3: recurrence step of chunk m-1 (reads only its operands:
-//                 T', -k e^G, v^T, K~^T, e^{G_C}, q e^G, M)             | barrier
-//  S2  waves 4-7: absolute references from the block sums; -k e^G, q e^G,
-//                 (k e^{G_C-G})^T, e^{G_C}, v^T (and M_RR)
-//      waves 0-3: the six off-diagonal block pairs of A (and M) with their
-//                 cross-block factors e^{G_m(R) - G_m(I)}                 | barrier
-//  S3  waves 4-7: T' column blocks                                        | barrier
-// State tiles: EXPAND, wave w owns columns 32w..32w+31 of S; COMPOSE, waves
-// 0-1 own 64 columns of P and waves 2-3 64 columns of R, advanced 32 columns
-// at a time.
+// Modes: COMPOSE runs the state [P | R] and hands every chunk's T' to the
+// expand pass; EXPAND (one segment per chain) forms everything itself;
+// EXPAND_LITE reads T' back and forms only M, the step's operands and the
+// outputs.
+//
+// Iteration i, chunk m = n0 + i (COMPOSE, EXPAND):
+//  S1  gate waves: gate, block-local running sums, k e^{G-G_m}, k e^{G_m-G}
+//                  (and q e^{G-G_m}); block sums and references
+//      state waves: recurrence step of chunk m-1 (reads only its operands:
+//                  T', -k e^G, v^T, K~^T, e^{G_C} (and q e^G, M))      | barrier
+//  S2  gate waves: absolute references; -k e^G, (k e^{G_C-G})^T, e^{G_C},
+//                  v^T (and q e^G); A_RR (and M_RR) on MFMA, then
+//                  D'_R = (I + beta_R A~_RR)^{-1} diag(beta_R)
+//      state waves: the six off-diagonal block pairs of A (and M) with their
+//                  cross-block factors e^{G_m(R) - G_m(I)}              | barrier
+//  S3  gate waves: T' column blocks (COMPOSE: state waves finish chunk
+//                  m-1's state update meanwhile)                        | barrier
+// EXPAND_LITE: S1 as above (no k e^{G-G_m}); S2 forms M_RR and the pairs
+// of M, the operands, stores T' from the compose pass and the next chunk's
+// running sums                                                          | barrier
+// State tiles: the expand modes, wave w owns columns 32w..32w+31 of S;
+// COMPOSE, waves 0-1 own 64 columns of P and waves 2-3 64 columns of R,
+// advanced 32 columns at a time.
 // ---------------------------------------------------------------------------
 template <int MODE>
 struct PLay {
@@ -1201,7 +1210,6 @@ template <int MODE, int NP>
 __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
     typedef PLay<MODE> L;
     typedef Mfma<bf16> MF;
-    constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK, LC = L::LC, LB = L::LB, DK = L::DK;
     int l = lane_id();
     asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
@@ -1514,21 +1522,12 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             if (valid < C) pmask<EXP>(in, valid, R);
             pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
             pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
-            // EXPAND_LITE: this chunk's T' from the compose pass, into
-            // registers now and into LDS after the barrier
-            f32x4 tpr[2];
-            if constexpr (LITE) {
-                const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(m));
-#pragma unroll
-                for (int j = 0; j < 2; ++j) tpr[j] = tg[(threadIdx.x - 256) + 256 * j];
-            }
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
             if constexpr (EXP) {
                 // products in flight while the operands are written
                 pipe_diag_mma<MODE>(R, smem, accA, accM);
                 pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
-                if constexpr (!VSTATE) pipe_vt<MODE>(pv, R, smem);
             } else {
                 pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
                 pipe_vt<MODE>(pv, R, smem);
@@ -1536,14 +1535,9 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             }
             pipe_diag_inv<MODE>(R, smem, accA, accM);
             if constexpr (!VSTATE) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
-            if constexpr (LITE) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
-            } else {
-                __syncthreads();   // S2 | S3
-                pipe_tsolve<MODE>(R, smem);
-            }
-            __syncthreads();   // S3 (S2 for EXPAND_LITE) | next S1
+            __syncthreads();   // S2 | S3
+            pipe_tsolve<MODE>(R, smem);
+            __syncthreads();   // S3 | next S1
         }
     }
 }
