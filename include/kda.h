@@ -90,9 +90,11 @@ const char* kda_version(void);
  *
  * Workspace: bf16 sequences split into segments when there are fewer than
  * 256 (batch, head) chains (the per-segment transition P, input term R and
- * entry state, fp32); a single segment needs no workspace.  fp32 sequences
- * also stage the per-chunk products (W, U^T, M, q e^G, (k e^{G_C-G})^T,
- * e^{G_C}).
+ * entry state, fp32; with dk = dv = 128 also every chunk's
+ * T' = (I + A)^-1 diag(beta), 64 x 64 bf16, which the pass that composes
+ * the segments hands to the pass that writes the outputs); a single segment
+ * needs no workspace.  fp32 sequences also stage the per-chunk products
+ * (W, U^T, M, q e^G, (k e^{G_C-G})^T, e^{G_C}).
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                      kda_dtype dt);
