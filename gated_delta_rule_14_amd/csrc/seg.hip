@@ -741,10 +741,18 @@ struct PLay {
     static constexpr bool EXP = MODE != COMPOSE;      // outputs O (and so q, M)
     static constexpr bool LITE = MODE == EXPAND_LITE; // T' read from the compose pass
     static constexpr bool SOLVE = !LITE;              // A, its inverses and T' formed here
-    static constexpr int LDK = DK + 8, LC = C + 8, LB = SUB + 8, BS = SUB * SUB + 16;
+    // Row pitches (bf16 elements).  A 16-row fragment read (16 bytes per
+    // lane, rows 16 apart in lanes) meets no LDS bank conflict on gfx950 when
+    // the pitch is 32 bytes (mod 64) past a multiple of 256; 272- and
+    // 144-byte rows cost two passes.  EXPAND has no LDS left for the wider
+    // rows and keeps LDK = 136, LT = 72.
+    static constexpr bool WIDE = MODE != EXPAND;
+    static constexpr int LDK = WIDE ? DK + 16 : DK + 8;   // [C][DK] operands: 288-byte rows
+    static constexpr int LT = WIDE ? C + 16 : C + 8;      // T' and M: 160-byte rows
+    static constexpr int LC = C + 8, LB = SUB + 8, BS = SUB * SUB + 16;
     static constexpr size_t TILE = (size_t)C * LDK * 2;
-    static constexpr size_t CC = a16((size_t)C * LC * 2);                 // one C x C bf16 operand
-    static constexpr size_t OFF_TP = 0;                                    // T' [C][LC] pcol
+    static constexpr size_t CC = a16((size_t)C * LT * 2);                 // one C x C bf16 operand
+    static constexpr size_t OFF_TP = 0;                                    // T' [C][LT] pcol
     static constexpr size_t OFF_KL = CC;                                   // [C][LDK] k e^{G_r - G_m(R)}
     static constexpr size_t OFF_KR = OFF_KL + TILE;                        // [C][LDK] k e^{G_m(R) - G_r}
     static constexpr size_t OFF_QL = OFF_KR + TILE;                        // [C][LDK] q e^{G_r - G_m(R)} (outputs)
@@ -756,7 +764,7 @@ struct PLay {
     static constexpr size_t KGT_SZ = a16((size_t)DK * LC * 2);
     static constexpr size_t OFF_KGT = OFF_RV + a16((size_t)DV * LC * 2);   // K~^T [DK][LC] pcol
     static constexpr size_t OFF_QG = OFF_KGT + NKB * KGT_SZ;               // q e^G [C][LDK] pcol (outputs)
-    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LC] pcol (outputs)
+    static constexpr size_t OFF_M = OFF_QG + (EXP ? TILE : 0);             // M [C][LT] pcol (outputs)
     static constexpr size_t OFF_AS = OFF_M + (EXP ? CC : 0);               // [4][BS] beta A~_RR^T
     static constexpr size_t OFF_AB = OFF_AS + (SOLVE ? (size_t)4 * BS * 4 : 0);             // [6][16][LB] -A~_RI
     static constexpr size_t OFF_DB = OFF_AB + (SOLVE ? a16((size_t)6 * SUB * LB * 2) : 0);  // [4][16][LB] D'_R
@@ -775,10 +783,10 @@ struct PLay {
 constexpr size_t TM_ELEMS = (size_t)C * C;
 
 // Piece p (16 bytes) of a chunk's T': row p / 8, eighth p % 8 of the row; its
-// place in LDS (padded rows of LC).
+// place in LDS (padded rows of LT).
 template <class L>
 __device__ __forceinline__ f32x4* tp_lds(unsigned char* smem, int p) {
-    return reinterpret_cast<f32x4*>(smem + L::OFF_TP + (size_t)(p >> 3) * L::LC * 2 + (p & 7) * 16);
+    return reinterpret_cast<f32x4*>(smem + L::OFF_TP + (size_t)(p >> 3) * L::LT * 2 + (p & 7) * 16);
 }
 
 // Recurrence step of the pipelined kernel, first part: V_new = T' Z with
@@ -845,8 +853,8 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
     if constexpr (EXP) {
 #pragma unroll
         for (int ot = 0; ot < 4; ++ot) {
-            mf[ot][0] = load_frag<bf16>(Ms, L::LC, ot * 16, 0);
-            mf[ot][1] = load_frag<bf16>(Ms, L::LC, ot * 16, 32);
+            mf[ot][0] = load_frag<bf16>(Ms, L::LT, ot * 16, 0);
+            mf[ot][1] = load_frag<bf16>(Ms, L::LT, ot * 16, 32);
         }
     }
     {
@@ -857,8 +865,8 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
             for (int ct = 0; ct < NTW; ++ct) zb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
 #pragma unroll
         for (int yt = 0; yt < 4; ++yt) {
-            const MF::frag t0 = load_frag<bf16>(Tp, L::LC, yt * 16, 0);
-            const MF::frag t1 = load_frag<bf16>(Tp, L::LC, yt * 16, 32);
+            const MF::frag t0 = load_frag<bf16>(Tp, L::LT, yt * 16, 0);
+            const MF::frag t1 = load_frag<bf16>(Tp, L::LT, yt * 16, 32);
 #pragma unroll
             for (int ct = 0; ct < NTW; ++ct) {
                 y[yt][ct] = MF::mma(t0, zb[0][ct], zero4());
@@ -1092,7 +1100,7 @@ __device__ __forceinline__ void pipe_diag_mma(int R, const unsigned char* smem, 
 template <int MODE>
 __device__ __forceinline__ void pipe_diag_inv(int R, unsigned char* smem, const f32x4& accA, f32x4 accM) {
     typedef PLay<MODE> L;
-    constexpr int LC = L::LC, LB = L::LB, BS = L::BS;
+    constexpr int LT = L::LT, LB = L::LB, BS = L::BS;
     int l = lane_id();
     asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
     bf16* Ms = reinterpret_cast<bf16*>(smem + L::OFF_M);
@@ -1103,7 +1111,7 @@ __device__ __forceinline__ void pipe_diag_inv(int R, unsigned char* smem, const 
     if constexpr (L::EXP) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) accM[e] = (ii + e <= rr) ? accM[e] : 0.f;
-        store4p(Ms + (R * SUB + rr) * LC + pcol(R * SUB + ii), accM[0], accM[1], accM[2], accM[3]);
+        store4p(Ms + (R * SUB + rr) * LT + pcol(R * SUB + ii), accM[0], accM[1], accM[2], accM[3]);
     }
     if constexpr (L::SOLVE) {
         const float br = bet[R * SUB + rr];
@@ -1210,7 +1218,7 @@ template <int MODE, int NP>
 __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
     typedef PLay<MODE> L;
     typedef Mfma<bf16> MF;
-    constexpr int LDK = L::LDK, LC = L::LC, LB = L::LB, DK = L::DK;
+    constexpr int LDK = L::LDK, LT = L::LT, LB = L::LB, DK = L::DK;
     int l = lane_id();
     asm volatile("" : "+v"(l));   // keep lane-derived constants out of the loop preheader
     const bf16* KL = reinterpret_cast<const bf16*>(smem + L::OFF_KL);
@@ -1275,7 +1283,7 @@ __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
             store4p(Ab + ((R * (R - 1) / 2 + I) * SUB + rr) * LB + ii, -accA[j][0], -accA[j][1], -accA[j][2],
                     -accA[j][3]);
         if constexpr (L::EXP)
-            store4p(Ms + (R * SUB + rr) * LC + pcol(I * SUB + ii), accM[j][0], accM[j][1], accM[j][2], accM[j][3]);
+            store4p(Ms + (R * SUB + rr) * LT + pcol(I * SUB + ii), accM[j][0], accM[j][1], accM[j][2], accM[j][3]);
     }
 }
 
@@ -1284,7 +1292,7 @@ __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
 template <int MODE>
 __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
     typedef PLay<MODE> L;
-    constexpr int LC = L::LC, LB = L::LB;
+    constexpr int LT = L::LT, LB = L::LB;
     int l = lane_id();
     asm volatile("" : "+v"(l));
     const int g = l >> 4, c = l & 15;
@@ -1300,7 +1308,7 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) eye[e] = (4 * g + e == c) ? 1.f : 0.f;
     bf16x4 xb[4];
-    bf16* tcol = Tp + 4 * g * LC + pcol(16 * wT + c);
+    bf16* tcol = Tp + 4 * g * LT + pcol(16 * wT + c);
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
         f32x4 x = zero4();
@@ -1313,7 +1321,7 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
         }
         xb[R] = to_bf4(x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tcol[(R * SUB + e) * LC] = xb[R][e];
+        for (int e = 0; e < 4; ++e) tcol[(R * SUB + e) * LT] = xb[R][e];
     }
 }
 
@@ -1348,7 +1356,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             const int p = w - 2;
             const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
             const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
-            store4p(reinterpret_cast<bf16*>(smem + LY::OFF_M) + (R * SUB + (l & 15)) * LY::LC +
+            store4p(reinterpret_cast<bf16*>(smem + LY::OFF_M) + (R * SUB + (l & 15)) * LY::LT +
                         pcol(I * SUB + 4 * (l >> 4)),
                     0.f, 0.f, 0.f, 0.f);
         }
