@@ -14,7 +14,14 @@ Also measured in the same run:
   * epilogue: RMSNorm x gate + projection of the training-shape workload
     (8 x 8192 tokens, 4096 -> 2304), against the bf16 MFMA peak;
   * cpu_baseline: the fp64 oracle on the host cores over the prefill
-    workload (all heads over the full 32k tokens).
+    workload (all heads over the full 32k tokens);
+  * workloads: kda_chunk_fwd over the other prefill shapes -- the tiny fp32
+    case (launch latency), the 8 x 8192 training shape, and the 1M-token
+    sequence followed by the RMSNorm x gate epilogue;
+  * ceilings: what this GPU reaches on plain torch kernels -- an in-place
+    fp32 scale (read-modify-write), a device copy and a large bf16 matmul --
+    so that each kernel's rate can be read against them as well as against
+    the published peaks.
 
 Counter support: --copy-only runs a 1 GiB device copy for counter
 calibration; --pmc-summary turns rocprofv3 FETCH_SIZE / WRITE_SIZE runs into
@@ -70,6 +77,9 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=32)
     p.add_argument("--no-epilogue", action="store_true")
+    p.add_argument("--no-workloads", action="store_true", help="skip the tiny, training and 1M-token shapes")
+    p.add_argument("--no-long", action="store_true", help="skip the 1M-token shape")
+    p.add_argument("--no-ceilings", action="store_true")
     p.add_argument("--copy-only", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -174,6 +184,82 @@ def bench_epilogue(torch, kda, ki, steps=5):
                          "kernel": "gate_kernel + hipBLASLt bf16 GEMM (projection FLOP only)"}}
 
 
+def _time_calls(torch, fn, calls, warmup=1):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(calls):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / calls
+
+
+def bench_workload(torch, kda, ki, name, seed, calls):
+    """One kda_chunk_fwd call over a named prefill workload (plus, where the
+    workload has it, the RMSNorm x gate epilogue without projection), inputs
+    resident in HBM.  Algorithmic bytes: the token tensors once each, S0 read
+    when it is given, S_final written; the gate workload adds its gate logits
+    read and y written (o stays counted once, as in a fused pass)."""
+    cfg = ki.WORKLOADS[name]
+    B, T, H, dk, dv, dt = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"]
+    dev = torch.device("cuda:0")
+    x = ki.workload_inputs(name, seed=seed, device=dev)
+    s0 = x["s0"] if cfg["s0_var"] > 0 else None
+    gate = cfg.get("epilogue") == "gate"
+    o = torch.empty((B, T, H, dv), dtype=dt, device=dev)
+    s = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt), 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((B, T, H * dv), dtype=dt, device=dev) if gate else None
+
+    def call():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, s0, o=o, s_final=s, workspace=ws)
+        if gate:
+            kda.out_gate(o, x["gate"], ki.EPS, y=y)
+
+    per = _time_calls(torch, call, calls)
+    esz = 2 if dt == torch.bfloat16 else 4
+    per_th = (3 * dk + 2 * dv) * esz + esz + (2 * dv * esz if gate else 0)   # q, k, z, v, o (+ gate, y); beta
+    nbytes = B * T * H * per_th + B * H * dk * dv * 4 * (2 if s0 is not None else 1)
+    out = {"workload": name, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+           "dtype": "bf16" if dt == torch.bfloat16 else "f32", "calls": calls,
+           "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
+           "kernels": "kda_chunk_fwd" + (" + kda_out_gate" if gate else "")}
+    if dk == 128 and dv == 128:
+        gbs = nbytes / per / 1e9
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes,
+                           "mfma_frac": round(B * T * H * PREFILL_FLOP_PER_TOKEN_HEAD / per / 1e12 /
+                                              BF16_PEAK_TFLOPS, 4)}
+    del x, o, s, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def measured_ceilings(torch):
+    """Rates this GPU reaches on plain torch kernels: in-place fp32 scale over
+    512 MiB (read + write), a 512 MiB device copy, a bf16 8192^3 matmul."""
+    dev = torch.device("cuda:0")
+    n = 128 * 1024 * 1024
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    t_rmw = _time_calls(torch, lambda: x.mul_(0.999999), 10, warmup=3)
+    d = torch.empty_like(x)
+    t_copy = _time_calls(torch, lambda: d.copy_(x), 10, warmup=3)
+    del x, d
+    m = 8192
+    a = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    b = torch.randn((m, m), device=dev).to(torch.bfloat16)
+    t_mm = _time_calls(torch, lambda: torch.matmul(a, b), 10, warmup=3)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_rmw_gbs": round(2 * n * 4 / t_rmw / 1e9, 1), "hbm_copy_gbs": round(2 * n * 4 / t_copy / 1e9, 1),
+            "mfma_bf16_tflops": round(2 * m ** 3 / t_mm / 1e12, 1),
+            "how": "torch x.mul_ in place (512 MiB fp32), torch copy_ (512 MiB), torch.matmul bf16 8192^3; "
+                   "HIP events, mean of 10 after 3 warm-up calls"}
+
+
 def copy_only(torch):
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
@@ -220,7 +306,8 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
                                              if "pipe_kernel" in k or "seg_kernel" in k or "scan_x3" in k
                                              or "seg_scan" in k or "chunk_intra" in k or "chain_kernel" in k),
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --no-cpu --steps 2 "
-                      "--warmup 1 --decode-steps 8 --no-epilogue; same with --copy-only for the scale factors"}
+                      "--warmup 1 --decode-steps 8 --no-epilogue --no-workloads --no-ceilings; same with --copy-only for the "
+                      "scale factors"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)
     print(json.dumps(out, indent=1))
@@ -312,6 +399,22 @@ def main():
         line["decode"] = bench_decode(torch, kda, ki, args.decode_steps)
     if not args.no_epilogue:
         line["epilogue"] = bench_epilogue(torch, kda, ki)
+    if not args.no_workloads:
+        wl = [bench_workload(torch, kda, ki, "tiny_fp32", 0, 20),
+              bench_workload(torch, kda, ki, "train_8x8k", 2, 5)]
+        if not args.no_long:
+            wl.append(bench_workload(torch, kda, ki, "long_1m", 4, 2))
+        line["workloads"] = wl
+    if not args.no_ceilings:
+        c = measured_ceilings(torch)
+        line["ceilings"] = c
+        line["roofline"]["frac_of_measured_copy"] = round(gbs / c["hbm_copy_gbs"], 4)
+        if "decode" in line:
+            line["decode"]["roofline"]["frac_of_measured_rmw"] = round(
+                line["decode"]["roofline"]["achieved"] / c["hbm_rmw_gbs"], 4)
+        if "epilogue" in line:
+            line["epilogue"]["roofline"]["frac_of_measured_matmul"] = round(
+                line["epilogue"]["roofline"]["achieved"] / c["mfma_bf16_tflops"], 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(torch, ki, args.cpu_heads)
     print(json.dumps(line), flush=True)
