@@ -141,13 +141,50 @@ def bench_decode(torch, kda, ki, nsteps):
     per = total / nsteps
     bytes_step = B * H * DECODE_BYTES_PER_HEAD_STEP
     gbs = bytes_step / per / 1e9
+    layer = bench_decode_layer(torch, kda, ki, state, steps[:min(nsteps, 256)], B, H, dv)
     return {
         "workload": "decode_256", "B": B, "H": H, "dk": dk, "dv": dv, "steps": nsteps,
         "value": B * nsteps / total, "unit": "tokens/s", "us_per_step": per * 1e6,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode"),
                      "algorithmic_bytes": bytes_step, "kernel": "decode_step_kernel"},
+        "layer_step": layer,
     }
+
+
+def bench_decode_layer(torch, kda, ki, state, steps, B, H, dv, d_model=2304):
+    """The whole layer per decode token (recurrence step, RMSNorm x gate,
+    projection to d_model): kda_recurrent_layer_step (epilogue fused into the
+    step's launch, then the GEMM) against kda_recurrent_step followed by
+    kda_out_gate (three launches)."""
+    dev = torch.device("cuda:0")
+    gates = [ki.gate_logits((B, H), dv, torch.bfloat16, 3, dev, step=t + 1) for t in range(len(steps))]
+    w = ki.projection(d_model, H * dv, 3, dev)
+    y = torch.empty((B, d_model), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+    lws = torch.empty(kda.recurrent_layer_step_workspace_bytes(B, H, dv, d_model, torch.bfloat16, True),
+                      dtype=torch.uint8, device=dev)
+    gws = torch.empty(kda.out_gate_workspace_bytes(B, 1, H, dv, d_model, torch.bfloat16, True), dtype=torch.uint8,
+                      device=dev)
+
+    def fused():
+        for d, g in zip(steps, gates):
+            kda.recurrent_layer_step(d["q"], d["k"], d["v"], d["z"], d["beta"], ki.G_MIN, state, g, ki.EPS, w, y=y,
+                                     workspace=lws)
+
+    def unfused():
+        for d, g in zip(steps, gates):
+            kda.recurrent_step(d["q"], d["k"], d["v"], d["z"], d["beta"], ki.G_MIN, state, o=o)
+            kda.out_gate(o.view(B, 1, H, dv), g.view(B, 1, H, dv), ki.EPS, w, y=y.view(B, 1, d_model),
+                         workspace=gws)
+
+    n = len(steps)
+    t_f = _time_calls(torch, fused, 1) / n
+    t_u = _time_calls(torch, unfused, 1) / n
+    return {"d_model": d_model, "steps": n, "us_per_step_fused": round(t_f * 1e6, 1),
+            "us_per_step_unfused": round(t_u * 1e6, 1),
+            "kernels": "fused: decode_step_kernel with the gate epilogue + hipBLASLt GEMM; "
+                       "unfused: decode_step_kernel + gate_kernel + hipBLASLt GEMM"}
 
 
 def bench_epilogue(torch, kda, ki, steps=5):

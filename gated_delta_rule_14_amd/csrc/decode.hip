@@ -19,6 +19,11 @@
 // VGPRs, the two column reductions (p and S'^T q) go through LDS, and the
 // updated state is written once.  The kernel is purely HBM-bound: 2 * 4 *
 // DK * DV bytes of state traffic against ~7 * DK * DV flops.
+//
+// kda_recurrent_layer_step runs the same kernel with the output epilogue
+// fused (RMS normalisation over d_v times sigmoid(gate)), so that one
+// decode token of the whole layer is one launch, plus the projection GEMM
+// when one is asked for.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -30,11 +35,17 @@
 
 namespace kda {
 
-template <class E, int DK, int DV, int NTH>
+// GATED: also the layer's output epilogue on the fp32 read-out o of each
+// (b, h): y = o / sqrt(mean(o^2) + eps) * sigmoid(gate), in dtype Y ("KDA
+// Recurrence" problem statement); the threads of row group 0, which hold
+// the d_v outputs four apiece, reduce the sum of squares by lane shuffles.
+// o is written only when it is not NULL.
+template <class E, int DK, int DV, int NTH, bool GATED, class Y>
 __global__ __launch_bounds__(NTH) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const E* __restrict__ beta, float g_min,
-    float* __restrict__ state, E* __restrict__ o) {
+    float* __restrict__ state, E* __restrict__ o, const E* __restrict__ gate, float eps,
+    Y* __restrict__ y) {
     constexpr int NQ = DV / 4;       // column quads
     constexpr int NRG = NTH / NQ;    // row groups
     constexpr int R = DK / NRG;      // rows per thread
@@ -95,9 +106,29 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
     for (int j = 0; j < 4; ++j) r[j] = b * (to_f32(vh[j]) - p[j]);
 
     if (rg == 0) {
-        E* oh = o + bh * DV + cq * 4;
+        f32x4 ov;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) oh[j] = from_f32<E>(sq[j] + kqt * r[j]);
+        for (int j = 0; j < 4; ++j) ov[j] = sq[j] + kqt * r[j];
+        if (o) {
+            E* oh = o + bh * DV + cq * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oh[j] = from_f32<E>(ov[j]);
+        }
+        if constexpr (GATED) {
+            // row group 0 is lanes 0 .. NQ-1 of wave 0
+            float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+            for (int off = NQ / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, NQ);
+            const float inv = 1.0f / sqrtf(ss * (1.0f / DV) + eps);
+            const E* gh = gate + bh * DV + cq * 4;
+            Y* yh = y + bh * DV + cq * 4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float gj = to_f32(gh[j]);
+                const float sg = sizeof(E) == 4 ? 1.0f / (1.0f + expf(-gj)) : sigmoidf_(gj);
+                yh[j] = from_f32<Y>(ov[j] * inv * sg);
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -109,9 +140,20 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
 template <class E, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
     constexpr int NTH = (DK == 128 && DV == 128) ? KDA_DECODE_THREADS : 256;
-    hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH>), dim3(a.B * a.H), dim3(NTH), 0,
-                       (hipStream_t)a.stream, (const E*)a.q, (const E*)a.k, (const E*)a.v,
-                       (const E*)a.z, (const E*)a.beta, a.g_min, a.state, (E*)a.o);
+    const dim3 grid(a.B * a.H), block(NTH);
+    hipStream_t st = (hipStream_t)a.stream;
+    if (!a.gate)
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH, false, E>), grid, block, 0, st, (const E*)a.q,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.state,
+                           (E*)a.o, nullptr, 0.f, nullptr);
+    else if (a.y_bf16)
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH, true, bf16>), grid, block, 0, st, (const E*)a.q,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.state,
+                           (E*)a.o, (const E*)a.gate, a.eps, (bf16*)a.y);
+    else
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH, true, E>), grid, block, 0, st, (const E*)a.q,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.state,
+                           (E*)a.o, (const E*)a.gate, a.eps, (E*)a.y);
     return hipGetLastError();
 }
 

@@ -121,4 +121,44 @@ kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* 
     return finish(kda::launch_out_gate(a), stream);
 }
 
+size_t kda_recurrent_layer_step_workspace_bytes(int B, int H, int dv, int d_model, kda_dtype dt,
+                                                int with_projection) {
+    (void)d_model; (void)dt;
+    if (B < 0 || H < 0 || !dim_ok(dv) || !with_projection) return 0;
+    // the gated row in bf16, 256-byte aligned, then the GEMM library's scratch
+    return ((size_t)B * H * dv * 2 + 255) / 256 * 256 + kda::projection_scratch_bytes();
+}
+
+kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                                    float g_min, float* state, const void* gate, float eps, const void* w, void* o,
+                                    void* y, int B, int H, int dk, int dv, int d_model, kda_dtype dt,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || d_model < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (w && (dt != KDA_BF16 || d_model % 16 != 0 || d_model == 0)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (w && ((B + 127) / 128 > 65535 || (long long)H * dv > (1 << 20))) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (!(eps >= 0.f) || !isfinite(eps)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !z || !beta || !state || !gate || !y) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(gate) || !aligned16(w) || !aligned16(o) || !aligned16(y) ||
+        !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t need = kda_recurrent_layer_step_workspace_bytes(B, H, dv, d_model, dt, w != nullptr);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    kda::DecodeArgs a{q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
+    a.gate = gate;
+    a.eps = eps;
+    a.y = w ? workspace : y;
+    a.y_bf16 = w != nullptr;
+    hipError_t err = kda::launch_decode(a);
+    if (err == hipSuccess && w) {
+        void* lws = (unsigned char*)workspace + ((size_t)B * H * dv * 2 + 255) / 256 * 256;
+        err = kda::launch_projection(workspace, w, y, B, d_model, H * dv, lws, stream);
+    }
+    return finish(err, stream);
+}
+
 }  // extern "C"

@@ -12,10 +12,16 @@ struct DecodeArgs {
     const void *q, *k, *v, *z, *beta;
     float g_min;
     float* state;
-    void* o;
+    void* o;               // raw read-out, or NULL
     int B, H, dk, dv;
     bool bf16;
     void* stream;
+    // fused epilogue (gate != NULL): y = RMSNorm(o) * sigmoid(gate), written
+    // to y in the token dtype, or as bf16 when y_bf16 is set
+    const void* gate = nullptr;
+    float eps = 0.f;
+    void* y = nullptr;
+    bool y_bf16 = false;
 };
 hipError_t launch_decode(const DecodeArgs& a);
 
@@ -51,5 +57,10 @@ struct GateArgs {
 };
 size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj);
 hipError_t launch_out_gate(const GateArgs& a);
+// out (M x N, bf16) = y (M x K, bf16) . w (N x K, bf16)^T; lt_ws is the
+// GEMM library's scratch (projection_scratch_bytes() bytes)
+size_t projection_scratch_bytes();
+hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* lt_ws,
+                             void* stream);
 
 }  // namespace kda

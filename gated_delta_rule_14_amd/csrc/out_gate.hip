@@ -241,6 +241,27 @@ const LtPlan* lt_plan(int dev, int M, int N, int K) {
 }
 }  // namespace
 
+size_t projection_scratch_bytes() { return LT_WS; }
+
+hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* lt_ws,
+                             void* stream) {
+    hipStream_t st = (hipStream_t)stream;
+    if (M == 0) return hipSuccess;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (const LtPlan* p = lt_plan(dev, M, N, K)) {
+        const float one = 1.f, zero = 0.f;
+        const hipblasStatus_t r = hipblasLtMatmul(lt_state().handle[dev], p->op, &one, w, p->a, y, p->b, &zero, out,
+                                                  p->c, out, p->c, &p->algo, lt_ws, p->ws, st);
+        return r == HIPBLAS_STATUS_SUCCESS ? hipGetLastError() : hipErrorLaunchFailure;
+    }
+    dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM);
+    hipLaunchKernelGGL(proj_gemm_kernel, grid, dim3(256), 0, st, (const bf16*)y, (const bf16*)w, (bf16*)out, M, N,
+                       K);
+    return hipGetLastError();
+}
+
 hipError_t launch_out_gate(const GateArgs& a) {
     hipStream_t st = (hipStream_t)a.stream;
     const size_t rows = (size_t)a.B * a.T * a.H;
@@ -250,22 +271,8 @@ hipError_t launch_out_gate(const GateArgs& a) {
     }
     hipError_t err = launch_gate<bf16>(a.o, a.gate, a.eps, a.workspace, rows, a.dv, st);
     if (err != hipSuccess) return err;
-    const int M = a.B * a.T, N = a.d_model, K = a.H * a.dv;
-    if (M == 0) return hipSuccess;
-    int dev = 0;
-    if ((err = hipGetDevice(&dev)) != hipSuccess) return err;
-    if (const LtPlan* p = lt_plan(dev, M, N, K)) {
-        const float one = 1.f, zero = 0.f;
-        void* lws = (unsigned char*)a.workspace + y_bytes(a.B, a.T, a.H, a.dv);
-        const hipblasStatus_t r =
-            hipblasLtMatmul(lt_state().handle[dev], p->op, &one, a.w, p->a, a.workspace, p->b, &zero, a.y, p->c, a.y,
-                            p->c, &p->algo, lws, p->ws, st);
-        return r == HIPBLAS_STATUS_SUCCESS ? hipGetLastError() : hipErrorLaunchFailure;
-    }
-    dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM);
-    hipLaunchKernelGGL(proj_gemm_kernel, grid, dim3(256), 0, st, (const bf16*)a.workspace,
-                       (const bf16*)a.w, (bf16*)a.y, M, N, K);
-    return hipGetLastError();
+    void* lws = (unsigned char*)a.workspace + y_bytes(a.B, a.T, a.H, a.dv);
+    return launch_projection(a.workspace, a.w, a.y, a.B * a.T, a.d_model, a.H * a.dv, lws, a.stream);
 }
 
 }  // namespace kda

@@ -7,6 +7,9 @@ Names follow the C ABI in include/kda.h:
   chunk_fwd       -> kda_chunk_fwd        chunkwise prefill
   recurrent_step  -> kda_recurrent_step   one decode token, state in place
   out_gate        -> kda_out_gate         RMSNorm x sigmoid gate (+ projection)
+  recurrent_layer_step -> kda_recurrent_layer_step: one decode token of the
+                     whole layer (step + RMSNorm x gate in one launch,
+                     then the projection)
   layer           -> kda_chunk_fwd + kda_out_gate, returning the
                      {"outputs", "final_state"} dictionary of the
                      "KDA Recurrence" problem (final_state kept in fp32)
@@ -130,6 +133,44 @@ def out_gate(o, gate, eps, w=None, *, y=None, workspace=None):
         _p(o), _p(gate), float(eps), _p(w), _p(y), B, T, H, dv, d_model, _dt(o),
         _p(workspace), ws_bytes, _stream(dev)))
     return y
+
+
+def recurrent_layer_step_workspace_bytes(B, H, dv, d_model, dtype, with_projection):
+    return int(lib().kda_recurrent_layer_step_workspace_bytes(
+        B, H, dv, d_model, KDA_BF16 if dtype == torch.bfloat16 else KDA_F32, int(bool(with_projection))))
+
+
+def recurrent_layer_step(q, k, v, z, beta, g_min, state, gate, eps, w=None, *, y=None, o=None,
+                         want_o=False, workspace=None):
+    """One decode token of the layer. q, k, z: (B,H,dk); v, gate: (B,H,dv);
+    beta: (B,H); state: (B,H,dk,dv) fp32, updated in place; w: (d_model, H*dv)
+    bf16 or None.  Returns y ((B, d_model) with w, else (B, H*dv)), or
+    (y, o) when want_o (o: the raw read-out, (B,H,dv))."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("state", state), ("gate", gate)):
+        _need(t, name, dev)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if state.dtype != torch.float32:
+        raise TypeError("libkda: state must be float32")
+    d_model = 0
+    if w is not None:
+        _need(w, "w", dev)
+        d_model = w.shape[0]
+        if w.dtype != torch.bfloat16:
+            raise TypeError("libkda: projection w must be bfloat16")
+    if y is None:
+        y = torch.empty((B, d_model if w is not None else H * dv), dtype=q.dtype, device=dev)
+    if want_o and o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    need = lib().kda_recurrent_layer_step_workspace_bytes(B, H, dv, d_model, _dt(q), int(w is not None))
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("kda_recurrent_layer_step", lib().kda_recurrent_layer_step(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(state), _p(gate), float(eps), _p(w),
+        _p(o), _p(y), B, H, dk, dv, d_model, _dt(q), _p(workspace), ws_bytes, _stream(dev)))
+    return (y, o) if want_o else y
 
 
 def layer(query, key, value, decay_logits, write_strength, output_gate_logits,

@@ -147,6 +147,38 @@ kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* 
                         int B, int T, int H, int dv, int d_model, kda_dtype dt,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * One decode token of the whole layer of the "KDA Recurrence" problem:
+ * the token step of kda_recurrent_step, then the output epilogue of
+ * kda_out_gate (RMS normalisation over the d_v values with eps inside the
+ * square root, times sigmoid(gate), heads concatenated, then y W^T when w
+ * is given).  The normalisation and gate run in the recurrence step's own
+ * launch, on the fp32 read-out before any rounding; the projection, when
+ * asked for, is a second launch (hipBLASLt, as in kda_out_gate).
+ *
+ *   q, k, z   (B, H, dk)  dtype dt
+ *   v, gate   (B, H, dv)  dtype dt
+ *   beta      (B, H)      dtype dt
+ *   g_min, eps            as for kda_recurrent_step and kda_out_gate
+ *   state     (B, H, dk, dv) fp32, read and updated IN PLACE
+ *   w         (d_model, H*dv) bf16, or NULL for no projection
+ *   o         (B, H, dv) dtype dt: the raw read-out S^T q (written), or
+ *             NULL to skip it
+ *   y         (B, H*dv) dtype dt when w is NULL, (B, d_model) dtype dt
+ *             otherwise (written)
+ *   workspace kda_recurrent_layer_step_workspace_bytes() bytes (0 when w is
+ *             NULL): the gated row in bf16 and the projection's scratch
+ * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.
+ * Every other rule is that of kda_recurrent_step and kda_out_gate.
+ */
+size_t kda_recurrent_layer_step_workspace_bytes(int B, int H, int dv, int d_model, kda_dtype dt,
+                                                int with_projection);
+kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v, const void* z,
+                                    const void* beta, float g_min, float* state, const void* gate,
+                                    float eps, const void* w, void* o, void* y, int B, int H, int dk,
+                                    int dv, int d_model, kda_dtype dt, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,33 @@ def test_out_gate_rejects_bad_arguments(lib):
     assert gate(lib, w=P, dm=64, ws=None) == WS
     assert gate(lib, w=P, dm=64, ws=P, wsb=10) == WS
     assert gate(lib, T=0) == OK
+
+
+def lstep(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, state=P, g=P, eps=1e-6, w=None, o=None, y=P, B=4, H=2,
+          dk=128, dv=128, dm=0, dt=BF16, ws=None, wsb=0):
+    return lib.kda_recurrent_layer_step(q, k, v, z, beta, g_min, state, g, eps, w, o, y, B, H, dk, dv, dm, dt,
+                                        ws, wsb, S)
+
+
+def test_recurrent_layer_step_workspace_and_bad_arguments(lib):
+    # the gated row in bf16 (256-byte aligned), then the projection GEMM's 32 MiB
+    assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 2304, BF16, 1) == 256 * 32 * 128 * 2 + (32 << 20)
+    assert lib.kda_recurrent_layer_step_workspace_bytes(3, 1, 64, 16, BF16, 1) == 512 + (32 << 20)
+    assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 0, BF16, 0) == 0
+    assert lstep(lib, g=None) == NULL
+    assert lstep(lib, y=None) == NULL
+    assert lstep(lib, state=None) == NULL
+    assert lstep(lib, dk=32) == UNSUP
+    assert lstep(lib, dt=2) == UNSUP
+    assert lstep(lib, B=-1) == SHAPE
+    assert lstep(lib, g_min=0.0) == ARG
+    assert lstep(lib, eps=-1.0) == ARG
+    assert lstep(lib, eps=float("inf")) == ARG
+    assert lstep(lib, g=MIS) == ALIGN
+    assert lstep(lib, o=MIS) == ALIGN
+    assert lstep(lib, w=P, dm=100, ws=P, wsb=1 << 30) == UNSUP       # d_model % 16
+    assert lstep(lib, w=P, dm=64, dt=F32, ws=P, wsb=1 << 30) == UNSUP  # projection needs bf16
+    assert lstep(lib, w=P, dm=64, ws=None) == WS
+    assert lstep(lib, w=P, dm=64, ws=P, wsb=10) == WS
+    assert lstep(lib, B=0) == OK
+    assert lstep(lib, H=0) == OK
