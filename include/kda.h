@@ -36,6 +36,13 @@
  *    "KDA Recurrence" constraints).  g_min must be finite and < 0.
  *  - The library keeps no state between calls and is re-entrant; calls on
  *    different streams may run concurrently if their buffers are disjoint.
+ *    The one cache is the projection's: per device a hipBLASLt handle and,
+ *    per GEMM shape, the chosen algorithm, created by that shape's first
+ *    call.
+ *  - Calls may be captured into a HIP graph (they allocate nothing, record
+ *    no memset and never synchronise, unless KDA_DEBUG_SYNC=1).  A call
+ *    with a projection must have run once outside capture for its shape,
+ *    so that the GEMM plan exists before capture.
  */
 #ifndef KDA_H
 #define KDA_H
