@@ -10,7 +10,8 @@
  *     alpha_t = exp(g_min * sigmoid(z_t)),  g_min < 0   ("KDA Recurrence")
  *
  * with one d_k x d_v state per (batch, head).  Three calls cover the path:
- * chunkwise prefill, one decode token, and the output epilogue.
+ * chunkwise prefill, one decode token, and the output epilogue; a fourth
+ * runs one decode token of the whole layer (step and epilogue together).
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
