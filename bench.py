@@ -17,7 +17,8 @@ Also measured in the same run:
     workload (all heads over the full 32k tokens);
   * workloads: kda_chunk_fwd over the other prefill shapes -- the tiny fp32
     case (launch latency), the 8 x 8192 training shape, and the 1M-token
-    sequence followed by the RMSNorm x gate epilogue;
+    sequence followed by the RMSNorm x gate epilogue -- and the scalar-gate
+    (Gated DeltaNet) prefill at the 32k shape;
   * ceilings: what this GPU reaches on plain torch kernels -- an in-place
     fp32 scale (read-modify-write), a device copy and a large bf16 matmul --
     so that each kernel's rate can be read against them as well as against
@@ -275,6 +276,34 @@ def bench_workload(torch, kda, ki, name, seed, calls):
     return out
 
 
+def bench_gdn_prefill(torch, kda, ki, calls=10):
+    """The scalar-gate (Gated DeltaNet) prefill at the 32k shape: z is one
+    logit per (token, head), broadcast over the channels into the workspace,
+    then the channel-wise kernels.  Algorithmic bytes count z at 2 B per
+    token-head."""
+    cfg = ki.WORKLOADS["prefill_32k"]
+    B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    dev = torch.device("cuda:0")
+    x = ki.workload_inputs("prefill_32k", seed=1, device=dev)
+    zs = x["z"][..., 0].contiguous()
+    del x["z"]
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    per = _time_calls(torch, lambda: kda.gdn_chunk_fwd(x["q"], x["k"], x["v"], zs, x["beta"], ki.G_MIN, x["s0"],
+                                                       o=o, s_final=s, workspace=ws), calls)
+    nbytes = B * T * H * ((2 * dk + 2 * dv) * 2 + 2 + 2) + 2 * B * H * dk * dv * 4
+    gbs = nbytes / per / 1e9
+    del x, zs, o, s, ws
+    torch.cuda.empty_cache()
+    return {"workload": "prefill_32k scalar gate (Gated DeltaNet)", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+            "dtype": "bf16", "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1),
+            "unit": "tokens/s", "kernels": "kda_gdn_chunk_fwd (broadcast_gate_kernel + the kda_chunk_fwd kernels)",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
+
+
 def measured_ceilings(torch):
     """Rates this GPU reaches on plain torch kernels: in-place fp32 scale over
     512 MiB (read + write), a 512 MiB device copy, a bf16 8192^3 matmul."""
@@ -439,6 +468,7 @@ def main():
     if not args.no_workloads:
         wl = [bench_workload(torch, kda, ki, "tiny_fp32", 0, 20),
               bench_workload(torch, kda, ki, "train_8x8k", 2, 5)]
+        wl.append(bench_gdn_prefill(torch, kda, ki))
         if not args.no_long:
             wl.append(bench_workload(torch, kda, ki, "long_1m", 4, 2))
         line["workloads"] = wl

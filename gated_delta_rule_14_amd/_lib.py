@@ -24,6 +24,11 @@ SIGNATURES = {
                                 _i, _i, _i, _i, _i, _vp]),
     "kda_out_gate_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "kda_out_gate": (_i, [_vp, _vp, _f, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "kda_gdn_chunk_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_gdn_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
+                               _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "kda_gdn_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
+                                    _i, _i, _i, _i, _i, _vp]),
     "kda_recurrent_layer_step_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "kda_recurrent_layer_step": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _f, _vp, _vp, _vp,
                                       _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),

@@ -40,7 +40,9 @@ namespace kda {
 // Recurrence" problem statement); the threads of row group 0, which hold
 // the d_v outputs four apiece, reduce the sum of squares by lane shuffles.
 // o is written only when it is not NULL.
-template <class E, int DK, int DV, int NTH, bool GATED, class Y>
+// ZS: z holds one logit per (b, h), the same for every key channel (the
+// scalar-decay case).
+template <class E, int DK, int DV, int NTH, bool GATED, class Y, bool ZS = false>
 __global__ __launch_bounds__(NTH) void decode_step_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const E* __restrict__ beta, float g_min,
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
     float* S = state + bh * DK * DV;
     const E* qh = q + bh * DK;
     const E* kh = k + bh * DK;
-    const E* zh = z + bh * DK;
+    const E* zh = ZS ? z + bh : z + bh * DK;
 
     f32x4 s[R];
 #pragma unroll
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(NTH) void decode_step_kernel(
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int c = rg + i * NRG;
-        const float zc = to_f32(zh[c]);
+        const float zc = to_f32(zh[ZS ? 0 : c]);
         const float a = __expf(g_min * sigmoidf_(zc));
         const float kc = to_f32(kh[c]);
         const float qc = to_f32(qh[c]);
@@ -142,7 +144,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
     constexpr int NTH = (DK == 128 && DV == 128) ? KDA_DECODE_THREADS : 256;
     const dim3 grid(a.B * a.H), block(NTH);
     hipStream_t st = (hipStream_t)a.stream;
-    if (!a.gate)
+    if (a.z_scalar)
+        hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH, false, E, true>), grid, block, 0, st, (const E*)a.q,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.state,
+                           (E*)a.o, nullptr, 0.f, nullptr);
+    else if (!a.gate)
         hipLaunchKernelGGL((decode_step_kernel<E, DK, DV, NTH, false, E>), grid, block, 0, st, (const E*)a.q,
                            (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.state,
                            (E*)a.o, nullptr, 0.f, nullptr);

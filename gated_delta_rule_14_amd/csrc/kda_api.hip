@@ -121,6 +121,60 @@ kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* 
     return finish(kda::launch_out_gate(a), stream);
 }
 
+size_t kda_gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    // the channel-wise operator's workspace (256-byte aligned), then the
+    // logits broadcast over the d_k channels
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const size_t base = (kda::chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16) + 255) / 256 * 256;
+    return base + (size_t)B * T * H * dk * esz;
+}
+
+kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                             float g_min, const float* s0, void* o, float* s_final, int B, int T, int H, int dk,
+                             int dv, int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (chunk != 64 || !dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (B > 65535 || H > 65535 || (long long)B * H * T > (1LL << 40)) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(s0) || !aligned16(o) || !aligned16(s_final) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    const size_t need = kda_gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dt);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    const size_t esz = dt == KDA_BF16 ? 2 : 4;
+    const size_t zbytes = (size_t)B * T * H * dk * esz;
+    void* zfull = zbytes ? (unsigned char*)workspace + (need - zbytes) : nullptr;
+    hipError_t err = kda::launch_broadcast_gate(z, zfull, (size_t)B * T * H, dk, dt == KDA_BF16, stream);
+    if (err != hipSuccess) return finish(err, stream);
+    const size_t base = need - zbytes;
+    kda::ChunkArgs a{q, k, v, zfull, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16,
+                     base ? workspace : nullptr, stream};
+    return finish(kda::launch_chunk(a), stream);
+}
+
+kda_status kda_gdn_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                                  float g_min, float* state, void* o, int B, int H, int dk, int dv, kda_dtype dt,
+                                  void* stream) {
+    if (B < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !z || !beta || !state || !o) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(state) || !aligned16(o))
+        return KDA_ERR_ALIGN;
+    kda::DecodeArgs a{q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
+    a.z_scalar = true;
+    return finish(kda::launch_decode(a), stream);
+}
+
 size_t kda_recurrent_layer_step_workspace_bytes(int B, int H, int dv, int d_model, kda_dtype dt,
                                                 int with_projection) {
     (void)d_model; (void)dt;

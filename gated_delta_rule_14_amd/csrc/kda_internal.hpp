@@ -22,8 +22,12 @@ struct DecodeArgs {
     float eps = 0.f;
     void* y = nullptr;
     bool y_bf16 = false;
+    // z holds one logit per (b, h) for all d_k channels (scalar decay)
+    bool z_scalar = false;
 };
 hipError_t launch_decode(const DecodeArgs& a);
+// zfull (rows x dk) = each of the rows scalar logits zs repeated dk times
+hipError_t launch_broadcast_gate(const void* zs, void* zfull, size_t rows, int dk, bool bf16, void* stream);
 
 struct ChunkArgs {
     const void *q, *k, *v, *z, *beta;

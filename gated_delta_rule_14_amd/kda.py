@@ -7,6 +7,8 @@ Names follow the C ABI in include/kda.h:
   chunk_fwd       -> kda_chunk_fwd        chunkwise prefill
   recurrent_step  -> kda_recurrent_step   one decode token, state in place
   out_gate        -> kda_out_gate         RMSNorm x sigmoid gate (+ projection)
+  gdn_chunk_fwd   -> kda_gdn_chunk_fwd       scalar-gate prefill, z (B,T,H)
+  gdn_recurrent_step -> kda_gdn_recurrent_step scalar-gate decode, z (B,H)
   recurrent_layer_step -> kda_recurrent_layer_step: one decode token of the
                      whole layer (step + RMSNorm x gate in one launch,
                      then the projection)
@@ -98,6 +100,63 @@ def recurrent_step(q, k, v, z, beta, g_min, state, *, o=None):
     if o is None:
         o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
     check("kda_recurrent_step", lib().kda_recurrent_step(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(state), _p(o),
+        B, H, dk, dv, _dt(q), _stream(dev)))
+    return o
+
+
+def gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return int(lib().kda_gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK,
+                                                       KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def gdn_chunk_fwd(q, k, v, z, beta, g_min, s0=None, *, o=None, s_final=None, workspace=None, want_state=True):
+    """Scalar-gate (Gated DeltaNet) prefill: as chunk_fwd, but z is (B,T,H),
+    one decay logit per token and head."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(z.shape) != (B, T, H):
+        raise ValueError(f"libkda: scalar-gate z must be (B, T, H) = {(B, T, H)}, got {tuple(z.shape)}")
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    need = lib().kda_gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK, _dt(q))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    check("kda_gdn_chunk_fwd", lib().kda_gdn_chunk_fwd(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(o), _p(s_final),
+        B, T, H, dk, dv, CHUNK, _dt(q), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev)))
+    return o, s_final
+
+
+def gdn_recurrent_step(q, k, v, z, beta, g_min, state, *, o=None):
+    """Scalar-gate (Gated DeltaNet) decode token: as recurrent_step, but z is
+    (B,H)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("state", state)):
+        _need(t, name, dev)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if tuple(z.shape) != (B, H):
+        raise ValueError(f"libkda: scalar-gate z must be (B, H) = {(B, H)}, got {tuple(z.shape)}")
+    if state.dtype != torch.float32:
+        raise TypeError("libkda: state must be float32")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    check("kda_gdn_recurrent_step", lib().kda_gdn_recurrent_step(
         _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(state), _p(o),
         B, H, dk, dv, _dt(q), _stream(dev)))
     return o

@@ -11,7 +11,8 @@
  *
  * with one d_k x d_v state per (batch, head).  Three calls cover the path:
  * chunkwise prefill, one decode token, and the output epilogue; a fourth
- * runs one decode token of the whole layer (step and epilogue together).
+ * runs one decode token of the whole layer (step and epilogue together),
+ * and two more take the scalar-gate (Gated DeltaNet) special case.
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
@@ -186,6 +187,34 @@ kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v,
                                     float eps, const void* w, void* o, void* y, int B, int H, int dk,
                                     int dv, int d_model, kda_dtype dt, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * The Gated DeltaNet special case: one decay logit per (token, head), so
+ * alpha_t = exp(g_min * sigmoid(z_t)) is a scalar and Diag(alpha_t) =
+ * alpha_t I (Kimi Linear tech report, section 3, where KDA refines Gated
+ * DeltaNet's scalar gate into a channel-wise one).  Same operator, readout
+ * and conventions as kda_chunk_fwd / kda_recurrent_step, except:
+ *
+ *   z   (B, T, H) for kda_gdn_chunk_fwd, (B, H) for kda_gdn_recurrent_step,
+ *       dtype dt
+ *
+ * The prefill runs on the channel-wise kernels: the logits are first
+ * written across the d_k channels of the workspace, whose size
+ * kda_gdn_chunk_fwd_workspace_bytes() returns (that of kda_chunk_fwd,
+ * rounded up to 256 bytes, plus B*T*H*dk elements).  Decode reads the
+ * scalar directly and needs no workspace.  The results equal those of the
+ * channel-wise calls given z repeated over the channels, bit for bit.
+ */
+size_t kda_gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                         kda_dtype dt);
+kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                             const void* beta, float g_min, const float* s0, void* o,
+                             float* s_final, int B, int T, int H, int dk, int dv, int chunk,
+                             kda_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream);
+kda_status kda_gdn_recurrent_step(const void* q, const void* k, const void* v, const void* z,
+                                  const void* beta, float g_min, float* state, void* o,
+                                  int B, int H, int dk, int dv, kda_dtype dt, void* stream);
 
 #ifdef __cplusplus
 }

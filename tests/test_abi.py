@@ -181,3 +181,38 @@ def test_recurrent_layer_step_workspace_and_bad_arguments(lib):
     assert lstep(lib, w=P, dm=64, ws=P, wsb=10) == WS
     assert lstep(lib, B=0) == OK
     assert lstep(lib, H=0) == OK
+
+
+def test_scalar_gate_calls_workspace_and_bad_arguments(lib):
+    # the channel-wise workspace rounded up to 256 bytes, then z over the d_k channels
+    kda_ws = lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16)
+    assert lib.kda_gdn_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == \
+        (kda_ws + 255) // 256 * 256 + 32768 * 32 * 128 * 2
+    assert lib.kda_gdn_chunk_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, BF16) == 8 * 8192 * 32 * 128 * 2
+    assert lib.kda_gdn_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32) == \
+        (lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32) + 255) // 256 * 256 + 256 * 64 * 4
+    assert lib.kda_gdn_chunk_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, F32) == 0
+
+    def g(q=P, z=P, g_min=-5.0, B=1, T=128, H=2, dk=128, dv=128, chunk=64, dt=BF16, ws=P, wsb=1 << 30):
+        return lib.kda_gdn_chunk_fwd(q, P, P, z, P, g_min, None, P, P, B, T, H, dk, dv, chunk, dt, ws, wsb, S)
+
+    assert g(z=None) == NULL
+    assert g(q=None) == NULL
+    assert g(dk=96) == UNSUP
+    assert g(chunk=32) == UNSUP
+    assert g(B=-1) == SHAPE
+    assert g(g_min=0.0) == ARG
+    assert g(z=MIS) == ALIGN
+    assert g(ws=None, wsb=0) == WS
+    assert g(wsb=16) == WS
+    assert g(H=0) == OK
+
+    def d(z=P, g_min=-5.0, B=4, H=2, dk=128, dv=128, dt=BF16, o=P):
+        return lib.kda_gdn_recurrent_step(P, P, P, z, P, g_min, P, o, B, H, dk, dv, dt, S)
+
+    assert d(z=None) == NULL
+    assert d(o=None) == NULL
+    assert d(dv=32) == UNSUP
+    assert d(g_min=float("nan")) == ARG
+    assert d(z=MIS) == ALIGN
+    assert d(B=0) == OK
