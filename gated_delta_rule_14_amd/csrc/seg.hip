@@ -863,14 +863,21 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int ct = 0; ct < NTW; ++ct) zb[kb][ct] = pack8(y[2 * kb][ct], y[2 * kb + 1][ct]);
+        // T' fragments one row tile ahead
+        MF::frag tf[2][2];
+        tf[0][0] = load_frag<bf16>(Tp, L::LT, 0, 0);
+        tf[0][1] = load_frag<bf16>(Tp, L::LT, 0, 32);
 #pragma unroll
         for (int yt = 0; yt < 4; ++yt) {
-            const MF::frag t0 = load_frag<bf16>(Tp, L::LT, yt * 16, 0);
-            const MF::frag t1 = load_frag<bf16>(Tp, L::LT, yt * 16, 32);
+            const int cur = yt & 1, nxt = cur ^ 1;
+            if (yt + 1 < 4) {
+                tf[nxt][0] = load_frag<bf16>(Tp, L::LT, (yt + 1) * 16, 0);
+                tf[nxt][1] = load_frag<bf16>(Tp, L::LT, (yt + 1) * 16, 32);
+            }
 #pragma unroll
             for (int ct = 0; ct < NTW; ++ct) {
-                y[yt][ct] = MF::mma(t0, zb[0][ct], zero4());
-                y[yt][ct] = MF::mma(t1, zb[1][ct], y[yt][ct]);
+                y[yt][ct] = MF::mma(tf[cur][0], zb[0][ct], zero4());
+                y[yt][ct] = MF::mma(tf[cur][1], zb[1][ct], y[yt][ct]);
             }
         }
     }
@@ -902,18 +909,23 @@ __device__ __forceinline__ void chain_b(f32x4 (&xs)[8][NTW], const bf16x8 (&yb)[
                                         const float* egc) {
     typedef Mfma<bf16> MF;
     const int g = lane_id() >> 4;
-    MF::frag kf[2][2];
-    f32x4 dv[2];
-    kf[0][0] = load_frag<bf16>(KGT, L::LC, 0, 0);
-    kf[0][1] = load_frag<bf16>(KGT, L::LC, 0, 32);
-    dv[0] = *reinterpret_cast<const f32x4*>(egc + 4 * g);
+    // fragments read two row tiles ahead: one tile's four MFMAs do not
+    // cover an LDS read under load
+    MF::frag kf[3][2];
+    f32x4 dv[3];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        kf[p][0] = load_frag<bf16>(KGT, L::LC, p * 16, 0);
+        kf[p][1] = load_frag<bf16>(KGT, L::LC, p * 16, 32);
+        dv[p] = *reinterpret_cast<const f32x4*>(egc + p * 16 + 4 * g);
+    }
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt) {
-        const int cur = rt & 1, nxt = cur ^ 1;
-        if (rt + 1 < 8) {
-            kf[nxt][0] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 0);
-            kf[nxt][1] = load_frag<bf16>(KGT, L::LC, (rt + 1) * 16, 32);
-            dv[nxt] = *reinterpret_cast<const f32x4*>(egc + (rt + 1) * 16 + 4 * g);
+        const int cur = rt % 3, nxt = (rt + 2) % 3;
+        if (rt + 2 < 8) {
+            kf[nxt][0] = load_frag<bf16>(KGT, L::LC, (rt + 2) * 16, 0);
+            kf[nxt][1] = load_frag<bf16>(KGT, L::LC, (rt + 2) * 16, 32);
+            dv[nxt] = *reinterpret_cast<const f32x4*>(egc + (rt + 2) * 16 + 4 * g);
         }
 #pragma unroll
         for (int ct = 0; ct < NTW; ++ct) {
