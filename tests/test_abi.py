@@ -216,3 +216,23 @@ def test_scalar_gate_calls_workspace_and_bad_arguments(lib):
     assert d(g_min=float("nan")) == ARG
     assert d(z=MIS) == ALIGN
     assert d(B=0) == OK
+
+
+def test_plain_c_caller(tmp_path):
+    """The header compiles as C (gcc, -std=c11 -Wall -Werror) and a C program
+    linked against libkda.so gets the documented host-side behaviour."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libkda.so is not built; run __graft_entry__.build() first")
+    exe = tmp_path / "abi_check"
+    src = os.path.join(ROOT, "tests", "c_abi", "abi_check.c")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                    "-L", libdir, "-lkda", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "ok"
