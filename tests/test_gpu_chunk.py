@@ -176,6 +176,18 @@ def test_two_level_split_resume():
     assert rel(f64(sb), f64(s)) < 1e-5
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 255, 1024), (2, 128, 1024), (1, 128, 1000), (4, 64, 1536)])
+def test_segment_plan_boundaries(B, H, T):
+    """bf16, d = 128, around the plan's switch points: 255 chains of 16
+    chunks split into two segments of exactly eight chunks; 256 chains run
+    one pass; 128 chains with a ragged last chunk; 256 chains of 24 chunks.
+    The oracle runs on sampled heads."""
+    x = ki.prefill_inputs(B, T, H, 128, 128, torch.bfloat16, seed=B * 1000 + H, device=DEV, s0_var=0.01,
+                          z_mean=-3.0)
+    heads = sorted({0, H // 2, H - 1})
+    check(x, "bf16", heads=heads, label=f"plan B={B} H={H} T={T}")
+
+
 # ------------------------------------------------------------------ full sizes
 def test_prefill_32k_full_size_sampled():
     """B=1, T=32768, H=32, d=128, bf16, S0 ~ N(0, 0.01): the prefill workload
