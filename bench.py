@@ -413,8 +413,15 @@ def cpu_baseline(torch, ki, nheads):
     oracle.forward(h["q"], h["k"], h["v"], h["z"], h["beta"], ki.G_MIN, s0, nthreads=threads)
     dt = time.perf_counter() - t0
     # a token is one (b, t) position over all H heads: scale the sample by nheads / H
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": T * nheads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill_32k, {nheads} of {H} heads over all {T} tokens, fp64, {dt:.1f} s"}
+            "sample": f"prefill_32k, {nheads} of {H} heads over all {T} tokens, fp64, {dt:.1f} s",
+            "cpu_model": model}
 
 
 def main():
@@ -484,6 +491,7 @@ def main():
                 line["epilogue"]["roofline"]["achieved"] / c["mfma_bf16_tflops"], 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(torch, ki, args.cpu_heads)
+        line["cpu_baseline"]["gpu_over_oracle"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
 
