@@ -32,6 +32,39 @@ kda_status finish(hipError_t err, void* stream) {
     return KDA_OK;
 }
 
+// Checks shared by the prefill calls, in the order the header documents.
+// KDA_OK with B * H == 0 means there is nothing to launch (pointers are not
+// examined then).
+kda_status check_chunk_args(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                            float g_min, const float* s0, const void* o, const float* s_final, int B, int T, int H,
+                            int dk, int dv, int chunk, kda_dtype dt, const void* workspace) {
+    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (chunk != 64 || !dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (B > 65535 || H > 65535 || (long long)B * H * T > (1LL << 40)) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
+        !aligned16(s0) || !aligned16(o) || !aligned16(s_final) || !aligned16(workspace))
+        return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+// Checks shared by the decode calls (the state and token tensors of one step).
+kda_status check_step_args(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                           float g_min, const float* state, int B, int H, int dk, int dv, kda_dtype dt) {
+    if (B < 0 || H < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
+    if (B == 0 || H == 0) return KDA_OK;
+    if (!q || !k || !v || !z || !beta || !state) return KDA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) || !aligned16(state))
+        return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,16 +95,9 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          float g_min, const float* s0, void* o, float* s_final, int B, int T, int H,
                          int dk, int dv, int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (chunk != 64 || !dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16))
-        return KDA_ERR_UNSUPPORTED;
-    if (B > 65535 || H > 65535 || (long long)B * H * T > (1LL << 40)) return KDA_ERR_SHAPE;
-    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
-    if (B == 0 || H == 0) return KDA_OK;
-    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
-        !aligned16(s0) || !aligned16(o) || !aligned16(s_final) || !aligned16(workspace))
-        return KDA_ERR_ALIGN;
+    const kda_status st = check_chunk_args(q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, chunk, dt,
+                                           workspace);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
     const size_t need = kda::chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16,
@@ -82,15 +108,10 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
                               float g_min, float* state, void* o, int B, int H, int dk, int dv, kda_dtype dt,
                               void* stream) {
-    if (B < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
-    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
-    if (B == 0 || H == 0) return KDA_OK;
-    if (!q || !k || !v || !z || !beta || !state || !o) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
-        !aligned16(state) || !aligned16(o))
-        return KDA_ERR_ALIGN;
+    const kda_status st = check_step_args(q, k, v, z, beta, g_min, state, B, H, dk, dv, dt);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (!o) return KDA_ERR_NULL;
+    if (!aligned16(o)) return KDA_ERR_ALIGN;
     kda::DecodeArgs a{q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
     return finish(kda::launch_decode(a), stream);
 }
@@ -135,16 +156,9 @@ kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
                              float g_min, const float* s0, void* o, float* s_final, int B, int T, int H, int dk,
                              int dv, int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
                              void* stream) {
-    if (B < 0 || T < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (chunk != 64 || !dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16))
-        return KDA_ERR_UNSUPPORTED;
-    if (B > 65535 || H > 65535 || (long long)B * H * T > (1LL << 40)) return KDA_ERR_SHAPE;
-    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
-    if (B == 0 || H == 0) return KDA_OK;
-    if (T > 0 && (!q || !k || !v || !z || !beta || !o)) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
-        !aligned16(s0) || !aligned16(o) || !aligned16(s_final) || !aligned16(workspace))
-        return KDA_ERR_ALIGN;
+    const kda_status st = check_chunk_args(q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, chunk, dt,
+                                           workspace);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
     const size_t need = kda_gdn_chunk_fwd_workspace_bytes(B, T, H, dk, dv, chunk, dt);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     const size_t esz = dt == KDA_BF16 ? 2 : 4;
@@ -161,15 +175,10 @@ kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
 kda_status kda_gdn_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
                                   float g_min, float* state, void* o, int B, int H, int dk, int dv, kda_dtype dt,
                                   void* stream) {
-    if (B < 0 || H < 0) return KDA_ERR_SHAPE;
-    if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
-    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
-    if (B == 0 || H == 0) return KDA_OK;
-    if (!q || !k || !v || !z || !beta || !state || !o) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
-        !aligned16(state) || !aligned16(o))
-        return KDA_ERR_ALIGN;
+    const kda_status st = check_step_args(q, k, v, z, beta, g_min, state, B, H, dk, dv, dt);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (!o) return KDA_ERR_NULL;
+    if (!aligned16(o)) return KDA_ERR_ALIGN;
     kda::DecodeArgs a{q, k, v, z, beta, g_min, state, o, B, H, dk, dv, dt == KDA_BF16, stream};
     a.z_scalar = true;
     return finish(kda::launch_decode(a), stream);
@@ -187,18 +196,16 @@ kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v,
                                     float g_min, float* state, const void* gate, float eps, const void* w, void* o,
                                     void* y, int B, int H, int dk, int dv, int d_model, kda_dtype dt,
                                     void* workspace, size_t workspace_bytes, void* stream) {
+    // the projection's own checks first, in the order kda_out_gate makes them
     if (B < 0 || H < 0 || d_model < 0) return KDA_ERR_SHAPE;
     if (!dim_ok(dk) || !dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
     if (w && (dt != KDA_BF16 || d_model % 16 != 0 || d_model == 0)) return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (w && ((B + 127) / 128 > 65535 || (long long)H * dv > (1 << 20))) return KDA_ERR_SHAPE;
-    if (!(g_min < 0.f) || !isfinite(g_min)) return KDA_ERR_ARG;
     if (!(eps >= 0.f) || !isfinite(eps)) return KDA_ERR_ARG;
-    if (B == 0 || H == 0) return KDA_OK;
-    if (!q || !k || !v || !z || !beta || !state || !gate || !y) return KDA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(z) || !aligned16(beta) ||
-        !aligned16(state) || !aligned16(gate) || !aligned16(w) || !aligned16(o) || !aligned16(y) ||
-        !aligned16(workspace))
+    const kda_status st = check_step_args(q, k, v, z, beta, g_min, state, B, H, dk, dv, dt);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (!gate || !y) return KDA_ERR_NULL;
+    if (!aligned16(gate) || !aligned16(w) || !aligned16(o) || !aligned16(y) || !aligned16(workspace))
         return KDA_ERR_ALIGN;
     const size_t need = kda_recurrent_layer_step_workspace_bytes(B, H, dv, d_model, dt, w != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
