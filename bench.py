@@ -57,10 +57,14 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_14_amd", "csrc")
 
 def kernel_source_hash():
     """Hash of the kernel sources with comments and blank lines removed, so
-    that the stored counters stay attached to the code they were taken on."""
+    that the stored counters stay attached to the code they were taken on.
+    kda_api.hip (argument checks and dispatch to the launchers, no kernels)
+    is not part of it."""
     import re
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if os.path.basename(f) == "kda_api.hip":
+            continue
         text = open(f, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
