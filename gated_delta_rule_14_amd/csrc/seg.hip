@@ -1550,12 +1550,17 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
             } else {
                 pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
-                pipe_vt<MODE>(pv, R, smem);
                 pipe_diag_mma<MODE>(R, smem, accA, accM);
             }
             pipe_diag_inv<MODE>(R, smem, accA, accM);
-            if constexpr (!VSTATE) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+            if constexpr (EXP && !VSTATE) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
             __syncthreads();   // S2 | S3
+            if constexpr (!EXP) {
+                // compose: v^T and the next chunk's v in S3, beside the
+                // state waves' deferred update (S2 is the gate waves' longer step)
+                pipe_vt<MODE>(pv, R, smem);
+                pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+            }
             pipe_tsolve<MODE>(R, smem);
             __syncthreads();   // S3 | next S1
         }
