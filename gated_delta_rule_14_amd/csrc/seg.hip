@@ -1443,8 +1443,11 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 1>(w, smem);
             if constexpr (!LITE) {
                 __syncthreads();   // S2 | S3
-                if constexpr (!EXP)
+                if constexpr (!EXP) {
                     if (upd) update(n - 1);
+                } else {
+                    pipe_tsolve<MODE>(w, smem);   // the gate waves form the next chunk's sums meanwhile
+                }
             }
             __syncthreads();   // S3 (S2 for EXPAND_LITE) | next S1
         };
@@ -1477,10 +1480,12 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                             xo[(ob + row) * NX + col] = xs[hh][rt][ct][e];
                         }
         }
-    } else if constexpr (LITE) {
-        // ---------------- gate waves, EXPAND_LITE: block R of each chunk.
-        // The next chunk's running sums of sigmoid(z) are formed in S2, where
-        // the state waves' M pairs leave room, and kept in registers.
+    } else if constexpr (EXP) {
+        // ---------------- gate waves, EXPAND and EXPAND_LITE: block R of each
+        // chunk.  The next chunk's running sums of sigmoid(z) are formed in
+        // the last step (S2 for EXPAND_LITE, where the state waves' M pairs
+        // leave room; S3 for EXPAND, where the state waves solve for T') and
+        // kept in registers.
         const int R = w - 4;
         const float kg2 = g_min * LOG2E;
         PIn<true> in;
@@ -1489,7 +1494,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         {
             const int valid = min(C, T - n0 * C);
             pfetch_zkq<true>(in, q, k, z, beta, row_of(n0), valid, H, R);
-            pfetch_v(pv, v, row_of(n0), valid, H, R);
+            if constexpr (LITE) pfetch_v(pv, v, row_of(n0), valid, H, R);
             if (valid < C) pmask<true>(in, valid, R);
             gate_sums<true>(in, S);
         }
@@ -1502,9 +1507,10 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             pfetch_z<true>(in, z, row_of(mn), valid_n, H, R);   // this chunk's z is consumed
             gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
             pfetch_kq<true>(in, q, k, beta, row_of(mn), valid_n, H, R);
-            // this chunk's T' from the compose pass, into LDS after the barrier
-            f32x4 tpr[2];
-            {
+            // EXPAND_LITE: this chunk's T' from the compose pass, into LDS
+            // after the barrier
+            f32x4 tpr[LITE ? 2 : 1];
+            if constexpr (LITE) {
                 const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(m));
 #pragma unroll
                 for (int j = 0; j < 2; ++j) tpr[j] = tg[(threadIdx.x - 256) + 256 * j];
@@ -1513,54 +1519,49 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             f32x4 accA, accM;
             pipe_diag_mma<MODE>(R, smem, accA, accM);
             pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
-            pipe_vt<MODE>(pv, R, smem);
+            if constexpr (LITE) pipe_vt<MODE>(pv, R, smem);
             pipe_diag_inv<MODE>(R, smem, accA, accM);
-            pfetch_v(pv, v, row_of(mn), valid_n, H, R);
+            if constexpr (LITE) {
+                pfetch_v(pv, v, row_of(mn), valid_n, H, R);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
+                for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
+            } else {
+                __syncthreads();   // S2 | S3
+            }
             if (valid_n < C) pmask<true>(in, valid_n, R);
             gate_sums<true>(in, S);
-            __syncthreads();   // S2 | next S1
+            __syncthreads();   // S2 (S3 for EXPAND) | next S1
         }
     } else {
-        // ---------------- gate waves: block R of each chunk
+        // ---------------- gate waves, COMPOSE: block R of each chunk
         const int R = w - 4;
         const float kg2 = g_min * LOG2E;
-        PIn<EXP> in;
+        PIn<false> in;
         PV pv;
         {
             const int valid = min(C, T - n0 * C);
-            pfetch_zkq<EXP>(in, q, k, z, beta, row_of(n0), valid, H, R);
-            if constexpr (!VSTATE) pfetch_v(pv, v, row_of(n0), valid, H, R);
+            pfetch_zkq<false>(in, q, k, z, beta, row_of(n0), valid, H, R);
+            pfetch_v(pv, v, row_of(n0), valid, H, R);
         }
-        float kl[SUB][2], kr[SUB][2], ql[EXP ? SUB : 1][2];
+        float kl[SUB][2], kr[SUB][2], ql[1][2];
         for (int i = 0; i < nL; ++i) {
             const int m = n0 + i;
             const int valid = min(C, T - m * C);
             const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
             const int valid_n = min(C, T - mn * C);
-            if (valid < C) pmask<EXP>(in, valid, R);
+            if (valid < C) pmask<false>(in, valid, R);
             pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
-            pfetch_zkq<EXP>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
+            pfetch_zkq<false>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
-            if constexpr (EXP) {
-                // products in flight while the operands are written
-                pipe_diag_mma<MODE>(R, smem, accA, accM);
-                pipe_abs<MODE>(R, smem, kl, kr, ql, 0);
-            } else {
-                pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
-                pipe_diag_mma<MODE>(R, smem, accA, accM);
-            }
+            pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
+            pipe_diag_mma<MODE>(R, smem, accA, accM);
             pipe_diag_inv<MODE>(R, smem, accA, accM);
-            if constexpr (EXP && !VSTATE) pfetch_v(pv, v, row_of(mn), valid_n, H, R);
             __syncthreads();   // S2 | S3
-            if constexpr (!EXP) {
-                // compose: v^T and the next chunk's v in S3, beside the
-                // state waves' deferred update (S2 is the gate waves' longer step)
-                pipe_vt<MODE>(pv, R, smem);
-                pfetch_v(pv, v, row_of(mn), valid_n, H, R);
-            }
+            // v^T and the next chunk's v in S3, beside the state waves'
+            // deferred update (S2 is the gate waves' longer step)
+            pipe_vt<MODE>(pv, R, smem);
+            pfetch_v(pv, v, row_of(mn), valid_n, H, R);
             pipe_tsolve<MODE>(R, smem);
             __syncthreads();   // S3 | next S1
         }
