@@ -17,8 +17,11 @@ Also measured in the same run:
     workload (all heads over the full 32k tokens);
   * workloads: kda_chunk_fwd over the other prefill shapes -- the tiny fp32
     case (launch latency), the 8 x 8192 training shape, and the 1M-token
-    sequence followed by the RMSNorm x gate epilogue -- and the scalar-gate
-    (Gated DeltaNet) prefill at the 32k shape;
+    sequence with the RMSNorm x gate epilogue (kda_chunk_layer_fwd, the
+    epilogue inside the prefill kernels, timed beside kda_chunk_fwd +
+    kda_out_gate) -- the training-shape layer with its projection
+    (kda_chunk_layer_fwd, likewise), and the scalar-gate (Gated DeltaNet)
+    prefill at the 32k shape;
   * ceilings: what this GPU reaches on plain torch kernels -- an in-place
     fp32 scale (read-modify-write), a device copy and a large bf16 matmul --
     so that each kernel's rate can be read against them as well as against
@@ -240,11 +243,13 @@ def _time_calls(torch, fn, calls, warmup=1):
 
 
 def bench_workload(torch, kda, ki, name, seed, calls):
-    """One kda_chunk_fwd call over a named prefill workload (plus, where the
-    workload has it, the RMSNorm x gate epilogue without projection), inputs
-    resident in HBM.  Algorithmic bytes: the token tensors once each, S0 read
-    when it is given, S_final written; the gate workload adds its gate logits
-    read and y written (o stays counted once, as in a fused pass)."""
+    """One kda_chunk_fwd call over a named prefill workload, or where the
+    workload has the RMSNorm x gate epilogue (no projection) one
+    kda_chunk_layer_fwd call (raw outputs not kept), timed beside
+    kda_chunk_fwd + kda_out_gate; inputs resident in HBM.  Algorithmic bytes:
+    the token tensors once each, S0 read when it is given, S_final written;
+    the gate workload counts its gate logits read and y written in place of
+    o."""
     cfg = ki.WORKLOADS[name]
     B, T, H, dk, dv, dt = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["dtype"]
     dev = torch.device("cuda:0")
@@ -255,29 +260,76 @@ def bench_workload(torch, kda, ki, name, seed, calls):
     s = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, dt), 16), dtype=torch.uint8, device=dev)
     y = torch.empty((B, T, H * dv), dtype=dt, device=dev) if gate else None
+    lws = None
+    if gate:
+        need = kda.chunk_layer_fwd_workspace_bytes(B, T, H, dk, dv, 0, dt, False)
+        lws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def call():
         kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, s0, o=o, s_final=s, workspace=ws)
         if gate:
             kda.out_gate(o, x["gate"], ki.EPS, y=y)
 
-    per = _time_calls(torch, call, calls)
+    def layer_call():
+        kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["gate"], ki.EPS, None, s0,
+                            y=y, s_final=s, workspace=lws)
+
+    per = _time_calls(torch, layer_call if gate else call, calls)
     esz = 2 if dt == torch.bfloat16 else 4
-    per_th = (3 * dk + 2 * dv) * esz + esz + (2 * dv * esz if gate else 0)   # q, k, z, v, o (+ gate, y); beta
+    per_th = (3 * dk + 2 * dv) * esz + esz + (dv * esz if gate else 0)   # q, k, z, v, o or y (+ gate); beta
     nbytes = B * T * H * per_th + B * H * dk * dv * 4 * (2 if s0 is not None else 1)
     out = {"workload": name, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
            "dtype": "bf16" if dt == torch.bfloat16 else "f32", "calls": calls,
            "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
-           "kernels": "kda_chunk_fwd" + (" + kda_out_gate" if gate else "")}
+           "kernels": "kda_chunk_layer_fwd (epilogue in the prefill kernels)" if gate else "kda_chunk_fwd"}
+    if gate:
+        out["us_per_call_two_calls"] = round(_time_calls(torch, call, calls) * 1e6, 1)
     if dk == 128 and dv == 128:
         gbs = nbytes / per / 1e9
         out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes,
                            "mfma_frac": round(B * T * H * PREFILL_FLOP_PER_TOKEN_HEAD / per / 1e12 /
                                               BF16_PEAK_TFLOPS, 4)}
-    del x, o, s, ws, y
+    del x, o, s, ws, y, lws
     torch.cuda.empty_cache()
     return out
+
+
+def bench_train_layer(torch, kda, ki, calls=5):
+    """The training-shape layer end to end (8 x 8192 tokens, H = 32, d = 128:
+    chunkwise prefill, RMSNorm x gate, projection 4096 -> 2304) as one
+    kda_chunk_layer_fwd call (raw outputs not kept), beside kda_chunk_fwd +
+    kda_out_gate."""
+    cfg = ki.WORKLOADS["train_8x8k"]
+    B, T, H, dk, dv, dm = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"], cfg["d_model"]
+    dev = torch.device("cuda:0")
+    x = ki.workload_inputs("train_8x8k", seed=2, device=dev)
+    s0 = x["s0"] if cfg["s0_var"] > 0 else None
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=dev)
+    s = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    lws = torch.empty(max(kda.chunk_layer_fwd_workspace_bytes(B, T, H, dk, dv, dm, torch.bfloat16, True), 16),
+                      dtype=torch.uint8, device=dev)
+    per = _time_calls(torch, lambda: kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN,
+                                                         x["gate"], ki.EPS, x["w"], s0, y=y, s_final=s,
+                                                         workspace=lws), calls)
+    del lws
+    o = torch.empty((B, T, H, dv), dtype=torch.bfloat16, device=dev)
+    cws = torch.empty(max(kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, torch.bfloat16), 16), dtype=torch.uint8,
+                      device=dev)
+    gws = torch.empty(kda.out_gate_workspace_bytes(B, T, H, dv, dm, torch.bfloat16, True), dtype=torch.uint8,
+                      device=dev)
+
+    def two():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, s0, o=o, s_final=s, workspace=cws)
+        kda.out_gate(o, x["gate"], ki.EPS, x["w"], y=y, workspace=gws)
+
+    per2 = _time_calls(torch, two, calls)
+    del x, y, s, o, cws, gws
+    torch.cuda.empty_cache()
+    return {"workload": "train_8x8k layer", "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "d_model": dm,
+            "dtype": "bf16", "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1),
+            "unit": "tokens/s", "us_per_call_two_calls": round(per2 * 1e6, 1),
+            "kernels": "kda_chunk_layer_fwd (epilogue in the prefill kernels, then the hipBLASLt projection)"}
 
 
 def bench_gdn_prefill(torch, kda, ki, calls=10):
@@ -478,7 +530,8 @@ def main():
         line["epilogue"] = bench_epilogue(torch, kda, ki)
     if not args.no_workloads:
         wl = [bench_workload(torch, kda, ki, "tiny_fp32", 0, 20),
-              bench_workload(torch, kda, ki, "train_8x8k", 2, 5)]
+              bench_workload(torch, kda, ki, "train_8x8k", 2, 5),
+              bench_train_layer(torch, kda, ki)]
         wl.append(bench_gdn_prefill(torch, kda, ki))
         if not args.no_long:
             wl.append(bench_workload(torch, kda, ki, "long_1m", 4, 2))

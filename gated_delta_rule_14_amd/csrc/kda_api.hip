@@ -223,3 +223,82 @@ kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v,
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace of kda_chunk_layer_fwd: the prefill's (256-byte aligned); then,
+// when the epilogue is not fused into the prefill kernels, room for o; then
+// the epilogue's (the gated rows in bf16 and the GEMM scratch, with a
+// projection only).
+struct LayerWs {
+    size_t chunk, obuf, gate, total;
+};
+LayerWs layer_ws(int B, int T, int H, int dk, int dv, int d_model, kda_dtype dt, bool proj) {
+    const bool bf = dt == KDA_BF16;
+    LayerWs r;
+    r.chunk = (kda::chunk_workspace_bytes(B, T, H, dk, dv, bf) + 255) / 256 * 256;
+    r.obuf = kda::chunk_gate_fused(B, T, H, dk, dv, bf) ? 0 : ((size_t)B * T * H * dv * (bf ? 2 : 4) + 255) / 256 * 256;
+    r.gate = kda::gate_workspace_bytes(B, T, H, dv, d_model, bf, proj);
+    r.total = r.chunk + r.obuf + r.gate;
+    return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_chunk_layer_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, int d_model,
+                                           kda_dtype dt, int with_projection) {
+    if (B < 0 || T < 0 || H < 0 || d_model < 0 || chunk != 64 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    return layer_ws(B, T, H, dk, dv, d_model, dt, with_projection != 0).total;
+}
+
+kda_status kda_chunk_layer_fwd(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                               float g_min, const float* s0, const void* gate, float eps, const void* w, void* o,
+                               void* y, float* s_final, int B, int T, int H, int dk, int dv, int chunk,
+                               int d_model, kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream) {
+    // the epilogue's own checks first, in the order kda_out_gate makes them
+    if (B < 0 || T < 0 || H < 0 || d_model < 0) return KDA_ERR_SHAPE;
+    if (!dim_ok(dv) || (dt != KDA_F32 && dt != KDA_BF16)) return KDA_ERR_UNSUPPORTED;
+    if (w && (dt != KDA_BF16 || d_model % 16 != 0 || d_model == 0)) return KDA_ERR_UNSUPPORTED;
+    if (w && (((long long)B * T + 127) / 128 > 65535 || (long long)H * dv > (1 << 20))) return KDA_ERR_SHAPE;
+    if (!(eps >= 0.f) || !isfinite(eps)) return KDA_ERR_ARG;
+    // then the prefill's, with y in the place of the required output
+    const kda_status st = check_chunk_args(q, k, v, z, beta, g_min, s0, y, s_final, B, T, H, dk, dv, chunk, dt,
+                                           workspace);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (T > 0 && !gate) return KDA_ERR_NULL;
+    if (!aligned16(gate) || !aligned16(w) || !aligned16(o)) return KDA_ERR_ALIGN;
+    const LayerWs ws = layer_ws(B, T, H, dk, dv, d_model, dt, w != nullptr);
+    if (ws.total > 0 && (!workspace || workspace_bytes < ws.total)) return KDA_ERR_WORKSPACE;
+    unsigned char* wsb = (unsigned char*)workspace;
+    void* chunk_ws = ws.chunk ? wsb : nullptr;
+    void* gate_ws = ws.gate ? wsb + ws.chunk + ws.obuf : nullptr;
+    const bool bf = dt == KDA_BF16;
+    kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, bf, chunk_ws, stream};
+    hipError_t err;
+    if (T > 0 && kda::chunk_gate_fused(B, T, H, dk, dv, bf)) {
+        // y, or with a projection its bf16 input rows, from the prefill kernels
+        a.gate = gate;
+        a.eps = eps;
+        a.y = w ? gate_ws : y;
+        err = kda::launch_chunk(a);
+        if (err == hipSuccess && w) {
+            const size_t ybytes = ws.gate - kda::projection_scratch_bytes();
+            err = kda::launch_projection(gate_ws, w, y, B * T, d_model, H * dv, (unsigned char*)gate_ws + ybytes,
+                                         stream);
+        }
+        return finish(err, stream);
+    }
+    // other sizes: the prefill into o (or the workspace), then the epilogue
+    if (!a.o) a.o = wsb + ws.chunk;
+    err = kda::launch_chunk(a);
+    if (err == hipSuccess && T > 0) {
+        kda::GateArgs g{a.o, gate, eps, w, y, B, T, H, dv, d_model, bf, gate_ws, stream};
+        err = kda::launch_out_gate(g);
+    }
+    return finish(err, stream);
+}
+
+}  // extern "C"

@@ -39,8 +39,17 @@ struct ChunkArgs {
     bool bf16;
     void* workspace;
     void* stream;
+    // fused output epilogue (gate != NULL; only where chunk_gate_fused()):
+    // y = RMSNorm(o) * sigmoid(gate), laid out like o; o may then be NULL
+    const void* gate = nullptr;
+    float eps = 0.f;
+    void* y = nullptr;
 };
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
+// whether the prefill kernels for these sizes run the output epilogue in
+// their own launches (bf16 tokens, d_k = d_v = 128, the pipelined kernels on
+// a segmented plan, whose light expand has LDS to stage the outputs)
+bool chunk_gate_fused(int B, int T, int H, int dk, int dv, bool bf16);
 hipError_t launch_chunk(const ChunkArgs& a);
 // bf16 tokens: fused segment kernels (seg.hip); fp32 tokens: per-chunk
 // workspace kernels (chunk.hip).  Both use the segment scan of chunk.hip.

@@ -774,6 +774,9 @@ struct PLay {
     static constexpr size_t OFF_MLOC = OFF_TOT + 4 * (size_t)DK * 4;       // [4][DK] G_m(R) - G_{16R-1}
     static constexpr size_t OFF_BET = OFF_MLOC + 4 * (size_t)DK * 4;
     static constexpr size_t LDS = OFF_BET + C * 4;
+    // EXPAND_LITE forms no A, so the KL tile is free: with the output
+    // epilogue fused it holds the chunk's outputs O [C][LDK] in bf16
+    static constexpr size_t OFF_OT = OFF_KL;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -792,9 +795,12 @@ __device__ __forceinline__ f32x4* tp_lds(unsigned char* smem, int p) {
 // Recurrence step of the pipelined kernel, first part: V_new = T' Z with
 // Z = V - (K e^G) S, left in yb as bf16 B fragments, and for EXPAND the
 // outputs O = (Q e^G) S + M V_new.  Same register layouts as chain_step.
-template <int MODE, int NTW, class L>
+// GATED (EXPAND_LITE with the output epilogue fused): the outputs, rounded
+// to bf16, go to the staging tile for the epilogue, and to o only when orow0
+// is not NULL.
+template <int MODE, int NTW, class L, bool GATED = false>
 __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[2][NTW], bool hasu, int ucol0,
-                                        const unsigned char* smem, bf16* __restrict__ orow0, int valid,
+                                        unsigned char* smem, bf16* __restrict__ orow0, int valid,
                                         size_t ostride) {
     typedef Mfma<bf16> MF;
     constexpr bool EXP = L::EXP;
@@ -894,11 +900,79 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
                 ov[ot][ct] = MF::mma(yb[0][ct], mf[ot][0], ov[ot][ct]);
                 ov[ot][ct] = MF::mma(yb[1][ct], mf[ot][1], ov[ot][ct]);
             }
-            if (ot * 16 + c < valid) {
+            if constexpr (GATED) {
+                bf16x4 ob[NTW];
+#pragma unroll
+                for (int ct = 0; ct < NTW; ++ct) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) ob[ct][e] = (bf16)ov[ot][ct][e];
+                    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(smem + L::OFF_OT) +
+                                               (ot * 16 + c) * L::LDK + ucol0 + ct * 16 + 4 * g) = ob[ct];
+                }
+                if (orow0 && ot * 16 + c < valid) {
+                    int lg = l;
+                    asm volatile("" : "+v"(lg));
+                    char* orow = reinterpret_cast<char*>(orow0) +
+                                 (unsigned)(ot * 16 + (lg & 15)) * ((unsigned)ostride * 2u) + 8u * (unsigned)(lg >> 4);
+#pragma unroll
+                    for (int ct = 0; ct < NTW; ++ct) *reinterpret_cast<bf16x4*>(orow + ct * 32) = ob[ct];
+                }
+            } else if (ot * 16 + c < valid) {
                 bf16* orow = orow0 + (size_t)(ot * 16 + c) * ostride + 4 * g;
 #pragma unroll
                 for (int ct = 0; ct < NTW; ++ct) store4<bf16>(orow + ct * 16, ov[ot][ct]);
             }
+        }
+    }
+}
+
+// Fused output epilogue: y = o / sqrt(mean(o^2) + eps) * sigmoid(gate) over
+// the 128 values of each (token, head) row of the chunk, for NP passes of four
+// rows from row r0 (lane: row r0 + 4p + l/16, values 8 (l%16) .. +7), from the
+// bf16 outputs in the staging tile.  The gate logits come from gate_fetch.
+// Addresses: a wave-uniform chunk base plus 32-bit byte offsets, derived
+// from the lane inside the loop (not hoisted into registers held across it).
+template <int NP>
+__device__ __forceinline__ void gate_fetch(bf16x8 (&gk)[6], const bf16* __restrict__ grow0, int r0, int valid,
+                                           size_t ostride) {
+    int l = lane_id();
+    asm volatile("" : "+v"(l));
+    const char* gb = reinterpret_cast<const char*>(grow0);
+    const unsigned rs = (unsigned)ostride * 2u, lo = 16u * (unsigned)(l & 15);
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        gk[p] = *reinterpret_cast<const bf16x8*>(gb + (unsigned)min(r0 + 4 * p + (l >> 4), valid - 1) * rs + lo);
+}
+template <int NP, class L>
+__device__ __forceinline__ void gate_epilogue(const bf16x8 (&gk)[6], const unsigned char* smem, float eps,
+                                              bf16* __restrict__ yrow0, int r0, int valid, size_t ostride) {
+    int l = lane_id();
+    asm volatile("" : "+v"(l));
+    const bf16* OT = reinterpret_cast<const bf16*>(smem + L::OFF_OT);
+    char* yb = reinterpret_cast<char*>(yrow0);
+    const unsigned rs = (unsigned)ostride * 2u;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int r = r0 + 4 * p + (l >> 4);
+        const bf16x8 ob = *reinterpret_cast<const bf16x8*>(OT + r * L::LDK + 8 * (l & 15));
+        float x[8], ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            x[j] = (float)ob[j];
+            ss += x[j] * x[j];
+        }
+        // sum over the row's 16 lanes (one DPP row): xor 1, xor 2, then the
+        // half-row and row mirrors
+        ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0xB1, 0xF, 0xF, false));
+        ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x4E, 0xF, 0xF, false));
+        ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x141, 0xF, 0xF, false));
+        ss += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, ss), 0x140, 0xF, 0xF, false));
+        const float inv = __builtin_amdgcn_rsqf(ss * (1.0f / 128) + eps);
+        if (r < valid) {
+            bf16x8 out;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) out[j] = (bf16)(x[j] * inv * sigmoidf_((float)gk[p][j]));
+            *reinterpret_cast<bf16x8*>(yb + (unsigned)r * rs + 16u * (unsigned)(l & 15)) = out;
         }
     }
 }
@@ -1339,14 +1413,20 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
 
 // Same grid and arguments as seg_kernel, plus tm: the per-chunk T'
 // ([chain][chunk] x TM_ELEMS bf16) that COMPOSE writes and EXPAND_LITE reads
-// (unused by EXPAND, which forms it itself).
-template <int MODE>
+// (unused by EXPAND, which forms it itself).  GATED (EXPAND_LITE): the
+// output epilogue y = RMSNorm(o) * sigmoid(gate) is fused, with gate and y
+// laid out like o; o is written only when not NULL.  Chunk m's outputs are
+// staged in LDS in S1 and its epilogue runs in S2, on the state waves (rows
+// 0-15 on waves 0-1, whose M pairs are the longer, rows 16-63 on waves 2-3).
+template <int MODE, bool GATED = false>
 __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const bf16* __restrict__ z,
                                                    const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
                                                    int L, int nchain, const float* __restrict__ xin,
                                                    float* __restrict__ xo0, float* __restrict__ xo1,
-                                                   bf16* __restrict__ o, bf16* __restrict__ tm) {
+                                                   bf16* __restrict__ o, bf16* __restrict__ tm,
+                                                   const bf16* __restrict__ gate, float eps, bf16* __restrict__ y) {
+    static_assert(!GATED || MODE == EXPAND_LITE, "the epilogue is fused into the light expand only");
     typedef PLay<MODE> LY;
     constexpr int DK = 128, DV = 128;
     constexpr bool EXP = LY::EXP, LITE = LY::LITE;
@@ -1401,6 +1481,23 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         PV pv;
         if constexpr (VSTATE) pfetch_v(pv, v, row_of(n0), min(C, T - n0 * C), H, w);
         bf16x8 yb[NH][2][2];
+        // GATED: chunk n's gate logits for this wave's rows, then its y
+        bf16x8 gk[6];
+        const int er0 = w < 2 ? 8 * w : 16 + 24 * (w - 2);
+        auto fetch_gate = [&](int n) __attribute__((always_inline)) {
+            const bf16* g0 = gate + row_of(n) * DV;
+            if (w < 2)
+                gate_fetch<2>(gk, g0, er0, min(C, T - n * C), ostride);
+            else
+                gate_fetch<6>(gk, g0, er0, min(C, T - n * C), ostride);
+        };
+        auto epilogue = [&](int n) __attribute__((always_inline)) {
+            bf16* y0 = y + row_of(n) * DV;
+            if (w < 2)
+                gate_epilogue<2, LY>(gk, smem, eps, y0, er0, min(C, T - n * C), ostride);
+            else
+                gate_epilogue<6, LY>(gk, smem, eps, y0, er0, min(C, T - n * C), ostride);
+        };
         // state update of chunk n from V_new in yb (COMPOSE defers it to S3)
         auto update = [&](int n) __attribute__((always_inline)) {
             const int bufn = LY::NKB == 2 ? (n & 1) : 0;
@@ -1424,7 +1521,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
                 const int col0 = cbase + 32 * hh;
-                chain_a<MODE, 2, LY>(xs[hh], yb[hh], hasu, col0, smem, o + row_of(m) * DV + col0, valid, ostride);
+                chain_a<MODE, 2, LY, GATED>(xs[hh], yb[hh], hasu, col0, smem, o ? o + row_of(m) * DV + col0 : nullptr,
+                                            valid, ostride);
                 __builtin_amdgcn_sched_barrier(0);   // one half's working set at a time
             }
         };
@@ -1432,6 +1530,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         // (COMPOSE: the previous chunk's state update in S3, while the gate
         // waves solve for T')
         auto rest = [&](int n, bool upd) __attribute__((always_inline)) {
+            if constexpr (GATED)
+                if (upd) fetch_gate(n - 1);
             if constexpr (VSTATE) {
                 pipe_vt<MODE>(pv, w, smem);
                 const int mn = min(n + 1, n1 - 1);
@@ -1441,6 +1541,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 2>(w, smem);
             else
                 pipe_pairs<MODE, 1>(w, smem);
+            if constexpr (GATED)
+                if (upd) epilogue(n - 1);
             if constexpr (!LITE) {
                 __syncthreads();   // S2 | S3
                 if constexpr (!EXP) {
@@ -1463,7 +1565,12 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             rest(m, true);
         }
         chain(n1 - 1);
+        if constexpr (GATED) fetch_gate(n1 - 1);
         update(n1 - 1);
+        if constexpr (GATED) {
+            __syncthreads();   // every wave's sums of squares of the last chunk
+            epilogue(n1 - 1);
+        }
         float* xo = EXP ? xo0 : (ptile ? xo0 : xo1);
         if (xo) {
             const size_t ob = EXP ? bh * DK : xblk;
@@ -1532,6 +1639,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             gate_sums<true>(in, S);
             __syncthreads();   // S2 (S3 for EXPAND) | next S1
         }
+        if constexpr (GATED) __syncthreads();   // the state waves' last epilogue
     } else {
         // ---------------- gate waves, COMPOSE: block R of each chunk
         const int R = w - 4;
@@ -1755,18 +1863,22 @@ static hipError_t launch_scan(const ChunkArgs& a, const Plan& p, float* Pb, floa
 
 // d_k = d_v = 128: compose (writing every chunk's T'), scan, and the light
 // expand; one full expand pass when one segment per chain suffices.
-static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
+template <bool GATED>
+static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
     const bf16 *q = (const bf16*)a.q, *k = (const bf16*)a.k, *v = (const bf16*)a.v, *z = (const bf16*)a.z,
-               *beta = (const bf16*)a.beta;
+               *beta = (const bf16*)a.beta, *gate = (const bf16*)a.gate;
+    bf16* y = (bf16*)a.y;
     hipError_t err;
     if (p.nseg == 1) {
+        // the epilogue is fused into the light expand only (segmented plans)
+        if (GATED) return hipErrorInvalidValue;
         if ((err = set_lds(pipe_kernel<EXPAND>, PLay<EXPAND>::LDS)) != hipSuccess) return err;
-        hipLaunchKernelGGL(pipe_kernel<EXPAND>, dim3(nchain), dim3(NTH), PLay<EXPAND>::LDS, st, q, k, v, z, beta,
+        hipLaunchKernelGGL((pipe_kernel<EXPAND>), dim3(nchain), dim3(NTH), PLay<EXPAND>::LDS, st, q, k, v, z, beta,
                            a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o,
-                           (bf16*)nullptr);
+                           (bf16*)nullptr, (const bf16*)nullptr, 0.f, (bf16*)nullptr);
         return hipGetLastError();
     }
     unsigned char* ws = (unsigned char*)a.workspace;
@@ -1776,14 +1888,18 @@ static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
     bf16* TM = reinterpret_cast<bf16*>(ws + p.tm_off);
     if ((err = set_lds(pipe_kernel<COMPOSE>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
     hipLaunchKernelGGL(pipe_kernel<COMPOSE>, dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
-                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr, TM);
+                       beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr, TM,
+                       (const bf16*)nullptr, 0.f, (bf16*)nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_scan<128, 128>(a, p, Pb, Rb, Eb)) != hipSuccess) return err;
-    if ((err = set_lds(pipe_kernel<EXPAND_LITE>, PLay<EXPAND_LITE>::LDS)) != hipSuccess) return err;
-    hipLaunchKernelGGL(pipe_kernel<EXPAND_LITE>, dim3(p.nseg * nchain), dim3(NTH), PLay<EXPAND_LITE>::LDS, st, q, k,
-                       v, z, beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr,
-                       (float*)nullptr, (bf16*)a.o, TM);
+    if ((err = set_lds(pipe_kernel<EXPAND_LITE, GATED>, PLay<EXPAND_LITE>::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((pipe_kernel<EXPAND_LITE, GATED>), dim3(p.nseg * nchain), dim3(NTH), PLay<EXPAND_LITE>::LDS,
+                       st, q, k, v, z, beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr,
+                       (float*)nullptr, (bf16*)a.o, TM, gate, a.eps, y);
     return hipGetLastError();
+}
+static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
+    return a.gate ? launch_pipe_t<true>(a, p) : launch_pipe_t<false>(a, p);
 }
 
 template <int DK, int DV>
@@ -1823,6 +1939,10 @@ static hipError_t launch_t(const ChunkArgs& a) {
 }  // namespace segk
 
 size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) { return segk::plan(B, T, H, dk, dv).total; }
+
+bool chunk_gate_fused(int B, int T, int H, int dk, int dv, bool bf16) {
+    return bf16 && dk == 128 && dv == 128 && segk::use_pipe() && segk::plan(B, T, H, dk, dv).nseg > 1;
+}
 
 hipError_t launch_chunk_seg(const ChunkArgs& a) {
     if (a.dk == 128 && a.dv == 128) return segk::launch_t<128, 128>(a);

@@ -12,7 +12,10 @@ Names follow the C ABI in include/kda.h:
   recurrent_layer_step -> kda_recurrent_layer_step: one decode token of the
                      whole layer (step + RMSNorm x gate in one launch,
                      then the projection)
-  layer           -> kda_chunk_fwd + kda_out_gate, returning the
+  chunk_layer_fwd -> kda_chunk_layer_fwd: the prefill of the whole layer
+                     (chunkwise recurrence with RMSNorm x gate in its
+                     kernels, then the projection)
+  layer           -> kda_chunk_layer_fwd, returning the
                      {"outputs", "final_state"} dictionary of the
                      "KDA Recurrence" problem (final_state kept in fp32)
 """
@@ -232,6 +235,56 @@ def recurrent_layer_step(q, k, v, z, beta, g_min, state, gate, eps, w=None, *, y
     return (y, o) if want_o else y
 
 
+def chunk_layer_fwd_workspace_bytes(B, T, H, dk, dv, d_model, dtype, with_projection):
+    return int(lib().kda_chunk_layer_fwd_workspace_bytes(
+        B, T, H, dk, dv, CHUNK, d_model, KDA_BF16 if dtype == torch.bfloat16 else KDA_F32,
+        int(bool(with_projection))))
+
+
+def chunk_layer_fwd(q, k, v, z, beta, g_min, gate, eps, w=None, s0=None, *, y=None, o=None,
+                    want_o=False, s_final=None, want_state=True, workspace=None):
+    """Prefill of the layer. q, k, z: (B,T,H,dk); v, gate: (B,T,H,dv);
+    beta: (B,T,H); s0: (B,H,dk,dv) fp32 or None; w: (d_model, H*dv) bf16 or
+    None.  Returns (y, s_final): y is (B,T,d_model) with w, else (B,T,H*dv);
+    s_final is fp32, or None when want_state is False.  With want_o, returns
+    (y, s_final, o) with o the raw outputs (B,T,H,dv)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("gate", gate)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    d_model = 0
+    if w is not None:
+        _need(w, "w", dev)
+        d_model = w.shape[0]
+        if w.dtype != torch.bfloat16:
+            raise TypeError("libkda: projection w must be bfloat16")
+    if y is None:
+        y = torch.empty((B, T, d_model if w is not None else H * dv), dtype=q.dtype, device=dev)
+    if want_o and o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    need = lib().kda_chunk_layer_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK, d_model, _dt(q),
+                                                     int(w is not None))
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("kda_chunk_layer_fwd", lib().kda_chunk_layer_fwd(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(gate), float(eps), _p(w),
+        _p(o), _p(y), _p(s_final), B, T, H, dk, dv, CHUNK, d_model, _dt(q), _p(workspace), ws_bytes,
+        _stream(dev)))
+    return (y, s_final, o) if want_o else (y, s_final)
+
+
 def layer(query, key, value, decay_logits, write_strength, output_gate_logits,
           output_projection, initial_state, g_min, eps):
     """The KDA layer of the "KDA Recurrence" problem: recurrence (chunkwise),
@@ -240,6 +293,6 @@ def layer(query, key, value, decay_logits, write_strength, output_gate_logits,
     s0 = initial_state
     if s0 is not None and s0.dtype != torch.float32:
         s0 = s0.float().contiguous()
-    o, s = chunk_fwd(query, key, value, decay_logits, write_strength, g_min, s0)
-    out = out_gate(o, output_gate_logits, eps, output_projection)
+    out, s = chunk_layer_fwd(query, key, value, decay_logits, write_strength, g_min, output_gate_logits,
+                             eps, output_projection, s0)
     return {"outputs": out, "final_state": s}

@@ -10,9 +10,10 @@
  *     alpha_t = exp(g_min * sigmoid(z_t)),  g_min < 0   ("KDA Recurrence")
  *
  * with one d_k x d_v state per (batch, head).  Three calls cover the path:
- * chunkwise prefill, one decode token, and the output epilogue; a fourth
- * runs one decode token of the whole layer (step and epilogue together),
- * and two more take the scalar-gate (Gated DeltaNet) special case.
+ * chunkwise prefill, one decode token, and the output epilogue; two more
+ * run the whole layer (recurrence and epilogue together), one for a prefill
+ * and one for a decode token, and two take the scalar-gate (Gated DeltaNet)
+ * special case.
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
@@ -187,6 +188,38 @@ kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v,
                                     float eps, const void* w, void* o, void* y, int B, int H, int dk,
                                     int dv, int d_model, kda_dtype dt, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * The prefill of the whole layer of the "KDA Recurrence" problem:
+ * kda_chunk_fwd, then the output epilogue of kda_out_gate (RMS normalisation
+ * over each (token, head)'s d_v values with eps inside the square root,
+ * times sigmoid(gate), heads concatenated, then y W^T when w is given).
+ *
+ *   q, k, z, v, beta, g_min, s0, s_final   as for kda_chunk_fwd
+ *   gate      (B, T, H, dv)   dtype dt    output-gate logits
+ *   eps, w, d_model                        as for kda_out_gate
+ *   o         (B, T, H, dv)   dtype dt    the raw outputs (written), or NULL
+ *                                          to skip them
+ *   y         (B, T, H*dv) dtype dt when w is NULL, (B, T, d_model) dtype dt
+ *             otherwise (written)
+ *   workspace kda_chunk_layer_fwd_workspace_bytes() bytes: that of
+ *             kda_chunk_fwd (256-byte aligned), then room for o where the
+ *             epilogue is a launch of its own, then that of kda_out_gate
+ * With bf16 tokens, d_k = d_v = 128 and a sequence split into segments
+ * (fewer than 256 (batch, head) chains and at least 16 chunks), the
+ * normalisation and gate run inside the prefill's last kernel, on the
+ * outputs rounded to bf16 (the values kda_out_gate would read back), so o
+ * need not be written; the projection, when asked for, is a launch of its
+ * own.  Other sizes run kda_chunk_fwd's kernels and then kda_out_gate's.
+ * Every other rule is that of kda_chunk_fwd and kda_out_gate.
+ */
+size_t kda_chunk_layer_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                           int d_model, kda_dtype dt, int with_projection);
+kda_status kda_chunk_layer_fwd(const void* q, const void* k, const void* v, const void* z,
+                               const void* beta, float g_min, const float* s0, const void* gate,
+                               float eps, const void* w, void* o, void* y, float* s_final, int B,
+                               int T, int H, int dk, int dv, int chunk, int d_model, kda_dtype dt,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The Gated DeltaNet special case: one decay logit per (token, head), so

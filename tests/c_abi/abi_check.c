@@ -62,6 +62,13 @@ int main(void) {
                             (size_t)1 << 30, NULL) == KDA_ERR_NULL);
     CHECK(kda_gdn_recurrent_step(P, P, P, MIS, P, -5.f, PF, P, 4, 2, 128, 128, KDA_BF16, NULL) == KDA_ERR_ALIGN);
 
+    CHECK(kda_chunk_layer_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, 2304, KDA_BF16, 1) ==
+          (size_t)2 * 8 * 8192 * 4096 * 2 + ((size_t)32 << 20));
+    CHECK(kda_chunk_layer_fwd(P, P, P, P, P, -5.f, NULL, NULL, 1e-6f, NULL, NULL, P, NULL, 1, 128, 2, 128, 128,
+                              64, 0, KDA_BF16, P, (size_t)1 << 30, NULL) == KDA_ERR_NULL);
+    CHECK(kda_chunk_layer_fwd(P, P, P, P, P, -5.f, NULL, P, 1e-6f, P, NULL, P, NULL, 1, 128, 2, 128, 128, 64,
+                              64, KDA_BF16, NULL, 0, NULL) == KDA_ERR_WORKSPACE);
+
     if (failures) {
         fprintf(stderr, "%d checks failed\n", failures);
         return 1;

@@ -218,6 +218,53 @@ def test_scalar_gate_calls_workspace_and_bad_arguments(lib):
     assert d(B=0) == OK
 
 
+def test_chunk_layer_fwd_workspace_and_bad_arguments(lib):
+    # bf16, d_k = d_v = 128 and a segmented plan (32 chains of 512 chunks)
+    # fuse the epilogue into the prefill kernels: the prefill's workspace,
+    # then (with a projection) the gated rows in bf16 and the GEMM's 32 MiB
+    kda_ws = lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16)
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 0, BF16, 0) == \
+        (kda_ws + 255) // 256 * 256
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 2304, BF16, 1) == \
+        (kda_ws + 255) // 256 * 256 + 32768 * 4096 * 2 + (32 << 20)
+    # one pass (256 chains) and other sizes run the two calls' kernels, with
+    # room for o in between
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, 0, BF16, 0) == 8 * 8192 * 4096 * 2
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, 2304, BF16, 1) == \
+        2 * 8 * 8192 * 4096 * 2 + (32 << 20)
+    f32_ws = lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32)
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, 0, F32, 0) == \
+        (f32_ws + 255) // 256 * 256 + 256 * 64 * 4
+    assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, 0, F32, 0) == 0
+
+    def c(q=P, z=P, g_min=-5.0, s0=None, g=P, eps=1e-6, w=None, o=None, y=P, sf=None, B=1, T=128, H=2, dk=128,
+          dv=128, chunk=64, dm=0, dt=BF16, ws=P, wsb=1 << 30):
+        return lib.kda_chunk_layer_fwd(q, P, P, z, P, g_min, s0, g, eps, w, o, y, sf, B, T, H, dk, dv, chunk, dm,
+                                       dt, ws, wsb, S)
+
+    assert c(g=None) == NULL
+    assert c(y=None) == NULL
+    assert c(q=None) == NULL
+    assert c(dk=96) == UNSUP
+    assert c(dv=96) == UNSUP
+    assert c(chunk=32) == UNSUP
+    assert c(dt=2) == UNSUP
+    assert c(w=P, dm=100) == UNSUP                 # d_model % 16
+    assert c(w=P, dm=64, dt=F32) == UNSUP          # projection needs bf16
+    assert c(B=-1) == SHAPE
+    assert c(g_min=0.0) == ARG
+    assert c(eps=-1.0) == ARG
+    assert c(eps=float("nan")) == ARG
+    assert c(g=MIS) == ALIGN
+    assert c(o=MIS) == ALIGN
+    assert c(y=MIS) == ALIGN
+    assert c(w=P, dm=64, ws=None, wsb=0) == WS
+    assert c(w=P, dm=64, wsb=1024) == WS
+    assert c(T=4096, ws=None, wsb=0) == WS         # 2 chains: segmented, needs the scan's workspace
+    assert c(H=0) == OK
+    assert c(T=0, g=None, ws=None, wsb=0) == OK    # nothing to compute, no state asked for
+
+
 def test_plain_c_caller(tmp_path):
     """The header compiles as C (gcc, -std=c11 -Wall -Werror) and a C program
     linked against libkda.so gets the documented host-side behaviour."""

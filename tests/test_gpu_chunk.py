@@ -205,15 +205,16 @@ def test_train_8x8k_full_size_sampled():
 
 
 def test_long_1m_full_size_sampled():
-    """B=1, T=1,048,576, H=32, d=128, bf16, z ~ N(2,1), S0 = 0, then the
-    RMSNorm x gate epilogue: the long-context workload at full size (16,384
-    chunks per head in 8 segments, all heads launched); the oracle runs one sampled
-    head over all tokens, and the epilogue on sampled rows."""
+    """B=1, T=1,048,576, H=32, d=128, bf16, z ~ N(2,1), S0 = 0, with the
+    RMSNorm x gate epilogue in the prefill kernels (kda_chunk_layer_fwd, raw
+    outputs kept): the long-context workload at full size (16,384 chunks per
+    head in 8 segments, all heads launched); the oracle runs one sampled head
+    over all tokens, and the epilogue on sampled rows."""
     import oracle
     from helpers import host
     x = ki.workload_inputs("long_1m", seed=4, device=DEV)
-    o, s = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
-    y = kda.out_gate(o, x["gate"], ki.EPS)
+    y, s, o = kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["gate"], ki.EPS, None,
+                                  x["s0"], want_o=True)
     torch.cuda.synchronize()
     h = 13
     hsel = [h]

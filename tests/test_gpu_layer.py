@@ -1,0 +1,139 @@
+"""GPU parity of kda_chunk_layer_fwd, the prefill of the whole layer
+(chunkwise recurrence, RMSNorm x sigmoid gate, optional projection).
+
+With bf16 tokens, d = 128 and a segmented plan the epilogue runs inside the
+light expand kernel: its raw outputs and final state must equal
+kda_chunk_fwd's bit for bit, its y must agree with kda_out_gate applied to
+those outputs up to rounding (sum of squares order, reciprocal square root),
+and y must match the fp64 oracle (recurrence, then the epilogue) within the
+bf16 bars.  Other sizes run the two calls' kernels.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import oracle
+from gated_delta_rule_14_amd import kda
+from helpers import f64, host, oracle_prefill, rel
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def inputs(B, T, H, d, dtype, seed, d_model=None):
+    return ki.prefill_inputs(B, T, H, d, d, dtype, seed=seed, device=DEV, s0_var=0.01, gate=True,
+                             d_model=d_model)
+
+
+def two_calls(x, w=None):
+    o, s = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
+    y = kda.out_gate(o, x["gate"], ki.EPS, w)
+    return y, s, o
+
+
+def fused(x, w=None, want_o=True):
+    return kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["gate"], ki.EPS, w,
+                               x["s0"], want_o=want_o)
+
+
+def oracle_layer_y(x, w=None, heads=None):
+    """Oracle outputs (recurrence, then the epilogue) on host copies; with
+    heads, the epilogue of those heads only (no projection)."""
+    ro, rs = oracle_prefill(x, heads=heads)
+    g = host(x["gate"])
+    if heads is not None:
+        g = np.ascontiguousarray(g[:, :, heads])
+    ry = oracle.out_gate(ro, g, ki.EPS, None if w is None else host(w))
+    return ry, rs
+
+
+# B, T, H: segmented (epilogue fused) with a ragged last chunk; one pass (two
+# kernels) with a ragged last chunk; 8 segments (fused); one chunk; one token
+SHAPES = [(1, 1000, 3), (2, 200, 2), (1, 4096, 2), (1, 64, 1), (1, 1, 1)]
+
+
+@pytest.mark.parametrize("B,T,H", SHAPES)
+def test_fused_layer_against_two_calls_and_oracle(B, T, H):
+    x = inputs(B, T, H, 128, torch.bfloat16, seed=10 * B + T % 97 + H)
+    y, s, o = fused(x)
+    y2, s2, o2 = two_calls(x)
+    torch.cuda.synchronize()
+    assert y.shape == (B, T, H * 128) and y.dtype == torch.bfloat16
+    assert torch.equal(o, o2), "raw outputs differ from kda_chunk_fwd"
+    assert torch.equal(s, s2), "final state differs from kda_chunk_fwd"
+    e_calls = rel(f64(y), f64(y2))
+    ry, rs = oracle_layer_y(x)
+    ey, es = rel(f64(y), ry), rel(f64(s), rs)
+    print(f"layer B={B} T={T} H={H}: y vs two calls {e_calls:.2e}, vs oracle {ey:.2e}, state {es:.2e}")
+    assert e_calls < 2e-3 and ey < 2e-2 and es < 1e-2
+
+
+@pytest.mark.parametrize("B,T,H,d_model", [(1, 1000, 3, 48), (2, 200, 2, 272)])
+def test_fused_layer_with_projection(B, T, H, d_model):
+    x = inputs(B, T, H, 128, torch.bfloat16, seed=7 + T, d_model=d_model)
+    y, s, o = fused(x, x["w"])
+    y2, _, _ = two_calls(x, x["w"])
+    torch.cuda.synchronize()
+    assert y.shape == (B, T, d_model)
+    e_calls = rel(f64(y), f64(y2))
+    ry, rs = oracle_layer_y(x, x["w"])
+    ey, es = rel(f64(y), ry), rel(f64(s), rs)
+    print(f"layer + projection B={B} T={T} H={H} d_model={d_model}: vs two calls {e_calls:.2e}, "
+          f"vs oracle {ey:.2e}, state {es:.2e}")
+    assert e_calls < 2e-3 and ey < 2e-2 and es < 1e-2
+
+
+@pytest.mark.parametrize("T", [200, 1000])
+def test_fused_layer_without_raw_outputs(T):
+    """o = NULL skips the raw outputs only: y and the state are unchanged."""
+    x = inputs(1, T, 3, 128, torch.bfloat16, seed=T)
+    y, s, _ = fused(x)
+    yn, sn = fused(x, want_o=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yn) and torch.equal(s, sn)
+
+
+@pytest.mark.parametrize("dtype,d,tol", [(torch.float32, 64, 1e-5), (torch.bfloat16, 64, 2e-2),
+                                         (torch.float32, 128, 1e-5)])
+def test_layer_other_sizes_run_both_calls(dtype, d, tol):
+    """fp32 tokens or d = 64: the prefill, then the epilogue kernel; y equals
+    the two calls' bit for bit and matches the oracle."""
+    x = inputs(1, 300, 2, d, dtype, seed=d + (dtype == torch.float32))
+    y, s, o = fused(x)
+    y2, s2, o2 = two_calls(x)
+    yn, _ = fused(x, want_o=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(s, s2) and torch.equal(o, o2) and torch.equal(y, yn)
+    ry, rs = oracle_layer_y(x)
+    ey, es = rel(f64(y), ry), rel(f64(s), rs)
+    print(f"layer {dtype} d={d}: y {ey:.2e} state {es:.2e}")
+    assert ey < tol and es < tol
+
+
+def test_layer_empty_sequence():
+    """T = 0: y is empty and the state passes through."""
+    x = inputs(2, 0, 2, 128, torch.bfloat16, seed=3)
+    y, s = fused(x, want_o=False)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 256)
+    assert torch.equal(s, x["s0"])
+
+
+def test_prefill_32k_layer_sampled():
+    """The 32k prefill workload with the gate epilogue at full size: y against
+    the two calls over all heads, and against the oracle on two sampled heads."""
+    x = ki.workload_inputs("prefill_32k", seed=11, device=DEV)
+    x["gate"] = ki.gate_logits(x["v"].shape[:3], 128, torch.bfloat16, seed=11, device=DEV)
+    y, s = fused(x, want_o=False)
+    y2, s2, _ = two_calls(x)
+    torch.cuda.synchronize()
+    assert torch.equal(s, s2)
+    e_calls = rel(f64(y), f64(y2))
+    heads = [4, 29]
+    ry, rs = oracle_layer_y(x, heads=heads)
+    B, T, H, dv = x["v"].shape
+    yh = f64(y).reshape(B, T, H, dv)[:, :, heads].reshape(B, T, len(heads) * dv)
+    ey, es = rel(yh, ry), rel(f64(s)[:, heads], rs)
+    print(f"prefill_32k layer: y vs two calls {e_calls:.2e}, heads {heads} vs oracle {ey:.2e}, state {es:.2e}")
+    assert e_calls < 2e-3 and ey < 2e-2 and es < 1e-2
