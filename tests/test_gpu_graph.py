@@ -93,3 +93,41 @@ def test_chunk_fwd_graph_replays():
         ro, rs = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
         torch.cuda.synchronize()
         assert torch.equal(got_o, ro) and torch.equal(got_s, rs), f"replay with inputs {i}"
+
+
+def test_chunk_layer_fwd_graph_replays():
+    """The prefill of the layer with the epilogue fused (segmented plan) and
+    the projection, captured once: replays with new inputs copied into the
+    static slots match eager calls."""
+    B, T, H, d, dm = 1, 4096, 4, 128, 192
+    xs = [ki.prefill_inputs(B, T, H, d, d, torch.bfloat16, 70 + i, DEV, s0_var=0.01, gate=True) for i in range(3)]
+    w = ki.projection(dm, H * d, 70, DEV)
+    slot = {n: torch.empty_like(t) for n, t in xs[0].items()}
+    y = torch.empty((B, T, dm), dtype=torch.bfloat16, device=DEV)
+    s = torch.empty((B, H, d, d), dtype=torch.float32, device=DEV)
+    ws = torch.empty(kda.chunk_layer_fwd_workspace_bytes(B, T, H, d, d, dm, torch.bfloat16, True),
+                     dtype=torch.uint8, device=DEV)
+
+    def call():
+        kda.chunk_layer_fwd(slot["q"], slot["k"], slot["v"], slot["z"], slot["beta"], ki.G_MIN, slot["gate"],
+                            ki.EPS, w, slot["s0"], y=y, s_final=s, workspace=ws)
+
+    for n in slot:
+        slot[n].copy_(xs[0][n])
+    call()     # eager: creates the GEMM plan outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in (1, 2, 0):
+        for n in slot:
+            slot[n].copy_(xs[i][n])
+        g.replay()
+        torch.cuda.synchronize()
+        got_y, got_s = y.clone(), s.clone()
+        x = xs[i]
+        ry, rs = kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["gate"], ki.EPS, w,
+                                     x["s0"])
+        torch.cuda.synchronize()
+        assert torch.equal(got_y, ry) and torch.equal(got_s, rs), f"replay with inputs {i}"
