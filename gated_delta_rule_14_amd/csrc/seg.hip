@@ -1530,6 +1530,15 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         // (COMPOSE: the previous chunk's state update in S3, while the gate
         // waves solve for T')
         auto rest = [&](int n, bool upd) __attribute__((always_inline)) {
+            // EXPAND_LITE: chunk n's T' from the compose pass, into LDS after
+            // the M pairs (the state waves have room in S2; the gate waves'
+            // S1 is the longer step)
+            f32x4 tpr[LITE ? 2 : 1];
+            if constexpr (LITE) {
+                const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(n));
+#pragma unroll
+                for (int j = 0; j < 2; ++j) tpr[j] = tg[threadIdx.x + 256 * j];
+            }
             if constexpr (GATED)
                 if (upd) fetch_gate(n - 1);
             if constexpr (VSTATE) {
@@ -1541,6 +1550,10 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
                 pipe_pairs<MODE, 2>(w, smem);
             else
                 pipe_pairs<MODE, 1>(w, smem);
+            if constexpr (LITE) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, threadIdx.x + 256 * j) = tpr[j];
+            }
             if constexpr (GATED)
                 if (upd) epilogue(n - 1);
             if constexpr (!LITE) {
@@ -1614,14 +1627,6 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             pfetch_z<true>(in, z, row_of(mn), valid_n, H, R);   // this chunk's z is consumed
             gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
             pfetch_kq<true>(in, q, k, beta, row_of(mn), valid_n, H, R);
-            // EXPAND_LITE: this chunk's T' from the compose pass, into LDS
-            // after the barrier
-            f32x4 tpr[LITE ? 2 : 1];
-            if constexpr (LITE) {
-                const f32x4* tg = reinterpret_cast<const f32x4*>(tm_of(m));
-#pragma unroll
-                for (int j = 0; j < 2; ++j) tpr[j] = tg[(threadIdx.x - 256) + 256 * j];
-            }
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
             pipe_diag_mma<MODE>(R, smem, accA, accM);
@@ -1630,8 +1635,6 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             pipe_diag_inv<MODE>(R, smem, accA, accM);
             if constexpr (LITE) {
                 pfetch_v(pv, v, row_of(mn), valid_n, H, R);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) *tp_lds<LY>(smem, (threadIdx.x - 256) + 256 * j) = tpr[j];
             } else {
                 __syncthreads();   // S2 | S3
             }
