@@ -917,6 +917,30 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
 #pragma unroll
                     for (int ct = 0; ct < NTW; ++ct) *reinterpret_cast<bf16x4*>(orow + ct * 32) = ob[ct];
                 }
+            } else if constexpr (NTW == 2) {
+                // lanes 16 apart swap halves, so that each holds 8 consecutive
+                // columns of its row (even l/16: 4g..4g+7, odd: 4g+12..4g+19)
+                // and one store covers 64 contiguous bytes per row
+                bf16x4 b[2];
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) b[ct][e] = (bf16)ov[ot][ct][e];
+                // lane-derived values recomputed here, not held across the loop
+                int lx = l;
+                asm volatile("" : "+v"(lx));
+                const bool odd = (lx >> 4) & 1;
+                const uint2 send = __builtin_bit_cast(uint2, odd ? b[0] : b[1]);
+                const int src = (lx ^ 16) << 2;
+                const uint2 recv = {(unsigned)__builtin_amdgcn_ds_bpermute(src, (int)send.x),
+                                    (unsigned)__builtin_amdgcn_ds_bpermute(src, (int)send.y)};
+                const bf16x4 r = __builtin_bit_cast(bf16x4, recv);
+                const bf16x4 lo4 = odd ? r : b[0], hi4 = odd ? b[1] : r;
+                const bf16x8 out = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                if (ot * 16 + (lx & 15) < valid)
+                    *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(orow0) +
+                                               (unsigned)(ot * 16 + (lx & 15)) * ((unsigned)ostride * 2u) +
+                                               8u * (unsigned)(lx >> 4) + (odd ? 24u : 0u)) = out;
             } else if (ot * 16 + c < valid) {
                 bf16* orow = orow0 + (size_t)(ot * 16 + c) * ostride + 4 * g;
 #pragma unroll
