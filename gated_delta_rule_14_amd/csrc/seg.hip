@@ -917,7 +917,8 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
 #pragma unroll
                     for (int ct = 0; ct < NTW; ++ct) *reinterpret_cast<bf16x4*>(orow + ct * 32) = ob[ct];
                 }
-            } else if constexpr (NTW == 2) {
+            } else {
+                static_assert(NTW == 2, "the paired stores assume two column tiles");
                 // lanes 16 apart swap halves, so that each holds 8 consecutive
                 // columns of its row (even l/16: 4g..4g+7, odd: 4g+12..4g+19)
                 // and one store covers 64 contiguous bytes per row
@@ -941,10 +942,6 @@ __device__ __forceinline__ void chain_a(const f32x4 (&xs)[8][NTW], bf16x8 (&yb)[
                     *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(orow0) +
                                                (unsigned)(ot * 16 + (lx & 15)) * ((unsigned)ostride * 2u) +
                                                8u * (unsigned)(lx >> 4) + (odd ? 24u : 0u)) = out;
-            } else if (ot * 16 + c < valid) {
-                bf16* orow = orow0 + (size_t)(ot * 16 + c) * ostride + 4 * g;
-#pragma unroll
-                for (int ct = 0; ct < NTW; ++ct) store4<bf16>(orow + ct * 16, ov[ot][ct]);
             }
         }
     }
