@@ -48,9 +48,10 @@ def oracle_layer_y(x, w=None, heads=None):
     return ry, rs
 
 
-# B, T, H: segmented (epilogue fused) with a ragged last chunk; one pass (two
-# kernels) with a ragged last chunk; 8 segments (fused); one chunk; one token
-SHAPES = [(1, 1000, 3), (2, 200, 2), (1, 4096, 2), (1, 64, 1), (1, 1, 1)]
+# B, T, H: segmented (epilogue fused) with a ragged last chunk, for one and
+# two sequences; one pass (two kernels) with a ragged last chunk; 8 segments
+# (fused); one chunk; one token
+SHAPES = [(1, 1000, 3), (2, 1000, 2), (2, 200, 2), (1, 4096, 2), (1, 64, 1), (1, 1, 1)]
 
 
 @pytest.mark.parametrize("B,T,H", SHAPES)
@@ -109,6 +110,18 @@ def test_layer_other_sizes_run_both_calls(dtype, d, tol):
     ey, es = rel(f64(y), ry), rel(f64(s), rs)
     print(f"layer {dtype} d={d}: y {ey:.2e} state {es:.2e}")
     assert ey < tol and es < tol
+
+
+def test_fused_layer_state_in_place():
+    """s_final may be s0: the state is read before it is overwritten."""
+    x = inputs(2, 1000, 2, 128, torch.bfloat16, seed=21)
+    y, s = fused(x, want_o=False)
+    st = x["s0"].clone()
+    y2, s2 = kda.chunk_layer_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["gate"], ki.EPS, None, st,
+                                 s_final=st)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == st.data_ptr()
+    assert torch.equal(y, y2) and torch.equal(s, st)
 
 
 def test_layer_empty_sequence():
