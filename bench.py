@@ -22,6 +22,8 @@ Also measured in the same run:
     kda_out_gate) -- the training-shape layer with its projection
     (kda_chunk_layer_fwd, likewise), and the scalar-gate (Gated DeltaNet)
     prefill at the 32k shape;
+  * backward: kda_recurrent_bwd (the recurrence's gradients, token-sequential)
+    on the 8 x 8192 training shape;
   * ceilings: what this GPU reaches on plain torch kernels -- an in-place
     fp32 scale (read-modify-write), a device copy and a large bf16 matmul --
     so that each kernel's rate can be read against them as well as against
@@ -332,6 +334,34 @@ def bench_train_layer(torch, kda, ki, calls=5):
             "kernels": "kda_chunk_layer_fwd (epilogue in the prefill kernels, then the hipBLASLt projection)"}
 
 
+def bench_backward(torch, kda, ki, calls=2):
+    """kda_recurrent_bwd on the training shape (B=8, T=8192, H=32, d=128, bf16
+    tokens): the gradients with respect to q, k, v, z, beta and S0 for given
+    gradients of o and S_final.  Algorithmic bytes per token-head: the token
+    inputs and the output gradient (bf16, 5 x 256 + 2) and the fp32 gradients
+    written (4 x 512 + 4)."""
+    cfg = ki.WORKLOADS["train_8x8k"]
+    B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    dev = torch.device("cuda:0")
+    x = ki.workload_inputs("train_8x8k", seed=2, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    do = torch.randn((B, T, H, dv), generator=g, device=dev).to(torch.bfloat16)
+    dsf = torch.randn((B, H, dk, dv), generator=g, device=dev)
+    ws = torch.empty(kda.recurrent_bwd_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8, device=dev)
+    per = _time_calls(torch, lambda: kda.recurrent_bwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, None,
+                                                       do, dsf, workspace=ws), calls)
+    nbytes = B * T * H * (5 * 256 + 2 + 4 * 512 + 4) + 2 * B * H * dk * dv * 4
+    gbs = nbytes / per / 1e9
+    del x, do, dsf, ws
+    torch.cuda.empty_cache()
+    return {"workload": "train_8x8k backward", "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "dtype": "bf16",
+            "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
+            "kernels": "kda_recurrent_bwd (recurrent_bwd_kernel, token-sequential)",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
+
+
 def bench_gdn_prefill(torch, kda, ki, calls=10):
     """The scalar-gate (Gated DeltaNet) prefill at the 32k shape: z is one
     logit per (token, head), broadcast over the channels into the workspace,
@@ -536,6 +566,8 @@ def main():
         if not args.no_long:
             wl.append(bench_workload(torch, kda, ki, "long_1m", 4, 2))
         line["workloads"] = wl
+    if not args.no_workloads:
+        line["backward"] = bench_backward(torch, kda, ki)
     if not args.no_ceilings:
         c = measured_ceilings(torch)
         line["ceilings"] = c

@@ -33,6 +33,9 @@ SIGNATURES = {
     "kda_recurrent_layer_step": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _f, _vp, _vp, _vp,
                                       _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_layer_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "kda_recurrent_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "kda_recurrent_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _f, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
 }

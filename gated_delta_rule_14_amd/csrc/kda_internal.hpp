@@ -76,4 +76,21 @@ size_t projection_scratch_bytes();
 hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* lt_ws,
                              void* stream);
 
+// Gradients of the recurrence (bwd.hip): token-sequential, one workgroup
+// per (b, h); fp32 gradients.
+struct BwdArgs {
+    const void *q, *k, *v, *z, *beta;
+    float g_min;
+    const float* s0;
+    const void* dout;
+    const float* ds_final;
+    float *dq, *dk, *dv, *dz, *dbeta, *ds0;
+    int B, T, H, dk_dim, dv_dim;
+    bool bf16;
+    void* workspace;
+    void* stream;
+};
+size_t bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+hipError_t launch_bwd(const BwdArgs& a);
+
 }  // namespace kda

@@ -15,6 +15,8 @@ Names follow the C ABI in include/kda.h:
   chunk_layer_fwd -> kda_chunk_layer_fwd: the prefill of the whole layer
                      (chunkwise recurrence with RMSNorm x gate in its
                      kernels, then the projection)
+  recurrent_bwd   -> kda_recurrent_bwd: gradients of the recurrence with
+                     respect to q, k, v, z, beta and s0 (fp32)
   layer           -> kda_chunk_layer_fwd, returning the
                      {"outputs", "final_state"} dictionary of the
                      "KDA Recurrence" problem (final_state kept in fp32)
@@ -283,6 +285,43 @@ def chunk_layer_fwd(q, k, v, z, beta, g_min, gate, eps, w=None, s0=None, *, y=No
         _p(o), _p(y), _p(s_final), B, T, H, dk, dv, CHUNK, d_model, _dt(q), _p(workspace), ws_bytes,
         _stream(dev)))
     return (y, s_final, o) if want_o else (y, s_final)
+
+
+def recurrent_bwd_workspace_bytes(B, T, H, dk, dv):
+    return int(lib().kda_recurrent_bwd_workspace_bytes(B, T, H, dk, dv))
+
+
+def recurrent_bwd(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final=None, *, want_s0=True, workspace=None):
+    """Gradients of the recurrence (the backward of chunk_fwd). Inputs as for
+    chunk_fwd; grad_o: (B,T,H,dv) in the token dtype; grad_s_final:
+    (B,H,dk,dv) fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dz,
+    dbeta and ds0 (None when want_s0 is False)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("grad_o", grad_o)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    for name, t in (("s0", s0), ("grad_s_final", grad_s_final)):
+        if t is not None:
+            _need(t, name, dev)
+            if t.dtype != torch.float32:
+                raise TypeError(f"libkda: {name} must be float32")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+           "dv": torch.empty((B, T, H, dv), **f32), "dz": torch.empty((B, T, H, dk), **f32),
+           "dbeta": torch.empty((B, T, H), **f32),
+           "ds0": torch.empty((B, H, dk, dv), **f32) if want_s0 else None}
+    need = lib().kda_recurrent_bwd_workspace_bytes(B, T, H, dk, dv)
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("kda_recurrent_bwd", lib().kda_recurrent_bwd(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(grad_o), _p(grad_s_final),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dz"]), _p(out["dbeta"]), _p(out["ds0"]),
+        B, T, H, dk, dv, _dt(q), _p(workspace), ws_bytes, _stream(dev)))
+    return out
 
 
 def layer(query, key, value, decay_logits, write_strength, output_gate_logits,

@@ -12,8 +12,8 @@
  * with one d_k x d_v state per (batch, head).  Three calls cover the path:
  * chunkwise prefill, one decode token, and the output epilogue; two more
  * run the whole layer (recurrence and epilogue together), one for a prefill
- * and one for a decode token, and two take the scalar-gate (Gated DeltaNet)
- * special case.
+ * and one for a decode token, two take the scalar-gate (Gated DeltaNet)
+ * special case, and one gives the recurrence's gradients for training.
  *
  * Conventions shared by every call
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
@@ -248,6 +248,41 @@ kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
 kda_status kda_gdn_recurrent_step(const void* q, const void* k, const void* v, const void* z,
                                   const void* beta, float g_min, float* state, void* o,
                                   int B, int H, int dk, int dv, kda_dtype dt, void* stream);
+
+/*
+ * Gradients of the recurrence of Eq. 1 (with the decay and readout of
+ * "KDA Recurrence") for a loss whose gradients with respect to the outputs o
+ * and the final state are given: the backward of kda_chunk_fwd, and of a
+ * run of kda_recurrent_step.  The pages give no gradient formulas; these are
+ * the chain rule through one token, S' = Diag(alpha) S, w = v - S'^T k,
+ * S_t = S' + beta k w^T, o = S_t^T q, taken in reverse:
+ *   dq = S_t do, dS += q do^T, u = dS^T k, dbeta = u . w, dv = beta u,
+ *   dk = beta dS w - beta S' u, dalpha = rowsum(S_{t-1} * (dS - beta k u^T)),
+ *   dz = dalpha * alpha * g_min * sigmoid(z) (1 - sigmoid(z)),
+ *   dS <- Diag(alpha) (dS - beta k u^T).
+ *
+ *   q, k, v, z, beta, g_min, s0   the forward's inputs, as for kda_chunk_fwd
+ *   grad_o        (B, T, H, dv) dtype dt   gradient with respect to o
+ *   grad_s_final  (B, H, dk, dv) fp32      gradient with respect to the final
+ *                                           state, or NULL for zeros
+ *   grad_q, grad_k, grad_z (B, T, H, dk), grad_v (B, T, H, dv),
+ *   grad_beta (B, T, H): fp32 (written)
+ *   grad_s0       (B, H, dk, dv) fp32 (written), or NULL to skip
+ *   workspace     kda_recurrent_bwd_workspace_bytes() bytes: per (batch,
+ *                 head) the state at the start of every 64-token interval
+ *                 and one interval's per-token states (min(64, T) of them),
+ *                 fp32; none when T == 0
+ * Token-sequential: one workgroup per (batch, head) recomputes the states
+ * from the stored interval starts and steps back through the tokens; all
+ * arithmetic in fp32.  Every other rule is that of kda_chunk_fwd.
+ */
+size_t kda_recurrent_bwd_workspace_bytes(int B, int T, int H, int dk, int dv);
+kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const void* z,
+                             const void* beta, float g_min, const float* s0, const void* grad_o,
+                             const float* grad_s_final, float* grad_q, float* grad_k, float* grad_v,
+                             float* grad_z, float* grad_beta, float* grad_s0, int B, int T, int H,
+                             int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 #ifdef __cplusplus
 }

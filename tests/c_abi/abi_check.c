@@ -69,6 +69,10 @@ int main(void) {
     CHECK(kda_chunk_layer_fwd(P, P, P, P, P, -5.f, NULL, P, 1e-6f, P, NULL, P, NULL, 1, 128, 2, 128, 128, 64,
                               64, KDA_BF16, NULL, 0, NULL) == KDA_ERR_WORKSPACE);
 
+    CHECK(kda_recurrent_bwd_workspace_bytes(1, 32768, 32, 128, 128) == (size_t)32 * 576 * 128 * 128 * 4);
+    CHECK(kda_recurrent_bwd(P, P, P, P, P, -5.f, NULL, P, NULL, PF, PF, PF, PF, NULL, NULL, 1, 128, 2, 128, 128,
+                            KDA_BF16, P, (size_t)1 << 30, NULL) == KDA_ERR_NULL);
+
     if (failures) {
         fprintf(stderr, "%d checks failed\n", failures);
         return 1;

@@ -265,6 +265,36 @@ def test_chunk_layer_fwd_workspace_and_bad_arguments(lib):
     assert c(T=0, g=None, ws=None, wsb=0) == OK    # nothing to compute, no state asked for
 
 
+def test_recurrent_bwd_workspace_and_bad_arguments(lib):
+    # per (batch, head): the state at the start of every 64-token interval and
+    # one interval's per-token states, fp32
+    assert lib.kda_recurrent_bwd_workspace_bytes(1, 32768, 32, 128, 128) == 32 * (512 + 64) * 128 * 128 * 4
+    assert lib.kda_recurrent_bwd_workspace_bytes(2, 100, 3, 64, 128) == 6 * (2 + 64) * 64 * 128 * 4
+    assert lib.kda_recurrent_bwd_workspace_bytes(1, 10, 1, 64, 64) == (1 + 10) * 64 * 64 * 4
+    assert lib.kda_recurrent_bwd_workspace_bytes(1, 0, 4, 64, 64) == 0
+    assert lib.kda_recurrent_bwd_workspace_bytes(1, 100, 1, 96, 64) == 0
+
+    def bw(q=P, go=P, gq=P, gb=P, gs0=None, g_min=-5.0, B=1, T=128, H=2, dk=128, dv=128, dt=BF16, ws=P,
+           wsb=1 << 30):
+        return lib.kda_recurrent_bwd(q, P, P, P, P, g_min, None, go, None, gq, P, P, P, gb, gs0, B, T, H, dk, dv,
+                                     dt, ws, wsb, S)
+
+    assert bw(q=None) == NULL
+    assert bw(go=None) == NULL
+    assert bw(gq=None) == NULL
+    assert bw(gb=None) == NULL
+    assert bw(dk=96) == UNSUP
+    assert bw(dt=2) == UNSUP
+    assert bw(B=-1) == SHAPE
+    assert bw(g_min=0.0) == ARG
+    assert bw(gq=MIS) == ALIGN
+    assert bw(gs0=MIS) == ALIGN
+    assert bw(ws=None, wsb=0) == WS
+    assert bw(wsb=1024) == WS
+    assert bw(H=0) == OK
+    assert bw(T=0, q=None, go=None, gq=None, gb=None, ws=None, wsb=0) == OK   # no tokens, no ds0 asked for
+
+
 def test_plain_c_caller(tmp_path):
     """The header compiles as C (gcc, -std=c11 -Wall -Werror) and a C program
     linked against libkda.so gets the documented host-side behaviour."""
