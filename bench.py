@@ -60,17 +60,20 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_32k_traffic.json")
 CSRC = os.path.join(ROOT, "gated_delta_rule_14_amd", "csrc")
 
 
+# the sources of the kernels whose counters the traffic record holds (the
+# prefill's pipelined kernels and segment scan, the decode step, the gate
+# kernel) and the device header they include
+TRAFFIC_SOURCES = ("seg.hip", "decode.hip", "out_gate.hip", "kda_device.hpp")
+
+
 def kernel_source_hash():
-    """Hash of the kernel sources with comments and blank lines removed, so
-    that the stored counters stay attached to the code they were taken on.
-    kda_api.hip (argument checks and dispatch to the launchers, no kernels)
-    is not part of it."""
+    """Hash of the measured kernels' sources with comments and blank lines
+    removed, so that the stored counters stay attached to the code they were
+    taken on."""
     import re
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
-        if os.path.basename(f) == "kda_api.hip":
-            continue
-        text = open(f, encoding="utf-8").read()
+    for name in TRAFFIC_SOURCES:
+        text = open(os.path.join(CSRC, name), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
         h.update("\n".join(ln for ln in lines if ln).encode())
