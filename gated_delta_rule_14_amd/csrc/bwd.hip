@@ -19,8 +19,8 @@
 // workspace; the backward sweep then takes the intervals in reverse: it
 // recomputes the interval's states forward (storing each token's incoming
 // state in the workspace and w in LDS) and steps back through its tokens
-// with dS in registers.  Token-sequential: every token costs three
-// workgroup barriers in each direction.
+// with dS in registers.  Token-sequential: every token costs two workgroup
+// barriers in each direction.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -76,9 +76,11 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
     auto row_of = [&](int t) { return ((size_t)b * T + t) * H + h; };
 
     // A token's inputs are fetched into registers (item i of q | k | z |
-    // v or do | beta per thread, i = tid + u NTH) one step ahead, and put
-    // into the staging buffer of its step at the end of the step before,
-    // so that their load latency hides behind that step.
+    // v or do | beta per thread, i = tid + u NTH) one step ahead and put
+    // into the staging buffer of its step between the last two barriers of
+    // the step before, whose last barrier publishes them: their load latency
+    // hides behind that step, and a step needs two barriers (the column-sum
+    // partials, then the column sums and the next token).
     constexpr int NIT = 3 * DK + DV + 1;
     constexpr int IPT = (NIT + L::NTH - 1) / L::NTH;
     E fv[IPT];   // raw: converted when put, so that the loads stay in flight
@@ -135,13 +137,13 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
     };
 
     float s[SW], ds[SW];
-    // one token forward: s <- S_t from S_{t-1}, the token staged in buffer
-    // par; with keep_w, w into wbuf[j].  tn >= 0: the next step's token,
-    // fetched here (forward step when fn) and staged in buffer par ^ 1.
+    // one token forward: s <- S_t from S_{t-1}, the token staged (and
+    // published) in buffer par; with keep_w, w into wbuf[j].  tn >= 0: the
+    // next step's token, fetched here (forward step when fn) and staged in
+    // buffer par ^ 1.
     auto fwd_step = [&](int par, bool keep_w, int j, int tn, bool fn) {
         float* tb = tok_buf(par);
         if (tn >= 0) fetch(tn, fn);
-        __syncthreads();
         const float a = tb[2 * DK + r], kr = tb[DK + r], bt = tb[4 * DK + DV];
 #pragma unroll
         for (int c = 0; c < SW; ++c) {
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
         }
         __syncthreads();
         col_sums();
+        if (tn >= 0) put(tok_buf(par ^ 1));
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < SW; ++c) {
@@ -157,7 +160,6 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
             if (keep_w && r == 0) wbuf[j * DV + c0 + c] = w;
             s[c] += bt * kr * w;
         }
-        if (tn >= 0) put(tok_buf(par ^ 1));
     };
 
     // ---- forward sweep: the state at the start of every interval
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
     if (T > 0) {
         fetch(0, true);
         put(tok_buf(0));
+        __syncthreads();
     }
     for (int n = 0; n < NC; ++n) {
 #pragma unroll
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
         __syncthreads();   // the previous step's reads of both staging buffers done
         fetch(t0, true);
         put(tok_buf(par));
+        __syncthreads();
         for (int j = 0; j < len; ++j, par ^= 1) {
 #pragma unroll
             for (int c = 0; c < SW; c += 4)
@@ -217,7 +221,6 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
                 sp[c + 3] = x[3];
             }
             if (j > 0) fetch(t - 1, false);
-            __syncthreads();
             const float a = tb[2 * DK + r], kr = tb[DK + r], qr = tb[r], bt = tb[4 * DK + DV];
             const float* dov = tb + 4 * DK;
             float acc = 0.f;
@@ -232,6 +235,7 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
             }
             __syncthreads();
             col_sums();
+            if (j > 0) put(tok_buf(par ^ 1));
             __syncthreads();
             float dbt = 0.f, dkr = 0.f, dal = 0.f;
 #pragma unroll
@@ -254,7 +258,6 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
                 dk[rt * DK + r] = dkr;
                 dz[rt * DK + r] = dal * tb[3 * DK + r];
             }
-            if (j > 0) put(tok_buf(par ^ 1));
         }
     }
     if (ds0) {
