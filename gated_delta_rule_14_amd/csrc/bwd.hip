@@ -83,9 +83,10 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
     // partials, then the column sums and the next token).
     constexpr int NIT = 3 * DK + DV + 1;
     constexpr int IPT = (NIT + L::NTH - 1) / L::NTH;
-    E fv[IPT];   // raw: converted when put, so that the loads stay in flight
-    // (the source is selected first and loaded without a branch, so that
-    // the load stays in flight until the value is put)
+    // The source is selected first and loaded without a branch, and the raw
+    // value is converted only when put, so that the load stays in flight
+    // until then.
+    E fv[IPT];
     auto fetch = [&](int t, bool fwd) {
         const size_t rt = row_of(t);
 #pragma unroll
