@@ -34,16 +34,17 @@ struct BLay {
     static constexpr int NTH = 4 * DK;
     static constexpr int SW = DV / 4;           // columns per thread
     static constexpr int RP = DV + 4;           // row pitch of the column-sum partials (floats)
+    static constexpr int NPR = NTH / 16;        // partial rows: one per 16-lane group (4 state rows)
     static constexpr int TPC = NTH / DV;        // threads per column in the column sums
-    static constexpr int RPT = DK / TPC;        // rows per thread in the column sums
+    static constexpr int RPT = NPR / TPC;       // partial rows per thread in the column sums
     // one staged token: q, k, alpha, the dz factor (DK each), v or do (DV), beta
     static constexpr int TOK = 4 * DK + DV + 4;
-    static constexpr int OFF_RED = 0;                     // [DK][RP]
+    static constexpr int OFF_RED = 0;                     // [NPR][RP] (allocated [DK][RP])
     static constexpr int OFF_COL = OFF_RED + DK * RP;     // [DV]
     static constexpr int OFF_W = OFF_COL + DV;            // [C][DV]
     static constexpr int OFF_TOK = OFF_W + C * DV;        // [2][TOK]
     static constexpr int FLOATS = OFF_TOK + 2 * TOK;
-    static_assert(NTH % DV == 0 && DK % TPC == 0 && SW % 4 == 0, "layout");
+    static_assert(NTH % DV == 0 && NPR % TPC == 0 && SW % 4 == 0, "layout");
 };
 
 // per (b, h): the NC interval starts, then up to C per-token states
@@ -121,7 +122,26 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
         }
     };
     auto tok_buf = [&](int par) { return lds + L::OFF_TOK + par * L::TOK; };
-    // col[c] = sum over rows of red[.][c] (rows taken TPC apart by the threads of a column)
+    // Column sums of x[c] (this thread's row, its quarter's columns) over
+    // all rows: the four rows held by the lanes of a 16-lane DPP row that
+    // share a quarter are summed by two row rotations, lanes 16k + g write
+    // partial row (16-lane group) to red, and after the barrier col_sums adds
+    // the partial rows.
+    auto partial_rows = [&](float (&x)[SW]) {
+#pragma unroll
+        for (int c = 0; c < SW; ++c) {
+            float y = x[c];
+            y += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), 0x124, 0xF, 0xF, false));
+            y += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), 0x128, 0xF, 0xF, false));
+            x[c] = y;
+        }
+        if ((tid & 12) == 0) {
+            float* pr = red + (tid >> 4) * L::RP + c0;
+#pragma unroll
+            for (int c = 0; c < SW; c += 4) *reinterpret_cast<f32x4*>(pr + c) = f32x4{x[c], x[c + 1], x[c + 2], x[c + 3]};
+        }
+    };
+    // col[c] = sum over the partial rows of red[.][c] (taken TPC apart by the threads of a column)
     auto col_sums = [&]() {
         const int cc = tid / L::TPC, jj = tid % L::TPC;
         float acc = 0.f;
@@ -146,11 +166,13 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
         float* tb = tok_buf(par);
         if (tn >= 0) fetch(tn, fn);
         const float a = tb[2 * DK + r], kr = tb[DK + r], bt = tb[4 * DK + DV];
+        float x[SW];
 #pragma unroll
         for (int c = 0; c < SW; ++c) {
             s[c] *= a;
-            red[r * L::RP + c0 + c] = s[c] * kr;
+            x[c] = s[c] * kr;
         }
+        partial_rows(x);
         __syncthreads();
         col_sums();
         if (tn >= 0) put(tok_buf(par ^ 1));
@@ -229,11 +251,13 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
             for (int c = 0; c < SW; ++c) acc += s[c] * dov[c0 + c];
             acc = quad_sum(acc);
             if (g == 0) dq[rt * DK + r] = acc;
+            float x[SW];
 #pragma unroll
             for (int c = 0; c < SW; ++c) {
                 ds[c] += qr * dov[c0 + c];
-                red[r * L::RP + c0 + c] = ds[c] * kr;
+                x[c] = ds[c] * kr;
             }
+            partial_rows(x);
             __syncthreads();
             col_sums();
             if (j > 0) put(tok_buf(par ^ 1));
