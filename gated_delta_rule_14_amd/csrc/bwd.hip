@@ -44,7 +44,7 @@ struct BLay {
     static constexpr int OFF_W = OFF_COL + DV;            // [C][DV]
     static constexpr int OFF_TOK = OFF_W + C * DV;        // [2][TOK]
     static constexpr int FLOATS = OFF_TOK + 2 * TOK;
-    static_assert(NTH % DV == 0 && NPR % TPC == 0 && SW % 4 == 0, "layout");
+    static_assert(NTH % DV == 0 && NPR % TPC == 0 && SW % 4 == 0 && TPC >= 2 && TPC <= 8, "layout");
 };
 
 // per (b, h): the NC interval starts, then up to C per-token states
@@ -141,19 +141,27 @@ __global__ __launch_bounds__(4 * DK) void recurrent_bwd_kernel(
             for (int c = 0; c < SW; c += 4) *reinterpret_cast<f32x4*>(pr + c) = f32x4{x[c], x[c + 1], x[c + 2], x[c + 3]};
         }
     };
+    // lane exchanges within a group of four lanes (DPP quad permutes)
+    auto xor1 = [](float x) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    };
+    auto xor2 = [](float x) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    };
     // col[c] = sum over the partial rows of red[.][c] (taken TPC apart by the threads of a column)
     auto col_sums = [&]() {
         const int cc = tid / L::TPC, jj = tid % L::TPC;
         float acc = 0.f;
 #pragma unroll 8
         for (int i = 0; i < L::RPT; ++i) acc += red[(i * L::TPC + jj) * L::RP + cc];
-#pragma unroll
-        for (int off = 1; off < L::TPC; off <<= 1) acc += __shfl_xor(acc, off);
+        acc += xor1(acc);
+        if constexpr (L::TPC >= 4) acc += xor2(acc);
+        if constexpr (L::TPC >= 8) acc += __shfl_xor(acc, 4);
         if (jj == 0) col[cc] = acc;
     };
     auto quad_sum = [&](float x) {
-        x += __shfl_xor(x, 1);
-        x += __shfl_xor(x, 2);
+        x += xor1(x);
+        x += xor2(x);
         return x;
     };
 
