@@ -39,6 +39,7 @@ Prints one JSON line.
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -497,20 +498,63 @@ def cpu_baseline(torch, ki, nheads):
     h = {n: np.ascontiguousarray(ki.to_host_bits(x[n])[:, :, heads]) for n in ("q", "k", "v", "z", "beta")}
     s0 = np.ascontiguousarray(ki.to_host_bits(x["s0"])[:, heads])
     del x
-    threads = oracle.default_threads()
+    share, logical, why = host_cpu_share()
+    threads = share
     t0 = time.perf_counter()
     oracle.forward(h["q"], h["k"], h["v"], h["z"], h["beta"], ki.G_MIN, s0, nthreads=threads)
     dt = time.perf_counter() - t0
     # a token is one (b, t) position over all H heads: scale the sample by nheads / H
-    model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
-    except OSError:
-        pass
     return {"value": T * nheads / H / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prefill_32k, {nheads} of {H} heads over all {T} tokens, fp64, {dt:.1f} s",
-            "cpu_model": model}
+            "sample": f"prefill_32k, {nheads} of {H} heads over all {T} tokens, fp64, {dt:.1f} s "
+                      f"on {threads} threads ({dt * threads:.0f} s of CPU time)",
+            "host_logical_cpus": logical, "cores_reason": why, "cpu_model": cpu_model()}
+
+
+def host_cpu_share():
+    """Threads the oracle may use: the CPUs this process is allowed to run on
+    (its affinity mask), capped by OMP_NUM_THREADS when the host sets it (a
+    shared host gives each GPU a share of its cores).  Returns (threads,
+    logical CPUs of the host, how the count was reached)."""
+    logical = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = logical
+    why = f"{allowed} CPUs in this process's affinity mask of {logical} logical CPUs"
+    share = allowed
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and 0 < int(omp) < share:
+        share = int(omp)
+        why += f", capped at the host's per-job share OMP_NUM_THREADS={omp}"
+    return share, logical, why
+
+
+def cpu_model():
+    """The host CPU's model string, family/model/stepping and hypervisor, as
+    lscpu and /proc/cpuinfo report them."""
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for ln in out.splitlines():
+            if ":" in ln:
+                k, v = ln.split(":", 1)
+                info[k.strip()] = v.strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if "Model name" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                info["Model name"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                                          "")
+        except OSError:
+            pass
+    parts = [info.get("Vendor ID", ""), info.get("Model name", ""),
+             f"family {info.get('CPU family', '?')} model {info.get('Model', '?')} stepping {info.get('Stepping', '?')}",
+             f"{info.get('Socket(s)', '?')} socket(s) x {info.get('Core(s) per socket', '?')} cores x "
+             f"{info.get('Thread(s) per core', '?')} threads"]
+    if info.get("Hypervisor vendor"):
+        parts.append(f"hypervisor {info['Hypervisor vendor']}")
+    return ", ".join(p for p in parts if p)
 
 
 def main():

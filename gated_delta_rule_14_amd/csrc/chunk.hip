@@ -33,8 +33,13 @@
 // chunk (|G| reaches 64 * |g_min|, far beyond the fp32 range).  A and M are
 // evaluated per 16x16 block (R, I) with reference rows m(R) = 16R + 7:
 //   e^{G_r - G_i} = e^{G_r - G_m(R)} * e^{G_m(R) - G_m(I)} * e^{G_m(I) - G_i}.
-// The outer factors have exponents bounded by 8 |g_min|; the middle one is
-// <= 1 (it underflows to 0 only when the exact product is negligible).
+// The outer factors have exponents bounded by 8 |g_min| (at most 2^93 in
+// log2 terms for g_min >= -8, the chunkwise limit).  The middle factor is
+// <= 1 but spans 16 or more rows, so alone it can underflow while the key
+// factor it multiplies is 2^93: it is applied as its square root twice,
+// (k e^{G_m(I) - G_i} s) s with s = e^{(G_m(R) - G_m(I)) / 2}, so that s stays
+// normal whenever the product is above 2^-126, and what underflow drops
+// stays below 2^-45 after the row factor (at most 2^81).
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -130,7 +135,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     float* Xs = Ts + C * LT;                            // [3][16][16]
     CT* RT = reinterpret_cast<CT*>(smem + L::OFF_RT);   // [DK][LC] R_K^T = (beta k e^G)^T
     CT* RV = reinterpret_cast<CT*>(smem + L::OFF_RV);   // [DV][LC] R_V^T = (beta v)^T (after phase 3)
-    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{G_m(R) - G_m(I)}
+    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{(G_m(R) - G_m(I)) / 2}
     float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);     // [5][DK] G2_m(R), G2_C
     float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);   // [NPART][DK]
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);   // [C]
@@ -255,7 +260,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
         const int p = idx / DK, cc = idx % DK;
         const int R = p < 1 ? 1 : (p < 3 ? 2 : 3);
         const int I = p - R * (R - 1) / 2;
-        dsc[idx] = dexp2<E>(gm[R * DK + cc] - gm[I * DK + cc]);
+        dsc[idx] = dexp2<E>(0.5f * (gm[R * DK + cc] - gm[I * DK + cc]));   // applied twice
     }
     __syncthreads();
 
@@ -277,7 +282,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
                 MF::to_floats(ak, t);
                 const int cc = kk + (l >> 4) * MF::KPL;
 #pragma unroll
-                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] *= dv[cc + jj];
+                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] = (t[jj] * dv[cc + jj]) * dv[cc + jj];
                 ak = MF::from_floats(t);
             }
             accA = MF::mma(ak, load_frag<CT>(KL, LDK, R * SUB, kk), accA);
@@ -901,6 +906,7 @@ hipError_t launch_chunk(const ChunkArgs& a) {
                            dim3(256), 0, (hipStream_t)a.stream, a.s0, a.s_final, n);
         return hipGetLastError();
     }
+    if (a.g_min < CHUNK_G_MIN_LIMIT) return launch_seq(a);
     return a.bf16 ? launch_chunk_seg(a) : launch_chunk_e<float>(a);
 }
 

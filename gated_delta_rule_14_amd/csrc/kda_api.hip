@@ -8,6 +8,8 @@
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
 
+static_assert(kda::CHUNK_G_MIN_LIMIT == KDA_CHUNK_G_MIN_LIMIT, "one decay bound");
+
 namespace {
 
 bool debug_sync() {
@@ -278,8 +280,9 @@ kda_status kda_chunk_layer_fwd(const void* q, const void* k, const void* v, cons
     const bool bf = dt == KDA_BF16;
     kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, bf, chunk_ws, stream};
     hipError_t err;
-    if (T > 0 && kda::chunk_gate_fused(B, T, H, dk, dv, bf)) {
+    if (T > 0 && (g_min < kda::CHUNK_G_MIN_LIMIT || kda::chunk_gate_fused(B, T, H, dk, dv, bf))) {
         // y, or with a projection its bf16 input rows, from the prefill kernels
+        // (the token-sequential kernel for g_min below the chunkwise limit)
         a.gate = gate;
         a.eps = eps;
         a.y = w ? gate_ws : y;

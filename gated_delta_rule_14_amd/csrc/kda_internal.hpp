@@ -29,6 +29,11 @@ hipError_t launch_decode(const DecodeArgs& a);
 // zfull (rows x dk) = each of the rows scalar logits zs repeated dk times
 hipError_t launch_broadcast_gate(const void* zs, void* zfull, size_t rows, int dk, bool bf16, void* stream);
 
+// The chunkwise kernels' decay factors are bounded (finite, with negligible
+// underflow) for g_min >= CHUNK_G_MIN_LIMIT; below it the prefill calls run
+// the token-sequential kernel (seq.hip), exact for any g_min < 0.
+constexpr float CHUNK_G_MIN_LIMIT = -8.0f;
+
 struct ChunkArgs {
     const void *q, *k, *v, *z, *beta;
     float g_min;
@@ -51,6 +56,9 @@ size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
 // a segmented plan, whose light expand has LDS to stage the outputs)
 bool chunk_gate_fused(int B, int T, int H, int dk, int dv, bool bf16);
 hipError_t launch_chunk(const ChunkArgs& a);
+// token-sequential prefill (any g_min; with gate != NULL also the epilogue,
+// y in the token dtype)
+hipError_t launch_seq(const ChunkArgs& a);
 // bf16 tokens: fused segment kernels (seg.hip); fp32 tokens: per-chunk
 // workspace kernels (chunk.hip).  Both use the segment scan of chunk.hip.
 size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv);

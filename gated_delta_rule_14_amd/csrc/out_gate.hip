@@ -21,7 +21,7 @@
 #include <hipblaslt/hipblaslt.h>
 
 #include <mutex>
-#include <vector>
+#include <deque>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -195,7 +195,7 @@ struct LtPlan {
 struct LtState {
     std::mutex mu;
     hipblasLtHandle_t handle[64] = {};
-    std::vector<LtPlan> plans;
+    std::deque<LtPlan> plans;   // push_back keeps references to earlier plans valid
 };
 LtState& lt_state() {
     static LtState s;

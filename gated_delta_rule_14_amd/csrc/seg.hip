@@ -33,7 +33,9 @@
 //
 // Overflow handling of the decay factors is that of the fp32 path: A and M
 // per 16x16 block pair with reference rows m(R) = 16R + 7, decay exponents in
-// log2 units so that every factor is one v_exp_f32.
+// log2 units so that every factor is one v_exp_f32, and the cross-block
+// factor e^{G_m(R) - G_m(I)} applied as its square root twice (it spans 16
+// or more rows and alone could underflow next to a key factor of 2^93).
 //
 // Two kernels walk the segments.  pipe_kernel (d_k = d_v = 128) splits the
 // waves into state waves, which advance the state, and gate waves, which
@@ -408,7 +410,7 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
     bf16* Ab = reinterpret_cast<bf16*>(smem + L::OFF_AB);   // [6][16][LB] -A_RJ
     bf16* Db = reinterpret_cast<bf16*>(smem + L::OFF_DB);   // [4][16][LB] (I + A_RR)^{-1}
     float* egc = reinterpret_cast<float*>(smem + L::OFF_EGC);
-    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{G_m(R) - G_m(I)}
+    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);   // [6][DK] e^{(G_m(R) - G_m(I)) / 2}
     float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);   // [NPART][DK]
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);   // [C]
 
@@ -472,7 +474,7 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
                     if (Rp == t) a = gm[t][j];
                     if (Ip == t) b = gm[t][j];
                 }
-                dsc[part * DK + c0 + j] = __builtin_amdgcn_exp2f(a - b);
+                dsc[part * DK + c0 + j] = __builtin_amdgcn_exp2f(0.5f * (a - b));   // applied twice
             }
         }
         float kg[2][RP];
@@ -532,7 +534,7 @@ __device__ __forceinline__ void intra(In<DK, DV, MODE>& in, int valid, float g_m
                 MF::to_floats(ak, t);
                 const int cc = kk + (l >> 4) * MF::KPL;
 #pragma unroll
-                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] *= dv[cc + jj];
+                for (int jj = 0; jj < MF::KPL; ++jj) t[jj] = (t[jj] * dv[cc + jj]) * dv[cc + jj];
                 ak = MF::from_floats(t);
             }
             accA = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA);
@@ -769,7 +771,7 @@ struct PLay {
     static constexpr size_t OFF_AB = OFF_AS + (SOLVE ? (size_t)4 * BS * 4 : 0);             // [6][16][LB] -A~_RI
     static constexpr size_t OFF_DB = OFF_AB + (SOLVE ? a16((size_t)6 * SUB * LB * 2) : 0);  // [4][16][LB] D'_R
     static constexpr size_t OFF_EGC = OFF_DB + (SOLVE ? a16((size_t)4 * SUB * LB * 2) : 0);
-    static constexpr size_t OFF_DSC = OFF_EGC + NKB * (size_t)DK * 4;      // [6][DK] e^{G_m(R) - G_m(I)}
+    static constexpr size_t OFF_DSC = OFF_EGC + NKB * (size_t)DK * 4;      // [6][DK] e^{(G_m(R) - G_m(I)) / 2}
     static constexpr size_t OFF_TOT = OFF_DSC + 6 * (size_t)DK * 4;        // [4][DK] block sums
     static constexpr size_t OFF_MLOC = OFF_TOT + 4 * (size_t)DK * 4;       // [4][DK] G_m(R) - G_{16R-1}
     static constexpr size_t OFF_BET = OFF_MLOC + 4 * (size_t)DK * 4;
@@ -1317,7 +1319,7 @@ __device__ __forceinline__ void pipe_abs(int R, unsigned char* smem,
 // 0-1, one each for waves 2-3.
 __constant__ int kPipePairs[4][2][2] = {{{1, 0}, {3, 0}}, {{2, 0}, {3, 1}}, {{2, 1}, {-1, -1}}, {{3, 2}, {-1, -1}}};
 
-// S2 of a state wave: the cross-block factors e^{G_m(R) - G_m(I)} of its NP
+// S2 of a state wave: the cross-block factors e^{(G_m(R) - G_m(I)) / 2} of its NP
 // pairs into LDS (read back by the same wave only), then -A~_RI (without the
 // row factor beta_r, which the inverses carry) and M_RI, the NP pairs
 // interleaved in one pass over the key channels.
@@ -1355,7 +1357,7 @@ __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
                 d1 += t.y;
             }
         *reinterpret_cast<float2*>(dsc + (R * (R - 1) / 2 + I) * DK + c0) =
-            float2{__builtin_amdgcn_exp2f(d0), __builtin_amdgcn_exp2f(d1)};
+            float2{__builtin_amdgcn_exp2f(0.5f * d0), __builtin_amdgcn_exp2f(0.5f * d1)};   // applied twice
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // this wave's dsc rows
     f32x4 accA[NP], accM[NP];
@@ -1374,8 +1376,8 @@ __device__ __forceinline__ void pipe_pairs(int w, unsigned char* smem) {
             MF::to_floats(ak, t);
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                t[jj] *= d0[jj];
-                t[jj + 4] *= d1[jj];
+                t[jj] = (t[jj] * d0[jj]) * d0[jj];
+                t[jj + 4] = (t[jj + 4] * d1[jj]) * d1[jj];
             }
             ak = MF::from_floats(t);
             if constexpr (L::SOLVE) accA[j] = MF::mma(ak, load_frag<bf16>(KL, LDK, R * SUB, kk), accA[j]);

@@ -69,6 +69,22 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
+/*
+ * Decay bound of the chunkwise kernels.  Inside a 64-token chunk the decay
+ * products e^{G_r - G_i} (tech report, appendix B, gamma_{i->r}) are split
+ * into per-row and per-column factors around 16-row block references; each
+ * factor spans up to eight tokens of decay, at most 8 |g_min| nats, and the
+ * factor between two blocks is applied as its square root twice.  For
+ * g_min >= KDA_CHUNK_G_MIN_LIMIT every factor is finite in fp32 and bf16 (at
+ * most 2^93) and what underflow drops is below 2^-40.  For g_min below it the
+ * prefill calls (kda_chunk_fwd, kda_chunk_layer_fwd, kda_gdn_chunk_fwd) run a
+ * token-sequential kernel instead: one workgroup per (batch, head) applies
+ * alpha_t token by token, exact for any g_min < 0 but latency-bound (about a
+ * microsecond per token).  Decode and the backward are token steps already
+ * and have no such bound.
+ */
+#define KDA_CHUNK_G_MIN_LIMIT (-8.0f)
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* kda_status_str(kda_status s);
 
@@ -97,6 +113,9 @@ const char* kda_version(void);
  *                                        kda_chunk_fwd_workspace_bytes()
  *                                        bytes; may be NULL when that is 0
  * The result is deterministic: identical inputs give identical bits.
+ *
+ * g_min below KDA_CHUNK_G_MIN_LIMIT runs the token-sequential kernel (see
+ * there); it needs no workspace, but the size query does not depend on g_min.
  *
  * Workspace: bf16 sequences split into segments when there are fewer than
  * 256 (batch, head) chains (the per-segment transition P, input term R and

@@ -41,3 +41,27 @@ def oracle_prefill(x, g_min=ki.G_MIN, heads=None, batches=None):
     beta = cut(x["beta"], 2)
     s0 = cut(x["s0"], 1) if x.get("s0") is not None else None
     return oracle.forward(q, k, v, z, beta, g_min, s0)
+
+
+def block_rel_max(got, ref, block=64):
+    """Largest error of one block of `block` tokens of one (batch, head):
+    ||got - ref||_F over the block, divided by that head's ||ref||_F scaled
+    to the block's share of the sequence, sqrt(block_len / T).  With o laid
+    out (B, T, H, d), a defect confined to a few tokens shows up here at
+    full size instead of being averaged over the whole tensor."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    B, T, H = ref.shape[:3]
+    if T == 0:
+        return 0.0
+    d = (got - ref).reshape(B, T, H, -1)
+    r = ref.reshape(B, T, H, -1)
+    head = np.sqrt((r * r).sum(axis=(1, 3)))                      # (B, H)
+    nb = (T + block - 1) // block
+    pad = nb * block - T
+    d2 = np.pad((d * d).sum(axis=3), ((0, 0), (0, pad), (0, 0)))   # (B, nb*block, H)
+    blk = np.sqrt(d2.reshape(B, nb, block, H).sum(axis=2))         # (B, nb, H)
+    lens = np.full(nb, block, np.float64)
+    lens[-1] = T - (nb - 1) * block
+    scale = head[:, None, :] * np.sqrt(lens / T)[None, :, None]
+    return float((blk / np.maximum(scale, 1e-300)).max())

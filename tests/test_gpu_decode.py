@@ -18,26 +18,27 @@ DEV = "cuda:0"
 
 def run_steps(B, H, dk, dv, dtype, steps, seed, s0_var=0.01, heads=None, z_mean=0.0):
     """Run `steps` decode steps on the GPU; return GPU outputs / state and the
-    oracle's, restricted to the flat (b*H + h) indices in `heads`."""
+    oracle's, restricted to the flat (b*H + h) indices in `heads` (selected
+    on the device, so that only those heads are copied to the host)."""
     state = ki.initial_state(B, H, dk, dv, s0_var, seed, DEV)
-    s0_host = state.double().cpu().numpy().reshape(B * H, dk, dv)
     sel = np.arange(B * H) if heads is None else np.asarray(heads)
+    sel_d = torch.as_tensor(sel, device=DEV)
+    s0_host = state.reshape(B * H, dk, dv)[sel_d].double().cpu().numpy()
     outs, ins = [], {n: [] for n in ("q", "k", "v", "z", "beta")}
     for t in range(steps):
         d = ki.decode_step_inputs(B, H, dk, dv, dtype, seed, t, DEV, z_mean=z_mean)
         o = kda.recurrent_step(d["q"], d["k"], d["v"], d["z"], d["beta"], ki.G_MIN, state)
-        outs.append(f64(o).reshape(B * H, dv)[sel])
+        outs.append(o.reshape(B * H, dv)[sel_d].double())
         for n in ins:
-            a = host(d[n])
-            a = a.reshape((B * H,) + a.shape[2:])[sel]
-            ins[n].append(a)
+            a = d[n]
+            ins[n].append(a.reshape((B * H,) + tuple(a.shape[2:]))[sel_d].clone())
     torch.cuda.synchronize()
     # oracle layout: (batch = selected head, T = steps, H = 1, d)
-    stack = {n: np.ascontiguousarray(np.stack(v, axis=1)[:, :, None]) for n, v in ins.items()}
+    stack = {n: np.ascontiguousarray(host(torch.stack(v, dim=1))[:, :, None]) for n, v in ins.items()}
     ro, rs = oracle.forward(stack["q"], stack["k"], stack["v"], stack["z"], stack["beta"], ki.G_MIN,
-                            np.ascontiguousarray(s0_host[sel][:, None]))
-    go = np.stack(outs, axis=1)                       # (sel, steps, dv)
-    gs = state.double().cpu().numpy().reshape(B * H, dk, dv)[sel]
+                            np.ascontiguousarray(s0_host[:, None]))
+    go = torch.stack(outs, dim=1).cpu().numpy()       # (sel, steps, dv)
+    gs = state.reshape(B * H, dk, dv)[sel_d].double().cpu().numpy()
     return go, gs, ro[:, :, 0], rs[:, 0]
 
 
@@ -78,13 +79,18 @@ def test_decode_state_in_place_and_deterministic():
 
 def test_decode_full_size_sampled():
     """B=256 sequences, H=32, d=128, fp32 state, bf16 tokens: the full decode
-    workload shape for 64 steps, all 8192 heads launched, 24 heads checked."""
+    workload, all 1024 steps with all 8192 heads launched; 64 heads checked
+    over every step, as a whole and step by step."""
     rng = np.random.default_rng(0)
-    heads = np.sort(rng.choice(256 * 32, 24, replace=False))
-    go, gs, ro, rs = run_steps(256, 32, 128, 128, torch.bfloat16, steps=64, seed=3, heads=heads)
+    heads = np.sort(rng.choice(256 * 32, 64, replace=False))
+    go, gs, ro, rs = run_steps(256, 32, 128, 128, torch.bfloat16, steps=1024, seed=3, heads=heads)
     eo, es = rel(go, ro), rel(gs, rs)
-    print(f"decode full size (64 steps, 24 sampled heads): o {eo:.2e} state {es:.2e}")
-    assert eo < 2e-2 and es < 1e-2
+    # per step and head, against that head's average step
+    d = np.sqrt(((go - ro) ** 2).sum(axis=2))
+    scale = np.sqrt((ro ** 2).sum(axis=(1, 2)) / ro.shape[1])[:, None]
+    ew = float((d / scale).max())
+    print(f"decode full size (1024 steps, 64 sampled heads): o {eo:.2e} (worst step {ew:.2e}) state {es:.2e}")
+    assert eo < 2e-2 and es < 1e-2 and ew < 2e-2
 
 
 def run_layer_steps(B, H, dk, dv, dtype, steps, seed, d_model=0, batches=None, s0_var=0.01):
