@@ -20,6 +20,8 @@ SIGNATURES = {
     "kda_chunk_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "kda_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
                            _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
+    "kda_chunk_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
+                                   _i, _i, _i, _i, _i, _i, _i, _vp]),
     "kda_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                 _i, _i, _i, _i, _i, _vp]),
     "kda_out_gate_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_internal.hpp"
 
@@ -81,6 +83,8 @@ const char* kda_status_str(kda_status s) {
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: pointer not 16-byte aligned";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: HIP launch or execution error";
+        case KDA_ERR_SCRATCH:
+            return "KDA_ERR_SCRATCH: the call needs more scratch than kda_chunk_fwd_noalloc's static array holds";
     }
     return "KDA_ERR_?: unknown status";
 }
@@ -104,6 +108,51 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16,
                      workspace, stream};
+    return finish(kda::launch_chunk(a), stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of kda_chunk_fwd_noalloc.  In host code `scratch` names a
+// host-side stand-in, not the device array: its device address, one per GPU
+// (each GPU holds its own copy), comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is passed on.
+__device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch array (NULL on failure).
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                                 float g_min, const float* s0, void* o, float* s_final, int B, int T, int H,
+                                 int dk, int dv, int chunk, kda_dtype dt, void* stream) {
+    const kda_status st = check_chunk_args(q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, chunk, dt,
+                                           nullptr);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    const size_t need = kda::chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+    if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && !(ws = scratch_address())) return KDA_ERR_HIP;
+    kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16, ws, stream};
     return finish(kda::launch_chunk(a), stream);
 }
 

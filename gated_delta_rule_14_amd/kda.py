@@ -5,6 +5,8 @@ used for device memory (outputs, workspaces) and for the current HIP stream.
 Names follow the C ABI in include/kda.h:
 
   chunk_fwd       -> kda_chunk_fwd        chunkwise prefill
+  chunk_fwd_noalloc -> kda_chunk_fwd_noalloc  the same without a workspace,
+                     on the library's static scratch array (no allocation)
   recurrent_step  -> kda_recurrent_step   one decode token, state in place
   out_gate        -> kda_out_gate         RMSNorm x sigmoid gate (+ projection)
   gdn_chunk_fwd   -> kda_gdn_chunk_fwd       scalar-gate prefill, z (B,T,H)
@@ -89,6 +91,36 @@ def chunk_fwd(q, k, v, z, beta, g_min, s0=None, *, o=None, s_final=None, workspa
         _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(o), _p(s_final),
         B, T, H, dk, dv, CHUNK, _dt(q), _p(workspace), workspace.numel() * workspace.element_size(),
         _stream(dev)))
+    return o, s_final
+
+
+NOALLOC_SCRATCH_BYTES = 192 << 20
+
+
+def chunk_fwd_noalloc(q, k, v, z, beta, g_min, s0=None, *, o=None, s_final=None, want_state=True):
+    """chunk_fwd on the library's static scratch array (kda_chunk_fwd_noalloc):
+    no workspace is passed and the library allocates nothing.  Calls on one
+    GPU share that array and must not overlap."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    check("kda_chunk_fwd_noalloc", lib().kda_chunk_fwd_noalloc(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(o), _p(s_final),
+        B, T, H, dk, dv, CHUNK, _dt(q), _stream(dev)))
     return o, s_final
 
 

@@ -64,7 +64,9 @@ typedef enum {
     KDA_ERR_ARG = 4,          /* g_min not finite and negative, eps < 0 ...  */
     KDA_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than required     */
     KDA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned            */
-    KDA_ERR_HIP = 7           /* a HIP launch or execution error             */
+    KDA_ERR_HIP = 7,          /* a HIP launch or execution error             */
+    KDA_ERR_SCRATCH = 8       /* the call needs more scratch than the static */
+                              /* array of kda_chunk_fwd_noalloc holds         */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -132,6 +134,31 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const void
                          float* s_final, int B, int T, int H, int dk, int dv, int chunk,
                          kda_dtype dt, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * kda_chunk_fwd without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The scratch space kda_chunk_fwd takes from its workspace comes instead from
+ * one static device array of KDA_NOALLOC_SCRATCH_BYTES per GPU, which the
+ * library holds from its first use on that GPU until the process ends.
+ * Arguments and results are exactly those of kda_chunk_fwd (same kernels,
+ * bit-identical results).  A call whose kda_chunk_fwd_workspace_bytes()
+ * exceeds KDA_NOALLOC_SCRATCH_BYTES returns KDA_ERR_SCRATCH and launches
+ * nothing; 176 MiB covers the 32-head, 32768-token bf16 prefill.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap on one GPU (on different streams, or from
+ * different threads) race and must be serialised by the caller.  Nothing in
+ * the array needs to start at any value: the kernels write every slot
+ * before they read it.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+kda_status kda_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* z,
+                                 const void* beta, float g_min, const float* s0, void* o,
+                                 float* s_final, int B, int T, int H, int dk, int dv, int chunk,
+                                 kda_dtype dt, void* stream);
 
 /*
  * One decode token for every (batch, head): the fused recurrent step.

@@ -50,6 +50,9 @@ int main(void) {
           KDA_ERR_WORKSPACE);
     CHECK(kda_chunk_fwd(P, P, P, P, P, -5.f, NULL, P, PF, 0, 128, 2, 128, 128, 64, KDA_BF16, NULL, 0, NULL) ==
           KDA_OK);
+    CHECK(kda_chunk_fwd_noalloc(P, P, P, P, P, -5.f, NULL, P, PF, 1, 32768, 64, 128, 128, 64, KDA_BF16, NULL) ==
+          KDA_ERR_SCRATCH);
+    CHECK(kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, KDA_BF16) <= KDA_NOALLOC_SCRATCH_BYTES);
     CHECK(kda_recurrent_step(P, P, P, P, P, -5.f, NULL, P, 4, 2, 128, 128, KDA_BF16, NULL) == KDA_ERR_NULL);
     CHECK(kda_recurrent_step(P, P, P, P, P, -5.f, PF, P, -1, 2, 128, 128, KDA_BF16, NULL) == KDA_ERR_SHAPE);
     CHECK(kda_out_gate(P, P, -1.f, NULL, P, 2, 8, 4, 128, 0, KDA_BF16, NULL, 0, NULL) == KDA_ERR_ARG);

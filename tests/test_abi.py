@@ -17,7 +17,7 @@ from gated_delta_rule_14_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL, SHAPE, UNSUP, ARG, WS, ALIGN, HIP = range(8)
+OK, NULL, SHAPE, UNSUP, ARG, WS, ALIGN, HIP, SCRATCH = range(9)
 F32, BF16 = 0, 1
 P = ctypes.c_void_p(0x100000)      # a fake, 16-byte aligned "device" address
 MIS = ctypes.c_void_p(0x100002)    # misaligned
@@ -46,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         s = lib.kda_status_str(code).decode()
         assert s.startswith("KDA_")
     assert lib.kda_status_str(99).decode().startswith("KDA_ERR_?")
@@ -313,3 +313,28 @@ def test_plain_c_caller(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "ok"
+
+
+def test_noalloc_rejects_what_its_scratch_cannot_hold(lib):
+    """kda_chunk_fwd_noalloc checks the arguments as kda_chunk_fwd does, then
+    returns KDA_ERR_SCRATCH, before touching any device, when the call would
+    need more than the static array's KDA_NOALLOC_SCRATCH_BYTES."""
+    text = open(HEADER).read()
+    cap = int(re.search(r"KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text).group(1)) << 20
+    f = lib.kda_chunk_fwd_noalloc
+
+    def call(B, T, H, dk=128, dv=128, dt=BF16, g_min=-5.0, q=P):
+        return f(q, P, P, P, P, g_min, None, P, P, B, T, H, dk, dv, 64, dt, S)
+
+    # the 32-head 32k prefill fits; 64 heads of 32k tokens do not
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) <= cap
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 64, 128, 128, 64, BF16) > cap
+    assert call(1, 32768, 64) == SCRATCH
+    assert call(1, 1 << 20, 32) == SCRATCH
+    # argument errors come first, as for kda_chunk_fwd
+    assert call(1, 32768, 64, q=None) == NULL
+    assert call(1, 32768, 64, q=MIS) == ALIGN
+    assert call(1, 32768, 64, g_min=0.0) == ARG
+    assert call(1, 32768, 64, dk=96) == UNSUP
+    assert call(-1, 32768, 64) == SHAPE
+    assert call(0, 32768, 64) == OK
