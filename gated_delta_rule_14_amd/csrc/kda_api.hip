@@ -237,10 +237,10 @@ kda_status kda_gdn_recurrent_step(const void* q, const void* k, const void* v, c
 
 size_t kda_recurrent_layer_step_workspace_bytes(int B, int H, int dv, int d_model, kda_dtype dt,
                                                 int with_projection) {
-    (void)d_model; (void)dt;
-    if (B < 0 || H < 0 || !dim_ok(dv) || !with_projection) return 0;
-    // the gated row in bf16, 256-byte aligned, then the GEMM library's scratch
-    return ((size_t)B * H * dv * 2 + 255) / 256 * 256 + kda::projection_scratch_bytes();
+    (void)dt;
+    if (B < 0 || H < 0 || d_model < 0 || !dim_ok(dv) || !with_projection) return 0;
+    // the gated row in bf16, 256-byte aligned, then the GEMM's scratch
+    return ((size_t)B * H * dv * 2 + 255) / 256 * 256 + kda::projection_scratch_bytes(B, d_model, H * dv);
 }
 
 kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v, const void* z, const void* beta,
@@ -337,7 +337,7 @@ kda_status kda_chunk_layer_fwd(const void* q, const void* k, const void* v, cons
         a.y = w ? gate_ws : y;
         err = kda::launch_chunk(a);
         if (err == hipSuccess && w) {
-            const size_t ybytes = ws.gate - kda::projection_scratch_bytes();
+            const size_t ybytes = ws.gate - kda::projection_scratch_bytes(B * T, d_model, H * dv);
             err = kda::launch_projection(gate_ws, w, y, B * T, d_model, H * dv, (unsigned char*)gate_ws + ybytes,
                                          stream);
         }

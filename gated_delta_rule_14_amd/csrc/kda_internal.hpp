@@ -78,10 +78,12 @@ struct GateArgs {
 };
 size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj);
 hipError_t launch_out_gate(const GateArgs& a);
-// out (M x N, bf16) = y (M x K, bf16) . w (N x K, bf16)^T; lt_ws is the
-// GEMM library's scratch (projection_scratch_bytes() bytes)
-size_t projection_scratch_bytes();
-hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* lt_ws,
+// out (M x N, bf16) = y (M x K, bf16) . w (N x K, bf16)^T (gemm.hip); N a
+// multiple of 16, K of 64; scratch holds projection_scratch_bytes(M, N, K)
+// bytes (fp32 partial tiles of a split K range for small M, else none)
+size_t projection_scratch_bytes(int M, int N, int K);
+bool gemm_small_m(int M);
+hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* scratch,
                              void* stream);
 
 // Gradients of the recurrence (bwd.hip): token-sequential, one workgroup

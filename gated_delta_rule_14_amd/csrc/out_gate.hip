@@ -8,21 +8,8 @@
 //
 //  * gate_kernel: one row of d_v values per 1..2 dozen lanes, 16-byte loads,
 //    shuffle reduction of the sum of squares; HBM-bound elementwise work.
-//  * the projection out (M x N) = y (M x K) . W (N x K)^T is a plain bf16
-//    GEMM with fp32 accumulation: it runs on hipBLASLt (one library handle per
-//    device, one heuristic query per shape, both cached), with a library
-//    workspace appended to the y buffer.  When the library offers no
-//    algorithm for a shape, proj_gemm_kernel below computes it.
-//  * proj_gemm_kernel: out (M x N) = y (M x K) . W (N x K)^T in bf16 with
-//    fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Both operands are
-//    K-contiguous, which is the native operand layout of the MFMA, so tiles
-//    go global -> registers -> LDS without any transpose.  128x128 block
-//    tile, 64-deep K stages, double-buffered LDS, 4 waves of 64x64.
-#include <hipblaslt/hipblaslt.h>
-
-#include <mutex>
-#include <deque>
-
+//  * the projection is libkda's own GEMM (gemm.hip) on the gated rows, which
+//    the gate kernel writes in bf16 to the workspace.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -74,83 +61,6 @@ __global__ __launch_bounds__(256) void gate_kernel(const E* __restrict__ o, cons
     }
 }
 
-// ---------------------------------------------------------------------------
-// Projection GEMM: out[m][n] = sum_k y[m][k] * w[n][k]
-// ---------------------------------------------------------------------------
-constexpr int GBM = 128, GBN = 128, GBK = 64, GLD = GBK + 8;
-
-__device__ __forceinline__ void gemm_gload(u32x4 (&ra)[4], u32x4 (&rb)[4], const bf16* __restrict__ A,
-                                           const bf16* __restrict__ Bw, int M, int N, int K, int m0, int n0,
-                                           int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int v = threadIdx.x + i * 256, r = v >> 3, cv = v & 7;
-        const int am = min(m0 + r, M - 1), bn = min(n0 + r, N - 1);
-        ra[i] = *reinterpret_cast<const u32x4*>(A + (size_t)am * K + k0 + cv * 8);
-        rb[i] = *reinterpret_cast<const u32x4*>(Bw + (size_t)bn * K + k0 + cv * 8);
-    }
-}
-
-__device__ __forceinline__ void gemm_sstore(const u32x4 (&ra)[4], const u32x4 (&rb)[4], bf16* As, bf16* Bs) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int v = threadIdx.x + i * 256, r = v >> 3, cv = v & 7;
-        *reinterpret_cast<u32x4*>(&As[r * GLD + cv * 8]) = ra[i];
-        *reinterpret_cast<u32x4*>(&Bs[r * GLD + cv * 8]) = rb[i];
-    }
-}
-
-__global__ __launch_bounds__(256) void proj_gemm_kernel(const bf16* __restrict__ A, const bf16* __restrict__ Bw,
-                                                        bf16* __restrict__ out, int M, int N, int K) {
-    __shared__ __align__(16) bf16 As[2][GBM * GLD];
-    __shared__ __align__(16) bf16 Bs[2][GBN * GLD];
-    const int tid = threadIdx.x, w = wave_id();
-    const int wm = w >> 1, wn = w & 1;                  // 2 x 2 waves of 64 x 64
-    const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * GBN;
-
-    u32x4 ra[4], rb[4];   // global -> register staging, 4 x 8 bf16 per operand per thread
-
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-    const int nk = K / GBK;
-    gemm_gload(ra, rb, A, Bw, M, N, K, m0, n0, 0);
-    gemm_sstore(ra, rb, As[0], Bs[0]);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gemm_gload(ra, rb, A, Bw, M, N, K, m0, n0, (kt + 1) * GBK);
-#pragma unroll
-        for (int ks = 0; ks < GBK; ks += 32) {
-            bf16x8 fa[4], fb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) fa[i] = load_frag<bf16>(As[buf], GLD, wm * 64 + i * 16, ks);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) fb[j] = load_frag<bf16>(Bs[buf], GLD, wn * 64 + j * 16, ks);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<bf16>::mma(fa[i], fb[j], acc[i][j]);
-        }
-        if (kt + 1 < nk) gemm_sstore(ra, rb, As[buf ^ 1], Bs[buf ^ 1]);
-        __syncthreads();
-    }
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = m0 + wm * 64 + i * 16 + acc_row(e);
-                const int n = n0 + wn * 64 + j * 16 + acc_col();
-                if (m < M && n < N) out[(size_t)m * N + n] = (bf16)acc[i][j][e];
-            }
-}
-
 template <class E>
 static hipError_t launch_gate(const void* o, const void* gate, float eps, void* y, size_t rows, int dv,
                               hipStream_t st) {
@@ -169,97 +79,13 @@ static hipError_t launch_gate(const void* o, const void* gate, float eps, void* 
     return hipGetLastError();
 }
 
-// Library workspace for the projection GEMM, after the y buffer.
-constexpr size_t LT_WS = (size_t)32 << 20;
-
 static size_t y_bytes(int B, int T, int H, int dv) { return ((size_t)B * T * H * dv * 2 + 255) / 256 * 256; }
 
 size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj) {
-    (void)d_model; (void)bf16;
+    (void)bf16;
     if (!proj) return 0;
-    return y_bytes(B, T, H, dv) + LT_WS;   // gated activations y (bf16), then the GEMM's workspace
-}
-
-namespace {
-// One hipBLASLt handle per device and the chosen algorithm per (device, M,
-// N, K), created on first use.  Column-major view: out^T (N x M) =
-// W (stored K x N, transposed) . y^T (stored K x M).
-struct LtPlan {
-    int dev, M, N, K;
-    bool ok;
-    hipblasLtMatmulDesc_t op;
-    hipblasLtMatrixLayout_t a, b, c;
-    hipblasLtMatmulAlgo_t algo;
-    size_t ws;
-};
-struct LtState {
-    std::mutex mu;
-    hipblasLtHandle_t handle[64] = {};
-    std::deque<LtPlan> plans;   // push_back keeps references to earlier plans valid
-};
-LtState& lt_state() {
-    static LtState s;
-    return s;
-}
-
-const LtPlan* lt_plan(int dev, int M, int N, int K) {
-    LtState& s = lt_state();
-    std::lock_guard<std::mutex> lock(s.mu);
-    for (const LtPlan& p : s.plans)
-        if (p.dev == dev && p.M == M && p.N == N && p.K == K) return p.ok ? &p : nullptr;
-    LtPlan p{dev, M, N, K, false, nullptr, nullptr, nullptr, nullptr, {}, 0};
-    if (dev < 0 || dev >= 64) return nullptr;
-    if (!s.handle[dev] && hipblasLtCreate(&s.handle[dev]) != HIPBLAS_STATUS_SUCCESS) s.handle[dev] = nullptr;
-    hipblasLtHandle_t h = s.handle[dev];
-    const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
-    const uint64_t wsmax = LT_WS;
-    hipblasLtMatmulPreference_t pref = nullptr;
-    hipblasLtMatmulHeuristicResult_t res{};
-    int count = 0;
-    bool ok = h && hipblasLtMatmulDescCreate(&p.op, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof(ta)) ==
-                  HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatmulDescSetAttribute(p.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof(tb)) ==
-                  HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, K, N, K) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, K, M, K) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatrixLayoutCreate(&p.c, HIP_R_16BF, N, M, N) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatmulPreferenceCreate(&pref) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsmax,
-                                                    sizeof(wsmax)) == HIPBLAS_STATUS_SUCCESS &&
-              hipblasLtMatmulAlgoGetHeuristic(h, p.op, p.a, p.b, p.c, p.c, pref, 1, &res, &count) ==
-                  HIPBLAS_STATUS_SUCCESS &&
-              count > 0 && res.workspaceSize <= LT_WS;
-    if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-    if (ok) {
-        p.algo = res.algo;
-        p.ws = res.workspaceSize;
-    }
-    p.ok = ok;
-    s.plans.push_back(p);
-    return ok ? &s.plans.back() : nullptr;
-}
-}  // namespace
-
-size_t projection_scratch_bytes() { return LT_WS; }
-
-hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* lt_ws,
-                             void* stream) {
-    hipStream_t st = (hipStream_t)stream;
-    if (M == 0) return hipSuccess;
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    if (const LtPlan* p = lt_plan(dev, M, N, K)) {
-        const float one = 1.f, zero = 0.f;
-        const hipblasStatus_t r = hipblasLtMatmul(lt_state().handle[dev], p->op, &one, w, p->a, y, p->b, &zero, out,
-                                                  p->c, out, p->c, &p->algo, lt_ws, p->ws, st);
-        return r == HIPBLAS_STATUS_SUCCESS ? hipGetLastError() : hipErrorLaunchFailure;
-    }
-    dim3 grid((N + GBN - 1) / GBN, (M + GBM - 1) / GBM);
-    hipLaunchKernelGGL(proj_gemm_kernel, grid, dim3(256), 0, st, (const bf16*)y, (const bf16*)w, (bf16*)out, M, N,
-                       K);
-    return hipGetLastError();
+    // gated activations y (bf16), then the GEMM's scratch
+    return y_bytes(B, T, H, dv) + projection_scratch_bytes(B * T, d_model, H * dv);
 }
 
 hipError_t launch_out_gate(const GateArgs& a) {

@@ -38,14 +38,10 @@
  *  - Not checked on the device: beta in [0, 1] and finite inputs (the
  *    "KDA Recurrence" constraints).  g_min must be finite and < 0.
  *  - The library keeps no state between calls and is re-entrant; calls on
- *    different streams may run concurrently if their buffers are disjoint.
- *    The one cache is the projection's: per device a hipBLASLt handle and,
- *    per GEMM shape, the chosen algorithm, created by that shape's first
- *    call.
+ *    different streams may run concurrently if their buffers are disjoint
+ *    (kda_chunk_fwd_noalloc excepted: it shares one scratch array per GPU).
  *  - Calls may be captured into a HIP graph (they allocate nothing, record
- *    no memset and never synchronise, unless KDA_DEBUG_SYNC=1).  A call
- *    with a projection must have run once outside capture for its shape,
- *    so that the GEMM plan exists before capture.
+ *    no memset and never synchronise, unless KDA_DEBUG_SYNC=1).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -194,8 +190,10 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  *   workspace kda_out_gate_workspace_bytes() bytes (0 when w is NULL): the
  *             gated activations y and the projection GEMM's scratch
  * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.  The
- * projection runs on hipBLASLt (bf16 inputs, fp32 accumulation); a shape the
- * library has no algorithm for runs on libkda's own GEMM kernel.
+ * projection is libkda's own GEMM (bf16 MFMA, fp32 accumulation, output
+ * rounded to bf16); for up to 1024 rows with d_model a multiple of 128 it
+ * splits the K range in four and adds the fp32 partials in a fixed order,
+ * using M * d_model * 16 bytes of the workspace.
  */
 size_t kda_out_gate_workspace_bytes(int B, int T, int H, int dv, int d_model, kda_dtype dt,
                                     int with_projection);
@@ -210,7 +208,7 @@ kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* 
  * square root, times sigmoid(gate), heads concatenated, then y W^T when w
  * is given).  The normalisation and gate run in the recurrence step's own
  * launch, on the fp32 read-out before any rounding; the projection, when
- * asked for, is a second launch (hipBLASLt, as in kda_out_gate).
+ * asked for, is a second launch (libkda's GEMM, as in kda_out_gate).
  *
  *   q, k, z   (B, H, dk)  dtype dt
  *   v, gate   (B, H, dv)  dtype dt
@@ -223,7 +221,7 @@ kda_status kda_out_gate(const void* o, const void* gate, float eps, const void* 
  *   y         (B, H*dv) dtype dt when w is NULL, (B, d_model) dtype dt
  *             otherwise (written)
  *   workspace kda_recurrent_layer_step_workspace_bytes() bytes (0 when w is
- *             NULL): the gated row in bf16 and the projection's scratch
+ *             NULL): the gated rows in bf16 and the projection's scratch
  * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.
  * Every other rule is that of kda_recurrent_step and kda_out_gate.
  */

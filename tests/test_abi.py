@@ -78,8 +78,10 @@ def test_workspace_sizes(lib):
     assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, F32) == 32 * 512 * per + seg32
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 96, 64, 64, F32) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 32, F32) == 0
-    # gated activations y (bf16), then 32 MiB for the projection GEMM's library workspace
-    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2 + (32 << 20)
+    # gated activations y (bf16); a large M needs no GEMM scratch
+    assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2
+    # a small M splits K in four: fp32 partial tiles after the rows
+    assert lib.kda_out_gate_workspace_bytes(1, 256, 32, 128, 2304, BF16, 1) == 256 * 4096 * 2 + 4 * 256 * 2304 * 4
     assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 0, BF16, 0) == 0
 
 
@@ -160,9 +162,11 @@ def lstep(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, state=P, g=P, eps=1e-6, w
 
 
 def test_recurrent_layer_step_workspace_and_bad_arguments(lib):
-    # the gated row in bf16 (256-byte aligned), then the projection GEMM's 32 MiB
-    assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 2304, BF16, 1) == 256 * 32 * 128 * 2 + (32 << 20)
-    assert lib.kda_recurrent_layer_step_workspace_bytes(3, 1, 64, 16, BF16, 1) == 512 + (32 << 20)
+    # the gated row in bf16 (256-byte aligned), then the GEMM's fp32 partial
+    # tiles of its four K splits (d_model a multiple of 128; none otherwise)
+    assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 2304, BF16, 1) == \
+        256 * 32 * 128 * 2 + 4 * 256 * 2304 * 4
+    assert lib.kda_recurrent_layer_step_workspace_bytes(3, 1, 64, 16, BF16, 1) == 512
     assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 0, BF16, 0) == 0
     assert lstep(lib, g=None) == NULL
     assert lstep(lib, y=None) == NULL
@@ -221,17 +225,17 @@ def test_scalar_gate_calls_workspace_and_bad_arguments(lib):
 def test_chunk_layer_fwd_workspace_and_bad_arguments(lib):
     # bf16, d_k = d_v = 128 and a segmented plan (32 chains of 512 chunks)
     # fuse the epilogue into the prefill kernels: the prefill's workspace,
-    # then (with a projection) the gated rows in bf16 and the GEMM's 32 MiB
+    # then (with a projection) the gated rows in bf16
     kda_ws = lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16)
     assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 0, BF16, 0) == \
         (kda_ws + 255) // 256 * 256
     assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, 2304, BF16, 1) == \
-        (kda_ws + 255) // 256 * 256 + 32768 * 4096 * 2 + (32 << 20)
+        (kda_ws + 255) // 256 * 256 + 32768 * 4096 * 2
     # one pass (256 chains) and other sizes run the two calls' kernels, with
     # room for o in between
     assert lib.kda_chunk_layer_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, 0, BF16, 0) == 8 * 8192 * 4096 * 2
     assert lib.kda_chunk_layer_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, 2304, BF16, 1) == \
-        2 * 8 * 8192 * 4096 * 2 + (32 << 20)
+        2 * 8 * 8192 * 4096 * 2
     f32_ws = lib.kda_chunk_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, F32)
     assert lib.kda_chunk_layer_fwd_workspace_bytes(1, 256, 1, 64, 64, 64, 0, F32, 0) == \
         (f32_ws + 255) // 256 * 256 + 256 * 64 * 4

@@ -101,3 +101,61 @@ def test_train_8x8k_layer_sampled():
     e_s = rel(f64(res["final_state"])[b:b + 1], rs)
     print(f"train_8x8k layer (batch {b}, 32 rows): outputs {e_out:.2e} final_state {e_s:.2e}")
     assert e_out < 2e-2 and e_s < 1e-2
+
+
+# ------------------------------------------------------------------ projection GEMM
+def _gemm_case(B, T, H, dv, dm, seed, rows=None):
+    """kda_out_gate with the projection against numpy fp64 on the exact bf16
+    gated rows kda_out_gate returns without it: isolates libkda's GEMM (fp32
+    accumulation, output rounded to bf16).  rows: sampled row indices of the
+    B*T rows (all rows when None).  Returns the relative error and the worst
+    row's error against the matrix's average row."""
+    o, gate = synth(B, T, H, dv, torch.bfloat16, seed)
+    w = ki.projection(dm, H * dv, seed=seed, device=DEV)
+    y = kda.out_gate(o, gate, ki.EPS)                  # (B, T, H*dv) bf16, no projection
+    out = kda.out_gate(o, gate, ki.EPS, w)             # (B, T, dm)
+    torch.cuda.synchronize()
+    M = B * T
+    yr = f64(y).reshape(M, H * dv)
+    got = f64(out).reshape(M, dm)
+    if rows is not None:
+        yr, got = yr[rows], got[rows]
+    ref = yr @ f64(w).T
+    e = rel(got, ref)
+    d = np.sqrt(((got - ref) ** 2).sum(axis=1))
+    ew = float(d.max() / max(np.sqrt((ref ** 2).sum(axis=1)).mean(), 1e-300))
+    return e, ew
+
+
+@pytest.mark.parametrize("B,T,H,dv,dm", [
+    (1, 1000, 8, 128, 512),      # 256 x 256 tiles, ragged last M tile
+    (1, 1283, 4, 128, 384),      # 128 x 128 tiles (N a multiple of 128 only), ragged M
+    (2, 1500, 2, 64, 272),       # 64 x 16 tiles (N = 17 * 16), ragged M
+    (1, 256, 32, 128, 2304),     # decode batch: K split in four, fp32 partials summed in order
+    (1, 1024, 32, 128, 2304),    # the largest split-K M
+    (1, 1025, 32, 128, 2304),    # the smallest whole-K M with ragged tiles
+    (1, 3, 1, 64, 16),           # K = 64 (one stage), tiny M and N
+])
+def test_projection_gemm_shapes(B, T, H, dv, dm):
+    e, ew = _gemm_case(B, T, H, dv, dm, seed=T + dm)
+    print(f"projection GEMM M={B * T} K={H * dv} N={dm}: rel {e:.2e} worst row {ew:.2e}")
+    assert e < 5e-3 and ew < 1e-2
+
+
+def test_projection_gemm_full_training_shape():
+    """M = 65,536 (8 x 8192), K = 4096, N = 2304: the training-shape
+    projection at full size; 2048 rows sampled across all 256 M tiles."""
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(8 * 8192, 2048, replace=False))
+    e, ew = _gemm_case(8, 8192, 32, 128, 2304, seed=9, rows=rows)
+    print(f"projection GEMM 65536 x 4096 -> 2304 (2048 rows): rel {e:.2e} worst row {ew:.2e}")
+    assert e < 5e-3 and ew < 1e-2
+
+
+def test_projection_gemm_deterministic():
+    o, gate = synth(1, 300, 32, 128, torch.bfloat16, 11)
+    w = ki.projection(2304, 4096, seed=11, device=DEV)
+    a = kda.out_gate(o, gate, ki.EPS, w)
+    b = kda.out_gate(o, gate, ki.EPS, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
