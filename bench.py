@@ -197,8 +197,8 @@ def bench_decode_layer(torch, kda, ki, state, steps, B, H, dv, d_model=2304):
     t_u = _time_calls(torch, unfused, 1) / n
     return {"d_model": d_model, "steps": n, "us_per_step_fused": round(t_f * 1e6, 1),
             "us_per_step_unfused": round(t_u * 1e6, 1),
-            "kernels": "fused: decode_step_kernel with the gate epilogue + hipBLASLt GEMM; "
-                       "unfused: decode_step_kernel + gate_kernel + hipBLASLt GEMM"}
+            "kernels": "fused: decode_step_kernel with the gate epilogue + split-K proj_gemm_kernel<64,128> "
+                       "+ split_sum_kernel; unfused: decode_step_kernel + gate_kernel + the same GEMM"}
 
 
 def bench_epilogue(torch, kda, ki, steps=5):
@@ -228,11 +228,22 @@ def bench_epilogue(torch, kda, ki, steps=5):
     per = a.elapsed_time(b) * 1e-3 / steps
     flop = 2.0 * B * T * H * dv * dm
     tf = flop / per / 1e12
+    # the gate kernel alone (no projection), and a vendor GEMM on the same
+    # gated rows for comparison (torch's F.linear: y W^T on hipBLASLt); the
+    # comparison is context only, nothing of libkda runs on it
+    yg = torch.empty((B, T, H * dv), dtype=torch.bfloat16, device=dev)
+    t_gate = _time_calls(torch, lambda: kda.out_gate(o, gate, ki.EPS, y=yg), steps)
+    y2 = yg.view(B * T, H * dv)
+    t_vendor = _time_calls(torch, lambda: torch.nn.functional.linear(y2, w), steps)
+    t_gemm = per - t_gate
     return {"workload": "train_8x8k epilogue", "M": B * T, "K": H * dv, "N": dm, "us_per_call": round(per * 1e6, 1),
             "value": round(B * T / per, 1), "unit": "tokens/s",
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "gate_kernel + hipBLASLt bf16 GEMM (projection FLOP only)"}}
+                         "kernel": "gate_kernel + proj_gemm_kernel<256,256> (projection FLOP only)"},
+            "gate_us": round(t_gate * 1e6, 1), "gemm_us": round(t_gemm * 1e6, 1),
+            "gemm_tflops": round(flop / t_gemm / 1e12, 1), "gemm_frac": round(flop / t_gemm / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "vendor_gemm_us_for_comparison": round(t_vendor * 1e6, 1)}
 
 
 def _time_calls(torch, fn, calls, warmup=1):
@@ -335,7 +346,7 @@ def bench_train_layer(torch, kda, ki, calls=5):
     return {"workload": "train_8x8k layer", "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "d_model": dm,
             "dtype": "bf16", "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1),
             "unit": "tokens/s", "us_per_call_two_calls": round(per2 * 1e6, 1),
-            "kernels": "kda_chunk_layer_fwd (epilogue in the prefill kernels, then the hipBLASLt projection)"}
+            "kernels": "kda_chunk_layer_fwd (epilogue in the prefill kernels, then libkda's projection GEMM)"}
 
 
 def bench_backward(torch, kda, ki, calls=2):
@@ -394,12 +405,18 @@ def bench_gdn_prefill(torch, kda, ki, calls=10):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
 
 
-def measured_ceilings(torch):
-    """Rates this GPU reaches on plain torch kernels: in-place fp32 scale over
-    512 MiB (read + write), a 512 MiB device copy, a bf16 8192^3 matmul."""
+def measured_ceilings(torch, kda):
+    """Rates this GPU reaches: libkda's streaming read-modify-write kernel
+    (kda_stream_scale: in-place fp32 scale over 512 MiB, the decode state's
+    access pattern; every variant, the best kept), the same through torch's
+    x.mul_, a 512 MiB device copy, and a bf16 8192^3 matmul."""
     dev = torch.device("cuda:0")
     n = 128 * 1024 * 1024
     x = torch.ones(n, dtype=torch.float32, device=dev)
+    best = (0.0, None)
+    for var in [u | (nt << 2) | (w << 3) for u in range(4) for nt in (0, 1) for w in (0, 8)]:
+        t = _time_calls(torch, lambda: kda.stream_scale(x, 0.999999, var), 10, warmup=3)
+        best = max(best, (2 * n * 4 / t / 1e9, var))
     t_rmw = _time_calls(torch, lambda: x.mul_(0.999999), 10, warmup=3)
     d = torch.empty_like(x)
     t_copy = _time_calls(torch, lambda: d.copy_(x), 10, warmup=3)
@@ -410,10 +427,14 @@ def measured_ceilings(torch):
     t_mm = _time_calls(torch, lambda: torch.matmul(a, b), 10, warmup=3)
     del a, b
     torch.cuda.empty_cache()
-    return {"hbm_rmw_gbs": round(2 * n * 4 / t_rmw / 1e9, 1), "hbm_copy_gbs": round(2 * n * 4 / t_copy / 1e9, 1),
+    v = best[1]
+    return {"hbm_rmw_hip_gbs": round(best[0], 1),
+            "hbm_rmw_hip_variant": {"float4_per_thread": 1 << (v & 3), "nontemporal": bool(v & 4),
+                                    "waves_per_cu": (v >> 3) or "one pass"},
+            "hbm_rmw_gbs": round(2 * n * 4 / t_rmw / 1e9, 1), "hbm_copy_gbs": round(2 * n * 4 / t_copy / 1e9, 1),
             "mfma_bf16_tflops": round(2 * m ** 3 / t_mm / 1e12, 1),
-            "how": "torch x.mul_ in place (512 MiB fp32), torch copy_ (512 MiB), torch.matmul bf16 8192^3; "
-                   "HIP events, mean of 10 after 3 warm-up calls"}
+            "how": "kda_stream_scale (HIP, 16 variants, best kept) and torch x.mul_ in place over 512 MiB fp32, "
+                   "torch copy_ (512 MiB), torch.matmul bf16 8192^3; HIP events, mean of 10 after 3 warm-up calls"}
 
 
 def copy_only(torch):
@@ -616,12 +637,14 @@ def main():
     if not args.no_workloads:
         line["backward"] = bench_backward(torch, kda, ki)
     if not args.no_ceilings:
-        c = measured_ceilings(torch)
+        c = measured_ceilings(torch, kda)
         line["ceilings"] = c
         line["roofline"]["frac_of_measured_copy"] = round(gbs / c["hbm_copy_gbs"], 4)
         if "decode" in line:
             line["decode"]["roofline"]["frac_of_measured_rmw"] = round(
                 line["decode"]["roofline"]["achieved"] / c["hbm_rmw_gbs"], 4)
+            line["decode"]["roofline"]["frac_of_hip_rmw_ceiling"] = round(
+                line["decode"]["roofline"]["achieved"] / c["hbm_rmw_hip_gbs"], 4)
         if "epilogue" in line:
             line["epilogue"]["roofline"]["frac_of_measured_matmul"] = round(
                 line["epilogue"]["roofline"]["achieved"] / c["mfma_bf16_tflops"], 4)

@@ -356,6 +356,16 @@ def recurrent_bwd(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final=None, *, wan
     return out
 
 
+def stream_scale(x, s, variant=6):
+    """x <- s * x in place (fp32, 16-byte accesses): the read-modify-write
+    rate of the GPU's HBM, the ceiling of the decode step (kda_stream_scale)."""
+    _need(x, "x", x.device)
+    if x.dtype != torch.float32:
+        raise TypeError("libkda: stream_scale takes float32")
+    check("kda_stream_scale", lib().kda_stream_scale(_p(x), x.numel(), float(s), int(variant), _stream(x.device)))
+    return x
+
+
 def layer(query, key, value, decay_logits, write_strength, output_gate_logits,
           output_projection, initial_state, g_min, eps):
     """The KDA layer of the "KDA Recurrence" problem: recurrence (chunkwise),

@@ -328,6 +328,17 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
                              int dk, int dv, kda_dtype dt, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * Measurement helper: x <- s * x in place over n fp32 values (n a multiple
+ * of 4, x 16-byte aligned), every byte read once and written once with
+ * 16-byte accesses -- the access pattern of the decode step's state.  It
+ * gives the read-modify-write rate the GPU's HBM sustains, against which
+ * kda_recurrent_step is measured.  variant: bits 0-1 pick 1, 2, 4 or 8 float4
+ * in flight per thread, bit 2 non-temporal accesses, bits 3 and up the waves
+ * per compute unit of a grid-stride launch (0: one workgroup per slice).
+ */
+kda_status kda_stream_scale(float* x, size_t n, float s, int variant, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
