@@ -383,4 +383,28 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
     return finish(kda::launch_bwd(a), stream);
 }
 
+kda_status kda_dplr_fwd(const void* q, const void* k, const void* v, const void* z, const void* a, const void* b,
+                        float g_min, const float* s0, void* o, float* s_final, int B, int T, int H, int dk, int dv,
+                        kda_dtype dt, void* stream) {
+    // the prefill's checks, with a in beta's place, then those of b
+    const kda_status st = check_chunk_args(q, k, v, z, a, g_min, s0, o, s_final, B, T, H, dk, dv, 64, dt, nullptr);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (T > 0 && !b) return KDA_ERR_NULL;
+    if (!aligned16(b)) return KDA_ERR_ALIGN;
+    if (T == 0 && !s_final) return KDA_OK;
+    kda::DplrArgs x{q, k, v, z, a, b, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16, false, stream};
+    return finish(kda::launch_dplr(x), stream);
+}
+
+kda_status kda_dplr_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* a,
+                                   const void* b, float g_min, float* state, void* o, int B, int H, int dk, int dv,
+                                   kda_dtype dt, void* stream) {
+    const kda_status st = check_step_args(q, k, v, z, a, g_min, state, B, H, dk, dv, dt);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (!b || !o) return KDA_ERR_NULL;
+    if (!aligned16(b) || !aligned16(o)) return KDA_ERR_ALIGN;
+    kda::DplrArgs x{q, k, v, z, a, b, g_min, nullptr, o, state, B, 1, H, dk, dv, dt == KDA_BF16, true, stream};
+    return finish(kda::launch_dplr(x), stream);
+}
+
 }  // extern "C"

@@ -26,6 +26,20 @@ struct DecodeArgs {
     bool z_scalar = false;
 };
 hipError_t launch_decode(const DecodeArgs& a);
+
+// The DPLR recurrence: the whole sequence (step false) or one token on a
+// state held in HBM (step true: s_final is that state, T unused).
+struct DplrArgs {
+    const void *q, *k, *v, *z, *a, *b;
+    float g_min;
+    const float* s0;
+    void* o;
+    float* s_final;
+    int B, T, H, dk, dv;
+    bool bf16, step;
+    void* stream;
+};
+hipError_t launch_dplr(const DplrArgs& x);
 // zfull (rows x dk) = each of the rows scalar logits zs repeated dk times
 hipError_t launch_broadcast_gate(const void* zs, void* zfull, size_t rows, int dk, bool bf16, void* stream);
 

@@ -19,6 +19,11 @@ Names follow the C ABI in include/kda.h:
                      kernels, then the projection)
   recurrent_bwd   -> kda_recurrent_bwd: gradients of the recurrence with
                      respect to q, k, v, z, beta and s0 (fp32)
+  dplr_fwd        -> kda_dplr_fwd: the general diagonal-plus-low-rank
+                     recurrence S = (Diag(alpha) - a b^T) S + k v^T over a
+                     sequence (token-sequential)
+  dplr_recurrent_step -> kda_dplr_recurrent_step: one DPLR token, state
+                     in place
   layer           -> kda_chunk_layer_fwd, returning the
                      {"outputs", "final_state"} dictionary of the
                      "KDA Recurrence" problem (final_state kept in fp32)
@@ -354,6 +359,59 @@ def recurrent_bwd(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final=None, *, wan
         _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dz"]), _p(out["dbeta"]), _p(out["ds0"]),
         B, T, H, dk, dv, _dt(q), _p(workspace), ws_bytes, _stream(dev)))
     return out
+
+
+def dplr_fwd(q, k, v, z, a, b, g_min, s0=None, *, o=None, s_final=None, want_state=True):
+    """DPLR recurrence over a sequence. q, k, z, a, b: (B,T,H,dk); v: (B,T,H,dv);
+    s0: (B,H,dk,dv) fp32 or None.  Returns (o, s_final), s_final fp32 (None
+    when want_state is False)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("a", a), ("b", b)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("k", k), ("z", z), ("a", a), ("b", b)):
+        if tuple(t.shape) != (B, T, H, dk):
+            raise ValueError(f"libkda: {name} must be {(B, T, H, dk)}, got {tuple(t.shape)}")
+    if tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"libkda: v must be (B, T, H, dv), got {tuple(v.shape)}")
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    check("kda_dplr_fwd", lib().kda_dplr_fwd(
+        _p(q), _p(k), _p(v), _p(z), _p(a), _p(b), float(g_min), _p(s0), _p(o), _p(s_final),
+        B, T, H, dk, dv, _dt(q), _stream(dev)))
+    return o, s_final
+
+
+def dplr_recurrent_step(q, k, v, z, a, b, g_min, state, *, o=None):
+    """One DPLR token. q, k, z, a, b: (B,H,dk); v: (B,H,dv); state (B,H,dk,dv)
+    fp32, updated in place.  Returns o (B,H,dv)."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("a", a), ("b", b), ("state", state)):
+        _need(t, name, dev)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("k", k), ("z", z), ("a", a), ("b", b)):
+        if tuple(t.shape) != (B, H, dk):
+            raise ValueError(f"libkda: {name} must be {(B, H, dk)}, got {tuple(t.shape)}")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, dk, dv):
+        raise TypeError("libkda: state must be float32 (B, H, dk, dv)")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=q.dtype, device=dev)
+    check("kda_dplr_recurrent_step", lib().kda_dplr_recurrent_step(
+        _p(q), _p(k), _p(v), _p(z), _p(a), _p(b), float(g_min), _p(state), _p(o),
+        B, H, dk, dv, _dt(q), _stream(dev)))
+    return o
 
 
 def stream_scale(x, s, variant=6):

@@ -329,6 +329,40 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
                              void* stream);
 
 /*
+ * The general diagonal-plus-low-rank (DPLR) recurrence ("Diagonal-Plus-Low-
+ * Rank Matrices and Kimi Delta Attention", sections 1 and 3):
+ *
+ *   S_t = (Diag(alpha_t) - a_t b_t^T) S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,
+ *
+ * with two independent directions a_t and b_t, the decay alpha_t =
+ * exp(g_min * sigmoid(z_t)) of "KDA Recurrence", and the output read from
+ * the updated state.  Section 3's binding a_t = beta_t k_t, b_t = k_t *
+ * alpha_t with the write key beta_t k_t gives KDA (kda_chunk_fwd).
+ *
+ *   q, k, z, a, b   (B, T, H, dk)  dtype dt      (no T for the step)
+ *   v               (B, T, H, dv)  dtype dt
+ *   g_min           < 0, finite
+ *   s0              (B, H, dk, dv) fp32, or NULL for zeros
+ *   o               (B, T, H, dv)  dtype dt (written)
+ *   s_final         (B, H, dk, dv) fp32 (written), or NULL to skip
+ *   state           (B, H, dk, dv) fp32, read and updated IN PLACE (step)
+ * Per token, c = S_{t-1}^T b_t is read from the state before the update,
+ * S_t = Diag(alpha) S_{t-1} - a c^T + k v^T and o = (Diag(alpha)
+ * S_{t-1})^T q - (a . q) c + (k . q) v; all arithmetic in fp32.
+ * kda_dplr_fwd is token-sequential, one workgroup per (batch, head) with
+ * the state in registers; it needs no workspace, and T may be 0 (then
+ * s_final = s0).  kda_dplr_recurrent_step reads the state once and writes it
+ * once.  dk, dv in {64, 128}; every pointer 16-byte aligned; B, H at most
+ * 65535 for kda_dplr_fwd; other errors as for kda_chunk_fwd.
+ */
+kda_status kda_dplr_fwd(const void* q, const void* k, const void* v, const void* z, const void* a,
+                        const void* b, float g_min, const float* s0, void* o, float* s_final,
+                        int B, int T, int H, int dk, int dv, kda_dtype dt, void* stream);
+kda_status kda_dplr_recurrent_step(const void* q, const void* k, const void* v, const void* z,
+                                   const void* a, const void* b, float g_min, float* state, void* o,
+                                   int B, int H, int dk, int dv, kda_dtype dt, void* stream);
+
+/*
  * Measurement helper: x <- s * x in place over n fp32 values (n a multiple
  * of 4, x 16-byte aligned), every byte read once and written once with
  * 16-byte accesses -- the access pattern of the decode step's state.  It

@@ -20,6 +20,7 @@ d_k = d_v = 128, 64-token chunks):
 
 Generators: q, k ~ N(0,1), L2-normalised over d_k per (b, t, h), q then scaled
 by d_k^-1/2; v ~ N(0,1); decay logits z ~ N(z_mean, 1); beta = sigmoid(N(0,1));
+for the general DPLR recurrence a = sigmoid(N(0,1)) x a unit row, b a unit row;
 output-gate logits ~ N(0,1); N(mu, x) takes x as a variance.  Normal draws are
 made in fp32 on the requested device with a torch.Generator seeded per
 tensor, then rounded (round-to-nearest-even) to the workload dtype.
@@ -45,7 +46,7 @@ G_MIN = -5.0
 EPS = 1e-6
 
 # tensor ids, mixed into the per-tensor seed
-_Q, _K, _V, _Z, _BETA, _GATE, _S0, _W = range(8)
+_Q, _K, _V, _Z, _BETA, _GATE, _S0, _W, _A, _B = range(10)
 
 
 def _gen(seed, tensor_id, step, device):
@@ -118,6 +119,22 @@ def workload_inputs(name, seed, device="cpu", **override):
 def decode_step_inputs(B, H, dk, dv, dtype, seed, step, device="cpu", z_mean=0.0):
     """One decode token per sequence: q, k, z (B, H, dk); v (B, H, dv); beta (B, H)."""
     return token_inputs((B, H), dk, dv, dtype, seed, device, z_mean, step=step + 1)
+
+
+def dplr_inputs(lead, dk, dv, dtype, seed, device="cpu", z_mean=0.0, step=0):
+    """Inputs of the general diagonal-plus-low-rank recurrence: q, k, v, z as
+    token_inputs draws them, and two independent low-rank directions drawn
+    like KDA's bound ones but from their own streams: a = sigmoid(N(0,1)) x
+    a unit row (the scale of beta k), b = a unit row (the scale of k)."""
+    lead = tuple(lead)
+    out = token_inputs(lead, dk, dv, dtype, seed, device, z_mean, step)
+    del out["beta"]
+    sa = torch.sigmoid(_randn(lead + (1,), seed, _A, step + 1_000, device))
+    a = _unit_rows(_randn(lead + (dk,), seed, _A, step, device)) * sa
+    b = _unit_rows(_randn(lead + (dk,), seed, _B, step, device))
+    out["a"] = a.to(dtype).contiguous()
+    out["b"] = b.to(dtype).contiguous()
+    return out
 
 
 def to_host_bits(t):

@@ -76,6 +76,11 @@ int main(void) {
     CHECK(kda_recurrent_bwd(P, P, P, P, P, -5.f, NULL, P, NULL, PF, PF, PF, PF, NULL, NULL, 1, 128, 2, 128, 128,
                             KDA_BF16, P, (size_t)1 << 30, NULL) == KDA_ERR_NULL);
 
+    CHECK(kda_dplr_fwd(P, P, P, P, P, NULL, -5.f, NULL, P, PF, 1, 128, 2, 128, 128, KDA_BF16, NULL) ==
+          KDA_ERR_NULL);
+    CHECK(kda_dplr_recurrent_step(P, P, P, P, P, P, -5.f, PF, P, 4, 2, 64, 96, KDA_F32, NULL) ==
+          KDA_ERR_UNSUPPORTED);
+
     if (failures) {
         fprintf(stderr, "%d checks failed\n", failures);
         return 1;

@@ -299,6 +299,38 @@ def test_recurrent_bwd_workspace_and_bad_arguments(lib):
     assert bw(T=0, q=None, go=None, gq=None, gb=None, ws=None, wsb=0) == OK   # no tokens, no ds0 asked for
 
 
+def test_dplr_calls_reject_bad_arguments(lib):
+    def fwd(q=P, b=P, o=P, sf=P, g_min=-5.0, B=1, T=128, H=2, dk=128, dv=128, dt=BF16):
+        return lib.kda_dplr_fwd(q, P, P, P, P, b, g_min, None, o, sf, B, T, H, dk, dv, dt, S)
+
+    assert fwd(q=None) == NULL
+    assert fwd(b=None) == NULL
+    assert fwd(o=None) == NULL
+    assert fwd(dk=96) == UNSUP
+    assert fwd(dt=2) == UNSUP
+    assert fwd(T=-1) == SHAPE
+    assert fwd(B=70000) == SHAPE
+    assert fwd(g_min=0.0) == ARG
+    assert fwd(g_min=float("nan")) == ARG
+    assert fwd(b=MIS) == ALIGN
+    assert fwd(sf=MIS) == ALIGN
+    assert fwd(H=0) == OK
+    assert fwd(T=0, q=None, b=None, o=None, sf=None) == OK      # nothing to compute or write
+
+    def step(q=P, b=P, o=P, st=P, g_min=-5.0, B=4, H=2, dk=128, dv=128, dt=BF16):
+        return lib.kda_dplr_recurrent_step(q, P, P, P, P, b, g_min, st, o, B, H, dk, dv, dt, S)
+
+    assert step(b=None) == NULL
+    assert step(o=None) == NULL
+    assert step(st=None) == NULL
+    assert step(dv=32) == UNSUP
+    assert step(B=-1) == SHAPE
+    assert step(g_min=1.0) == ARG
+    assert step(b=MIS) == ALIGN
+    assert step(o=MIS) == ALIGN
+    assert step(B=0) == OK
+
+
 def test_plain_c_caller(tmp_path):
     """The header compiles as C (gcc, -std=c11 -Wall -Werror) and a C program
     linked against libkda.so gets the documented host-side behaviour."""
