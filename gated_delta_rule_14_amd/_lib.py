@@ -43,6 +43,9 @@ SIGNATURES = {
                           _i, _i, _i, _i, _i, _i, _vp]),
     "kda_dplr_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                      _i, _i, _i, _i, _i, _vp]),
+    "kda_dplr_chunk_fwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_dplr_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
+                                _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_chunk_layer_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _f, _vp, _vp, _vp, _vp,
                                  _i, _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
 }

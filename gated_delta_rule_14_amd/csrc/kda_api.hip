@@ -396,6 +396,29 @@ kda_status kda_dplr_fwd(const void* q, const void* k, const void* v, const void*
     return finish(kda::launch_dplr(x), stream);
 }
 
+size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    return kda::dplr_chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+}
+
+kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* z, const void* a,
+                              const void* b, float g_min, const float* s0, void* o, float* s_final, int B, int T,
+                              int H, int dk, int dv, int chunk, kda_dtype dt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    const kda_status st = check_chunk_args(q, k, v, z, a, g_min, s0, o, s_final, B, T, H, dk, dv, chunk, dt,
+                                           workspace);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (T > 0 && !b) return KDA_ERR_NULL;
+    if (!aligned16(b)) return KDA_ERR_ALIGN;
+    if (T == 0 && !s_final) return KDA_OK;
+    const bool chunked = T > 0 && g_min >= KDA_CHUNK_G_MIN_LIMIT;
+    const size_t need = chunked ? kda::dplr_chunk_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    kda::DplrArgs x{q, k, v, z, a, b, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16, false, stream};
+    return finish(kda::launch_dplr_chunk(x, workspace), stream);
+}
+
 kda_status kda_dplr_recurrent_step(const void* q, const void* k, const void* v, const void* z, const void* a,
                                    const void* b, float g_min, float* state, void* o, int B, int H, int dk, int dv,
                                    kda_dtype dt, void* stream) {

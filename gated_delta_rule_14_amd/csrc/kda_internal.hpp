@@ -40,6 +40,10 @@ struct DplrArgs {
     void* stream;
 };
 hipError_t launch_dplr(const DplrArgs& x);
+// chunkwise DPLR prefill (dplr_chunk.hip); the workspace holds
+// dplr_chunk_workspace_bytes() bytes
+size_t dplr_chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
+hipError_t launch_dplr_chunk(const DplrArgs& x, void* workspace);
 // zfull (rows x dk) = each of the rows scalar logits zs repeated dk times
 hipError_t launch_broadcast_gate(const void* zs, void* zfull, size_t rows, int dk, bool bf16, void* stream);
 

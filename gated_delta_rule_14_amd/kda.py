@@ -24,6 +24,8 @@ Names follow the C ABI in include/kda.h:
                      sequence (token-sequential)
   dplr_recurrent_step -> kda_dplr_recurrent_step: one DPLR token, state
                      in place
+  dplr_chunk_fwd  -> kda_dplr_chunk_fwd: the DPLR recurrence by 64-token
+                     chunks (decayed products per 16-token block pair)
   layer           -> kda_chunk_layer_fwd, returning the
                      {"outputs", "final_state"} dictionary of the
                      "KDA Recurrence" problem (final_state kept in fp32)
@@ -390,6 +392,46 @@ def dplr_fwd(q, k, v, z, a, b, g_min, s0=None, *, o=None, s_final=None, want_sta
     check("kda_dplr_fwd", lib().kda_dplr_fwd(
         _p(q), _p(k), _p(v), _p(z), _p(a), _p(b), float(g_min), _p(s0), _p(o), _p(s_final),
         B, T, H, dk, dv, _dt(q), _stream(dev)))
+    return o, s_final
+
+
+def dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return int(lib().kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK,
+                                                        KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def dplr_chunk_fwd(q, k, v, z, a, b, g_min, s0=None, *, o=None, s_final=None, workspace=None,
+                   want_state=True):
+    """Chunkwise DPLR prefill; arguments and results as dplr_fwd."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("a", a), ("b", b)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("k", k), ("z", z), ("a", a), ("b", b)):
+        if tuple(t.shape) != (B, T, H, dk):
+            raise ValueError(f"libkda: {name} must be {(B, T, H, dk)}, got {tuple(t.shape)}")
+    if tuple(v.shape[:3]) != (B, T, H):
+        raise ValueError(f"libkda: v must be (B, T, H, dv), got {tuple(v.shape)}")
+    if s0 is not None:
+        _need(s0, "s0", dev)
+        if s0.dtype != torch.float32:
+            raise TypeError("libkda: s0 must be float32")
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=dev)
+    if want_state and s_final is None:
+        s_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if not want_state:
+        s_final = None
+    need = lib().kda_dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, CHUNK, _dt(q))
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=dev)
+    check("kda_dplr_chunk_fwd", lib().kda_dplr_chunk_fwd(
+        _p(q), _p(k), _p(v), _p(z), _p(a), _p(b), float(g_min), _p(s0), _p(o), _p(s_final),
+        B, T, H, dk, dv, CHUNK, _dt(q), _p(workspace), workspace.numel() * workspace.element_size(),
+        _stream(dev)))
     return o, s_final
 
 

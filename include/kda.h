@@ -363,6 +363,35 @@ kda_status kda_dplr_recurrent_step(const void* q, const void* k, const void* v, 
                                    int B, int H, int dk, int dv, kda_dtype dt, void* stream);
 
 /*
+ * The same DPLR recurrence by 64-token chunks: per chunk, with G the
+ * chunk-local cumulative log-decay (G- the one before each token) and T =
+ * (I + L)^{-1},
+ *   L_ri = b_r . e^{G-_r - G_i} a_i (i < r),   X = T (B e^{G-}) S + T Mbk V,
+ *   O    = (Q e^G) S + Mqk V - Mqa X,
+ *   S'   = Diag(e^{G_C}) S + (K e^{G_C - G})^T V - (A e^{G_C - G})^T X,
+ * where Mbk, Mqk, Mqa are the decayed products of b with k, q with k and q
+ * with a (Mbk strictly, the other two inclusively lower triangular): four
+ * decayed products per chunk, evaluated per 16-token block pair around
+ * reference rows (section 3's secondary chunking), where KDA's binding needs
+ * two.  Arguments as for kda_dplr_fwd, plus:
+ *   chunk      64
+ *   workspace  kda_dplr_chunk_fwd_workspace_bytes() bytes (per chunk the
+ *              products, T-weighted terms and decayed operands in the compute
+ *              precision, bf16 for bf16 tokens, else fp32; for sequences of at
+ *              least 32 chunks also per 16-chunk segment a d_k x d_k
+ *              transition, an input term and an entering state, fp32)
+ * For g_min below KDA_CHUNK_G_MIN_LIMIT, and for T == 0, the call runs the
+ * token-sequential kernel of kda_dplr_fwd (the workspace is then unused).
+ * bf16 tokens: products in bf16 on MFMA with fp32 accumulation, state fp32.
+ */
+size_t kda_dplr_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
+                                          kda_dtype dt);
+kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const void* z,
+                              const void* a, const void* b, float g_min, const float* s0, void* o,
+                              float* s_final, int B, int T, int H, int dk, int dv, int chunk,
+                              kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement helper: x <- s * x in place over n fp32 values (n a multiple
  * of 4, x 16-byte aligned), every byte read once and written once with
  * 16-byte accesses -- the access pattern of the decode step's state.  It

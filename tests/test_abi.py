@@ -331,6 +331,31 @@ def test_dplr_calls_reject_bad_arguments(lib):
     assert step(B=0) == OK
 
 
+def test_dplr_chunk_workspace_and_bad_arguments(lib):
+    ws = lib.kda_dplr_chunk_fwd_workspace_bytes
+    # per 64-token chunk: W, U^T, V^T, Q e^G, (K e^{G_C-G})^T, (A e^{G_C-G})^T
+    # (C x d each, d = dk or dv), two C x C products, e^{G_C} in fp32
+    per_chunk_bf16 = (64 * 128 * 6 + 64 * 64 * 2) * 2 + 128 * 4
+    assert ws(1, 150, 2, 128, 128, 64, BF16) == 2 * 3 * per_chunk_bf16
+    # 32 chunks or more: per 16-chunk segment a d_k x d_k transition, an input
+    # term and an entering state, fp32
+    nseg = 32
+    assert ws(1, 32768, 1, 128, 128, 64, BF16) == 512 * per_chunk_bf16 + nseg * (3 * 128 * 128 * 4)
+    assert ws(1, 100, 1, 96, 64, 64, F32) == 0
+    assert ws(1, 100, 1, 64, 64, 32, F32) == 0
+
+    def call(q=P, b=P, g_min=-5.0, B=1, T=128, H=2, dk=128, dv=128, chunk=64, dt=BF16, w=P, wb=1 << 30):
+        return lib.kda_dplr_chunk_fwd(q, P, P, P, P, b, g_min, None, P, P, B, T, H, dk, dv, chunk, dt, w, wb, S)
+
+    assert call(b=None) == NULL
+    assert call(chunk=32) == UNSUP
+    assert call(g_min=0.0) == ARG
+    assert call(b=MIS) == ALIGN
+    assert call(w=None, wb=0) == WS
+    assert call(wb=1024) == WS
+    assert call(H=0) == OK
+
+
 def test_plain_c_caller(tmp_path):
     """The header compiles as C (gcc, -std=c11 -Wall -Werror) and a C program
     linked against libkda.so gets the documented host-side behaviour."""

@@ -187,3 +187,127 @@ def test_dplr_inputs_untouched_and_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
     for n, t in x.items():
         assert torch.equal(t, before[n]), n
+
+
+# ---------------------------------------------------------------- chunkwise
+def gpu_chunk(x, g_min=ki.G_MIN, workspace=None):
+    return kda.dplr_chunk_fwd(*(x[n] for n in NAMES), g_min, x["s0"], workspace=workspace)
+
+
+@pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128), (64, 128), (128, 64)])
+@pytest.mark.parametrize("T", [150, 2100])
+def test_dplr_chunk_small(dtype, tag, dk, dv, T):
+    """150 tokens: one chain per column tile over three chunks (the last
+    ragged); 2100 tokens: 33 chunks, the two-level plan (segments of 16
+    chunks, a ragged last segment and chunk)."""
+    x = inputs(2, T, 2, dk, dv, dtype, seed=80 + dk + dv + T)
+    o, s = gpu_chunk(x)
+    torch.cuda.synchronize()
+    ro, rs = oracle_of(x)
+    to, ts = TOL[tag]
+    eo, es, eb = rel(f64(o), ro), rel(f64(s), rs), block_rel_max(f64(o), ro)
+    print(f"dplr chunk {tag} dk={dk} dv={dv} T={T}: o {eo:.2e} state {es:.2e} worst block {eb:.2e}")
+    assert eo < to and es < ts and eb < 2 * to
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 2048])
+def test_dplr_chunk_edges(T):
+    x = inputs(1, T, 3, 128, 128, torch.float32, seed=90 + T)
+    o, s = gpu_chunk(x)
+    torch.cuda.synchronize()
+    ro, rs = oracle_of(x)
+    assert rel(f64(o), ro) < 1e-5 and rel(f64(s), rs) < 1e-5
+
+
+def test_dplr_chunk_t0_returns_s0():
+    x = inputs(1, 0, 2, 64, 64, torch.float32, seed=1)
+    o, s = gpu_chunk(x)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(s, x["s0"])
+
+
+@pytest.mark.parametrize("g_min", [-0.5, -8.0])
+def test_dplr_chunk_decay_range(g_min):
+    """Up to the chunkwise decay bound (block factors reach 2^92 at -8)."""
+    x = inputs(1, 1100, 2, 128, 128, torch.float32, seed=31)
+    o, s = gpu_chunk(x, g_min)
+    torch.cuda.synchronize()
+    ro, rs = oracle_of(x, g_min)
+    eo, es, eb = rel(f64(o), ro), rel(f64(s), rs), block_rel_max(f64(o), ro)
+    print(f"dplr chunk g_min={g_min}: o {eo:.2e} state {es:.2e} worst block {eb:.2e}")
+    assert eo < 1e-5 and es < 1e-5 and eb < 2e-5
+
+
+def test_dplr_chunk_below_limit_runs_token_kernel():
+    """Below the bound the chunkwise call is the token-sequential kernel."""
+    x = inputs(1, 300, 2, 128, 128, torch.bfloat16, seed=33)
+    o1, s1 = gpu_chunk(x, -9.0)
+    o2, s2 = gpu_fwd(x, -9.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_dplr_chunk_long_memory():
+    """z ~ N(-6, 1): alpha near 1, the carried state matters over 4096 tokens
+    (two-level plan, 4 segments)."""
+    x = inputs(1, 4096, 2, 128, 128, torch.float32, seed=35, z_mean=-6.0)
+    o, s = gpu_chunk(x)
+    torch.cuda.synchronize()
+    ro, rs = oracle_of(x)
+    eo, es, eb = rel(f64(o), ro), rel(f64(s), rs), block_rel_max(f64(o), ro)
+    print(f"dplr chunk long memory: o {eo:.2e} state {es:.2e} worst block {eb:.2e}")
+    assert eo < 1e-5 and es < 1e-5 and eb < 2e-5
+
+
+def test_dplr_chunk_binding_gives_kda():
+    """Section 3's binding through the chunkwise DPLR kernels against libkda's
+    KDA prefill (bf16 tokens, both chunkwise)."""
+    B, T, H, d = 1, 2100, 4, 128
+    x = ki.prefill_inputs(B, T, H, d, d, torch.bfloat16, seed=23, device=DEV, s0_var=0.01)
+    alpha = torch.exp(ki.G_MIN * torch.sigmoid(x["z"].double()))
+    bk = (x["beta"].double()[..., None] * x["k"].double()).to(torch.bfloat16).contiguous()
+    b = (x["k"].double() * alpha).to(torch.bfloat16).contiguous()
+    o1, s1 = kda.dplr_chunk_fwd(x["q"], bk, x["v"], x["z"], bk, b, ki.G_MIN, x["s0"])
+    o2, s2 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
+    torch.cuda.synchronize()
+    eo, es = rel(f64(o1), f64(o2)), rel(f64(s1), f64(s2))
+    print(f"chunk binding: o {eo:.2e} state {es:.2e}")
+    assert eo < 2e-2 and es < 1e-2
+
+
+@pytest.mark.parametrize("T", [150, 2100])
+def test_dplr_chunk_nan_workspace(T):
+    """Every workspace byte the kernels read is written first in the same
+    call: a NaN-filled workspace gives the same bits as a fresh one."""
+    x = inputs(1, T, 2, 128, 128, torch.bfloat16, seed=37)
+    need = kda.dplr_chunk_fwd_workspace_bytes(1, T, 2, 128, 128, torch.bfloat16)
+    ws = torch.full((need // 4 + 1,), float("nan"), dtype=torch.float32, device=DEV)
+    o1, s1 = gpu_chunk(x, workspace=ws.view(torch.uint8))
+    o2, s2 = gpu_chunk(x)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_dplr_chunk_full_size_sampled():
+    """The 32-head, 32768-token bf16 prefill through the chunkwise kernels
+    (two-level plan, 32 segments): two heads against the oracle."""
+    B, T, H, d = 1, 32768, 32, 128
+    x = inputs(B, T, H, d, d, torch.bfloat16, seed=5)
+    o, s = gpu_chunk(x)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(s).all()
+    heads = [0, 31]
+    ro, rs = oracle_of(x, heads=heads)
+    go, gs = f64(o[:, :, heads]), f64(s[:, heads])
+    eo, es, eb = rel(go, ro), rel(gs, rs), block_rel_max(go, ro)
+    print(f"dplr chunk full size: o {eo:.2e} state {es:.2e} worst block {eb:.2e}")
+    assert eo < 2e-2 and es < 1e-2 and eb < 4e-2
+
+
+def test_dplr_chunk_deterministic():
+    x = inputs(1, 2100, 4, 128, 128, torch.bfloat16, seed=39)
+    o1, s1 = gpu_chunk(x)
+    o2, s2 = gpu_chunk(x)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
