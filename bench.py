@@ -55,6 +55,12 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
 PREFILL_BYTES_PER_TOKEN_HEAD = 4 * 128 * 2 + 2 + 128 * 2      # q, k, z, v in; beta; o out (bf16)
 PREFILL_FLOP_PER_TOKEN_HEAD = 163840                           # chunk form, d = 128, C = 64
+# The general DPLR chunk form (d = 128, C = 64, full tiles): four decayed C x C
+# products 4 * 2Cd, Mbk V 2Cd, W = T R_B and U = T (Mbk V) 2 * 2Cd, then per
+# token W S, (Q e^G) S 2 * 2d^2, [Mqk | Mqa][V; Y] 2 * 2C d and the state
+# update [K~ | A~]^T [V; Y] 4 d^2.
+DPLR_FLOP_PER_TOKEN_HEAD = 4 * 2 * 64 * 128 + 2 * 64 * 128 + 2 * 2 * 64 * 128 + 2 * 2 * 128 * 128 \
+    + 2 * 2 * 64 * 128 + 4 * 128 * 128                        # 278,528
 DECODE_BYTES_PER_HEAD_STEP = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 2 + 128 * 2
 DECODE_FLOP_PER_HEAD_STEP = 114688
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_32k_traffic.json")
@@ -63,8 +69,8 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_14_amd", "csrc")
 
 # the sources of the kernels whose counters the traffic record holds (the
 # prefill's pipelined kernels and segment scan, the decode step, the gate
-# kernel) and the device header they include
-TRAFFIC_SOURCES = ("seg.hip", "decode.hip", "out_gate.hip", "kda_device.hpp")
+# kernel, the projection GEMM) and the device header they include
+TRAFFIC_SOURCES = ("seg.hip", "decode.hip", "out_gate.hip", "gemm.hip", "kda_device.hpp")
 
 
 def kernel_source_hash():
@@ -94,6 +100,7 @@ def parse():
     p.add_argument("--no-workloads", action="store_true", help="skip the tiny, training and 1M-token shapes")
     p.add_argument("--no-long", action="store_true", help="skip the 1M-token shape")
     p.add_argument("--no-ceilings", action="store_true")
+    p.add_argument("--no-dplr", action="store_true", help="skip the KDA vs general DPLR comparison")
     p.add_argument("--copy-only", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -405,6 +412,71 @@ def bench_gdn_prefill(torch, kda, ki, calls=10):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
 
 
+def bench_dplr(torch, kda, ki, calls=5):
+    """KDA against the general DPLR recurrence S = (Diag(alpha) - a b^T) S +
+    k v^T with independent a, b, at the 32-head 32k-token bf16 prefill shape
+    and the 256 x 32 decode batch: KDA's chunkwise prefill beside the
+    chunkwise DPLR kernels (four decayed products per chunk where KDA has
+    two, contractions over twice the tokens in the chunk step) and the
+    token-sequential DPLR kernel; one decode step of each."""
+    cfg = ki.WORKLOADS["prefill_32k"]
+    B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
+    bf = torch.bfloat16
+    dev = torch.device("cuda:0")
+    s0 = ki.initial_state(B, H, dk, dv, cfg["s0_var"], seed=6, device=dev)
+    o = torch.empty((B, T, H, dv), dtype=bf, device=dev)
+    s = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    x = ki.prefill_inputs(B, T, H, dk, dv, bf, seed=6, device=dev)
+    ws = torch.empty(max(kda.chunk_fwd_workspace_bytes(B, T, H, dk, dv, bf), 16), dtype=torch.uint8, device=dev)
+    kda_s = _time_calls(torch, lambda: kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, s0,
+                                                     o=o, s_final=s, workspace=ws), calls)
+    del x, ws
+    x = ki.dplr_inputs((B, T, H), dk, dv, bf, seed=6, device=dev)
+    args = [x[n] for n in ("q", "k", "v", "z", "a", "b")]
+    ws = torch.empty(kda.dplr_chunk_fwd_workspace_bytes(B, T, H, dk, dv, bf), dtype=torch.uint8, device=dev)
+    chunk_s = _time_calls(torch, lambda: kda.dplr_chunk_fwd(*args, ki.G_MIN, s0, o=o, s_final=s, workspace=ws),
+                          calls)
+    ws_bytes = ws.numel()
+    del ws
+    seq_s = _time_calls(torch, lambda: kda.dplr_fwd(*args, ki.G_MIN, s0, o=o, s_final=s), 2)
+    del x, args, o, s, s0
+    torch.cuda.empty_cache()
+
+    dcfg = ki.WORKLOADS["decode_256"]
+    Bd = dcfg["B"]
+    state = ki.initial_state(Bd, H, dk, dv, dcfg["s0_var"], seed=7, device=dev)
+    od = torch.empty((Bd, H, dv), dtype=bf, device=dev)
+    d = ki.decode_step_inputs(Bd, H, dk, dv, bf, 7, 0, dev)
+    kda_step = _time_calls(torch, lambda: kda.recurrent_step(d["q"], d["k"], d["v"], d["z"], d["beta"], ki.G_MIN,
+                                                             state, o=od), 50, warmup=5)
+    dd = ki.dplr_inputs((Bd, H), dk, dv, bf, seed=7, device=dev, step=1)
+    dargs = [dd[n] for n in ("q", "k", "v", "z", "a", "b")]
+    dplr_step = _time_calls(torch, lambda: kda.dplr_recurrent_step(*dargs, ki.G_MIN, state, o=od), 50, warmup=5)
+    del state, od, d, dd, dargs
+    torch.cuda.empty_cache()
+    tokens = B * T
+    # token tensors once each (bf16): KDA q, k, z, v, beta, o; DPLR q, k, z, a, b, v, o
+    kda_bytes = tokens * H * (5 * 256 + 2) + 2 * B * H * dk * dv * 4
+    dplr_bytes = tokens * H * 7 * 256 + 2 * B * H * dk * dv * 4
+    return {
+        "workload": "prefill_32k shape, KDA vs general DPLR", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+        "dtype": "bf16",
+        "kda_chunk_us": round(kda_s * 1e6, 1), "kda_tokens_per_s": round(tokens / kda_s, 1),
+        "dplr_chunk_us": round(chunk_s * 1e6, 1), "dplr_chunk_tokens_per_s": round(tokens / chunk_s, 1),
+        "dplr_seq_us": round(seq_s * 1e6, 1), "dplr_seq_tokens_per_s": round(tokens / seq_s, 1),
+        "dplr_chunk_over_kda_time": round(chunk_s / kda_s, 3),
+        "flop_per_token_head": {"kda": PREFILL_FLOP_PER_TOKEN_HEAD, "dplr": DPLR_FLOP_PER_TOKEN_HEAD},
+        "algorithmic_bytes": {"kda": kda_bytes, "dplr": dplr_bytes},
+        "dplr_chunk_hbm_gbs": round(dplr_bytes / chunk_s / 1e9, 1),
+        "dplr_chunk_mfma_frac": round(tokens * H * DPLR_FLOP_PER_TOKEN_HEAD / chunk_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "dplr_chunk_workspace_bytes": ws_bytes,
+        "decode_step_us": {"kda": round(kda_step * 1e6, 1), "dplr": round(dplr_step * 1e6, 1)},
+        "kernels": "kda_chunk_fwd (pipe_kernel x2 + scan); kda_dplr_chunk_fwd (dplr_intra_kernel, "
+                   "dplr_chain_kernel x3, seg_scan_kernel); kda_dplr_fwd (dplr_seq_kernel); "
+                   "decode_step_kernel vs dplr_step_kernel",
+    }
+
+
 def measured_ceilings(torch, kda):
     """Rates this GPU reaches: libkda's streaming read-modify-write kernel
     (kda_stream_scale: in-place fp32 scale over 512 MiB, the decode state's
@@ -636,6 +708,8 @@ def main():
         line["workloads"] = wl
     if not args.no_workloads:
         line["backward"] = bench_backward(torch, kda, ki)
+    if not args.no_dplr:
+        line["dplr"] = bench_dplr(torch, kda, ki)
     if not args.no_ceilings:
         c = measured_ceilings(torch, kda)
         line["ceilings"] = c
