@@ -39,6 +39,9 @@ SIGNATURES = {
     "kda_recurrent_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_stream_scale": (_i, [_vp, _sz, _f, _i, _vp]),
+    "kda_chunk_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "kda_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _i, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]),
     "kda_dplr_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp,
                           _i, _i, _i, _i, _i, _i, _vp]),
     "kda_dplr_recurrent_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,

@@ -1,0 +1,835 @@
+// bwd_chunk.hip -- kda_chunk_bwd: gradients of the KDA recurrence by 64-token
+// chunks.  The pages give the forward only; this is the chain rule through
+// the chunk form (Kimi Linear tech report, section 3.1 and appendix B,
+// Eqs. 16-19, with the decay and readout of "KDA Recurrence").  Per chunk with
+// entering state S, g = g_min sigmoid(z), G its chunk-local cumulative sum,
+// Gam = e^G, Kg = K Gam, Kt = K / Gam, Kc = K e^{G_C - G}, Qg = Q Gam:
+//   A = tril_-1(diag(beta) Kg Kt^T), M = tril(Qg Kt^T), T = (I + A)^{-1},
+//   W = T diag(beta) Kg, U = T diag(beta) V, Vn = U - W S,
+//   O = Qg S + M Vn,   S' = Diag(e^{G_C}) S + Kc^T Vn.
+// With dO and dS' (the gradient of the state leaving the chunk) given:
+//   dVn = M^T dO + Kc dS',                dS  = e^{G_C} dS' + Qg^T dO - W^T dVn,
+//   dM  = tril(dO Vn^T),  dQg = dO S^T,   dKc = Vn dS'^T,   dW = -dVn S^T,
+//   dT  = dW (diag(beta) Kg)^T + dVn (diag(beta) V)^T,
+//   dBk = T^T dW, dBv = T^T dVn,          dA = tril_-1(-T^T dT T^T),
+//   dV  = beta dBv,  dbeta = rowsum(dBv V + dBk Kg + dA Ab)  (Ab = Kg Kt^T),
+//   dKg = beta dBk + (beta dA) Kt,  dKt = (beta dA)^T Kg + dM^T Qg,  dQg += dM Kt,
+// then dQ = dQg Gam, dK = dKg Gam + dKt / Gam + dKc e^{G_C - G},
+//   dG = dQ q + (dKg Gam - dKt / Gam - dKc e^{G_C - G}) k  (+ e^{G_C} rowsum(S dS')
+//        + colsum(dKc e^{G_C - G} k) on the last row),
+//   dg = reverse cumulative sum of dG,  dz = dg g_min sigmoid(z) (1 - sigmoid(z)).
+//
+// Kernels:
+//  * the forward half (chunk.hip): the per-chunk operands of both directions,
+//    then the chunk recurrence from S0 storing each chunk's S and Vn;
+//  * dchain_kernel, one workgroup per (batch, head): the chunks in reverse,
+//    dS in MFMA accumulators; per chunk dVn and the products with S, Vn and
+//    dS' (dQg, dW, dKc, dM and e^{G_C} rowsum(S dS')), written for the next
+//    kernel;
+//  * dintra_kernel, one workgroup per chunk: everything else, on fp32 MFMA.
+//    The products whose terms carry e^{G_r - G_i} are evaluated per 16-row
+//    block pair around reference rows m = 16R + 7, as in the forward, with
+//    the cross-block factor applied as its square root twice.
+#include "chunk_layout.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace bwdc {
+
+template <class E> __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+template <> __device__ __forceinline__ float dexp2<float>(float x) { return exp2f(x); }
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr size_t a256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Per chunk, fp32, written by dchain_kernel for dintra_kernel.
+template <int DK, int DV>
+struct Ob {
+    static constexpr size_t DVNT = 0;                       // (DV, C)  dVn^T
+    static constexpr size_t DQGT = DVNT + (size_t)DV * C;   // (DK, C)  (dO S^T)^T
+    static constexpr size_t DWT = DQGT + (size_t)DK * C;    // (DK, C)  (-dVn S^T)^T
+    static constexpr size_t DKCT = DWT + (size_t)DK * C;    // (DK, C)  (Vn dS'^T)^T
+    static constexpr size_t DMT = DKCT + (size_t)DK * C;    // (C, C)   tril(dO Vn^T)^T
+    static constexpr size_t DGC = DMT + (size_t)C * C;      // (DK)     e^{G_C} rowsum(S dS')
+    static constexpr size_t END = DGC + DK;
+    static constexpr size_t BYTES = END * 4;
+};
+
+struct Lay {
+    size_t fws, bws, st, vn, ob, total;
+};
+
+template <class CT, int DK, int DV>
+Lay lay_t(int B, int T, int H) {
+    const size_t nchunk = (size_t)B * H * (((size_t)T + C - 1) / C);
+    Lay lo{};
+    lo.fws = 0;
+    lo.bws = a256(nchunk * Ws<CT, DK, DV>::BYTES);
+    lo.st = lo.bws + a256(nchunk * WsB<CT, DK, DV>::BYTES);
+    lo.vn = lo.st + a256(nchunk * DK * DV * 4);
+    lo.ob = lo.vn + a256(nchunk * C * DV * sizeof(CT));
+    lo.total = lo.ob + nchunk * Ob<DK, DV>::BYTES;
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Reverse chunk recurrence of one chain (b, h), all d_v columns: 256 threads.
+// dS rows of wave w: w*DK/4 + rb*16 + 4(l/16) + e; columns ct*16 + l%16.
+// ---------------------------------------------------------------------------
+template <class E, int DK, int DV>
+struct DChain {
+    typedef typename Compute<E>::type CT;
+    typedef Mfma<CT> MF;
+    static constexpr int KS = MF::KSTEP, RB = DK / 64, NT = DV / 16;
+    static constexpr int LC = C + 8, LDK = DK + 8, LDV = DV + 8;
+    static constexpr size_t OFF_DOT = 0;                                                  // [DV][LC]  dO^T
+    static constexpr size_t OFF_DST = OFF_DOT + align16((size_t)DV * LC * sizeof(CT));   // [DV][LDK] dS^T
+    static constexpr size_t OFF_DSR = OFF_DST + align16((size_t)DV * LDK * sizeof(CT));  // [DK][LDV] dS
+    static constexpr size_t OFF_DVT = OFF_DSR + align16((size_t)DK * LDV * sizeof(CT));  // [DV][LC]  -dVn^T
+    static constexpr size_t OFF_DVR = OFF_DVT + align16((size_t)DV * LC * sizeof(CT));   // [C][LDV]  -dVn
+    static constexpr size_t LDS = OFF_DVR + align16((size_t)C * LDV * sizeof(CT));
+    static_assert(LDS <= 160 * 1024, "reverse chain LDS budget");
+};
+
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout, const float* __restrict__ ds_final,
+                                                     float* __restrict__ ds0, int T, int H, int NC,
+                                                     const unsigned char* __restrict__ fws,
+                                                     const unsigned char* __restrict__ bws,
+                                                     const float* __restrict__ states,
+                                                     const typename Compute<E>::type* __restrict__ vn,
+                                                     unsigned char* __restrict__ obuf) {
+    typedef DChain<E, DK, DV> L;
+    typedef typename L::CT CT;
+    typedef typename L::MF MF;
+    typedef Ws<CT, DK, DV> WL;
+    typedef WsB<CT, DK, DV> WB;
+    typedef Ob<DK, DV> OL;
+    constexpr int KS = L::KS, RB = L::RB, NT = L::NT, LC = L::LC, LDK = L::LDK, LDV = L::LDV;
+    constexpr int VE = 16 / sizeof(CT);   // elements per 16-byte access
+    extern __shared__ __align__(16) unsigned char smem[];
+    CT* dOT = reinterpret_cast<CT*>(smem + L::OFF_DOT);
+    CT* dST = reinterpret_cast<CT*>(smem + L::OFF_DST);
+    CT* dSR = reinterpret_cast<CT*>(smem + L::OFF_DSR);
+    CT* dVT = reinterpret_cast<CT*>(smem + L::OFF_DVT);
+    CT* dVR = reinterpret_cast<CT*>(smem + L::OFF_DVR);
+
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const size_t bh = blockIdx.x;
+    const int bb = (int)(bh / H), hh = (int)(bh % H);
+
+    f32x4 accD[RB][NT];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+            const int col = ct * 16 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                accD[rb][ct][e] = ds_final ? ds_final[(bh * DK + row + e) * DV + col] : 0.f;
+        }
+    auto store_ds = [&]() {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+                const int col = ct * 16 + (l & 15);
+                store4<CT>(dST + col * LDK + row, accD[rb][ct]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dSR[(row + e) * LDV + col] = from_f32<CT>(accD[rb][ct][e]);
+            }
+    };
+    store_ds();
+
+    for (int n = NC - 1; n >= 0; --n) {
+        const int valid = min(C, T - n * C);
+        const size_t cid = bh * NC + n;
+        const unsigned char* fb = fws + cid * WL::BYTES;
+        const CT* bk = reinterpret_cast<const CT*>(bws + cid * WB::BYTES);
+        const float* Sn = states + cid * DK * DV;
+        const CT* Vn = vn + cid * C * DV;
+        float* ob = reinterpret_cast<float*>(obuf + cid * OL::BYTES);
+        const E* dob = dout + (((size_t)bb * T + (size_t)n * C) * H + hh) * DV;   // row r at r * H * DV
+        const size_t rs = (size_t)H * DV;
+
+        // dO^T into LDS, zero past the end of the sequence
+        for (int u = tid; u < C * DV / VE; u += 256) {
+            const int r = u / (DV / VE), j0 = (u % (DV / VE)) * VE;
+            CT vals[VE];
+            if (r < valid) {
+                const CT* src = reinterpret_cast<const CT*>(dob + r * rs + j0);
+#pragma unroll
+                for (int x = 0; x < VE; ++x) vals[x] = src[x];
+            } else {
+#pragma unroll
+                for (int x = 0; x < VE; ++x) vals[x] = from_f32<CT>(0.f);
+            }
+#pragma unroll
+            for (int x = 0; x < VE; ++x) dOT[(j0 + x) * LC + r] = vals[x];
+        }
+        __syncthreads();
+
+        // dVn = M^T dO + Kc dS' (token rows 16w..)
+        f32x4 accV[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) accV[ct] = zero4();
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk) {
+            const typename MF::frag a = load_frag<CT>(bk + WB::MT, C, w * 16, kk * KS);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) accV[ct] = MF::mma(a, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accV[ct]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < DK / KS; ++kk) {
+            const typename MF::frag a = load_frag<CT>(bk + WB::KC, DK, w * 16, kk * KS);
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) accV[ct] = MF::mma(a, load_frag<CT>(dST, LDK, ct * 16, kk * KS), accV[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            const int col = ct * 16 + (l & 15), row = w * 16 + 4 * (l >> 4);
+            *reinterpret_cast<f32x4*>(ob + OL::DVNT + (size_t)col * C + row) = accV[ct];
+            store4<CT>(dVT + col * LC + row, -accV[ct]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dVR[(row + e) * LDV + col] = from_f32<CT>(-accV[ct][e]);
+        }
+        __syncthreads();
+
+        // dO rows 16w.. (zero past the end) and Vn rows 16w.. as A operands
+        typename MF::frag dof[DV / KS], vf[DV / KS];
+        {
+            const int r = w * 16 + (l & 15);
+            const bool ok = r < valid;
+            // the row address is clamped to the last token (in bounds); rows
+            // past the end are zeroed
+            const CT* drow = reinterpret_cast<const CT*>(dob + (size_t)min(r, valid - 1) * rs) + (l >> 4) * MF::KPL;
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) {
+                dof[kk] = *reinterpret_cast<const typename MF::frag*>(drow + kk * KS);
+                if (!ok) dof[kk] = typename MF::frag{};
+                vf[kk] = load_frag<CT>(Vn, DV, w * 16, kk * KS);
+            }
+        }
+        // dQg = dO S^T and dW = -dVn S^T (rows r, columns c)
+#pragma unroll 2
+        for (int cb = 0; cb < DK / 16; ++cb) {
+            f32x4 accQ = zero4(), accW = zero4(), accK = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) {
+                const typename MF::frag fs = load_frag_f32<CT>(Sn, DV, cb * 16, kk * KS);
+                accQ = MF::mma(dof[kk], fs, accQ);
+                accW = MF::mma(load_frag<CT>(dVR, LDV, w * 16, kk * KS), fs, accW);
+                accK = MF::mma(vf[kk], load_frag<CT>(dSR, LDV, cb * 16, kk * KS), accK);
+            }
+            const size_t off = (size_t)(cb * 16 + (l & 15)) * C + w * 16 + 4 * (l >> 4);
+            *reinterpret_cast<f32x4*>(ob + OL::DQGT + off) = accQ;
+            *reinterpret_cast<f32x4*>(ob + OL::DWT + off) = accW;
+            *reinterpret_cast<f32x4*>(ob + OL::DKCT + off) = accK;
+        }
+        // dM = tril(dO Vn^T) (rows r, columns i), stored transposed
+#pragma unroll
+        for (int ib = 0; ib < C / 16; ++ib) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < DV / KS; ++kk) acc = MF::mma(dof[kk], load_frag<CT>(Vn, DV, ib * 16, kk * KS), acc);
+            const int i = ib * 16 + (l & 15), r0 = w * 16 + 4 * (l >> 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = (i <= r0 + e) ? acc[e] : 0.f;
+            *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
+        }
+        // e^{G_C} rowsum(S dS'), rows of this wave
+        const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
+        f32x4 eg[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+            eg[rb] = *reinterpret_cast<const f32x4*>(egc + row);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float s = 0.f;
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) s += accD[rb][ct][e] * Sn[(size_t)(row + e) * DV + ct * 16 + (l & 15)];
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
+                if ((l & 15) == 0) ob[OL::DGC + row + e] = s * eg[rb][e];
+            }
+        }
+        // dS <- e^{G_C} dS' + Qg^T dO - W^T dVn
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) accD[rb][ct] *= eg[rb];
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const typename MF::frag aq = load_frag<CT>(bk + WB::QGT, C, w * (DK / 4) + rb * 16, kk * KS);
+                const typename MF::frag aw = load_frag<CT>(bk + WB::WT, C, w * (DK / 4) + rb * 16, kk * KS);
+#pragma unroll
+                for (int ct = 0; ct < NT; ++ct) {
+                    accD[rb][ct] = MF::mma(aq, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[rb][ct]);
+                    accD[rb][ct] = MF::mma(aw, load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[rb][ct]);
+                }
+            }
+        __syncthreads();   // this chunk's reads of dO^T, dS, dVn in LDS are done
+        store_ds();
+    }
+    if (ds0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
+                const int col = ct * 16 + (l & 15);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ds0[(bh * DK + row + e) * DV + col] = accD[rb][ct][e];
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk gradients: 256 threads, fp32 MFMA (16x16x4).  Wave w owns token
+// rows 16w..16w+15 of the C x d_k results dQ, dK and dG, held in registers in
+// the accumulator layout (rows 16w + 4(l/16) + e, column ct*16 + l%16).
+// ---------------------------------------------------------------------------
+template <class E, int DK, int DV>
+struct DIntra {
+    static constexpr int CP = DK / 2, NPART = 256 / CP, RP = C / NPART;
+    static constexpr int NCT = DK / 16;
+    static constexpr int DKP = DK + 4, LA = C + 4;
+    static constexpr size_t OFF_G = 0;                                  // [C][DKP] G (log2 units), then dG
+    static constexpr size_t OFF_K = OFF_G + (size_t)C * DKP * 4;        // [C][DKP] k
+    static constexpr size_t OFF_A = OFF_K + (size_t)C * DKP * 4;        // [C][LA]  Ab = tril_-1(Kg Kt^T)
+    static constexpr size_t OFF_T = OFF_A + (size_t)C * LA * 4;         // [C][LA]  T
+    static constexpr size_t OFF_S1 = OFF_T + (size_t)C * LA * 4;        // [C][LA]  dT, then beta dA
+    static constexpr size_t OFF_S2 = OFF_S1 + (size_t)C * LA * 4;       // [C][LA]  dT T^T, then dM
+    static constexpr size_t OFF_X = OFF_S2 + (size_t)C * LA * 4;        // [3][16][16]
+    static constexpr size_t OFF_DSC = OFF_X + 3 * SUB * SUB * 4;        // [6][DK]
+    static constexpr size_t OFF_GM = OFF_DSC + 6 * DK * 4;              // [5][DK] G_m(R), G_C
+    static constexpr size_t OFF_CAR = OFF_GM + 5 * DK * 4;              // [max(NPART, 4)][DK]
+    static constexpr size_t OFF_BET = OFF_CAR + (size_t)(NPART > 4 ? NPART : 4) * DK * 4;   // [C]
+    static constexpr size_t OFF_DB = OFF_BET + C * 4;                   // [C] dbeta
+    static constexpr size_t LDS = OFF_DB + C * 4;
+    static_assert(LDS <= 160 * 1024, "per-chunk gradient LDS budget");
+    static_assert(RP % 2 == 0 && 16 % RP == 0, "tiling");
+};
+
+// Block pairs (R, I), I <= R, of the 64 x 64 lower triangle, by wave.
+__constant__ int kPairsB[4][3][2] = {{{0, 0}, {1, 0}, {3, 3}},
+                                     {{1, 1}, {2, 0}, {3, 2}},
+                                     {{2, 1}, {2, 2}, {3, 1}},
+                                     {{3, 0}, {-1, -1}, {-1, -1}}};
+
+__device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }   // I < R
+
+template <class E, int DK, int DV>
+__global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                     const E* __restrict__ v, const E* __restrict__ z,
+                                                     const E* __restrict__ beta, float g_min, int T, int H, int NC,
+                                                     const unsigned char* __restrict__ obuf, float* __restrict__ dq,
+                                                     float* __restrict__ dk, float* __restrict__ dvo,
+                                                     float* __restrict__ dz, float* __restrict__ dbeta) {
+    typedef DIntra<E, DK, DV> L;
+    typedef Ob<DK, DV> OL;
+    constexpr int RP = L::RP, DKP = L::DKP, LA = L::LA, NCT = L::NCT;
+    constexpr float LOG2E = 1.4426950408889634f;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* Gs = reinterpret_cast<float*>(smem + L::OFF_G);
+    float* Ks = reinterpret_cast<float*>(smem + L::OFF_K);
+    float* As = reinterpret_cast<float*>(smem + L::OFF_A);
+    float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
+    float* S1 = reinterpret_cast<float*>(smem + L::OFF_S1);
+    float* S2 = reinterpret_cast<float*>(smem + L::OFF_S2);
+    float* Xs = reinterpret_cast<float*>(smem + L::OFF_X);
+    float* dsc = reinterpret_cast<float*>(smem + L::OFF_DSC);
+    float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);
+    float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);
+    float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
+    float* dbt = reinterpret_cast<float*>(smem + L::OFF_DB);
+
+    const int n = blockIdx.x, hh = blockIdx.y, bb = blockIdx.z;
+    const int valid = min(C, T - n * C), last = valid - 1;
+    const size_t row0 = ((size_t)bb * T + (size_t)n * C) * H + hh;   // token row of chunk row 0
+    const size_t rsk = (size_t)H * DK, rsv = (size_t)H * DV;
+    const float* ob = reinterpret_cast<const float*>(obuf + (((size_t)bb * H + hh) * NC + n) * OL::BYTES);
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int lr = l & 15, lg = l >> 4;
+
+    // ---- gate, chunk-local scan (log2 units), k into LDS
+    {
+        const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+        const float kg2 = g_min * LOG2E;
+        float G[RP][2];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+            const size_t off = (row0 + (size_t)min(r, last) * H) * DK + c0;
+            const typename Pair<E>::type zz = load2<E>(z + off), kk = load2<E>(k + off);
+            const bool ok = r < valid;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float g2 = kg2 * __builtin_amdgcn_rcpf(1.0f + dexp2<E>(-LOG2E * to_f32(zz[j])));
+                G[i][j] = ok ? g2 : 0.f;
+                Ks[r * DKP + c0 + j] = ok ? to_f32(kk[j]) : 0.f;
+            }
+            s0 += G[i][0];
+            s1 += G[i][1];
+            G[i][0] = s0;
+            G[i][1] = s1;
+        }
+        car[part * DK + c0] = s0;
+        car[part * DK + c0 + 1] = s1;
+        if (tid < C) {
+            bet[tid] = tid < valid ? to_f32(beta[row0 + (size_t)tid * H]) : 0.f;
+            dbt[tid] = 0.f;
+        }
+        __syncthreads();
+        float cr[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float t = car[p * DK + c0 + j];
+                if (p < part) cr[j] += t;
+                gC[j] += t;
+            }
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float g = G[i][j] + cr[j];
+                Gs[r * DKP + c0 + j] = g;
+                if ((r & 15) == 7) gm[(r >> 4) * DK + c0 + j] = g;
+            }
+        }
+        if (part == 0) {
+            gm[4 * DK + c0] = gC[0];
+            gm[4 * DK + c0 + 1] = gC[1];
+        }
+        __syncthreads();
+    }
+    for (int idx = tid; idx < 6 * DK; idx += 256) {
+        const int p = idx / DK, cc = idx % DK;
+        const int R = p < 1 ? 1 : (p < 3 ? 2 : 3);
+        const int I = p - R * (R - 1) / 2;
+        dsc[idx] = dexp2<E>(0.5f * (gm[R * DK + cc] - gm[I * DK + cc]));
+    }
+    __syncthreads();
+
+    // ---- Ab = tril_-1(Kg Kt^T) per block pair; upper blocks zero
+#pragma unroll
+    for (int jp = 0; jp < 3; ++jp) {
+        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
+        if (R < 0) break;
+        const float* dv = dsc + (I < R ? pair_index(R, I) : 0) * DK;
+        const int ra = R * 16 + lr, ib = I * 16 + lr;
+        f32x4 acc = zero4();
+        for (int kk = 0; kk < DK; kk += 4) {
+            const int c = kk + lg;
+            const float a = Ks[ra * DKP + c] * dexp2<E>(Gs[ra * DKP + c] - gm[R * DK + c]);
+            float b = Ks[ib * DKP + c] * dexp2<E>(gm[I * DK + c] - Gs[ib * DKP + c]);
+            if (I < R) b = (b * dv[c]) * dv[c];
+            acc = mma4(a, b, acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
+            As[r * LA + i] = i < r ? acc[e] : 0.f;
+        }
+    }
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += 256) {
+        const int p = idx / (SUB * SUB), e = idx % (SUB * SUB);
+        const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+        const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+        As[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+        Ts[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- T = (I + diag(beta) Ab)^{-1}, blocked forward substitution
+    if (w == 0) {
+        const int base = lg * SUB, col = lr;
+        float x[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+            float acc = (r == col) ? 1.f : 0.f;
+            const float br = bet[base + r];
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= br * As[(base + r) * LA + base + i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) Ts[(base + r) * LA + base + col] = x[r];
+    }
+    __syncthreads();
+    for (int R = 1; R < 4; ++R) {
+        if (w < R) {
+            const int I = w;
+            f32x4 x = zero4();
+            const float br = bet[R * SUB + lr];
+            for (int J = I; J < R; ++J)
+#pragma unroll
+                for (int kk = 0; kk < SUB; kk += 4) {
+                    const float a = br * As[(R * SUB + lr) * LA + J * SUB + kk + lg];
+                    const float b = Ts[(J * SUB + kk + lg) * LA + I * SUB + lr];
+                    x = mma4(a, b, x);
+                }
+            float* xs = Xs + I * SUB * SUB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xs[(4 * lg + e) * SUB + lr] = x[e];
+            f32x4 y = zero4();
+#pragma unroll
+            for (int kk = 0; kk < SUB; kk += 4) {
+                const float a = Ts[(R * SUB + lr) * LA + R * SUB + kk + lg];
+                const float b = xs[(kk + lg) * SUB + lr];
+                y = mma4(a, b, y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ts[(R * SUB + 4 * lg + e) * LA + I * SUB + lr] = -y[e];
+        }
+        __syncthreads();
+    }
+
+    // register fields of this wave's rows
+    f32x4 fQ[NCT], fK[NCT], fG[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) fQ[ct] = fK[ct] = fG[ct] = zero4();
+    const int rowA = w * 16 + lr;                 // A-operand row of this lane
+    const int rowD = w * 16 + 4 * lg;             // first accumulator row of this lane
+    auto qval = [&](int r, int c) -> float {
+        return r < valid ? to_f32(q[(row0 + (size_t)r * H) * DK + c]) : 0.f;
+    };
+    auto vval = [&](int r, int j) -> float {
+        return r < valid ? to_f32(v[(row0 + (size_t)r * H) * DV + j]) : 0.f;
+    };
+    // beta partial sums of this lane's 4 rows, reduced over the 16 lanes of a row group
+    auto add_dbeta = [&](f32x4 s) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float t = s[e];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off);
+            if (lr == 0) dbt[rowD + e] += t;
+        }
+    };
+
+    // ---- dT = (dW Kg^T + dVn V^T) diag(beta), lower block pairs
+#pragma unroll
+    for (int jp = 0; jp < 3; ++jp) {
+        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
+        if (R < 0) break;
+        const int ra = R * 16 + lr, ib = I * 16 + lr;
+        f32x4 acc = zero4();
+        for (int kk = 0; kk < DK; kk += 4) {
+            const int c = kk + lg;
+            acc = mma4(ob[OL::DWT + (size_t)c * C + ra], Ks[ib * DKP + c] * dexp2<E>(Gs[ib * DKP + c]), acc);
+        }
+        for (int kk = 0; kk < DV; kk += 4) {
+            const int j = kk + lg;
+            acc = mma4(ob[OL::DVNT + (size_t)j * C + ra], vval(ib, j), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
+            S1[r * LA + i] = i < r ? bet[i] * acc[e] : 0.f;
+        }
+    }
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += 256) {
+        const int p = idx / (SUB * SUB), e = idx % (SUB * SUB);
+        const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+        const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+        S1[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+    }
+
+    // ---- dBk = T^T dW (into dK, dG, dbeta) and dBv = T^T dVn (dV, dbeta), rows 16w..
+    {
+        f32x4 sb = zero4();
+#pragma unroll 2
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 acc = zero4();
+            for (int kk = 0; kk < C; kk += 4) {
+                const int r = kk + lg;
+                acc = mma4(Ts[r * LA + rowA], ob[OL::DWT + (size_t)(ct * 16 + lr) * C + r], acc);
+            }
+            const int c = ct * 16 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = rowD + e;
+                const float gam = dexp2<E>(Gs[i * DKP + c]), kv = Ks[i * DKP + c];
+                const float bk = bet[i] * acc[e] * gam;          // (beta dBk) e^G
+                sb[e] += acc[e] * kv * gam;                      // dBk . Kg
+                fK[ct][e] += bk;
+                fG[ct][e] += bk * kv;
+            }
+        }
+        for (int jt = 0; jt < DV / 16; ++jt) {
+            f32x4 acc = zero4();
+            for (int kk = 0; kk < C; kk += 4) {
+                const int r = kk + lg;
+                acc = mma4(Ts[r * LA + rowA], ob[OL::DVNT + (size_t)(jt * 16 + lr) * C + r], acc);
+            }
+            const int j = jt * 16 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = rowD + e;
+                const float vv = vval(i, j);
+                sb[e] += acc[e] * vv;
+                if (i < valid) dvo[(row0 + (size_t)i * H) * DV + j] = bet[i] * acc[e];
+            }
+        }
+        add_dbeta(sb);
+    }
+    __syncthreads();
+
+    // ---- dA = tril_-1(-T^T dT T^T): S2 = dT T^T, then rows 16w.. of dA
+    for (int it = 0; it < 4; ++it) {
+        f32x4 acc = zero4();
+        for (int kk = 0; kk < C; kk += 4) {
+            const int b = kk + lg;
+            acc = mma4(S1[rowA * LA + b], Ts[(it * 16 + lr) * LA + b], acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S2[(rowD + e) * LA + it * 16 + lr] = acc[e];
+    }
+    __syncthreads();
+    {
+        f32x4 sb = zero4();
+        f32x4 dA[4];
+        for (int it = 0; it < 4; ++it) {
+            f32x4 acc = zero4();
+            if (it <= w) {
+                for (int kk = 0; kk < C; kk += 4) {
+                    const int a = kk + lg;
+                    acc = mma4(Ts[a * LA + rowA], S2[a * LA + it * 16 + lr], acc);
+                }
+            }
+            const int i = it * 16 + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = rowD + e;
+                const float d = i < r ? -acc[e] : 0.f;
+                sb[e] += d * As[r * LA + i];
+                acc[e] = bet[r] * d;
+            }
+            dA[it] = acc;
+        }
+        add_dbeta(sb);
+        __syncthreads();   // S1 (dT) and S2 (dT T^T) are read by every wave above
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S1[(rowD + e) * LA + it * 16 + lr] = dA[it][e];
+        // dM (lower triangle, from the reverse chain) into S2
+        for (int idx = tid; idx < C * C; idx += 256) {
+            const int i = idx / C, r = idx % C;
+            S2[r * LA + i] = ob[OL::DMT + idx];
+        }
+    }
+    __syncthreads();
+
+    // ---- decayed products: rows r of block X = w against blocks Y <= X
+    //   (beta dA) Kt and dM Kt (row side), and columns i of block X against
+    //   blocks Y >= X: (beta dA)^T Kg and dM^T Qg (column side)
+    const int X = w;
+#pragma unroll 1
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = ct * 16 + lr;   // B-operand column of this lane
+        f32x4 accA = zero4(), accC = zero4(), accB = zero4(), accD = zero4();
+        for (int Y = 0; Y <= X; ++Y) {
+            const float s = Y < X ? dsc[pair_index(X, Y) * DK + c] : 1.f;
+#pragma unroll
+            for (int ks = 0; ks < SUB; ks += 4) {
+                const int y = Y * 16 + ks + lg;
+                const float bkr = ((Ks[y * DKP + c] * dexp2<E>(gm[Y * DK + c] - Gs[y * DKP + c])) * s) * s;
+                accA = mma4(S1[rowA * LA + y], bkr, accA);
+                accC = mma4(S2[rowA * LA + y], bkr, accC);
+            }
+        }
+        for (int Y = X; Y < 4; ++Y) {
+            const float s = Y > X ? dsc[pair_index(Y, X) * DK + c] : 1.f;
+#pragma unroll
+            for (int ks = 0; ks < SUB; ks += 4) {
+                const int y = Y * 16 + ks + lg;
+                const float el = (dexp2<E>(Gs[y * DKP + c] - gm[Y * DK + c]) * s) * s;
+                accB = mma4(S1[y * LA + rowA], Ks[y * DKP + c] * el, accB);
+                accD = mma4(S2[y * LA + rowA], qval(y, c) * el, accD);
+            }
+        }
+        const int cc = ct * 16 + lr;   // accumulator column
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowD + e;
+            const float gr = Gs[r * DKP + cc], gX = gm[X * DK + cc];
+            const float fr = dexp2<E>(gr - gX), fc = dexp2<E>(gX - gr);
+            const float kv = Ks[r * DKP + cc], qv = qval(r, cc);
+            const float a = accA[e] * fr, cq = accC[e] * fr, bt = (accB[e] + accD[e]) * fc;
+            fK[ct][e] += a + bt;
+            fQ[ct][e] += cq;
+            fG[ct][e] += a * kv + cq * qv - bt * kv;
+        }
+    }
+
+    // ---- terms from the reverse chain: dQg e^G, dKc e^{G_C - G}, and the
+    //      column sums of dKc e^{G_C - G} k for the last row's dG
+#pragma unroll 1
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = ct * 16 + lr;
+        const f32x4 dqg = *reinterpret_cast<const f32x4*>(ob + OL::DQGT + (size_t)c * C + rowD);
+        const f32x4 dkc = *reinterpret_cast<const f32x4*>(ob + OL::DKCT + (size_t)c * C + rowD);
+        float cs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowD + e;
+            const float g = Gs[r * DKP + c];
+            const float gam = dexp2<E>(g), ec = dexp2<E>(gm[4 * DK + c] - g);
+            const float kv = Ks[r * DKP + c], qv = qval(r, c);
+            fQ[ct][e] += dqg[e] * gam;
+            fK[ct][e] += dkc[e] * ec;
+            const float t = dkc[e] * ec * kv;
+            fG[ct][e] += dqg[e] * gam * qv - t;
+            cs += t;
+        }
+        cs += __shfl_xor(cs, 16);
+        cs += __shfl_xor(cs, 32);
+        if (lg == 0) car[w * DK + c] = cs;
+    }
+    __syncthreads();
+    if (w == 3 && lg == 3) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = ct * 16 + lr;
+            fG[ct][3] += ob[OL::DGC + c] + car[c] + car[DK + c] + car[2 * DK + c] + car[3 * DK + c];
+        }
+    }
+    // outputs dq, dk; dG into LDS (G is no longer read)
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = ct * 16 + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = rowD + e;
+            if (r < valid) {
+                dq[(row0 + (size_t)r * H) * DK + c] = fQ[ct][e];
+                dk[(row0 + (size_t)r * H) * DK + c] = fK[ct][e];
+            }
+        }
+    }
+    __syncthreads();   // every read of G and of the column sums is done
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Gs[(rowD + e) * DKP + ct * 16 + lr] = fG[ct][e];
+    __syncthreads();
+
+    // ---- dg = reverse cumulative sum of dG over the chunk, dz
+    {
+        const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+        float suf[RP][2];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = RP - 1; i >= 0; --i) {
+            s0 += Gs[(r0 + i) * DKP + c0];
+            s1 += Gs[(r0 + i) * DKP + c0 + 1];
+            suf[i][0] = s0;
+            suf[i][1] = s1;
+        }
+        car[part * DK + c0] = s0;
+        car[part * DK + c0 + 1] = s1;
+        __syncthreads();
+        float cr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (p > part) cr[j] += car[p * DK + c0 + j];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+            if (r < valid) {
+                const size_t off = (row0 + (size_t)r * H) * DK + c0;
+                const typename Pair<E>::type zz = load2<E>(z + off);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float sg = 1.0f / (1.0f + expf(-to_f32(zz[j])));
+                    dz[off + j] = (suf[i][j] + cr[j]) * g_min * sg * (1.0f - sg);
+                }
+            }
+        }
+    }
+    if (tid < valid) dbeta[row0 + (size_t)tid * H] = dbt[tid];
+}
+
+template <class E, int DK, int DV>
+hipError_t launch_t(const BwdArgs& a) {
+    typedef typename Compute<E>::type CT;
+    const Lay lo = lay_t<CT, DK, DV>(a.B, a.T, a.H);
+    unsigned char* ws = (unsigned char*)a.workspace;
+    hipStream_t st = (hipStream_t)a.stream;
+    const int NC = (a.T + C - 1) / C;
+    hipError_t err = launch_chunk_bwd_forward(a, ws + lo.fws, ws + lo.bws, (float*)(ws + lo.st), ws + lo.vn);
+    if (err != hipSuccess) return err;
+    typedef DChain<E, DK, DV> LC_;
+    if ((err = hipFuncSetAttribute((const void*)dchain_kernel<E, DK, DV>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LC_::LDS)) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((dchain_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(256), LC_::LDS, st, (const E*)a.dout,
+                       a.ds_final, a.ds0, a.T, a.H, NC, (const unsigned char*)(ws + lo.fws),
+                       (const unsigned char*)(ws + lo.bws), (const float*)(ws + lo.st), (const CT*)(ws + lo.vn),
+                       ws + lo.ob);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    typedef DIntra<E, DK, DV> LI;
+    if ((err = hipFuncSetAttribute((const void*)dintra_kernel<E, DK, DV>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS)) != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((dintra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(256), LI::LDS, st, (const E*)a.q,
+                       (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.T, a.H, NC,
+                       (const unsigned char*)(ws + lo.ob), a.dq, a.dk, a.dv, a.dz, a.dbeta);
+    return hipGetLastError();
+}
+
+// fp32 tokens: the reverse chain's LDS holds fp32 tiles, which fit for d_v = 64
+bool chunkwise(int dk, int dv, bool bf16) { return bf16 || dv == 64; }
+
+template <class CT>
+size_t ws_t(int B, int T, int H, int dk, int dv) {
+    if (dk == 128 && dv == 128) return lay_t<CT, 128, 128>(B, T, H).total;
+    if (dk == 128 && dv == 64) return lay_t<CT, 128, 64>(B, T, H).total;
+    if (dk == 64 && dv == 128) return lay_t<CT, 64, 128>(B, T, H).total;
+    return lay_t<CT, 64, 64>(B, T, H).total;
+}
+
+hipError_t launch_bf16(const BwdArgs& a) {
+    if (a.dk_dim == 128 && a.dv_dim == 128) return launch_t<bf16, 128, 128>(a);
+    if (a.dk_dim == 128 && a.dv_dim == 64) return launch_t<bf16, 128, 64>(a);
+    if (a.dk_dim == 64 && a.dv_dim == 128) return launch_t<bf16, 64, 128>(a);
+    return launch_t<bf16, 64, 64>(a);
+}
+
+hipError_t launch_f32(const BwdArgs& a) {   // d_v = 64 only (chunkwise())
+    if (a.dk_dim == 128) return launch_t<float, 128, 64>(a);
+    return launch_t<float, 64, 64>(a);
+}
+
+}  // namespace bwdc
+
+size_t chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, bool half) {
+    const size_t seq = bwd_workspace_bytes(B, T, H, dk, dv);
+    if (!bwdc::chunkwise(dk, dv, half)) return seq;
+    const size_t ch = half ? bwdc::ws_t<bf16>(B, T, H, dk, dv)
+                           : (dk == 128 ? bwdc::lay_t<float, 128, 64>(B, T, H).total
+                                        : bwdc::lay_t<float, 64, 64>(B, T, H).total);
+    return ch > seq ? ch : seq;
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs& a) {
+    if (a.T == 0 || a.g_min < CHUNK_G_MIN_LIMIT || !bwdc::chunkwise(a.dk_dim, a.dv_dim, a.bf16)) return launch_bwd(a);
+    return a.bf16 ? bwdc::launch_bf16(a) : bwdc::launch_f32(a);
+}
+
+}  // namespace kda

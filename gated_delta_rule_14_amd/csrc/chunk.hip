@@ -40,38 +40,10 @@
 // (k e^{G_m(I) - G_i} s) s with s = e^{(G_m(R) - G_m(I)) / 2}, so that s stays
 // normal whenever the product is above 2^-126, and what underflow drops
 // stays below 2^-45 after the row factor (at most 2^81).
-#include "kda_device.hpp"
+#include "chunk_layout.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
-
-constexpr int C = 64;     // chunk length
-constexpr int SUB = 16;   // block size of the triangular solve and of A / M
-
-template <class E> struct Compute { typedef bf16 type; };
-template <> struct Compute<float> { typedef float type; };
-
-// exp for decay factors: libm-accurate on the fp32 path, the hardware
-// exp2-based one on the bf16 path.
-template <class E> __device__ __forceinline__ float dexp(float x) { return __expf(x); }
-template <> __device__ __forceinline__ float dexp<float>(float x) { return expf(x); }
-template <class E> __device__ __forceinline__ float dsigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + dexp<E>(-x)); }
-
-constexpr size_t align16(size_t x) { return (x + 15) / 16 * 16; }
-constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-
-// Workspace block of one (b, h, chunk), offsets in elements of the compute
-// type CT; every part starts on a 16-byte boundary.
-template <class CT, int DK, int DV>
-struct Ws {
-    static constexpr size_t W = 0;                     // (C, DK)  row-major
-    static constexpr size_t UT = W + (size_t)C * DK;   // (DV, C)  U transposed
-    static constexpr size_t M = UT + (size_t)DV * C;   // (C, C)
-    static constexpr size_t QG = M + (size_t)C * C;    // (C, DK)  q * e^{G}
-    static constexpr size_t KGT = QG + (size_t)C * DK; // (DK, C)  (k * e^{G_C - G})^T
-    static constexpr size_t END = KGT + (size_t)DK * C;
-    static constexpr size_t BYTES = END * sizeof(CT) + DK * sizeof(float);  // + e^{G_C} fp32
-};
 
 // ---------------------------------------------------------------------------
 // Intra-chunk work of one (b, h, chunk): 256 threads.
@@ -115,11 +87,12 @@ __constant__ int kPairs[4][3][2] = {{{0, 0}, {1, 0}, {3, 3}},
 template <class E> __device__ __forceinline__ float dexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 template <> __device__ __forceinline__ float dexp2<float>(float x) { return exp2f(x); }
 
-template <class E, int DK, int DV>
+template <class E, int DK, int DV, bool BWD>
 __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __restrict__ k,
                                             const E* __restrict__ v, const E* __restrict__ z,
                                             const E* __restrict__ beta, float g_min, int valid, size_t row0,
-                                            int H, unsigned char* __restrict__ blk, unsigned char* smem) {
+                                            int H, unsigned char* __restrict__ blk, unsigned char* smem,
+                                            unsigned char* __restrict__ bblk) {
     typedef Intra<E, DK, DV> L;
     typedef typename L::CT CT;
     typedef Mfma<CT> MF;
@@ -146,6 +119,11 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     CT* gQG = reinterpret_cast<CT*>(blk) + WL::QG;
     CT* gKGT = reinterpret_cast<CT*>(blk) + WL::KGT;
     float* gEGC = reinterpret_cast<float*>(reinterpret_cast<CT*>(blk) + WL::END);
+    typedef WsB<CT, DK, DV> WB;
+    CT* gMT = reinterpret_cast<CT*>(bblk) + WB::MT;
+    CT* gKC = reinterpret_cast<CT*>(bblk) + WB::KC;
+    CT* gQGT = reinterpret_cast<CT*>(bblk) + WB::QGT;
+    CT* gWT = reinterpret_cast<CT*>(bblk) + WB::WT;
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int last = valid - 1;
@@ -228,7 +206,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             eGm[j] = dexp2<E>(gmR[j]);
             eCGm[j] = dexp2<E>(gC[j] - gmR[j]);
         }
-        float rk[2][RP], kg[2][RP];
+        float rk[2][RP], kg[2][RP], qg[BWD ? 2 : 1][BWD ? RP : 1];
 #pragma unroll
         for (int i = 0; i < RP; ++i) {
             const int r = r0 + i;
@@ -242,11 +220,13 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
                 kR[j] = kv[i][j] * right;
                 rk[j][i] = bet[r] * kl[j] * eGm[j];
                 kg[j][i] = kR[j] * eCGm[j];
+                if constexpr (BWD) qg[j][i] = ql[j] * eGm[j];
             }
             store2<CT>(KL + r * LDK + c0, kl[0], kl[1]);
             store2<CT>(QL + r * LDK + c0, ql[0], ql[1]);
             store2<CT>(KR + r * LDK + c0, kR[0], kR[1]);
             store2<CT>(gQG + r * DK + c0, ql[0] * eGm[0], ql[1] * eGm[1]);
+            if constexpr (BWD) store2<CT>(gKC + r * DK + c0, kg[0][i], kg[1][i]);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -254,6 +234,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             for (int i = 0; i < RP; i += 8) {
                 store8<CT>(RT + (c0 + j) * LC + r0 + i, &rk[j][i]);
                 store8<CT>(gKGT + (c0 + j) * C + r0 + i, &kg[j][i]);
+                if constexpr (BWD) store8<CT>(gQGT + (c0 + j) * C + r0 + i, &qg[j][i]);
             }
     }
     for (int idx = tid; idx < 6 * DK; idx += 256) {
@@ -297,6 +278,10 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             mv[e] = (i0 + e <= r) ? accM[e] : 0.f;
         }
         store4<CT>(gM + r * C + i0, mv);
+        if constexpr (BWD) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) gMT[(i0 + e) * C + r] = from_f32<CT>(mv[e]);
+        }
     }
     if (w == 3) {
         // strictly upper blocks of M are zero
@@ -305,6 +290,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
             const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
             store4<CT>(gM + (R * SUB + (l & 15)) * C + I * SUB + 4 * (l >> 4), zero4());
+            if constexpr (BWD) store4<CT>(gMT + (I * SUB + (l & 15)) * C + R * SUB + 4 * (l >> 4), zero4());
         }
     }
     __syncthreads();   // KL / QL / KR are dead from here on; As, Ts and R_V^T alias them
@@ -401,6 +387,11 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             for (int s2 = 0; s2 < NKS; ++s2)
                 if (s2 < ns) acc = MF::mma(load_frag<CT>(RT, LC, cb * 16, s2 * MF::KSTEP), tf[s2], acc);
             store4<CT>(gW + (w * SUB + (l & 15)) * DK + cb * 16 + 4 * (l >> 4), acc);
+            if constexpr (BWD) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    gWT[(cb * 16 + 4 * (l >> 4) + e) * C + w * SUB + (l & 15)] = from_f32<CT>(acc[e]);
+            }
         }
 #pragma unroll 2
         for (int cb = 0; cb < DV / 16; ++cb) {
@@ -413,18 +404,21 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     }
 }
 
-template <class E, int DK, int DV>
+// bws: with BWD, the base of the backward chain's operand blocks (WsB)
+template <class E, int DK, int DV, bool BWD = false>
 __global__ __launch_bounds__(256) void chunk_intra_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ z, const E* __restrict__ beta, float g_min, int T, int H, int NC,
-    unsigned char* __restrict__ ws) {
+    unsigned char* __restrict__ ws, unsigned char* __restrict__ bws = nullptr) {
     typedef typename Compute<E>::type CT;
     extern __shared__ __align__(16) unsigned char smem[];
     const int n = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int t0 = n * C;
     const size_t row0 = ((size_t)b * T + t0) * H + h;
-    unsigned char* blk = ws + (((size_t)b * H + h) * NC + n) * Ws<CT, DK, DV>::BYTES;
-    intra_chunk<E, DK, DV>(q, k, v, z, beta, g_min, min(C, T - t0), row0, H, blk, smem);
+    const size_t cid = ((size_t)b * H + h) * NC + n;
+    unsigned char* blk = ws + cid * Ws<CT, DK, DV>::BYTES;
+    unsigned char* bblk = BWD ? bws + cid * WsB<CT, DK, DV>::BYTES : nullptr;
+    intra_chunk<E, DK, DV, BWD>(q, k, v, z, beta, g_min, min(C, T - t0), row0, H, blk, smem, bblk);
 }
 
 // ---------------------------------------------------------------------------
@@ -441,7 +435,10 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(
 // for the next chunk straight from the workspace into registers while the
 // current chunk is computed; only X^T and V_new^T go through LDS.
 // ---------------------------------------------------------------------------
-enum { CM_EXPAND = 0, CM_COMPOSE_R = 1, CM_COMPOSE_P = 2 };
+//   CM_STATES    as CM_EXPAND without outputs, storing instead each chunk's
+//                entering state X (fp32) and V_new (compute type): the
+//                forward quantities the backward needs (kda_chunk_bwd).
+enum { CM_EXPAND = 0, CM_COMPOSE_R = 1, CM_COMPOSE_P = 2, CM_STATES = 3 };
 
 template <class E, int DK, int DV, int NCOL, int TV, int MODE>
 struct Chain {
@@ -504,7 +501,8 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
                                            int nfill, int T, int H, int b, int h, int col0,
                                            const unsigned char* chain, E* __restrict__ o,
                                            f32x4 (&accS)[DK / 64][TV / 16], typename Compute<E>::type* Sb0,
-                                           typename Compute<E>::type* Sb1, typename Compute<E>::type* Vn) {
+                                           typename Compute<E>::type* Sb1, typename Compute<E>::type* Vn,
+                                           float* __restrict__ st_out, typename Compute<E>::type* __restrict__ vn_out) {
     typedef Chain<E, DK, DV, NCOL, TV, MODE> L;
     typedef typename L::CT CT;
     typedef typename L::MF MF;
@@ -514,6 +512,18 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
     CT* sb = (n & 1) ? Sb1 : Sb0;
     CT* sbn = (n & 1) ? Sb0 : Sb1;
     L::load(fill, chain + (size_t)nfill * WL::BYTES, w, l, col0);
+    if constexpr (MODE == CM_STATES) {
+        // the state entering chunk n, rows w*DK/4 + rb*16 + 4(l/16) + e
+        float* so = st_out + (size_t)n * DK * DV;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    so[(size_t)(w * (DK / 4) + rb * 16 + 4 * (l >> 4) + e) * DV + col0 + ct * 16 + (l & 15)] =
+                        accS[rb][ct][e];
+    }
 
     // V_new = U - W X (rows 16w.. x TV) and O^T = X^T (Q e^G)^T (TV x rows 16w..)
     f32x4 accP[NT], accO[L::OUT ? NT : 1];
@@ -536,6 +546,12 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
         f32x4 vn = -accP[ct];
         if constexpr (L::HASU) vn += widen4(cur.u[ct]);
         store4<CT>(Vn + (ct * 16 + (l & 15)) * LC + w * 16 + 4 * (l >> 4), vn);
+        if constexpr (MODE == CM_STATES) {
+            // V_new row-major, (C, DV) per chunk
+            CT* vo = vn_out + (size_t)n * C * DV + (size_t)(w * 16 + 4 * (l >> 4)) * DV + col0 + ct * 16 + (l & 15);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vo[(size_t)e * DV] = from_f32<CT>(vn[e]);
+        }
     }
     __syncthreads();
 
@@ -576,10 +592,14 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
 //   xin : CM_EXPAND entry states [nseg][B*H][DK][NCOL] (NULL = zeros)
 //   xout: CM_EXPAND final state [B*H][DK][NCOL] when nseg == 1 (NULL = skip);
 //         CM_COMPOSE_* the range results [nseg][B*H][DK][NCOL]
+//   st_out, vn_out: CM_STATES per-chunk entering states [B*H][NC][DK][DV] and
+//         V_new [B*H][NC][C][DV] (single level only)
 template <class E, int DK, int DV, int NCOL, int TV, int MODE>
 __global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const float* __restrict__ xin,
                                                     float* __restrict__ xout, int T, int H, int NC, int L,
-                                                    int nchain, const unsigned char* __restrict__ ws) {
+                                                    int nchain, const unsigned char* __restrict__ ws,
+                                                    float* __restrict__ st_out = nullptr,
+                                                    typename Compute<E>::type* __restrict__ vn_out = nullptr) {
     typedef Chain<E, DK, DV, NCOL, TV, MODE> LC_;
     typedef typename LC_::CT CT;
     typedef Ws<CT, DK, DV> WL;
@@ -613,7 +633,8 @@ __global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const flo
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 float x = 0.f;
-                if constexpr (MODE == CM_EXPAND) x = xin ? xin[(xrow + row + e) * NCOL + col] : 0.f;
+                if constexpr (MODE == CM_EXPAND || MODE == CM_STATES)
+                    x = xin ? xin[(xrow + row + e) * NCOL + col] : 0.f;
                 if constexpr (MODE == CM_COMPOSE_P) x = (row + e == col) ? 1.f : 0.f;
                 accS[rb][ct][e] = x;
             }
@@ -621,16 +642,20 @@ __global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const flo
         }
 
     // two operand sets: chunk n is consumed while chunk n+1 loads
+    float* st = MODE == CM_STATES ? st_out + bh * NC * DK * DV : nullptr;
+    CT* vo = MODE == CM_STATES ? vn_out + bh * NC * C * DV : nullptr;
     typename LC_::Regs r0, r1;
     LC_::load(r0, chain + (size_t)n0 * WL::BYTES, w, l, col0);
     __syncthreads();
     int n = n0;
     for (; n + 2 <= n1; n += 2) {
-        chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n + 1, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+        chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n + 1, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn, st,
+                                              vo);
         chain_step<E, DK, DV, NCOL, TV, MODE>(r1, r0, n + 1, min(n + 2, n1 - 1), T, H, b, h, col0, chain, o, accS,
-                                              Sb0, Sb1, Vn);
+                                              Sb0, Sb1, Vn, st, vo);
     }
-    if (n < n1) chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn);
+    if (n < n1)
+        chain_step<E, DK, DV, NCOL, TV, MODE>(r0, r1, n, n, T, H, b, h, col0, chain, o, accS, Sb0, Sb1, Vn, st, vo);
 
     if (xout) {
         const size_t orow = MODE == CM_EXPAND ? bh * DK : xrow;
@@ -896,6 +921,47 @@ hipError_t launch_seg_scan(const float* P, const float* R, const float* s0, floa
     if (dk == 128 && dv == 64) return launch_scan_t<128, 64>(P, R, s0, Sent, s_final, nseg, nchain, st);
     if (dk == 64 && dv == 128) return launch_scan_t<64, 128>(P, R, s0, Sent, s_final, nseg, nchain, st);
     return launch_scan_t<64, 64>(P, R, s0, Sent, s_final, nseg, nchain, st);
+}
+
+// The forward half of kda_chunk_bwd: the per-chunk operands of both
+// directions (fws: Ws blocks, bws: WsB blocks), then the chunk recurrence
+// from s0 storing each chunk's entering state and V_new.
+template <class E, int DK, int DV>
+static hipError_t launch_bwd_forward_t(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+                                       void* vn) {
+    typedef typename Compute<E>::type CT;
+    constexpr int TVS = sizeof(CT) == 2 ? 32 : 16;
+    const int NC = (a.T + C - 1) / C;
+    const int nchain = a.B * a.H;
+    hipStream_t st = (hipStream_t)a.stream;
+    typedef Intra<E, DK, DV> LI;
+    hipError_t err = set_lds(chunk_intra_kernel<E, DK, DV, true>, LI::LDS);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((chunk_intra_kernel<E, DK, DV, true>), dim3(NC, a.H, a.B), dim3(256), LI::LDS, st,
+                       (const E*)a.q, (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.T,
+                       a.H, NC, fws, bws);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    typedef Chain<E, DK, DV, DV, TVS, CM_STATES> LX;
+    if ((err = set_lds(chain_kernel<E, DK, DV, DV, TVS, CM_STATES>, LX::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((chain_kernel<E, DK, DV, DV, TVS, CM_STATES>), dim3((DV / TVS) * nchain), dim3(256), LX::LDS,
+                       st, (E*)nullptr, a.s0, (float*)nullptr, a.T, a.H, NC, NC, nchain, (const unsigned char*)fws,
+                       states, (CT*)vn);
+    return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_bwd_forward_e(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+                                       void* vn) {
+    if (a.dk_dim == 128 && a.dv_dim == 128) return launch_bwd_forward_t<E, 128, 128>(a, fws, bws, states, vn);
+    if (a.dk_dim == 128 && a.dv_dim == 64) return launch_bwd_forward_t<E, 128, 64>(a, fws, bws, states, vn);
+    if (a.dk_dim == 64 && a.dv_dim == 128) return launch_bwd_forward_t<E, 64, 128>(a, fws, bws, states, vn);
+    return launch_bwd_forward_t<E, 64, 64>(a, fws, bws, states, vn);
+}
+
+hipError_t launch_chunk_bwd_forward(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+                                    void* vn) {
+    return a.bf16 ? launch_bwd_forward_e<bf16>(a, fws, bws, states, vn)
+                  : launch_bwd_forward_e<float>(a, fws, bws, states, vn);
 }
 
 hipError_t launch_chunk(const ChunkArgs& a) {

@@ -383,6 +383,32 @@ kda_status kda_recurrent_bwd(const void* q, const void* k, const void* v, const 
     return finish(kda::launch_bwd(a), stream);
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || chunk != 64 || !dim_ok(dk) || !dim_ok(dv)) return 0;
+    if (dt != KDA_F32 && dt != KDA_BF16) return 0;
+    return kda::chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, const void* beta, float g_min,
+                         const float* s0, const void* grad_o, const float* grad_s_final, float* grad_q,
+                         float* grad_k, float* grad_v, float* grad_z, float* grad_beta, float* grad_s0, int B, int T,
+                         int H, int dk, int dv, int chunk, kda_dtype dt, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    const kda_status st = check_chunk_args(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final, B, T, H, dk, dv, chunk,
+                                           dt, workspace);
+    if (st != KDA_OK || B == 0 || H == 0) return st;
+    if (T > 0 && (!grad_q || !grad_k || !grad_v || !grad_z || !grad_beta)) return KDA_ERR_NULL;
+    if (!aligned16(grad_q) || !aligned16(grad_k) || !aligned16(grad_v) || !aligned16(grad_z) ||
+        !aligned16(grad_beta) || !aligned16(grad_s0))
+        return KDA_ERR_ALIGN;
+    const size_t need = kda::chunk_bwd_workspace_bytes(B, T, H, dk, dv, dt == KDA_BF16);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    kda::BwdArgs a{q, k, v, z, beta, g_min, s0, grad_o, grad_s_final, grad_q, grad_k, grad_v, grad_z, grad_beta,
+                   grad_s0, B, T, H, dk, dv, dt == KDA_BF16, workspace, stream};
+    if (T == 0 && !grad_s0) return KDA_OK;
+    return finish(kda::launch_chunk_bwd(a), stream);
+}
+
 kda_status kda_dplr_fwd(const void* q, const void* k, const void* v, const void* z, const void* a, const void* b,
                         float g_min, const float* s0, void* o, float* s_final, int B, int T, int H, int dk, int dv,
                         kda_dtype dt, void* stream) {

@@ -19,6 +19,8 @@ Names follow the C ABI in include/kda.h:
                      kernels, then the projection)
   recurrent_bwd   -> kda_recurrent_bwd: gradients of the recurrence with
                      respect to q, k, v, z, beta and s0 (fp32)
+  chunk_bwd       -> kda_chunk_bwd: the same gradients by 64-token chunks
+                     on MFMA
   dplr_fwd        -> kda_dplr_fwd: the general diagonal-plus-low-rank
                      recurrence S = (Diag(alpha) - a b^T) S + k v^T over a
                      sequence (token-sequential)
@@ -360,6 +362,42 @@ def recurrent_bwd(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final=None, *, wan
         _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(grad_o), _p(grad_s_final),
         _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dz"]), _p(out["dbeta"]), _p(out["ds0"]),
         B, T, H, dk, dv, _dt(q), _p(workspace), ws_bytes, _stream(dev)))
+    return out
+
+
+def chunk_bwd_workspace_bytes(B, T, H, dk, dv, dtype):
+    return int(lib().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, CHUNK,
+                                                   KDA_BF16 if dtype == torch.bfloat16 else KDA_F32))
+
+
+def chunk_bwd(q, k, v, z, beta, g_min, s0, grad_o, grad_s_final=None, *, want_s0=True, workspace=None):
+    """Chunkwise gradients (kda_chunk_bwd); arguments and results as
+    recurrent_bwd."""
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("z", z), ("beta", beta), ("grad_o", grad_o)):
+        _need(t, name, dev)
+        if t.dtype != q.dtype:
+            raise TypeError(f"libkda: {name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    for name, t in (("s0", s0), ("grad_s_final", grad_s_final)):
+        if t is not None:
+            _need(t, name, dev)
+            if t.dtype != torch.float32:
+                raise TypeError(f"libkda: {name} must be float32")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = {"dq": torch.empty((B, T, H, dk), **f32), "dk": torch.empty((B, T, H, dk), **f32),
+           "dv": torch.empty((B, T, H, dv), **f32), "dz": torch.empty((B, T, H, dk), **f32),
+           "dbeta": torch.empty((B, T, H), **f32),
+           "ds0": torch.empty((B, H, dk, dv), **f32) if want_s0 else None}
+    need = lib().kda_chunk_bwd_workspace_bytes(B, T, H, dk, dv, CHUNK, _dt(q))
+    if workspace is None and need > 0:
+        workspace = torch.empty(int(need), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check("kda_chunk_bwd", lib().kda_chunk_bwd(
+        _p(q), _p(k), _p(v), _p(z), _p(beta), float(g_min), _p(s0), _p(grad_o), _p(grad_s_final),
+        _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dz"]), _p(out["dbeta"]), _p(out["ds0"]),
+        B, T, H, dk, dv, CHUNK, _dt(q), _p(workspace), ws_bytes, _stream(dev)))
     return out
 
 

@@ -392,6 +392,34 @@ kda_status kda_dplr_chunk_fwd(const void* q, const void* k, const void* v, const
                               kda_dtype dt, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same gradients as kda_recurrent_bwd by 64-token chunks, on MFMA: the
+ * chain rule through the chunk form (Kimi Linear tech report, section 3.1
+ * and appendix B, Eqs. 16-19) instead of through single tokens.  Per chunk
+ * with entering state S and the gradient dS' of the state leaving it:
+ *   dV_new = M^T dO + (K e^{G_C - G}) dS',
+ *   dS     = e^{G_C} dS' + (Q e^G)^T dO - W^T dV_new   (the chunks in reverse),
+ * and the token gradients from dV_new, S, dS' and the chunk's own products
+ * (the adjoint of T = (I + A)^{-1} is -T^T dT T^T; every product carrying
+ * e^{G_r - G_i} is evaluated per 16-token block pair around reference rows,
+ * as in the forward).  Arguments as for kda_recurrent_bwd, plus chunk (64);
+ * the workspace, kda_chunk_bwd_workspace_bytes() bytes, holds per chunk the
+ * forward operands of both directions, the entering state (fp32), V_new and
+ * the reverse pass's products for the per-chunk kernel (fp32).
+ * Precision: bf16 tokens run the chunk recurrences on bf16 MFMA with fp32
+ * accumulation and state (as kda_chunk_fwd does), so the gradients carry
+ * bf16 operand rounding; the per-chunk kernel runs on fp32 MFMA.  fp32 tokens
+ * run on fp32 MFMA throughout where d_v = 64; with fp32 tokens and d_v = 128,
+ * for g_min below KDA_CHUNK_G_MIN_LIMIT, and for T == 0, the call runs the
+ * token-sequential kernel of kda_recurrent_bwd.
+ */
+size_t kda_chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt);
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* z, const void* beta,
+                         float g_min, const float* s0, const void* grad_o, const float* grad_s_final,
+                         float* grad_q, float* grad_k, float* grad_v, float* grad_z, float* grad_beta,
+                         float* grad_s0, int B, int T, int H, int dk, int dv, int chunk, kda_dtype dt,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement helper: x <- s * x in place over n fp32 values (n a multiple
  * of 4, x 16-byte aligned), every byte read once and written once with
  * 16-byte accesses -- the access pattern of the decode step's state.  It
