@@ -357,11 +357,12 @@ def bench_train_layer(torch, kda, ki, calls=5):
 
 
 def bench_backward(torch, kda, ki, calls=2):
-    """kda_recurrent_bwd on the training shape (B=8, T=8192, H=32, d=128, bf16
-    tokens): the gradients with respect to q, k, v, z, beta and S0 for given
-    gradients of o and S_final.  Algorithmic bytes per token-head: the token
-    inputs and the output gradient (bf16, 5 x 256 + 2) and the fp32 gradients
-    written (4 x 512 + 4)."""
+    """The gradients with respect to q, k, v, z, beta and S0 for given
+    gradients of o and S_final on the training shape (B=8, T=8192, H=32,
+    d=128, bf16 tokens): kda_chunk_bwd (chunkwise, MFMA) and, beside it,
+    kda_recurrent_bwd (token-sequential).  Algorithmic bytes per token-head:
+    the token inputs and the output gradient (bf16, 5 x 256 + 2) and the fp32
+    gradients written (4 x 512 + 4)."""
     cfg = ki.WORKLOADS["train_8x8k"]
     B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
     dev = torch.device("cuda:0")
@@ -370,16 +371,25 @@ def bench_backward(torch, kda, ki, calls=2):
     g.manual_seed(3)
     do = torch.randn((B, T, H, dv), generator=g, device=dev).to(torch.bfloat16)
     dsf = torch.randn((B, H, dk, dv), generator=g, device=dev)
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(B, T, H, dk, dv, torch.bfloat16), dtype=torch.uint8,
+                     device=dev)
+    per = _time_calls(torch, lambda: kda.chunk_bwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, None,
+                                                   do, dsf, workspace=ws), 5)
+    ws_bytes = ws.numel()
+    del ws
     ws = torch.empty(kda.recurrent_bwd_workspace_bytes(B, T, H, dk, dv), dtype=torch.uint8, device=dev)
-    per = _time_calls(torch, lambda: kda.recurrent_bwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, None,
-                                                       do, dsf, workspace=ws), calls)
+    per_seq = _time_calls(torch, lambda: kda.recurrent_bwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN,
+                                                           None, do, dsf, workspace=ws), calls)
     nbytes = B * T * H * (5 * 256 + 2 + 4 * 512 + 4) + 2 * B * H * dk * dv * 4
     gbs = nbytes / per / 1e9
     del x, do, dsf, ws
     torch.cuda.empty_cache()
     return {"workload": "train_8x8k backward", "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "dtype": "bf16",
-            "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
-            "kernels": "kda_recurrent_bwd (recurrent_bwd_kernel, token-sequential)",
+            "calls": 5, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
+            "kernels": "kda_chunk_bwd (chunk_intra_kernel, chain_kernel storing states, dchain_kernel, "
+                       "dintra_kernel)",
+            "workspace_bytes": ws_bytes,
+            "token_sequential_us_per_call": round(per_seq * 1e6, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
 

@@ -26,7 +26,8 @@
 //    dS in MFMA accumulators; per chunk dVn and the products with S, Vn and
 //    dS' (dQg, dW, dKc, dM and e^{G_C} rowsum(S dS')), written for the next
 //    kernel;
-//  * dintra_kernel, one workgroup per chunk: everything else, on fp32 MFMA.
+//  * dintra_kernel, one 512-thread workgroup per chunk: everything else, on
+//    fp32 MFMA.
 //    The products whose terms carry e^{G_r - G_i} are evaluated per 16-row
 //    block pair around reference rows m = 16R + 7, as in the forward, with
 //    the cross-block factor applied as its square root twice.
@@ -293,15 +294,18 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
 }
 
 // ---------------------------------------------------------------------------
-// Per-chunk gradients: 256 threads, fp32 MFMA (16x16x4).  Wave w owns token
-// rows 16w..16w+15 of the C x d_k results dQ, dK and dG, held in registers in
-// the accumulator layout (rows 16w + 4(l/16) + e, column ct*16 + l%16).
+// Per-chunk gradients: 512 threads, fp32 MFMA (16x16x4).  Wave w owns token
+// rows 16X..16X+15 (X = w % 4) and one half of the d_k columns (w / 4) of the
+// C x d_k results dQ, dK and dG, held in registers in the accumulator layout
+// (rows 16X + 4(l/16) + e, column ct*16 + l%16).
 // ---------------------------------------------------------------------------
 template <class E, int DK, int DV>
 struct DIntra {
-    static constexpr int CP = DK / 2, NPART = 256 / CP, RP = C / NPART;
-    static constexpr int NCT = DK / 16;
+    static constexpr int NTH = 512, NW = 8;
+    static constexpr int CP = DK / 2, NPART = NTH / CP, RP = C / NPART;
+    static constexpr int NCT = DK / 16, NCTH = NCT / 2, NVTH = DV / 32;   // column tiles per half
     static constexpr int DKP = DK + 4, LA = C + 4;
+    static constexpr int NCAR = NPART > NW ? NPART : NW;
     static constexpr size_t OFF_G = 0;                                  // [C][DKP] G (log2 units), then dG
     static constexpr size_t OFF_K = OFF_G + (size_t)C * DKP * 4;        // [C][DKP] k
     static constexpr size_t OFF_A = OFF_K + (size_t)C * DKP * 4;        // [C][LA]  Ab = tril_-1(Kg Kt^T)
@@ -311,24 +315,28 @@ struct DIntra {
     static constexpr size_t OFF_X = OFF_S2 + (size_t)C * LA * 4;        // [3][16][16]
     static constexpr size_t OFF_DSC = OFF_X + 3 * SUB * SUB * 4;        // [6][DK]
     static constexpr size_t OFF_GM = OFF_DSC + 6 * DK * 4;              // [5][DK] G_m(R), G_C
-    static constexpr size_t OFF_CAR = OFF_GM + 5 * DK * 4;              // [max(NPART, 4)][DK]
-    static constexpr size_t OFF_BET = OFF_CAR + (size_t)(NPART > 4 ? NPART : 4) * DK * 4;   // [C]
-    static constexpr size_t OFF_DB = OFF_BET + C * 4;                   // [C] dbeta
-    static constexpr size_t LDS = OFF_DB + C * 4;
+    static constexpr size_t OFF_CAR = OFF_GM + 5 * DK * 4;              // [NCAR][DK]
+    static constexpr size_t OFF_BET = OFF_CAR + (size_t)NCAR * DK * 4;  // [C]
+    static constexpr size_t OFF_DB = OFF_BET + C * 4;                   // [2][C] dbeta, per column half
+    static constexpr size_t LDS = OFF_DB + 2 * C * 4;
     static_assert(LDS <= 160 * 1024, "per-chunk gradient LDS budget");
-    static_assert(RP % 2 == 0 && 16 % RP == 0, "tiling");
+    static_assert(RP % 2 == 0 && 16 % RP == 0 && NCT % 2 == 0 && DV % 32 == 0, "tiling");
 };
 
 // Block pairs (R, I), I <= R, of the 64 x 64 lower triangle, by wave.
-__constant__ int kPairsB[4][3][2] = {{{0, 0}, {1, 0}, {3, 3}},
-                                     {{1, 1}, {2, 0}, {3, 2}},
-                                     {{2, 1}, {2, 2}, {3, 1}},
-                                     {{3, 0}, {-1, -1}, {-1, -1}}};
+__constant__ int kPairsB[8][2][2] = {{{0, 0}, {1, 0}}, {{1, 1}, {2, 0}}, {{2, 1}, {-1, -1}}, {{2, 2}, {-1, -1}},
+                                     {{3, 0}, {-1, -1}}, {{3, 1}, {-1, -1}}, {{3, 2}, {-1, -1}},
+                                     {{3, 3}, {-1, -1}}};
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }   // I < R
 
+__device__ __forceinline__ void upper_block(int p, int& R, int& I) {   // p = 0..5, I > R
+    R = p < 3 ? 0 : (p < 5 ? 1 : 2);
+    I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+}
+
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                      const E* __restrict__ v, const E* __restrict__ z,
                                                      const E* __restrict__ beta, float g_min, int T, int H, int NC,
                                                      const unsigned char* __restrict__ obuf, float* __restrict__ dq,
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
                                                      float* __restrict__ dz, float* __restrict__ dbeta) {
     typedef DIntra<E, DK, DV> L;
     typedef Ob<DK, DV> OL;
-    constexpr int RP = L::RP, DKP = L::DKP, LA = L::LA, NCT = L::NCT;
+    constexpr int NTH = L::NTH, RP = L::RP, DKP = L::DKP, LA = L::LA, NCTH = L::NCTH, NVTH = L::NVTH;
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __align__(16) unsigned char smem[];
     float* Gs = reinterpret_cast<float*>(smem + L::OFF_G);
@@ -355,10 +363,12 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     const int n = blockIdx.x, hh = blockIdx.y, bb = blockIdx.z;
     const int valid = min(C, T - n * C), last = valid - 1;
     const size_t row0 = ((size_t)bb * T + (size_t)n * C) * H + hh;   // token row of chunk row 0
-    const size_t rsk = (size_t)H * DK, rsv = (size_t)H * DV;
     const float* ob = reinterpret_cast<const float*>(obuf + (((size_t)bb * H + hh) * NC + n) * OL::BYTES);
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int lr = l & 15, lg = l >> 4;
+    const int X = w & 3, hf = w >> 2;            // row block and column half of this wave
+    const int rowA = X * 16 + lr;                 // A-operand row of this lane
+    const int rowD = X * 16 + 4 * lg;             // first accumulator row of this lane
 
     // ---- gate, chunk-local scan (log2 units), k into LDS
     {
@@ -388,6 +398,7 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
         if (tid < C) {
             bet[tid] = tid < valid ? to_f32(beta[row0 + (size_t)tid * H]) : 0.f;
             dbt[tid] = 0.f;
+            dbt[C + tid] = 0.f;
         }
         __syncthreads();
         float cr[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
@@ -415,7 +426,7 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
         }
         __syncthreads();
     }
-    for (int idx = tid; idx < 6 * DK; idx += 256) {
+    for (int idx = tid; idx < 6 * DK; idx += NTH) {
         const int p = idx / DK, cc = idx % DK;
         const int R = p < 1 ? 1 : (p < 3 ? 2 : 3);
         const int I = p - R * (R - 1) / 2;
@@ -423,14 +434,15 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     }
     __syncthreads();
 
-    // ---- Ab = tril_-1(Kg Kt^T) per block pair; upper blocks zero
+    // ---- Ab = tril_-1(Kg Kt^T) per block pair; upper blocks of Ab and T zero
 #pragma unroll
-    for (int jp = 0; jp < 3; ++jp) {
+    for (int jp = 0; jp < 2; ++jp) {
         const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
         if (R < 0) break;
         const float* dv = dsc + (I < R ? pair_index(R, I) : 0) * DK;
         const int ra = R * 16 + lr, ib = I * 16 + lr;
         f32x4 acc = zero4();
+#pragma unroll 8
         for (int kk = 0; kk < DK; kk += 4) {
             const int c = kk + lg;
             const float a = Ks[ra * DKP + c] * dexp2<E>(Gs[ra * DKP + c] - gm[R * DK + c]);
@@ -444,10 +456,10 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
             As[r * LA + i] = i < r ? acc[e] : 0.f;
         }
     }
-    for (int idx = tid; idx < 6 * SUB * SUB; idx += 256) {
-        const int p = idx / (SUB * SUB), e = idx % (SUB * SUB);
-        const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
-        const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += NTH) {
+        int R, I;
+        upper_block(idx / (SUB * SUB), R, I);
+        const int e = idx % (SUB * SUB);
         As[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
         Ts[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
     }
@@ -497,40 +509,41 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
         __syncthreads();
     }
 
-    // register fields of this wave's rows
-    f32x4 fQ[NCT], fK[NCT], fG[NCT];
+    // register fields of this wave's rows and column half
+    f32x4 fQ[NCTH], fK[NCTH], fG[NCTH];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) fQ[ct] = fK[ct] = fG[ct] = zero4();
-    const int rowA = w * 16 + lr;                 // A-operand row of this lane
-    const int rowD = w * 16 + 4 * lg;             // first accumulator row of this lane
+    for (int ct = 0; ct < NCTH; ++ct) fQ[ct] = fK[ct] = fG[ct] = zero4();
     auto qval = [&](int r, int c) -> float {
         return r < valid ? to_f32(q[(row0 + (size_t)r * H) * DK + c]) : 0.f;
     };
     auto vval = [&](int r, int j) -> float {
         return r < valid ? to_f32(v[(row0 + (size_t)r * H) * DV + j]) : 0.f;
     };
-    // beta partial sums of this lane's 4 rows, reduced over the 16 lanes of a row group
+    // beta partial sums of this lane's 4 rows, reduced over the 16 lanes of a
+    // row group; one array per column half (no two waves write one slot)
     auto add_dbeta = [&](f32x4 s) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float t = s[e];
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off);
-            if (lr == 0) dbt[rowD + e] += t;
+            if (lr == 0) dbt[hf * C + rowD + e] += t;
         }
     };
 
     // ---- dT = (dW Kg^T + dVn V^T) diag(beta), lower block pairs
 #pragma unroll
-    for (int jp = 0; jp < 3; ++jp) {
+    for (int jp = 0; jp < 2; ++jp) {
         const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
         if (R < 0) break;
         const int ra = R * 16 + lr, ib = I * 16 + lr;
         f32x4 acc = zero4();
+#pragma unroll 8
         for (int kk = 0; kk < DK; kk += 4) {
             const int c = kk + lg;
             acc = mma4(ob[OL::DWT + (size_t)c * C + ra], Ks[ib * DKP + c] * dexp2<E>(Gs[ib * DKP + c]), acc);
         }
+#pragma unroll 8
         for (int kk = 0; kk < DV; kk += 4) {
             const int j = kk + lg;
             acc = mma4(ob[OL::DVNT + (size_t)j * C + ra], vval(ib, j), acc);
@@ -541,24 +554,26 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
             S1[r * LA + i] = i < r ? bet[i] * acc[e] : 0.f;
         }
     }
-    for (int idx = tid; idx < 6 * SUB * SUB; idx += 256) {
-        const int p = idx / (SUB * SUB), e = idx % (SUB * SUB);
-        const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
-        const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += NTH) {
+        int R, I;
+        upper_block(idx / (SUB * SUB), R, I);
+        const int e = idx % (SUB * SUB);
         S1[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
     }
 
-    // ---- dBk = T^T dW (into dK, dG, dbeta) and dBv = T^T dVn (dV, dbeta), rows 16w..
+    // ---- dBk = T^T dW (into dK, dG, dbeta) and dBv = T^T dVn (dV, dbeta):
+    //      rows 16X.., this wave's column half
     {
         f32x4 sb = zero4();
-#pragma unroll 2
-        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll 1
+        for (int ct = 0; ct < NCTH; ++ct) {
+            const int c = (hf * NCTH + ct) * 16 + lr;
             f32x4 acc = zero4();
+#pragma unroll 8
             for (int kk = 0; kk < C; kk += 4) {
                 const int r = kk + lg;
-                acc = mma4(Ts[r * LA + rowA], ob[OL::DWT + (size_t)(ct * 16 + lr) * C + r], acc);
+                acc = mma4(Ts[r * LA + rowA], ob[OL::DWT + (size_t)c * C + r], acc);
             }
-            const int c = ct * 16 + lr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = rowD + e;
@@ -569,18 +584,19 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
                 fG[ct][e] += bk * kv;
             }
         }
-        for (int jt = 0; jt < DV / 16; ++jt) {
+#pragma unroll 1
+        for (int jt = 0; jt < NVTH; ++jt) {
+            const int j = (hf * NVTH + jt) * 16 + lr;
             f32x4 acc = zero4();
+#pragma unroll 8
             for (int kk = 0; kk < C; kk += 4) {
                 const int r = kk + lg;
-                acc = mma4(Ts[r * LA + rowA], ob[OL::DVNT + (size_t)(jt * 16 + lr) * C + r], acc);
+                acc = mma4(Ts[r * LA + rowA], ob[OL::DVNT + (size_t)j * C + r], acc);
             }
-            const int j = jt * 16 + lr;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = rowD + e;
-                const float vv = vval(i, j);
-                sb[e] += acc[e] * vv;
+                sb[e] += acc[e] * vval(i, j);
                 if (i < valid) dvo[(row0 + (size_t)i * H) * DV + j] = bet[i] * acc[e];
             }
         }
@@ -588,9 +604,10 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     }
     __syncthreads();
 
-    // ---- dA = tril_-1(-T^T dT T^T): S2 = dT T^T, then rows 16w.. of dA
-    for (int it = 0; it < 4; ++it) {
+    // ---- dA = tril_-1(-T^T dT T^T): S2 = dT T^T, then rows 16X.. of dA
+    for (int it = 2 * hf; it < 2 * hf + 2; ++it) {
         f32x4 acc = zero4();
+#pragma unroll 8
         for (int kk = 0; kk < C; kk += 4) {
             const int b = kk + lg;
             acc = mma4(S1[rowA * LA + b], Ts[(it * 16 + lr) * LA + b], acc);
@@ -601,10 +618,13 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     __syncthreads();
     {
         f32x4 sb = zero4();
-        f32x4 dA[4];
-        for (int it = 0; it < 4; ++it) {
+        f32x4 dA[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int it = 2 * hf + u;
             f32x4 acc = zero4();
-            if (it <= w) {
+            if (it <= X) {
+#pragma unroll 8
                 for (int kk = 0; kk < C; kk += 4) {
                     const int a = kk + lg;
                     acc = mma4(Ts[a * LA + rowA], S2[a * LA + it * 16 + lr], acc);
@@ -618,56 +638,58 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
                 sb[e] += d * As[r * LA + i];
                 acc[e] = bet[r] * d;
             }
-            dA[it] = acc;
+            dA[u] = acc;
         }
         add_dbeta(sb);
         __syncthreads();   // S1 (dT) and S2 (dT T^T) are read by every wave above
-        for (int it = 0; it < 4; ++it)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) S1[(rowD + e) * LA + it * 16 + lr] = dA[it][e];
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S1[(rowD + e) * LA + (2 * hf + u) * 16 + lr] = dA[u][e];
         // dM (lower triangle, from the reverse chain) into S2
-        for (int idx = tid; idx < C * C; idx += 256) {
+        for (int idx = tid; idx < C * C; idx += NTH) {
             const int i = idx / C, r = idx % C;
             S2[r * LA + i] = ob[OL::DMT + idx];
         }
     }
     __syncthreads();
 
-    // ---- decayed products: rows r of block X = w against blocks Y <= X
+    // ---- decayed products: rows r of block X against blocks Y <= X,
     //   (beta dA) Kt and dM Kt (row side), and columns i of block X against
     //   blocks Y >= X: (beta dA)^T Kg and dM^T Qg (column side)
-    const int X = w;
 #pragma unroll 1
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int c = ct * 16 + lr;   // B-operand column of this lane
+    for (int ct = 0; ct < NCTH; ++ct) {
+        const int c = (hf * NCTH + ct) * 16 + lr;   // B-operand column = accumulator column of this lane
         f32x4 accA = zero4(), accC = zero4(), accB = zero4(), accD = zero4();
         for (int Y = 0; Y <= X; ++Y) {
             const float s = Y < X ? dsc[pair_index(X, Y) * DK + c] : 1.f;
+            const float gY = gm[Y * DK + c];
 #pragma unroll
             for (int ks = 0; ks < SUB; ks += 4) {
                 const int y = Y * 16 + ks + lg;
-                const float bkr = ((Ks[y * DKP + c] * dexp2<E>(gm[Y * DK + c] - Gs[y * DKP + c])) * s) * s;
+                const float bkr = ((Ks[y * DKP + c] * dexp2<E>(gY - Gs[y * DKP + c])) * s) * s;
                 accA = mma4(S1[rowA * LA + y], bkr, accA);
                 accC = mma4(S2[rowA * LA + y], bkr, accC);
             }
         }
         for (int Y = X; Y < 4; ++Y) {
             const float s = Y > X ? dsc[pair_index(Y, X) * DK + c] : 1.f;
+            const float gY = gm[Y * DK + c];
 #pragma unroll
             for (int ks = 0; ks < SUB; ks += 4) {
                 const int y = Y * 16 + ks + lg;
-                const float el = (dexp2<E>(Gs[y * DKP + c] - gm[Y * DK + c]) * s) * s;
+                const float el = (dexp2<E>(Gs[y * DKP + c] - gY) * s) * s;
                 accB = mma4(S1[y * LA + rowA], Ks[y * DKP + c] * el, accB);
                 accD = mma4(S2[y * LA + rowA], qval(y, c) * el, accD);
             }
         }
-        const int cc = ct * 16 + lr;   // accumulator column
+        const float gX = gm[X * DK + c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowD + e;
-            const float gr = Gs[r * DKP + cc], gX = gm[X * DK + cc];
+            const float gr = Gs[r * DKP + c];
             const float fr = dexp2<E>(gr - gX), fc = dexp2<E>(gX - gr);
-            const float kv = Ks[r * DKP + cc], qv = qval(r, cc);
+            const float kv = Ks[r * DKP + c], qv = qval(r, c);
             const float a = accA[e] * fr, cq = accC[e] * fr, bt = (accB[e] + accD[e]) * fc;
             fK[ct][e] += a + bt;
             fQ[ct][e] += cq;
@@ -678,8 +700,8 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     // ---- terms from the reverse chain: dQg e^G, dKc e^{G_C - G}, and the
     //      column sums of dKc e^{G_C - G} k for the last row's dG
 #pragma unroll 1
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int c = ct * 16 + lr;
+    for (int ct = 0; ct < NCTH; ++ct) {
+        const int c = (hf * NCTH + ct) * 16 + lr;
         const f32x4 dqg = *reinterpret_cast<const f32x4*>(ob + OL::DQGT + (size_t)c * C + rowD);
         const f32x4 dkc = *reinterpret_cast<const f32x4*>(ob + OL::DKCT + (size_t)c * C + rowD);
         float cs = 0.f;
@@ -697,20 +719,21 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
         }
         cs += __shfl_xor(cs, 16);
         cs += __shfl_xor(cs, 32);
-        if (lg == 0) car[w * DK + c] = cs;
+        if (lg == 0) car[w * DK + c] = cs;    // wave w covers only its half's columns
     }
     __syncthreads();
-    if (w == 3 && lg == 3) {
+    if (X == 3 && lg == 3) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const int c = ct * 16 + lr;
-            fG[ct][3] += ob[OL::DGC + c] + car[c] + car[DK + c] + car[2 * DK + c] + car[3 * DK + c];
+        for (int ct = 0; ct < NCTH; ++ct) {
+            const int c = (hf * NCTH + ct) * 16 + lr;
+            fG[ct][3] += ob[OL::DGC + c] + car[(4 * hf) * DK + c] + car[(4 * hf + 1) * DK + c] +
+                         car[(4 * hf + 2) * DK + c] + car[(4 * hf + 3) * DK + c];
         }
     }
     // outputs dq, dk; dG into LDS (G is no longer read)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int c = ct * 16 + lr;
+    for (int ct = 0; ct < NCTH; ++ct) {
+        const int c = (hf * NCTH + ct) * 16 + lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = rowD + e;
@@ -722,9 +745,9 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
     }
     __syncthreads();   // every read of G and of the column sums is done
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+    for (int ct = 0; ct < NCTH; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Gs[(rowD + e) * DKP + ct * 16 + lr] = fG[ct][e];
+        for (int e = 0; e < 4; ++e) Gs[(rowD + e) * DKP + (hf * NCTH + ct) * 16 + lr] = fG[ct][e];
     __syncthreads();
 
     // ---- dg = reverse cumulative sum of dG over the chunk, dz
@@ -762,7 +785,7 @@ __global__ __launch_bounds__(256) void dintra_kernel(const E* __restrict__ q, co
             }
         }
     }
-    if (tid < valid) dbeta[row0 + (size_t)tid * H] = dbt[tid];
+    if (tid < valid) dbeta[row0 + (size_t)tid * H] = dbt[tid] + dbt[C + tid];
 }
 
 template <class E, int DK, int DV>
@@ -787,7 +810,7 @@ hipError_t launch_t(const BwdArgs& a) {
     if ((err = hipFuncSetAttribute((const void*)dintra_kernel<E, DK, DV>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL((dintra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(256), LI::LDS, st, (const E*)a.q,
+    hipLaunchKernelGGL((dintra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(LI::NTH), LI::LDS, st, (const E*)a.q,
                        (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.T, a.H, NC,
                        (const unsigned char*)(ws + lo.ob), a.dq, a.dk, a.dv, a.dz, a.dbeta);
     return hipGetLastError();
