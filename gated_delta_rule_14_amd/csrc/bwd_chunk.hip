@@ -306,12 +306,16 @@ struct DIntra {
     static constexpr int NCT = DK / 16, NCTH = NCT / 2, NVTH = DV / 32;   // column tiles per half
     static constexpr int DKP = DK + 4, LA = C + 4;
     static constexpr int NCAR = NPART > NW ? NPART : NW;
+    static constexpr int DVP = DV + 4;
     static constexpr size_t OFF_G = 0;                                  // [C][DKP] G (log2 units), then dG
-    static constexpr size_t OFF_K = OFF_G + (size_t)C * DKP * 4;        // [C][DKP] k
-    static constexpr size_t OFF_A = OFF_K + (size_t)C * DKP * 4;        // [C][LA]  Ab = tril_-1(Kg Kt^T)
+    static constexpr size_t OFF_K = OFF_G + (size_t)C * DKP * 4;        // [C][DKP] k (token precision)
+    static constexpr size_t OFF_A = OFF_K + align16((size_t)C * DKP * sizeof(E));   // [C][LA] Ab, then q
     static constexpr size_t OFF_T = OFF_A + (size_t)C * LA * 4;         // [C][LA]  T
     static constexpr size_t OFF_S1 = OFF_T + (size_t)C * LA * 4;        // [C][LA]  dT, then beta dA
-    static constexpr size_t OFF_S2 = OFF_S1 + (size_t)C * LA * 4;       // [C][LA]  dT T^T, then dM
+    static constexpr size_t OFF_S2 = OFF_S1 + (size_t)C * LA * 4;       // [C][LA]  v, then dT T^T, then dM
+    // q is staged over Ab once Ab is dead, where it fits; else read from memory
+    static constexpr bool QLDS = (size_t)C * DKP * sizeof(E) <= (size_t)C * LA * 4;
+    static_assert((size_t)C * DVP * sizeof(E) <= (size_t)C * LA * 4, "v staged over S2");
     static constexpr size_t OFF_X = OFF_S2 + (size_t)C * LA * 4;        // [3][16][16]
     static constexpr size_t OFF_DSC = OFF_X + 3 * SUB * SUB * 4;        // [6][DK]
     static constexpr size_t OFF_GM = OFF_DSC + 6 * DK * 4;              // [5][DK] G_m(R), G_C
@@ -348,7 +352,10 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __align__(16) unsigned char smem[];
     float* Gs = reinterpret_cast<float*>(smem + L::OFF_G);
-    float* Ks = reinterpret_cast<float*>(smem + L::OFF_K);
+    E* Ks = reinterpret_cast<E*>(smem + L::OFF_K);
+    E* Vs = reinterpret_cast<E*>(smem + L::OFF_S2);   // until dT T^T is formed
+    E* Qs = reinterpret_cast<E*>(smem + L::OFF_A);    // once Ab is dead (QLDS)
+    constexpr int DVP = L::DVP;
     float* As = reinterpret_cast<float*>(smem + L::OFF_A);
     float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
     float* S1 = reinterpret_cast<float*>(smem + L::OFF_S1);
@@ -386,7 +393,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             for (int j = 0; j < 2; ++j) {
                 const float g2 = kg2 * __builtin_amdgcn_rcpf(1.0f + dexp2<E>(-LOG2E * to_f32(zz[j])));
                 G[i][j] = ok ? g2 : 0.f;
-                Ks[r * DKP + c0 + j] = ok ? to_f32(kk[j]) : 0.f;
+                Ks[r * DKP + c0 + j] = ok ? kk[j] : from_f32<E>(0.f);
             }
             s0 += G[i][0];
             s1 += G[i][1];
@@ -442,11 +449,11 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
         const float* dv = dsc + (I < R ? pair_index(R, I) : 0) * DK;
         const int ra = R * 16 + lr, ib = I * 16 + lr;
         f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll
         for (int kk = 0; kk < DK; kk += 4) {
             const int c = kk + lg;
-            const float a = Ks[ra * DKP + c] * dexp2<E>(Gs[ra * DKP + c] - gm[R * DK + c]);
-            float b = Ks[ib * DKP + c] * dexp2<E>(gm[I * DK + c] - Gs[ib * DKP + c]);
+            const float a = to_f32(Ks[ra * DKP + c]) * dexp2<E>(Gs[ra * DKP + c] - gm[R * DK + c]);
+            float b = to_f32(Ks[ib * DKP + c]) * dexp2<E>(gm[I * DK + c] - Gs[ib * DKP + c]);
             if (I < R) b = (b * dv[c]) * dv[c];
             acc = mma4(a, b, acc);
         }
@@ -462,6 +469,13 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
         const int e = idx % (SUB * SUB);
         As[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
         Ts[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+    }
+    // v into LDS (zero past the end), two elements per access
+    for (int idx = tid; idx < C * DV / 2; idx += NTH) {
+        const int r = idx / (DV / 2), j = 2 * (idx % (DV / 2));
+        const typename Pair<E>::type vv = load2<E>(v + (row0 + (size_t)min(r, last) * H) * DV + j);
+        Vs[r * DVP + j] = r < valid ? vv[0] : from_f32<E>(0.f);
+        Vs[r * DVP + j + 1] = r < valid ? vv[1] : from_f32<E>(0.f);
     }
     __syncthreads();
 
@@ -514,11 +528,11 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
 #pragma unroll
     for (int ct = 0; ct < NCTH; ++ct) fQ[ct] = fK[ct] = fG[ct] = zero4();
     auto qval = [&](int r, int c) -> float {
+        if constexpr (L::QLDS) return to_f32(Qs[r * DKP + c]);
         return r < valid ? to_f32(q[(row0 + (size_t)r * H) * DK + c]) : 0.f;
     };
-    auto vval = [&](int r, int j) -> float {
-        return r < valid ? to_f32(v[(row0 + (size_t)r * H) * DV + j]) : 0.f;
-    };
+    auto vval = [&](int r, int j) -> float { return to_f32(Vs[r * DVP + j]); };
+    auto kval = [&](int r, int c) -> float { return to_f32(Ks[r * DKP + c]); };
     // beta partial sums of this lane's 4 rows, reduced over the 16 lanes of a
     // row group; one array per column half (no two waves write one slot)
     auto add_dbeta = [&](f32x4 s) {
@@ -538,12 +552,12 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
         if (R < 0) break;
         const int ra = R * 16 + lr, ib = I * 16 + lr;
         f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll
         for (int kk = 0; kk < DK; kk += 4) {
             const int c = kk + lg;
-            acc = mma4(ob[OL::DWT + (size_t)c * C + ra], Ks[ib * DKP + c] * dexp2<E>(Gs[ib * DKP + c]), acc);
+            acc = mma4(ob[OL::DWT + (size_t)c * C + ra], kval(ib, c) * dexp2<E>(Gs[ib * DKP + c]), acc);
         }
-#pragma unroll 8
+#pragma unroll
         for (int kk = 0; kk < DV; kk += 4) {
             const int j = kk + lg;
             acc = mma4(ob[OL::DVNT + (size_t)j * C + ra], vval(ib, j), acc);
@@ -569,7 +583,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
         for (int ct = 0; ct < NCTH; ++ct) {
             const int c = (hf * NCTH + ct) * 16 + lr;
             f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll
             for (int kk = 0; kk < C; kk += 4) {
                 const int r = kk + lg;
                 acc = mma4(Ts[r * LA + rowA], ob[OL::DWT + (size_t)c * C + r], acc);
@@ -577,7 +591,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = rowD + e;
-                const float gam = dexp2<E>(Gs[i * DKP + c]), kv = Ks[i * DKP + c];
+                const float gam = dexp2<E>(Gs[i * DKP + c]), kv = kval(i, c);
                 const float bk = bet[i] * acc[e] * gam;          // (beta dBk) e^G
                 sb[e] += acc[e] * kv * gam;                      // dBk . Kg
                 fK[ct][e] += bk;
@@ -588,7 +602,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
         for (int jt = 0; jt < NVTH; ++jt) {
             const int j = (hf * NVTH + jt) * 16 + lr;
             f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll
             for (int kk = 0; kk < C; kk += 4) {
                 const int r = kk + lg;
                 acc = mma4(Ts[r * LA + rowA], ob[OL::DVNT + (size_t)j * C + r], acc);
@@ -607,7 +621,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
     // ---- dA = tril_-1(-T^T dT T^T): S2 = dT T^T, then rows 16X.. of dA
     for (int it = 2 * hf; it < 2 * hf + 2; ++it) {
         f32x4 acc = zero4();
-#pragma unroll 8
+#pragma unroll
         for (int kk = 0; kk < C; kk += 4) {
             const int b = kk + lg;
             acc = mma4(S1[rowA * LA + b], Ts[(it * 16 + lr) * LA + b], acc);
@@ -624,7 +638,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             const int it = 2 * hf + u;
             f32x4 acc = zero4();
             if (it <= X) {
-#pragma unroll 8
+#pragma unroll
                 for (int kk = 0; kk < C; kk += 4) {
                     const int a = kk + lg;
                     acc = mma4(Ts[a * LA + rowA], S2[a * LA + it * 16 + lr], acc);
@@ -651,6 +665,14 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             const int i = idx / C, r = idx % C;
             S2[r * LA + i] = ob[OL::DMT + idx];
         }
+        if constexpr (L::QLDS) {   // q over Ab (zero past the end)
+            for (int idx = tid; idx < C * DK / 2; idx += NTH) {
+                const int r = idx / (DK / 2), c = 2 * (idx % (DK / 2));
+                const typename Pair<E>::type qq = load2<E>(q + (row0 + (size_t)min(r, last) * H) * DK + c);
+                Qs[r * DKP + c] = r < valid ? qq[0] : from_f32<E>(0.f);
+                Qs[r * DKP + c + 1] = r < valid ? qq[1] : from_f32<E>(0.f);
+            }
+        }
     }
     __syncthreads();
 
@@ -667,7 +689,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
 #pragma unroll
             for (int ks = 0; ks < SUB; ks += 4) {
                 const int y = Y * 16 + ks + lg;
-                const float bkr = ((Ks[y * DKP + c] * dexp2<E>(gY - Gs[y * DKP + c])) * s) * s;
+                const float bkr = ((kval(y, c) * dexp2<E>(gY - Gs[y * DKP + c])) * s) * s;
                 accA = mma4(S1[rowA * LA + y], bkr, accA);
                 accC = mma4(S2[rowA * LA + y], bkr, accC);
             }
@@ -679,7 +701,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             for (int ks = 0; ks < SUB; ks += 4) {
                 const int y = Y * 16 + ks + lg;
                 const float el = (dexp2<E>(Gs[y * DKP + c] - gY) * s) * s;
-                accB = mma4(S1[y * LA + rowA], Ks[y * DKP + c] * el, accB);
+                accB = mma4(S1[y * LA + rowA], kval(y, c) * el, accB);
                 accD = mma4(S2[y * LA + rowA], qval(y, c) * el, accD);
             }
         }
@@ -689,7 +711,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             const int r = rowD + e;
             const float gr = Gs[r * DKP + c];
             const float fr = dexp2<E>(gr - gX), fc = dexp2<E>(gX - gr);
-            const float kv = Ks[r * DKP + c], qv = qval(r, c);
+            const float kv = kval(r, c), qv = qval(r, c);
             const float a = accA[e] * fr, cq = accC[e] * fr, bt = (accB[e] + accD[e]) * fc;
             fK[ct][e] += a + bt;
             fQ[ct][e] += cq;
@@ -710,7 +732,7 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
             const int r = rowD + e;
             const float g = Gs[r * DKP + c];
             const float gam = dexp2<E>(g), ec = dexp2<E>(gm[4 * DK + c] - g);
-            const float kv = Ks[r * DKP + c], qv = qval(r, c);
+            const float kv = kval(r, c), qv = qval(r, c);
             fQ[ct][e] += dqg[e] * gam;
             fK[ct][e] += dkc[e] * ec;
             const float t = dkc[e] * ec * kv;
