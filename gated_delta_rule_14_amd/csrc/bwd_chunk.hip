@@ -22,8 +22,8 @@
 // Kernels:
 //  * the forward half (chunk.hip): the per-chunk operands of both directions,
 //    then the chunk recurrence from S0 storing each chunk's S and Vn;
-//  * dchain_kernel, one workgroup per (batch, head): the chunks in reverse,
-//    dS in MFMA accumulators; per chunk dVn and the products with S, Vn and
+//  * dchain_kernel, one workgroup per (batch, head), one wave per 16 rows of
+//    dS: the chunks in reverse, dS in MFMA accumulators; per chunk dVn and the products with S, Vn and
 //    dS' (dQg, dW, dKc, dM and e^{G_C} rowsum(S dS')), written for the next
 //    kernel;
 //  * dintra_kernel, one 512-thread workgroup per chunk: everything else, on
@@ -77,14 +77,17 @@ Lay lay_t(int B, int T, int H) {
 }
 
 // ---------------------------------------------------------------------------
-// Reverse chunk recurrence of one chain (b, h), all d_v columns: 256 threads.
-// dS rows of wave w: w*DK/4 + rb*16 + 4(l/16) + e; columns ct*16 + l%16.
+// Reverse chunk recurrence of one chain (b, h), all d_v columns: one wave per
+// 16 rows of dS (d_k / 16 waves).  dS rows of wave w: 16w + 4(l/16) + e,
+// columns ct*16 + l%16.  The chunk's token-row products are split over the
+// waves as row block X = w % 4 times column group w / 4.
 // ---------------------------------------------------------------------------
 template <class E, int DK, int DV>
 struct DChain {
     typedef typename Compute<E>::type CT;
     typedef Mfma<CT> MF;
-    static constexpr int KS = MF::KSTEP, RB = DK / 64, NT = DV / 16;
+    static constexpr int NW = DK / 16, NTH = 64 * NW, NCG = NW / 4;   // column groups of the token-row products
+    static constexpr int KS = MF::KSTEP, NT = DV / 16;
     static constexpr int LC = C + 8, LDK = DK + 8, LDV = DV + 8;
     static constexpr size_t OFF_DOT = 0;                                                  // [DV][LC]  dO^T
     static constexpr size_t OFF_DST = OFF_DOT + align16((size_t)DV * LC * sizeof(CT));   // [DV][LDK] dS^T
@@ -93,23 +96,24 @@ struct DChain {
     static constexpr size_t OFF_DVR = OFF_DVT + align16((size_t)DV * LC * sizeof(CT));   // [C][LDV]  -dVn
     static constexpr size_t LDS = OFF_DVR + align16((size_t)C * LDV * sizeof(CT));
     static_assert(LDS <= 160 * 1024, "reverse chain LDS budget");
+    static_assert(NW % 4 == 0 && NT % NCG == 0 && (DK / 16) % NCG == 0 && (C / 16) % NCG == 0, "wave split");
 };
 
 template <class E, int DK, int DV>
-__global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout, const float* __restrict__ ds_final,
-                                                     float* __restrict__ ds0, int T, int H, int NC,
-                                                     const unsigned char* __restrict__ fws,
-                                                     const unsigned char* __restrict__ bws,
-                                                     const float* __restrict__ states,
-                                                     const typename Compute<E>::type* __restrict__ vn,
-                                                     unsigned char* __restrict__ obuf) {
+__global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ dout, const float* __restrict__ ds_final,
+                                                        float* __restrict__ ds0, int T, int H, int NC,
+                                                        const unsigned char* __restrict__ fws,
+                                                        const unsigned char* __restrict__ bws,
+                                                        const float* __restrict__ states,
+                                                        const typename Compute<E>::type* __restrict__ vn,
+                                                        unsigned char* __restrict__ obuf) {
     typedef DChain<E, DK, DV> L;
     typedef typename L::CT CT;
     typedef typename L::MF MF;
     typedef Ws<CT, DK, DV> WL;
     typedef WsB<CT, DK, DV> WB;
     typedef Ob<DK, DV> OL;
-    constexpr int KS = L::KS, RB = L::RB, NT = L::NT, LC = L::LC, LDK = L::LDK, LDV = L::LDV;
+    constexpr int KS = L::KS, NT = L::NT, LC = L::LC, LDK = L::LDK, LDV = L::LDV, NTH = L::NTH, NCG = L::NCG;
     constexpr int VE = 16 / sizeof(CT);   // elements per 16-byte access
     extern __shared__ __align__(16) unsigned char smem[];
     CT* dOT = reinterpret_cast<CT*>(smem + L::OFF_DOT);
@@ -119,31 +123,26 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
     CT* dVR = reinterpret_cast<CT*>(smem + L::OFF_DVR);
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int X = w & 3, cg = w >> 2;         // token-row block and column group of this wave
     const size_t bh = blockIdx.x;
     const int bb = (int)(bh / H), hh = (int)(bh % H);
+    const int srow = w * 16 + 4 * (l >> 4);   // first dS row of this lane
 
-    f32x4 accD[RB][NT];
+    f32x4 accD[NT];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int ct = 0; ct < NT; ++ct) {
+        const int col = ct * 16 + (l & 15);
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
-            const int col = ct * 16 + (l & 15);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                accD[rb][ct][e] = ds_final ? ds_final[(bh * DK + row + e) * DV + col] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) accD[ct][e] = ds_final ? ds_final[(bh * DK + srow + e) * DV + col] : 0.f;
+    }
     auto store_ds = [&]() {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int ct = 0; ct < NT; ++ct) {
+            const int col = ct * 16 + (l & 15);
+            store4<CT>(dST + col * LDK + srow, accD[ct]);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
-                const int col = ct * 16 + (l & 15);
-                store4<CT>(dST + col * LDK + row, accD[rb][ct]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) dSR[(row + e) * LDV + col] = from_f32<CT>(accD[rb][ct][e]);
-            }
+            for (int e = 0; e < 4; ++e) dSR[(srow + e) * LDV + col] = from_f32<CT>(accD[ct][e]);
+        }
     };
     store_ds();
 
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
         const size_t rs = (size_t)H * DV;
 
         // dO^T into LDS, zero past the end of the sequence
-        for (int u = tid; u < C * DV / VE; u += 256) {
+        for (int u = tid; u < C * DV / VE; u += NTH) {
             const int r = u / (DV / VE), j0 = (u % (DV / VE)) * VE;
             CT vals[VE];
             if (r < valid) {
@@ -175,25 +174,28 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
         }
         __syncthreads();
 
-        // dVn = M^T dO + Kc dS' (token rows 16w..)
-        f32x4 accV[NT];
+        // dVn = M^T dO + Kc dS' (token rows 16X.., this wave's column group)
+        constexpr int NTG = NT / NCG;
+        f32x4 accV[NTG];
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) accV[ct] = zero4();
+        for (int ct = 0; ct < NTG; ++ct) accV[ct] = zero4();
 #pragma unroll
         for (int kk = 0; kk < C / KS; ++kk) {
-            const typename MF::frag a = load_frag<CT>(bk + WB::MT, C, w * 16, kk * KS);
+            const typename MF::frag a = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) accV[ct] = MF::mma(a, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accV[ct]);
+            for (int ct = 0; ct < NTG; ++ct)
+                accV[ct] = MF::mma(a, load_frag<CT>(dOT, LC, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
         }
 #pragma unroll
         for (int kk = 0; kk < DK / KS; ++kk) {
-            const typename MF::frag a = load_frag<CT>(bk + WB::KC, DK, w * 16, kk * KS);
+            const typename MF::frag a = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) accV[ct] = MF::mma(a, load_frag<CT>(dST, LDK, ct * 16, kk * KS), accV[ct]);
+            for (int ct = 0; ct < NTG; ++ct)
+                accV[ct] = MF::mma(a, load_frag<CT>(dST, LDK, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
         }
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-            const int col = ct * 16 + (l & 15), row = w * 16 + 4 * (l >> 4);
+        for (int ct = 0; ct < NTG; ++ct) {
+            const int col = (cg * NTG + ct) * 16 + (l & 15), row = X * 16 + 4 * (l >> 4);
             *reinterpret_cast<f32x4*>(ob + OL::DVNT + (size_t)col * C + row) = accV[ct];
             store4<CT>(dVT + col * LC + row, -accV[ct]);
 #pragma unroll
@@ -201,10 +203,10 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
         }
         __syncthreads();
 
-        // dO rows 16w.. (zero past the end) and Vn rows 16w.. as A operands
+        // dO rows 16X.. (zero past the end) and Vn rows 16X.. as A operands
         typename MF::frag dof[DV / KS], vf[DV / KS];
         {
-            const int r = w * 16 + (l & 15);
+            const int r = X * 16 + (l & 15);
             const bool ok = r < valid;
             // the row address is clamped to the last token (in bounds); rows
             // past the end are zeroed
@@ -213,83 +215,76 @@ __global__ __launch_bounds__(256) void dchain_kernel(const E* __restrict__ dout,
             for (int kk = 0; kk < DV / KS; ++kk) {
                 dof[kk] = *reinterpret_cast<const typename MF::frag*>(drow + kk * KS);
                 if (!ok) dof[kk] = typename MF::frag{};
-                vf[kk] = load_frag<CT>(Vn, DV, w * 16, kk * KS);
+                vf[kk] = load_frag<CT>(Vn, DV, X * 16, kk * KS);
             }
         }
-        // dQg = dO S^T and dW = -dVn S^T (rows r, columns c)
+        // dQg = dO S^T, dW = -dVn S^T and dKc = Vn dS'^T (rows 16X.., this
+        // wave's group of d_k column tiles)
+        constexpr int NCB = DK / 16 / NCG;
 #pragma unroll 2
-        for (int cb = 0; cb < DK / 16; ++cb) {
+        for (int u = 0; u < NCB; ++u) {
+            const int cb = cg * NCB + u;
             f32x4 accQ = zero4(), accW = zero4(), accK = zero4();
 #pragma unroll
             for (int kk = 0; kk < DV / KS; ++kk) {
                 const typename MF::frag fs = load_frag_f32<CT>(Sn, DV, cb * 16, kk * KS);
                 accQ = MF::mma(dof[kk], fs, accQ);
-                accW = MF::mma(load_frag<CT>(dVR, LDV, w * 16, kk * KS), fs, accW);
+                accW = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fs, accW);
                 accK = MF::mma(vf[kk], load_frag<CT>(dSR, LDV, cb * 16, kk * KS), accK);
             }
-            const size_t off = (size_t)(cb * 16 + (l & 15)) * C + w * 16 + 4 * (l >> 4);
+            const size_t off = (size_t)(cb * 16 + (l & 15)) * C + X * 16 + 4 * (l >> 4);
             *reinterpret_cast<f32x4*>(ob + OL::DQGT + off) = accQ;
             *reinterpret_cast<f32x4*>(ob + OL::DWT + off) = accW;
             *reinterpret_cast<f32x4*>(ob + OL::DKCT + off) = accK;
         }
         // dM = tril(dO Vn^T) (rows r, columns i), stored transposed
+        constexpr int NIB = C / 16 / NCG;
 #pragma unroll
-        for (int ib = 0; ib < C / 16; ++ib) {
+        for (int u = 0; u < NIB; ++u) {
+            const int ib = cg * NIB + u;
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < DV / KS; ++kk) acc = MF::mma(dof[kk], load_frag<CT>(Vn, DV, ib * 16, kk * KS), acc);
-            const int i = ib * 16 + (l & 15), r0 = w * 16 + 4 * (l >> 4);
+            const int i = ib * 16 + (l & 15), r0 = X * 16 + 4 * (l >> 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (i <= r0 + e) ? acc[e] : 0.f;
             *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
         }
         // e^{G_C} rowsum(S dS'), rows of this wave
         const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
-        f32x4 eg[RB];
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + srow);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
-            eg[rb] = *reinterpret_cast<const f32x4*>(egc + row);
+        for (int e = 0; e < 4; ++e) {
+            float sacc = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float s = 0.f;
+            for (int ct = 0; ct < NT; ++ct) sacc += accD[ct][e] * Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)];
 #pragma unroll
-                for (int ct = 0; ct < NT; ++ct) s += accD[rb][ct][e] * Sn[(size_t)(row + e) * DV + ct * 16 + (l & 15)];
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) s += __shfl_xor(s, off);
-                if ((l & 15) == 0) ob[OL::DGC + row + e] = s * eg[rb][e];
-            }
+            for (int off = 1; off < 16; off <<= 1) sacc += __shfl_xor(sacc, off);
+            if ((l & 15) == 0) ob[OL::DGC + srow + e] = sacc * eg[e];
         }
         // dS <- e^{G_C} dS' + Qg^T dO - W^T dVn
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int ct = 0; ct < NT; ++ct) accD[ct] *= eg;
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) accD[rb][ct] *= eg[rb];
+        for (int kk = 0; kk < C / KS; ++kk) {
+            const typename MF::frag aq = load_frag<CT>(bk + WB::QGT, C, w * 16, kk * KS);
+            const typename MF::frag aw = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS);
 #pragma unroll
-        for (int kk = 0; kk < C / KS; ++kk)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const typename MF::frag aq = load_frag<CT>(bk + WB::QGT, C, w * (DK / 4) + rb * 16, kk * KS);
-                const typename MF::frag aw = load_frag<CT>(bk + WB::WT, C, w * (DK / 4) + rb * 16, kk * KS);
-#pragma unroll
-                for (int ct = 0; ct < NT; ++ct) {
-                    accD[rb][ct] = MF::mma(aq, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[rb][ct]);
-                    accD[rb][ct] = MF::mma(aw, load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[rb][ct]);
-                }
+            for (int ct = 0; ct < NT; ++ct) {
+                accD[ct] = MF::mma(aq, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[ct]);
+                accD[ct] = MF::mma(aw, load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[ct]);
             }
+        }
         __syncthreads();   // this chunk's reads of dO^T, dS, dVn in LDS are done
         store_ds();
     }
     if (ds0) {
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int ct = 0; ct < NT; ++ct) {
+            const int col = ct * 16 + (l & 15);
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) {
-                const int row = w * (DK / 4) + rb * 16 + 4 * (l >> 4);
-                const int col = ct * 16 + (l & 15);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ds0[(bh * DK + row + e) * DV + col] = accD[rb][ct][e];
-            }
+            for (int e = 0; e < 4; ++e) ds0[(bh * DK + srow + e) * DV + col] = accD[ct][e];
+        }
     }
 }
 
@@ -823,7 +818,7 @@ hipError_t launch_t(const BwdArgs& a) {
     if ((err = hipFuncSetAttribute((const void*)dchain_kernel<E, DK, DV>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)LC_::LDS)) != hipSuccess)
         return err;
-    hipLaunchKernelGGL((dchain_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(256), LC_::LDS, st, (const E*)a.dout,
+    hipLaunchKernelGGL((dchain_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(LC_::NTH), LC_::LDS, st, (const E*)a.dout,
                        a.ds_final, a.ds0, a.T, a.H, NC, (const unsigned char*)(ws + lo.fws),
                        (const unsigned char*)(ws + lo.bws), (const float*)(ws + lo.st), (const CT*)(ws + lo.vn),
                        ws + lo.ob);
