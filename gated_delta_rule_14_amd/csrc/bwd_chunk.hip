@@ -31,6 +31,8 @@
 //    The products whose terms carry e^{G_r - G_i} are evaluated per 16-row
 //    block pair around reference rows m = 16R + 7, as in the forward, with
 //    the cross-block factor applied as its square root twice.
+#include <type_traits>
+
 #include "chunk_layout.hpp"
 #include "kda_internal.hpp"
 
@@ -59,6 +61,31 @@ struct Ob {
     static constexpr size_t BYTES = END * 4;
 };
 
+// Per chunk, bf16 tokens: bf16 products, each stored in the orientation the
+// per-chunk kernel contracts it in (offsets in bf16 elements), then the fp32
+// e^{G_C} rowsum(S dS').  NP = -tril_-1(dVn Vn^T), which with
+// dT T^T = dVn Vn^T (I + A)^T T^T = dVn Vn^T gives dA = tril_-1(T^T NP).
+template <int DK, int DV>
+struct ObH {
+    static constexpr size_t DVNT = 0;                      // (DV, C)  dVn^T
+    static constexpr size_t DWT = DVNT + (size_t)DV * C;   // (DK, C)  (-dVn S^T)^T
+    static constexpr size_t DQG = DWT + (size_t)DK * C;    // (C, DK)  dO S^T
+    static constexpr size_t DKC = DQG + (size_t)C * DK;    // (C, DK)  Vn dS'^T
+    static constexpr size_t NPT = DKC + (size_t)C * DK;    // (C, C)   NP^T
+    static constexpr size_t DM = NPT + (size_t)C * C;      // (C, C)   tril(dO Vn^T)
+    static constexpr size_t DMT = DM + (size_t)C * C;      // (C, C)   its transpose
+    static constexpr size_t END = DMT + (size_t)C * C;
+    static constexpr size_t DGC_BYTE = END * 2;            // (DK) fp32
+    static constexpr size_t BYTES = DGC_BYTE + DK * 4;
+    static_assert(BYTES % 16 == 0, "16-byte aligned chunk blocks");
+};
+
+template <class CT, int DK, int DV>
+constexpr size_t ob_bytes() {
+    if constexpr (std::is_same<CT, bf16>::value) return ObH<DK, DV>::BYTES;
+    return Ob<DK, DV>::BYTES;
+}
+
 struct Lay {
     size_t fws, bws, st, vn, ob, total;
 };
@@ -72,7 +99,7 @@ Lay lay_t(int B, int T, int H) {
     lo.st = lo.bws + a256(nchunk * WsB<CT, DK, DV>::BYTES);
     lo.vn = lo.st + a256(nchunk * DK * DV * 4);
     lo.ob = lo.vn + a256(nchunk * C * DV * sizeof(CT));
-    lo.total = lo.ob + nchunk * Ob<DK, DV>::BYTES;
+    lo.total = lo.ob + nchunk * ob_bytes<CT, DK, DV>();
     return lo;
 }
 
@@ -113,6 +140,8 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
     typedef Ws<CT, DK, DV> WL;
     typedef WsB<CT, DK, DV> WB;
     typedef Ob<DK, DV> OL;
+    typedef ObH<DK, DV> OH;
+    constexpr bool H16 = std::is_same<CT, bf16>::value;   // bf16 products for dintra16_kernel
     constexpr int KS = L::KS, NT = L::NT, LC = L::LC, LDK = L::LDK, LDV = L::LDV, NTH = L::NTH, NCG = L::NCG;
     constexpr int VE = 16 / sizeof(CT);   // elements per 16-byte access
     extern __shared__ __align__(16) unsigned char smem[];
@@ -153,7 +182,8 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         const CT* bk = reinterpret_cast<const CT*>(bws + cid * WB::BYTES);
         const float* Sn = states + cid * DK * DV;
         const CT* Vn = vn + cid * C * DV;
-        float* ob = reinterpret_cast<float*>(obuf + cid * OL::BYTES);
+        float* ob = reinterpret_cast<float*>(obuf + cid * ob_bytes<CT, DK, DV>());
+        bf16* obh = reinterpret_cast<bf16*>(ob);
         const E* dob = dout + (((size_t)bb * T + (size_t)n * C) * H + hh) * DV;   // row r at r * H * DV
         const size_t rs = (size_t)H * DV;
 
@@ -196,7 +226,10 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
 #pragma unroll
         for (int ct = 0; ct < NTG; ++ct) {
             const int col = (cg * NTG + ct) * 16 + (l & 15), row = X * 16 + 4 * (l >> 4);
-            *reinterpret_cast<f32x4*>(ob + OL::DVNT + (size_t)col * C + row) = accV[ct];
+            if constexpr (H16)
+                store4<bf16>(obh + OH::DVNT + (size_t)col * C + row, accV[ct]);
+            else
+                *reinterpret_cast<f32x4*>(ob + OL::DVNT + (size_t)col * C + row) = accV[ct];
             store4<CT>(dVT + col * LC + row, -accV[ct]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) dVR[(row + e) * LDV + col] = from_f32<CT>(-accV[ct][e]);
@@ -228,14 +261,26 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
 #pragma unroll
             for (int kk = 0; kk < DV / KS; ++kk) {
                 const typename MF::frag fs = load_frag_f32<CT>(Sn, DV, cb * 16, kk * KS);
-                accQ = MF::mma(dof[kk], fs, accQ);
                 accW = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fs, accW);
-                accK = MF::mma(vf[kk], load_frag<CT>(dSR, LDV, cb * 16, kk * KS), accK);
+                if constexpr (H16) {   // (channel, token) orientation: rows of dO S^T and Vn dS'^T
+                    accQ = MF::mma(fs, dof[kk], accQ);
+                    accK = MF::mma(load_frag<CT>(dSR, LDV, cb * 16, kk * KS), vf[kk], accK);
+                } else {
+                    accQ = MF::mma(dof[kk], fs, accQ);
+                    accK = MF::mma(vf[kk], load_frag<CT>(dSR, LDV, cb * 16, kk * KS), accK);
+                }
             }
             const size_t off = (size_t)(cb * 16 + (l & 15)) * C + X * 16 + 4 * (l >> 4);
-            *reinterpret_cast<f32x4*>(ob + OL::DQGT + off) = accQ;
-            *reinterpret_cast<f32x4*>(ob + OL::DWT + off) = accW;
-            *reinterpret_cast<f32x4*>(ob + OL::DKCT + off) = accK;
+            if constexpr (H16) {
+                const size_t offr = (size_t)(X * 16 + (l & 15)) * DK + cb * 16 + 4 * (l >> 4);
+                store4<bf16>(obh + OH::DQG + offr, accQ);
+                store4<bf16>(obh + OH::DWT + off, accW);
+                store4<bf16>(obh + OH::DKC + offr, accK);
+            } else {
+                *reinterpret_cast<f32x4*>(ob + OL::DQGT + off) = accQ;
+                *reinterpret_cast<f32x4*>(ob + OL::DWT + off) = accW;
+                *reinterpret_cast<f32x4*>(ob + OL::DKCT + off) = accK;
+            }
         }
         // dM = tril(dO Vn^T) (rows r, columns i), stored transposed
         constexpr int NIB = C / 16 / NCG;
@@ -248,7 +293,28 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             const int i = ib * 16 + (l & 15), r0 = X * 16 + 4 * (l >> 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (i <= r0 + e) ? acc[e] : 0.f;
-            *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
+            if constexpr (H16) {
+                // dM row-major (rows 16X + l%16, columns ib*16 + 4(l/16) + e) and
+                // NP = -tril_-1(dVn Vn^T), stored transposed
+                f32x4 accR = zero4(), accP = zero4();
+#pragma unroll
+                for (int kk = 0; kk < DV / KS; ++kk) {
+                    const typename MF::frag fv = load_frag<CT>(Vn, DV, ib * 16, kk * KS);
+                    accR = MF::mma(fv, dof[kk], accR);
+                    accP = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fv, accP);
+                }
+                const int r = X * 16 + (l & 15), i0 = ib * 16 + 4 * (l >> 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    accR[e] = (i0 + e <= r) ? accR[e] : 0.f;
+                    accP[e] = (i < r0 + e) ? accP[e] : 0.f;
+                }
+                store4<bf16>(obh + OH::DMT + (size_t)i * C + r0, acc);
+                store4<bf16>(obh + OH::DM + (size_t)r * C + i0, accR);
+                store4<bf16>(obh + OH::NPT + (size_t)i * C + r0, accP);
+            } else {
+                *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
+            }
         }
         // e^{G_C} rowsum(S dS'), rows of this wave
         const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
@@ -260,7 +326,12 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             for (int ct = 0; ct < NT; ++ct) sacc += accD[ct][e] * Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)];
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) sacc += __shfl_xor(sacc, off);
-            if ((l & 15) == 0) ob[OL::DGC + srow + e] = sacc * eg[e];
+            if ((l & 15) == 0) {
+                if constexpr (H16)
+                    reinterpret_cast<float*>(obuf + cid * OH::BYTES + OH::DGC_BYTE)[srow + e] = sacc * eg[e];
+                else
+                    ob[OL::DGC + srow + e] = sacc * eg[e];
+            }
         }
         // dS <- e^{G_C} dS' + Qg^T dO - W^T dVn
 #pragma unroll
@@ -805,6 +876,480 @@ __global__ __launch_bounds__(512) void dintra_kernel(const E* __restrict__ q, co
     if (tid < valid) dbeta[row0 + (size_t)tid * H] = dbt[tid] + dbt[C + tid];
 }
 
+// ---------------------------------------------------------------------------
+// Per-chunk gradients, bf16 tokens: 512 threads on bf16 MFMA.  Wave w owns the
+// token block X = w % 4 and the channel half w / 4 of dQ, dK and dG, held in
+// registers in the (channel, token) orientation of the accumulators: rows
+// cb + 4(l/16) + e of a 16-channel tile, column (token) 16X + l%16, so that
+// each lane reads and writes four consecutive channels of one token.
+// The decayed products use three operand families, each built once per chunk
+// with one exponential per element and stored channel-major (token index
+// contiguous): Kr = k e^{G_m(Y) - G}, Kc = k e^{G - G_m(Y)} and
+// Qc = q e^{G - G_m(Y)}, Y the token's own 16-row block, so every factor lies
+// within e^{+-8|g_min|}.  A product over the token blocks Y accumulates block
+// by block, the accumulator scaled between blocks by the ratio of consecutive
+// reference factors e^{G_m(Y) - G_m(Y-1)} <= 1 (Horner's scheme).
+// dA comes from NP = -tril_-1(dVn Vn^T) (written by the reverse chain):
+// dT T^T = dVn Vn^T (I + A)^T T^T = dVn Vn^T, and tril_-1(T^T X T^T) only
+// reads the strictly lower part of X, so dA = tril_-1(-T^T dT T^T) =
+// tril_-1(T^T NP).
+// ---------------------------------------------------------------------------
+template <int DK, int DV>
+struct DIntraH {
+    static constexpr int NTH = 512, NW = 8;
+    static constexpr int CP = DK / 2, NPART = NTH / CP, RP = C / NPART;   // gate scan: channel pairs x row parts
+    static constexpr int NCTH = DK / 32, NVTH = DV / 32;                  // 16-wide tiles per half
+    static constexpr int DKP = DK + 4, LA = C + 4, LY = C + 8, LT = C + 8;
+    static constexpr int NCAR = NPART > 4 ? NPART : 4;
+    static constexpr size_t OFF_G = 0;                                   // [C][DKP] fp32 G (log2), then dG
+    static constexpr size_t OFF_KR = OFF_G + (size_t)C * DKP * 4;        // [DK][LY] bf16 Kr^T
+    static constexpr size_t OFF_KC = OFF_KR + (size_t)DK * LY * 2;       // [DK][LY] bf16 Kc^T
+    static constexpr size_t OFF_QC = OFF_KC + (size_t)DK * LY * 2;       // [DK][LY] bf16 Qc^T
+    static constexpr size_t OFF_A = OFF_QC + (size_t)DK * LY * 2;        // [C][LA] fp32 Ab, then (beta dA)^T bf16
+    static constexpr size_t OFF_T = OFF_A + (size_t)C * LA * 4;          // [C][LA] fp32 T, then beta dA bf16
+    static constexpr size_t OFF_TT = OFF_T + (size_t)C * LA * 4;         // [C][LT] bf16 T^T
+    static constexpr size_t OFF_X = OFF_TT + (size_t)C * LT * 2;         // [3][16][16] fp32 (solve)
+    static constexpr size_t OFF_GM = OFF_X + 3 * SUB * SUB * 4;          // [5][DK] G_m(0..3), G_C
+    static constexpr size_t OFF_RHO = OFF_GM + 5 * DK * 4;               // [3][DK] e^{G_m(Y+1) - G_m(Y)}
+    static constexpr size_t OFF_XP = OFF_RHO + 3 * DK * 4;               // [6][DK] e^{G_m(R) - G_m(I)}, I < R
+    static constexpr size_t OFF_CAR = OFF_XP + 6 * DK * 4;               // [NCAR][DK]
+    static constexpr size_t OFF_BET = OFF_CAR + (size_t)NCAR * DK * 4;   // [C]
+    static constexpr size_t OFF_DB = OFF_BET + C * 4;                    // [6][C] dbeta partials
+    static constexpr size_t LDS = OFF_DB + 6 * C * 4;
+    static_assert(LDS <= 160 * 1024, "per-chunk gradient LDS budget");
+    static_assert((size_t)C * LT * 2 <= (size_t)C * LA * 4, "bf16 64x64 tiles over fp32 ones");
+    static_assert(RP % 2 == 0 && 16 % RP == 0 && DK % 32 == 0 && DV % 32 == 0, "tiling");
+};
+
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                       const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                       const bf16* __restrict__ beta, float g_min, int T, int H,
+                                                       int NC, const unsigned char* __restrict__ obuf,
+                                                       float* __restrict__ dq, float* __restrict__ dk,
+                                                       float* __restrict__ dvo, float* __restrict__ dz,
+                                                       float* __restrict__ dbeta) {
+    typedef DIntraH<DK, DV> L;
+    typedef ObH<DK, DV> OH;
+    typedef Mfma<bf16> MF;
+    constexpr int NTH = L::NTH, RP = L::RP, DKP = L::DKP, LA = L::LA, LY = L::LY, LT = L::LT;
+    constexpr int NCTH = L::NCTH, NVTH = L::NVTH;
+    constexpr float LOG2E = 1.4426950408889634f;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float* Gs = reinterpret_cast<float*>(smem + L::OFF_G);
+    bf16* KRt = reinterpret_cast<bf16*>(smem + L::OFF_KR);
+    bf16* KCt = reinterpret_cast<bf16*>(smem + L::OFF_KC);
+    bf16* QCt = reinterpret_cast<bf16*>(smem + L::OFF_QC);
+    float* As = reinterpret_cast<float*>(smem + L::OFF_A);
+    float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
+    bf16* DAT = reinterpret_cast<bf16*>(smem + L::OFF_A);   // (beta dA)^T, once Ab is dead
+    bf16* DA = reinterpret_cast<bf16*>(smem + L::OFF_T);    // beta dA, once T is dead
+    bf16* TT = reinterpret_cast<bf16*>(smem + L::OFF_TT);
+    float* Xs = reinterpret_cast<float*>(smem + L::OFF_X);
+    float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);
+    float* rho = reinterpret_cast<float*>(smem + L::OFF_RHO);
+    float* xp = reinterpret_cast<float*>(smem + L::OFF_XP);
+    float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);
+    float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
+    float* dbp = reinterpret_cast<float*>(smem + L::OFF_DB);
+
+    const int n = blockIdx.x, hh = blockIdx.y, bb = blockIdx.z;
+    const int valid = min(C, T - n * C), last = valid - 1;
+    const size_t row0 = ((size_t)bb * T + (size_t)n * C) * H + hh;   // token row of chunk row 0
+    const unsigned char* obc = obuf + (((size_t)bb * H + hh) * NC + n) * OH::BYTES;
+    const bf16* ob = reinterpret_cast<const bf16*>(obc);
+    const float* dgc = reinterpret_cast<const float*>(obc + OH::DGC_BYTE);
+    const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+    const int lr = l & 15, lg = l >> 4;
+    const int X = w & 3, hf = w >> 2;   // token block and channel half of this wave
+    const int rX = X * 16 + lr;         // token (accumulator column) of this lane
+
+    // ---- gate, chunk-local scan (log2 units)
+    {
+        const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+        const float kg2 = g_min * LOG2E;
+        float G[RP][2];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+            const bf16x2 zz = load2<bf16>(z + (row0 + (size_t)min(r, last) * H) * DK + c0);
+            const bool ok = r < valid;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float g2 = kg2 * __builtin_amdgcn_rcpf(1.0f + dexp2<bf16>(-LOG2E * to_f32(zz[j])));
+                G[i][j] = ok ? g2 : 0.f;
+            }
+            s0 += G[i][0];
+            s1 += G[i][1];
+            G[i][0] = s0;
+            G[i][1] = s1;
+        }
+        car[part * DK + c0] = s0;
+        car[part * DK + c0 + 1] = s1;
+        if (tid < C) bet[tid] = tid < valid ? to_f32(beta[row0 + (size_t)tid * H]) : 0.f;
+        for (int idx = tid; idx < 6 * C; idx += NTH) dbp[idx] = 0.f;
+        __syncthreads();
+        float cr[2] = {0.f, 0.f}, gC[2] = {0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float t = car[p * DK + c0 + j];
+                if (p < part) cr[j] += t;
+                gC[j] += t;
+            }
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float g = G[i][j] + cr[j];
+                Gs[r * DKP + c0 + j] = g;
+                if ((r & 15) == 7) gm[(r >> 4) * DK + c0 + j] = g;
+            }
+        }
+        if (part == 0) {
+            gm[4 * DK + c0] = gC[0];
+            gm[4 * DK + c0 + 1] = gC[1];
+        }
+        __syncthreads();
+    }
+    // reference ratios e^{G_m(Y+1) - G_m(Y)} and cross-block factors e^{G_m(R) - G_m(I)}
+    for (int idx = tid; idx < 9 * DK; idx += NTH) {
+        const int p = idx / DK, cc = idx % DK;
+        if (p < 3) {
+            rho[idx] = dexp2<bf16>(gm[(p + 1) * DK + cc] - gm[p * DK + cc]);
+        } else {
+            const int pp = p - 3, R = pp < 1 ? 1 : (pp < 3 ? 2 : 3), I = pp - R * (R - 1) / 2;
+            xp[pp * DK + cc] = dexp2<bf16>(gm[R * DK + cc] - gm[I * DK + cc]);
+        }
+    }
+    // operand families, channel-major: two tokens x eight channels per item
+    for (int idx = tid; idx < (C / 2) * (DK / 8); idx += NTH) {
+        const int y0 = 2 * (idx % (C / 2)), c8 = (idx / (C / 2)) * 8, Y = y0 >> 4;
+        float kr[2][8], kc[2][8], qc[2][8];
+        const f32x4 ma = *reinterpret_cast<const f32x4*>(gm + Y * DK + c8);
+        const f32x4 mb = *reinterpret_cast<const f32x4*>(gm + Y * DK + c8 + 4);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int y = y0 + u;
+            const bool ok = y < valid;
+            const size_t off = (row0 + (size_t)min(y, last) * H) * DK + c8;
+            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(k + off);
+            const bf16x8 qq = *reinterpret_cast<const bf16x8*>(q + off);
+            const f32x4 ga = *reinterpret_cast<const f32x4*>(Gs + y * DKP + c8);
+            const f32x4 gb = *reinterpret_cast<const f32x4*>(Gs + y * DKP + c8 + 4);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float d = (j < 4 ? ma[j] : mb[j - 4]) - (j < 4 ? ga[j] : gb[j - 4]);
+                const float e1 = dexp2<bf16>(d), e2 = dexp2<bf16>(-d);
+                const float kv = ok ? to_f32(kk[j]) : 0.f, qv = ok ? to_f32(qq[j]) : 0.f;
+                kr[u][j] = kv * e1;
+                kc[u][j] = kv * e2;
+                qc[u][j] = qv * e2;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            store2<bf16>(KRt + (c8 + j) * LY + y0, kr[0][j], kr[1][j]);
+            store2<bf16>(KCt + (c8 + j) * LY + y0, kc[0][j], kc[1][j]);
+            store2<bf16>(QCt + (c8 + j) * LY + y0, qc[0][j], qc[1][j]);
+        }
+    }
+    __syncthreads();
+
+    // ---- Ab = tril_-1(Kg Kt^T) per block pair (R, I): (Kc rows of R) e^{G_m(R) - G_m(I)}
+    //      against (Kr rows of I), fp32 MFMA on the bf16 family values
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
+        if (R < 0) break;
+        const float* cx = xp + (I < R ? pair_index(R, I) : 0) * DK;
+        f32x4 acc = zero4();
+#pragma unroll 8
+        for (int kk = 0; kk < DK; kk += 4) {
+            const int c = kk + lg;
+            float a = to_f32(KCt[c * LY + R * 16 + lr]);
+            if (I < R) a *= cx[c];
+            acc = mma4(a, to_f32(KRt[c * LY + I * 16 + lr]), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
+            As[r * LA + i] = i < r ? acc[e] : 0.f;
+        }
+    }
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += NTH) {
+        int R, I;
+        upper_block(idx / (SUB * SUB), R, I);
+        const int e = idx % (SUB * SUB);
+        As[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+        Ts[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- T = (I + diag(beta) Ab)^{-1}, blocked forward substitution (fp32)
+    if (w == 0) {
+        const int base = lg * SUB, col = lr;
+        float x[SUB];
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) {
+            float acc = (r == col) ? 1.f : 0.f;
+            const float br = bet[base + r];
+#pragma unroll
+            for (int i = 0; i < r; ++i) acc -= br * As[(base + r) * LA + base + i] * x[i];
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < SUB; ++r) Ts[(base + r) * LA + base + col] = x[r];
+    }
+    __syncthreads();
+    for (int R = 1; R < 4; ++R) {
+        if (w < R) {
+            const int I = w;
+            f32x4 x = zero4();
+            const float br = bet[R * SUB + lr];
+            for (int J = I; J < R; ++J)
+#pragma unroll
+                for (int kk = 0; kk < SUB; kk += 4) {
+                    const float a = br * As[(R * SUB + lr) * LA + J * SUB + kk + lg];
+                    const float b = Ts[(J * SUB + kk + lg) * LA + I * SUB + lr];
+                    x = mma4(a, b, x);
+                }
+            float* xs = Xs + I * SUB * SUB;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xs[(4 * lg + e) * SUB + lr] = x[e];
+            f32x4 y = zero4();
+#pragma unroll
+            for (int kk = 0; kk < SUB; kk += 4) {
+                const float a = Ts[(R * SUB + lr) * LA + R * SUB + kk + lg];
+                const float b = xs[(kk + lg) * SUB + lr];
+                y = mma4(a, b, y);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Ts[(R * SUB + 4 * lg + e) * LA + I * SUB + lr] = -y[e];
+        }
+        __syncthreads();
+    }
+    // T^T in bf16, token index contiguous
+    for (int idx = tid; idx < C * (C / 8); idx += NTH) {
+        const int r = idx % C, a8 = (idx / C) * 8;
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = Ts[(a8 + j) * LA + r];
+        store8<bf16>(TT + r * LT + a8, t);
+    }
+    __syncthreads();
+
+    // ---- dA = tril_-1(T^T NP) per block pair, in both orientations; the
+    //      dA . Ab part of dbeta, one partial slot per column block I
+    f32x4 d1[2], d2[2];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
+        d1[jp] = d2[jp] = zero4();
+        if (R < 0) continue;
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb) {
+            const MF::frag ft = load_frag<bf16>(TT, LT, R * 16, kb * 32);
+            const MF::frag fp = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I * 16 + lr) * C + kb * 32 + lg * 8);
+            d1[jp] = MF::mma(ft, fp, d1[jp]);   // (row r, column i)
+            d2[jp] = MF::mma(fp, ft, d2[jp]);   // (row i, column r)
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
+            d1[jp][e] = i < r ? d1[jp][e] : 0.f;
+            float t = d1[jp][e] * As[r * LA + i];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off);
+            if (lr == 0) dbp[I * C + r] = t;
+            d2[jp][e] = (I * 16 + 4 * lg + e < R * 16 + lr) ? d2[jp][e] : 0.f;
+        }
+    }
+    __syncthreads();   // every read of Ab and T (fp32) is done
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
+        if (R < 0) continue;
+        const int r = R * 16 + lr, i0 = I * 16 + 4 * lg;
+        store4<bf16>(DA + r * LT + i0, d2[jp] * bet[r]);
+        const int i = I * 16 + lr, r0 = R * 16 + 4 * lg;
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = d1[jp][e] * bet[r0 + e];
+        store4<bf16>(DAT + i * LT + r0, t);
+    }
+    __syncthreads();
+
+    // ---- per channel tile: dBk = T^T dW, the decayed products and the
+    //      reverse chain's terms, into the register fields
+    const float brX = bet[rX];
+    const bool okX = rX < valid;
+    const size_t trow = row0 + (size_t)min(rX, last) * H;   // token row of rX, clamped in bounds
+    f32x4 fQ[NCTH], fK[NCTH], fG[NCTH];
+    float sb = 0.f;   // dbeta partial of token rX
+#pragma unroll 1
+    for (int ct = 0; ct < NCTH; ++ct) {
+        const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
+        f32x4 accK = zero4();
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + OH::DWT + (size_t)(cb + lr) * C + kb * 32 + lg * 8);
+            accK = MF::mma(a, load_frag<bf16>(TT, LT, X * 16, kb * 32), accK);
+        }
+        // row side: (beta dA) Kt and dM Kt over blocks Y <= X
+        f32x4 accA = zero4(), accC = zero4();
+        for (int Y = 0; Y <= X; ++Y) {
+            if (Y > 0) {
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(rho + (Y - 1) * DK + c4);
+                accA *= rr;
+                accC *= rr;
+            }
+            const bf16x4 fa = *reinterpret_cast<const bf16x4*>(KRt + (cb + lr) * LY + Y * 16 + 4 * lg);
+            const bf16x4 fb = *reinterpret_cast<const bf16x4*>(DA + rX * LT + Y * 16 + 4 * lg);
+            const bf16x4 fm = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
+            accA = mma16(fa, fb, accA);
+            accC = mma16(fa, fm, accC);
+        }
+        // column side: (beta dA)^T Kg and dM^T Qg over blocks Y >= X
+        f32x4 accB = zero4(), accD = zero4();
+        for (int Y = 3; Y >= X; --Y) {
+            if (Y < 3) {
+                const f32x4 rr = *reinterpret_cast<const f32x4*>(rho + Y * DK + c4);
+                accB *= rr;
+                accD *= rr;
+            }
+            const bf16x4 fk = *reinterpret_cast<const bf16x4*>(KCt + (cb + lr) * LY + Y * 16 + 4 * lg);
+            const bf16x4 fq = *reinterpret_cast<const bf16x4*>(QCt + (cb + lr) * LY + Y * 16 + 4 * lg);
+            const bf16x4 fb = *reinterpret_cast<const bf16x4*>(DAT + rX * LT + Y * 16 + 4 * lg);
+            const bf16x4 fm = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
+            accB = mma16(fk, fb, accB);
+            accD = mma16(fq, fm, accD);
+        }
+        const f32x4 G4 = *reinterpret_cast<const f32x4*>(Gs + rX * DKP + c4);
+        const f32x4 gX = *reinterpret_cast<const f32x4*>(gm + X * DK + c4);
+        const f32x4 gC = *reinterpret_cast<const f32x4*>(gm + 4 * DK + c4);
+        const f32x4 k4 = okX ? widen4(load_raw4<bf16>(k + trow * DK + c4)) : zero4();
+        const f32x4 q4 = okX ? widen4(load_raw4<bf16>(q + trow * DK + c4)) : zero4();
+        const f32x4 dqg = widen4(load_raw4<bf16>(ob + OH::DQG + (size_t)rX * DK + c4));
+        const f32x4 dkc = widen4(load_raw4<bf16>(ob + OH::DKC + (size_t)rX * DK + c4));
+        f32x4 cs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float gam = dexp2<bf16>(G4[e]), ec = dexp2<bf16>(gC[e] - G4[e]);
+            const float fr = dexp2<bf16>(G4[e] - gX[e]), fc = dexp2<bf16>(gX[e] - G4[e]);
+            const float bk = brX * accK[e] * gam;               // beta dBk e^G
+            sb += accK[e] * k4[e] * gam;                        // dBk . Kg
+            const float a = accA[e] * fr, cq = accC[e] * fr, bt = (accB[e] + accD[e]) * fc;
+            const float t = dkc[e] * ec * k4[e];
+            fQ[ct][e] = cq + dqg[e] * gam;
+            fK[ct][e] = bk + a + bt + dkc[e] * ec;
+            // the decayed products' dG terms take their k and q factors from the
+            // same rounded families as the MFMA operands (k_r e^{G_r - G_m(X)} is
+            // Kc of row r, and so on): the row-side and column-side terms then
+            // cancel in the chunk's sum of dG as they do exactly
+            const int co = (c4 + e) * LY + rX;
+            fG[ct][e] = bk * k4[e] + accA[e] * to_f32(KCt[co]) + accC[e] * to_f32(QCt[co]) -
+                        (accB[e] + accD[e]) * to_f32(KRt[co]) + dqg[e] * gam * q4[e] - t;
+            cs[e] = t;
+        }
+        // column sums of dKc e^{G_C - G} k over this wave's 16 tokens
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) cs[e] += __shfl_xor(cs[e], off);
+        if (lr == 0) *reinterpret_cast<f32x4*>(car + X * DK + c4) = cs;
+    }
+    // ---- dBv = T^T dVn: dV and the dBv . V part of dbeta
+#pragma unroll 1
+    for (int jt = 0; jt < NVTH; ++jt) {
+        const int jb = hf * (DV / 2) + jt * 16, j4 = jb + 4 * lg;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + (size_t)(jb + lr) * C + kb * 32 + lg * 8);
+            acc = MF::mma(a, load_frag<bf16>(TT, LT, X * 16, kb * 32), acc);
+        }
+        const f32x4 v4 = okX ? widen4(load_raw4<bf16>(v + trow * DV + j4)) : zero4();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sb += acc[e] * v4[e];
+        if (okX) *reinterpret_cast<f32x4*>(dvo + trow * DV + j4) = acc * brX;
+    }
+    sb += __shfl_xor(sb, 16);
+    sb += __shfl_xor(sb, 32);
+    if (lg == 0) dbp[(4 + hf) * C + rX] = sb;
+    __syncthreads();   // column sums complete
+    if (X == 3 && lr == 15) {   // the chunk's last row carries the G_C terms
+#pragma unroll
+        for (int ct = 0; ct < NCTH; ++ct) {
+            const int c4 = hf * (DK / 2) + ct * 16 + 4 * lg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c4 + e;
+                fG[ct][e] += dgc[c] + car[c] + car[DK + c] + car[2 * DK + c] + car[3 * DK + c];
+            }
+        }
+    }
+    if (okX) {
+#pragma unroll
+        for (int ct = 0; ct < NCTH; ++ct) {
+            const int c4 = hf * (DK / 2) + ct * 16 + 4 * lg;
+            *reinterpret_cast<f32x4*>(dq + trow * DK + c4) = fQ[ct];
+            *reinterpret_cast<f32x4*>(dk + trow * DK + c4) = fK[ct];
+        }
+    }
+    __syncthreads();   // every read of G and of the column sums is done
+#pragma unroll
+    for (int ct = 0; ct < NCTH; ++ct)
+        *reinterpret_cast<f32x4*>(Gs + rX * DKP + hf * (DK / 2) + ct * 16 + 4 * lg) = fG[ct];
+    __syncthreads();
+
+    // ---- dg = reverse cumulative sum of dG over the chunk, dz
+    {
+        const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+        float suf[RP][2];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = RP - 1; i >= 0; --i) {
+            s0 += Gs[(r0 + i) * DKP + c0];
+            s1 += Gs[(r0 + i) * DKP + c0 + 1];
+            suf[i][0] = s0;
+            suf[i][1] = s1;
+        }
+        car[part * DK + c0] = s0;
+        car[part * DK + c0 + 1] = s1;
+        __syncthreads();
+        float cr[2] = {0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < L::NPART; ++p)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (p > part) cr[j] += car[p * DK + c0 + j];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+            const int r = r0 + i;
+            if (r < valid) {
+                const size_t off = (row0 + (size_t)r * H) * DK + c0;
+                const bf16x2 zz = load2<bf16>(z + off);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float sg = 1.0f / (1.0f + expf(-to_f32(zz[j])));
+                    dz[off + j] = (suf[i][j] + cr[j]) * g_min * sg * (1.0f - sg);
+                }
+            }
+        }
+    }
+    if (tid < valid)
+        dbeta[row0 + (size_t)tid * H] = dbp[tid] + dbp[C + tid] + dbp[2 * C + tid] + dbp[3 * C + tid] +
+                                        dbp[4 * C + tid] + dbp[5 * C + tid];
+}
+
 template <class E, int DK, int DV>
 hipError_t launch_t(const BwdArgs& a) {
     typedef typename Compute<E>::type CT;
@@ -823,13 +1368,24 @@ hipError_t launch_t(const BwdArgs& a) {
                        (const unsigned char*)(ws + lo.bws), (const float*)(ws + lo.st), (const CT*)(ws + lo.vn),
                        ws + lo.ob);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    typedef DIntra<E, DK, DV> LI;
-    if ((err = hipFuncSetAttribute((const void*)dintra_kernel<E, DK, DV>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS)) != hipSuccess)
-        return err;
-    hipLaunchKernelGGL((dintra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(LI::NTH), LI::LDS, st, (const E*)a.q,
-                       (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.T, a.H, NC,
-                       (const unsigned char*)(ws + lo.ob), a.dq, a.dk, a.dv, a.dz, a.dbeta);
+    if constexpr (std::is_same<E, bf16>::value) {
+        typedef DIntraH<DK, DV> LI;
+        if ((err = hipFuncSetAttribute((const void*)dintra16_kernel<DK, DV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS)) != hipSuccess)
+            return err;
+        hipLaunchKernelGGL((dintra16_kernel<DK, DV>), dim3(NC, a.H, a.B), dim3(LI::NTH), LI::LDS, st,
+                           (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.z,
+                           (const bf16*)a.beta, a.g_min, a.T, a.H, NC, (const unsigned char*)(ws + lo.ob), a.dq,
+                           a.dk, a.dv, a.dz, a.dbeta);
+    } else {
+        typedef DIntra<E, DK, DV> LI;
+        if ((err = hipFuncSetAttribute((const void*)dintra_kernel<E, DK, DV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LI::LDS)) != hipSuccess)
+            return err;
+        hipLaunchKernelGGL((dintra_kernel<E, DK, DV>), dim3(NC, a.H, a.B), dim3(LI::NTH), LI::LDS, st, (const E*)a.q,
+                           (const E*)a.k, (const E*)a.v, (const E*)a.z, (const E*)a.beta, a.g_min, a.T, a.H, NC,
+                           (const unsigned char*)(ws + lo.ob), a.dq, a.dk, a.dv, a.dz, a.dbeta);
+    }
     return hipGetLastError();
 }
 
