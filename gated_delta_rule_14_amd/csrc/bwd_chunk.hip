@@ -968,6 +968,20 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
     const int X = w & 3, hf = w >> 2;   // token block and channel half of this wave
     const int rX = X * 16 + lr;         // token (accumulator column) of this lane
 
+    // the operand families' token loads (two tokens x eight channels per
+    // thread) are issued first, to be in flight during the gate scan
+    constexpr int NFAM = (C / 2) * (DK / 8);
+    static_assert(NFAM <= NTH, "one family item per thread");
+    const bool fam = tid < NFAM;
+    const int fy0 = 2 * (tid % (C / 2)), fc8 = (tid / (C / 2)) * 8 % DK;
+    bf16x8 fk[2], fq[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const size_t off = (row0 + (size_t)min(fy0 + u, last) * H) * DK + fc8;
+        fk[u] = *reinterpret_cast<const bf16x8*>(k + off);
+        fq[u] = *reinterpret_cast<const bf16x8*>(q + off);
+    }
+
     // ---- gate, chunk-local scan (log2 units)
     {
         const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
@@ -1029,26 +1043,23 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
             xp[pp * DK + cc] = dexp2<bf16>(gm[R * DK + cc] - gm[I * DK + cc]);
         }
     }
-    // operand families, channel-major: two tokens x eight channels per item
-    for (int idx = tid; idx < (C / 2) * (DK / 8); idx += NTH) {
-        const int y0 = 2 * (idx % (C / 2)), c8 = (idx / (C / 2)) * 8, Y = y0 >> 4;
+    // operand families, channel-major
+    if (fam) {
+        const int Y = fy0 >> 4;
         float kr[2][8], kc[2][8], qc[2][8];
-        const f32x4 ma = *reinterpret_cast<const f32x4*>(gm + Y * DK + c8);
-        const f32x4 mb = *reinterpret_cast<const f32x4*>(gm + Y * DK + c8 + 4);
+        const f32x4 ma = *reinterpret_cast<const f32x4*>(gm + Y * DK + fc8);
+        const f32x4 mb = *reinterpret_cast<const f32x4*>(gm + Y * DK + fc8 + 4);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int y = y0 + u;
+            const int y = fy0 + u;
             const bool ok = y < valid;
-            const size_t off = (row0 + (size_t)min(y, last) * H) * DK + c8;
-            const bf16x8 kk = *reinterpret_cast<const bf16x8*>(k + off);
-            const bf16x8 qq = *reinterpret_cast<const bf16x8*>(q + off);
-            const f32x4 ga = *reinterpret_cast<const f32x4*>(Gs + y * DKP + c8);
-            const f32x4 gb = *reinterpret_cast<const f32x4*>(Gs + y * DKP + c8 + 4);
+            const f32x4 ga = *reinterpret_cast<const f32x4*>(Gs + y * DKP + fc8);
+            const f32x4 gb = *reinterpret_cast<const f32x4*>(Gs + y * DKP + fc8 + 4);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float d = (j < 4 ? ma[j] : mb[j - 4]) - (j < 4 ? ga[j] : gb[j - 4]);
                 const float e1 = dexp2<bf16>(d), e2 = dexp2<bf16>(-d);
-                const float kv = ok ? to_f32(kk[j]) : 0.f, qv = ok ? to_f32(qq[j]) : 0.f;
+                const float kv = ok ? to_f32(fk[u][j]) : 0.f, qv = ok ? to_f32(fq[u][j]) : 0.f;
                 kr[u][j] = kv * e1;
                 kc[u][j] = kv * e2;
                 qc[u][j] = qv * e2;
@@ -1056,27 +1067,37 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            store2<bf16>(KRt + (c8 + j) * LY + y0, kr[0][j], kr[1][j]);
-            store2<bf16>(KCt + (c8 + j) * LY + y0, kc[0][j], kc[1][j]);
-            store2<bf16>(QCt + (c8 + j) * LY + y0, qc[0][j], qc[1][j]);
+            store2<bf16>(KRt + (fc8 + j) * LY + fy0, kr[0][j], kr[1][j]);
+            store2<bf16>(KCt + (fc8 + j) * LY + fy0, kc[0][j], kc[1][j]);
+            store2<bf16>(QCt + (fc8 + j) * LY + fy0, qc[0][j], qc[1][j]);
         }
     }
+    const size_t trow = row0 + (size_t)min(rX, last) * H;   // token row of rX, clamped in bounds
     __syncthreads();
 
+    // block pairs (R, I) of this wave
+    const int R0 = kPairsB[w][0][0], I0 = kPairsB[w][0][1], R1 = kPairsB[w][1][0], I1 = kPairsB[w][1][1];
+    const bool two = R1 >= 0;
     // ---- Ab = tril_-1(Kg Kt^T) per block pair (R, I): (Kc rows of R) e^{G_m(R) - G_m(I)}
-    //      against (Kr rows of I), fp32 MFMA on the bf16 family values
+    //      against (Kr rows of I), bf16 MFMA; the fragments gather eight
+    //      channels of one token from the channel-major families
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
-        const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
-        if (R < 0) break;
+        const int R = jp ? R1 : R0, I = jp ? I1 : I0;
+        if (jp && !two) break;
         const float* cx = xp + (I < R ? pair_index(R, I) : 0) * DK;
         f32x4 acc = zero4();
-#pragma unroll 8
-        for (int kk = 0; kk < DK; kk += 4) {
-            const int c = kk + lg;
-            float a = to_f32(KCt[c * LY + R * 16 + lr]);
-            if (I < R) a *= cx[c];
-            acc = mma4(a, to_f32(KRt[c * LY + I * 16 + lr]), acc);
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            const int c0 = kb * 32 + lg * 8;
+            MF::frag fa, fb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = to_f32(KCt[(c0 + j) * LY + R * 16 + lr]);
+                fa[j] = (bf16)(I < R ? x * cx[c0 + j] : x);
+                fb[j] = KRt[(c0 + j) * LY + I * 16 + lr];
+            }
+            acc = MF::mma(fa, fb, acc);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1136,6 +1157,22 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         }
         __syncthreads();
     }
+    // the later phases' reverse-chain operands, issued here to be in flight
+    // during the transpose of T: NP^T of this wave's pairs, dM and dM^T rows
+    // of its tokens (every block)
+    bf16x8 npf[2][C / 32];
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+        npf[0][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I0 * 16 + lr) * C + kb * 32 + lg * 8);
+        npf[1][kb] = two ? *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I1 * 16 + lr) * C + kb * 32 + lg * 8)
+                         : bf16x8{};
+    }
+    bf16x4 dmr[4], dmc[4];
+#pragma unroll
+    for (int Y = 0; Y < 4; ++Y) {
+        dmr[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
+        dmc[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
+    }
     // T^T in bf16, token index contiguous
     for (int idx = tid; idx < C * (C / 8); idx += NTH) {
         const int r = idx % C, a8 = (idx / C) * 8;
@@ -1157,9 +1194,8 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb) {
             const MF::frag ft = load_frag<bf16>(TT, LT, R * 16, kb * 32);
-            const MF::frag fp = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I * 16 + lr) * C + kb * 32 + lg * 8);
-            d1[jp] = MF::mma(ft, fp, d1[jp]);   // (row r, column i)
-            d2[jp] = MF::mma(fp, ft, d2[jp]);   // (row i, column r)
+            d1[jp] = MF::mma(ft, npf[jp][kb], d1[jp]);   // (row r, column i)
+            d2[jp] = MF::mma(npf[jp][kb], ft, d2[jp]);   // (row i, column r)
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -1185,61 +1221,103 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         for (int e = 0; e < 4; ++e) t[e] = d1[jp][e] * bet[r0 + e];
         store4<bf16>(DAT + i * LT + r0, t);
     }
+    // exact zeros outside the triangles: the upper blocks of beta dA and the
+    // lower blocks of its transpose
+    for (int idx = tid; idx < 6 * SUB * SUB; idx += NTH) {
+        int R, I;
+        upper_block(idx / (SUB * SUB), R, I);   // I > R
+        const int e = idx % (SUB * SUB);
+        DA[(R * SUB + e / SUB) * LT + I * SUB + e % SUB] = from_f32<bf16>(0.f);
+        DAT[(I * SUB + e / SUB) * LT + R * SUB + e % SUB] = from_f32<bf16>(0.f);
+    }
     __syncthreads();
 
     // ---- per channel tile: dBk = T^T dW, the decayed products and the
-    //      reverse chain's terms, into the register fields
+    //      reverse chain's terms, into the register fields; each tile's
+    //      global operands are loaded one tile ahead
     const float brX = bet[rX];
     const bool okX = rX < valid;
-    const size_t trow = row0 + (size_t)min(rX, last) * H;   // token row of rX, clamped in bounds
-    f32x4 fQ[NCTH], fK[NCTH], fG[NCTH];
+    struct Tile {
+        bf16x8 w[C / 32];
+        bf16x4 k4, q4, dqg, dkc;
+    };
+    auto load_tile = [&](int ct, Tile& t) {
+        const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb)
+            t.w[kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DWT + (size_t)(cb + lr) * C + kb * 32 + lg * 8);
+        t.k4 = load_raw4<bf16>(k + trow * DK + c4);
+        t.q4 = load_raw4<bf16>(q + trow * DK + c4);
+        t.dqg = load_raw4<bf16>(ob + OH::DQG + (size_t)rX * DK + c4);
+        t.dkc = load_raw4<bf16>(ob + OH::DKC + (size_t)rX * DK + c4);
+    };
+    f32x4 fG[NCTH];   // dq and dk are final within their tile and stored there
     float sb = 0.f;   // dbeta partial of token rX
+    bf16x8 dvf[NVTH][C / 32];   // dVn^T tiles of this wave's value half, and v
+    bf16x4 vr[NVTH];
+    Tile cur;
+    load_tile(0, cur);
 #pragma unroll 1
     for (int ct = 0; ct < NCTH; ++ct) {
+        Tile nxt;
+        if (ct + 1 < NCTH) {
+            load_tile(ct + 1, nxt);
+        } else {
+#pragma unroll
+            for (int jt = 0; jt < NVTH; ++jt) {
+                const int jb = hf * (DV / 2) + jt * 16;
+#pragma unroll
+                for (int kb = 0; kb < C / 32; ++kb)
+                    dvf[jt][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + (size_t)(jb + lr) * C + kb * 32 + lg * 8);
+                vr[jt] = load_raw4<bf16>(v + trow * DV + jb + 4 * lg);
+            }
+        }
         const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
         f32x4 accK = zero4();
 #pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + OH::DWT + (size_t)(cb + lr) * C + kb * 32 + lg * 8);
-            accK = MF::mma(a, load_frag<bf16>(TT, LT, X * 16, kb * 32), accK);
-        }
-        // row side: (beta dA) Kt and dM Kt over blocks Y <= X
+        for (int kb = 0; kb < C / 32; ++kb) accK = MF::mma(cur.w[kb], load_frag<bf16>(TT, LT, X * 16, kb * 32), accK);
+        // the token blocks Y accumulate by Horner's scheme, branch-free: the
+        // accumulator is scaled by e^{G_m(Y) - G_m(Y-1)} (row side, upward) or
+        // e^{G_m(Y+1) - G_m(Y)} (column side, downward) inside the triangle and
+        // by 1 outside it, where the products add exact zeros (upper blocks of
+        // beta dA and dM); the selects are on the wave-uniform X
+        const f32x4 one4 = f32x4{1.f, 1.f, 1.f, 1.f};
         f32x4 accA = zero4(), accC = zero4();
-        for (int Y = 0; Y <= X; ++Y) {
+#pragma unroll
+        for (int Y = 0; Y < 4; ++Y) {
+            const int fo = (cb + lr) * LY + Y * 16 + 4 * lg, ao = rX * LT + Y * 16 + 4 * lg;
+            const bf16x4 fa = *reinterpret_cast<const bf16x4*>(KRt + fo);
             if (Y > 0) {
                 const f32x4 rr = *reinterpret_cast<const f32x4*>(rho + (Y - 1) * DK + c4);
-                accA *= rr;
-                accC *= rr;
+                const f32x4 sc = Y <= X ? rr : one4;
+                accA *= sc;
+                accC *= sc;
             }
-            const bf16x4 fa = *reinterpret_cast<const bf16x4*>(KRt + (cb + lr) * LY + Y * 16 + 4 * lg);
-            const bf16x4 fb = *reinterpret_cast<const bf16x4*>(DA + rX * LT + Y * 16 + 4 * lg);
-            const bf16x4 fm = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
-            accA = mma16(fa, fb, accA);
-            accC = mma16(fa, fm, accC);
+            accA = mma16(fa, *reinterpret_cast<const bf16x4*>(DA + ao), accA);
+            accC = mma16(fa, dmr[Y], accC);
         }
-        // column side: (beta dA)^T Kg and dM^T Qg over blocks Y >= X
         f32x4 accB = zero4(), accD = zero4();
-        for (int Y = 3; Y >= X; --Y) {
+#pragma unroll
+        for (int Y = 3; Y >= 0; --Y) {
+            const int fo = (cb + lr) * LY + Y * 16 + 4 * lg, ao = rX * LT + Y * 16 + 4 * lg;
+            const bf16x4 fk = *reinterpret_cast<const bf16x4*>(KCt + fo);
+            const bf16x4 fq = *reinterpret_cast<const bf16x4*>(QCt + fo);
             if (Y < 3) {
                 const f32x4 rr = *reinterpret_cast<const f32x4*>(rho + Y * DK + c4);
-                accB *= rr;
-                accD *= rr;
+                const f32x4 sc = Y >= X ? rr : one4;
+                accB *= sc;
+                accD *= sc;
             }
-            const bf16x4 fk = *reinterpret_cast<const bf16x4*>(KCt + (cb + lr) * LY + Y * 16 + 4 * lg);
-            const bf16x4 fq = *reinterpret_cast<const bf16x4*>(QCt + (cb + lr) * LY + Y * 16 + 4 * lg);
-            const bf16x4 fb = *reinterpret_cast<const bf16x4*>(DAT + rX * LT + Y * 16 + 4 * lg);
-            const bf16x4 fm = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
-            accB = mma16(fk, fb, accB);
-            accD = mma16(fq, fm, accD);
+            accB = mma16(fk, *reinterpret_cast<const bf16x4*>(DAT + ao), accB);
+            accD = mma16(fq, dmc[Y], accD);
         }
         const f32x4 G4 = *reinterpret_cast<const f32x4*>(Gs + rX * DKP + c4);
         const f32x4 gX = *reinterpret_cast<const f32x4*>(gm + X * DK + c4);
         const f32x4 gC = *reinterpret_cast<const f32x4*>(gm + 4 * DK + c4);
-        const f32x4 k4 = okX ? widen4(load_raw4<bf16>(k + trow * DK + c4)) : zero4();
-        const f32x4 q4 = okX ? widen4(load_raw4<bf16>(q + trow * DK + c4)) : zero4();
-        const f32x4 dqg = widen4(load_raw4<bf16>(ob + OH::DQG + (size_t)rX * DK + c4));
-        const f32x4 dkc = widen4(load_raw4<bf16>(ob + OH::DKC + (size_t)rX * DK + c4));
-        f32x4 cs;
+        const f32x4 k4 = okX ? widen4(cur.k4) : zero4();
+        const f32x4 q4 = okX ? widen4(cur.q4) : zero4();
+        const f32x4 dqg = widen4(cur.dqg), dkc = widen4(cur.dkc);
+        f32x4 cs, fQ, fK;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float gam = dexp2<bf16>(G4[e]), ec = dexp2<bf16>(gC[e] - G4[e]);
@@ -1248,8 +1326,8 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
             sb += accK[e] * k4[e] * gam;                        // dBk . Kg
             const float a = accA[e] * fr, cq = accC[e] * fr, bt = (accB[e] + accD[e]) * fc;
             const float t = dkc[e] * ec * k4[e];
-            fQ[ct][e] = cq + dqg[e] * gam;
-            fK[ct][e] = bk + a + bt + dkc[e] * ec;
+            fQ[e] = cq + dqg[e] * gam;
+            fK[e] = bk + a + bt + dkc[e] * ec;
             // the decayed products' dG terms take their k and q factors from the
             // same rounded families as the MFMA operands (k_r e^{G_r - G_m(X)} is
             // Kc of row r, and so on): the row-side and column-side terms then
@@ -1265,18 +1343,20 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) cs[e] += __shfl_xor(cs[e], off);
         if (lr == 0) *reinterpret_cast<f32x4*>(car + X * DK + c4) = cs;
+        if (okX) {
+            *reinterpret_cast<f32x4*>(dq + trow * DK + c4) = fQ;
+            *reinterpret_cast<f32x4*>(dk + trow * DK + c4) = fK;
+        }
+        cur = nxt;
     }
     // ---- dBv = T^T dVn: dV and the dBv . V part of dbeta
-#pragma unroll 1
+#pragma unroll
     for (int jt = 0; jt < NVTH; ++jt) {
         const int jb = hf * (DV / 2) + jt * 16, j4 = jb + 4 * lg;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + (size_t)(jb + lr) * C + kb * 32 + lg * 8);
-            acc = MF::mma(a, load_frag<bf16>(TT, LT, X * 16, kb * 32), acc);
-        }
-        const f32x4 v4 = okX ? widen4(load_raw4<bf16>(v + trow * DV + j4)) : zero4();
+        for (int kb = 0; kb < C / 32; ++kb) acc = MF::mma(dvf[jt][kb], load_frag<bf16>(TT, LT, X * 16, kb * 32), acc);
+        const f32x4 v4 = okX ? widen4(vr[jt]) : zero4();
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb += acc[e] * v4[e];
         if (okX) *reinterpret_cast<f32x4*>(dvo + trow * DV + j4) = acc * brX;
@@ -1296,14 +1376,6 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
             }
         }
     }
-    if (okX) {
-#pragma unroll
-        for (int ct = 0; ct < NCTH; ++ct) {
-            const int c4 = hf * (DK / 2) + ct * 16 + 4 * lg;
-            *reinterpret_cast<f32x4*>(dq + trow * DK + c4) = fQ[ct];
-            *reinterpret_cast<f32x4*>(dk + trow * DK + c4) = fK[ct];
-        }
-    }
     __syncthreads();   // every read of G and of the column sums is done
 #pragma unroll
     for (int ct = 0; ct < NCTH; ++ct)
@@ -1312,6 +1384,10 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
 
     // ---- dg = reverse cumulative sum of dG over the chunk, dz
     {
+        // z is read again here; an opaque copy of the pointer keeps the
+        // compiler from holding the gate scan's loads in registers until now
+        const bf16* zl = z;
+        asm volatile("" : "+s"(zl));
         const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
         float suf[RP][2];
         float s0 = 0.f, s1 = 0.f;
@@ -1336,10 +1412,10 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
             const int r = r0 + i;
             if (r < valid) {
                 const size_t off = (row0 + (size_t)r * H) * DK + c0;
-                const bf16x2 zz = load2<bf16>(z + off);
+                const bf16x2 zz = load2<bf16>(zl + off);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float sg = 1.0f / (1.0f + expf(-to_f32(zz[j])));
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + dexp2<bf16>(-LOG2E * to_f32(zz[j])));
                     dz[off + j] = (suf[i][j] + cr[j]) * g_min * sg * (1.0f - sg);
                 }
             }
