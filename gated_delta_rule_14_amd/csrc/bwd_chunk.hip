@@ -97,7 +97,7 @@ Lay lay_t(int B, int T, int H) {
     lo.fws = 0;
     lo.bws = a256(nchunk * Ws<CT, DK, DV>::BYTES);
     lo.st = lo.bws + a256(nchunk * WsB<CT, DK, DV>::BYTES);
-    lo.vn = lo.st + a256(nchunk * DK * DV * 4);
+    lo.vn = lo.st + a256(nchunk * DK * DV * sizeof(CT));
     lo.ob = lo.vn + a256(nchunk * C * DV * sizeof(CT));
     lo.total = lo.ob + nchunk * ob_bytes<CT, DK, DV>();
     return lo;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                                                         float* __restrict__ ds0, int T, int H, int NC,
                                                         const unsigned char* __restrict__ fws,
                                                         const unsigned char* __restrict__ bws,
-                                                        const float* __restrict__ states,
+                                                        const typename Compute<E>::type* __restrict__ states,
                                                         const typename Compute<E>::type* __restrict__ vn,
                                                         unsigned char* __restrict__ obuf) {
     typedef DChain<E, DK, DV> L;
@@ -180,7 +180,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         const size_t cid = bh * NC + n;
         const unsigned char* fb = fws + cid * WL::BYTES;
         const CT* bk = reinterpret_cast<const CT*>(bws + cid * WB::BYTES);
-        const float* Sn = states + cid * DK * DV;
+        const CT* Sn = states + cid * DK * DV;
         const CT* Vn = vn + cid * C * DV;
         float* ob = reinterpret_cast<float*>(obuf + cid * ob_bytes<CT, DK, DV>());
         bf16* obh = reinterpret_cast<bf16*>(ob);
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             f32x4 accQ = zero4(), accW = zero4(), accK = zero4();
 #pragma unroll
             for (int kk = 0; kk < DV / KS; ++kk) {
-                const typename MF::frag fs = load_frag_f32<CT>(Sn, DV, cb * 16, kk * KS);
+                const typename MF::frag fs = load_frag<CT>(Sn, DV, cb * 16, kk * KS);
                 accW = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fs, accW);
                 if constexpr (H16) {   // (channel, token) orientation: rows of dO S^T and Vn dS'^T
                     accQ = MF::mma(fs, dof[kk], accQ);
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int e = 0; e < 4; ++e) {
             float sacc = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) sacc += accD[ct][e] * Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)];
+            for (int ct = 0; ct < NT; ++ct) sacc += accD[ct][e] * to_f32(Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)]);
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) sacc += __shfl_xor(sacc, off);
             if ((l & 15) == 0) {
@@ -925,6 +925,16 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
+// Sum over the 16 lanes of a DPP row, in every lane: quad swaps, then the
+// half-row and row mirrors.
+__device__ __forceinline__ float sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    return x;
+}
+
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const bf16* __restrict__ z,
@@ -1201,9 +1211,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         for (int e = 0; e < 4; ++e) {
             const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
             d1[jp][e] = i < r ? d1[jp][e] : 0.f;
-            float t = d1[jp][e] * As[r * LA + i];
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) t += __shfl_xor(t, off);
+            const float t = sum16(d1[jp][e] * As[r * LA + i]);
             if (lr == 0) dbp[I * C + r] = t;
             d2[jp][e] = (I * 16 + 4 * lg + e < R * 16 + lr) ? d2[jp][e] : 0.f;
         }
@@ -1339,9 +1347,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         }
         // column sums of dKc e^{G_C - G} k over this wave's 16 tokens
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) cs[e] += __shfl_xor(cs[e], off);
+        for (int e = 0; e < 4; ++e) cs[e] = sum16(cs[e]);
         if (lr == 0) *reinterpret_cast<f32x4*>(car + X * DK + c4) = cs;
         if (okX) {
             *reinterpret_cast<f32x4*>(dq + trow * DK + c4) = fQ;
@@ -1433,7 +1439,7 @@ hipError_t launch_t(const BwdArgs& a) {
     unsigned char* ws = (unsigned char*)a.workspace;
     hipStream_t st = (hipStream_t)a.stream;
     const int NC = (a.T + C - 1) / C;
-    hipError_t err = launch_chunk_bwd_forward(a, ws + lo.fws, ws + lo.bws, (float*)(ws + lo.st), ws + lo.vn);
+    hipError_t err = launch_chunk_bwd_forward(a, ws + lo.fws, ws + lo.bws, ws + lo.st, ws + lo.vn);
     if (err != hipSuccess) return err;
     typedef DChain<E, DK, DV> LC_;
     if ((err = hipFuncSetAttribute((const void*)dchain_kernel<E, DK, DV>,
@@ -1441,7 +1447,7 @@ hipError_t launch_t(const BwdArgs& a) {
         return err;
     hipLaunchKernelGGL((dchain_kernel<E, DK, DV>), dim3(a.B * a.H), dim3(LC_::NTH), LC_::LDS, st, (const E*)a.dout,
                        a.ds_final, a.ds0, a.T, a.H, NC, (const unsigned char*)(ws + lo.fws),
-                       (const unsigned char*)(ws + lo.bws), (const float*)(ws + lo.st), (const CT*)(ws + lo.vn),
+                       (const unsigned char*)(ws + lo.bws), (const CT*)(ws + lo.st), (const CT*)(ws + lo.vn),
                        ws + lo.ob);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if constexpr (std::is_same<E, bf16>::value) {

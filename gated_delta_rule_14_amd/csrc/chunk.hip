@@ -225,7 +225,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             store2<CT>(KL + r * LDK + c0, kl[0], kl[1]);
             store2<CT>(QL + r * LDK + c0, ql[0], ql[1]);
             store2<CT>(KR + r * LDK + c0, kR[0], kR[1]);
-            store2<CT>(gQG + r * DK + c0, ql[0] * eGm[0], ql[1] * eGm[1]);
+            if constexpr (!BWD) store2<CT>(gQG + r * DK + c0, ql[0] * eGm[0], ql[1] * eGm[1]);
             if constexpr (BWD) store2<CT>(gKC + r * DK + c0, kg[0][i], kg[1][i]);
         }
 #pragma unroll
@@ -277,7 +277,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             av[j][e] = (i0 + e < r) ? bet[r] * accA[e] : 0.f;
             mv[e] = (i0 + e <= r) ? accM[e] : 0.f;
         }
-        store4<CT>(gM + r * C + i0, mv);
+        if constexpr (!BWD) store4<CT>(gM + r * C + i0, mv);
         if constexpr (BWD) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) gMT[(i0 + e) * C + r] = from_f32<CT>(mv[e]);
@@ -289,7 +289,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
         for (int p = 0; p < 6; ++p) {
             const int R = p < 3 ? 0 : (p < 5 ? 1 : 2);
             const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
-            store4<CT>(gM + (R * SUB + (l & 15)) * C + I * SUB + 4 * (l >> 4), zero4());
+            if constexpr (!BWD) store4<CT>(gM + (R * SUB + (l & 15)) * C + I * SUB + 4 * (l >> 4), zero4());
             if constexpr (BWD) store4<CT>(gMT + (I * SUB + (l & 15)) * C + R * SUB + 4 * (l >> 4), zero4());
         }
     }
@@ -502,7 +502,8 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
                                            const unsigned char* chain, E* __restrict__ o,
                                            f32x4 (&accS)[DK / 64][TV / 16], typename Compute<E>::type* Sb0,
                                            typename Compute<E>::type* Sb1, typename Compute<E>::type* Vn,
-                                           float* __restrict__ st_out, typename Compute<E>::type* __restrict__ vn_out) {
+                                           typename Compute<E>::type* __restrict__ st_out,
+                                           typename Compute<E>::type* __restrict__ vn_out) {
     typedef Chain<E, DK, DV, NCOL, TV, MODE> L;
     typedef typename L::CT CT;
     typedef typename L::MF MF;
@@ -514,7 +515,7 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
     L::load(fill, chain + (size_t)nfill * WL::BYTES, w, l, col0);
     if constexpr (MODE == CM_STATES) {
         // the state entering chunk n, rows w*DK/4 + rb*16 + 4(l/16) + e
-        float* so = st_out + (size_t)n * DK * DV;
+        CT* so = st_out + (size_t)n * DK * DV;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -522,7 +523,7 @@ __device__ __forceinline__ void chain_step(typename Chain<E, DK, DV, NCOL, TV, M
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     so[(size_t)(w * (DK / 4) + rb * 16 + 4 * (l >> 4) + e) * DV + col0 + ct * 16 + (l & 15)] =
-                        accS[rb][ct][e];
+                        from_f32<CT>(accS[rb][ct][e]);
     }
 
     // V_new = U - W X (rows 16w.. x TV) and O^T = X^T (Q e^G)^T (TV x rows 16w..)
@@ -598,7 +599,7 @@ template <class E, int DK, int DV, int NCOL, int TV, int MODE>
 __global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const float* __restrict__ xin,
                                                     float* __restrict__ xout, int T, int H, int NC, int L,
                                                     int nchain, const unsigned char* __restrict__ ws,
-                                                    float* __restrict__ st_out = nullptr,
+                                                    typename Compute<E>::type* __restrict__ st_out = nullptr,
                                                     typename Compute<E>::type* __restrict__ vn_out = nullptr) {
     typedef Chain<E, DK, DV, NCOL, TV, MODE> LC_;
     typedef typename LC_::CT CT;
@@ -642,7 +643,7 @@ __global__ __launch_bounds__(256) void chain_kernel(E* __restrict__ o, const flo
         }
 
     // two operand sets: chunk n is consumed while chunk n+1 loads
-    float* st = MODE == CM_STATES ? st_out + bh * NC * DK * DV : nullptr;
+    CT* st = MODE == CM_STATES ? st_out + bh * NC * DK * DV : nullptr;
     CT* vo = MODE == CM_STATES ? vn_out + bh * NC * C * DV : nullptr;
     typename LC_::Regs r0, r1;
     LC_::load(r0, chain + (size_t)n0 * WL::BYTES, w, l, col0);
@@ -927,7 +928,7 @@ hipError_t launch_seg_scan(const float* P, const float* R, const float* s0, floa
 // directions (fws: Ws blocks, bws: WsB blocks), then the chunk recurrence
 // from s0 storing each chunk's entering state and V_new.
 template <class E, int DK, int DV>
-static hipError_t launch_bwd_forward_t(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+static hipError_t launch_bwd_forward_t(const BwdArgs& a, unsigned char* fws, unsigned char* bws, void* states,
                                        void* vn) {
     typedef typename Compute<E>::type CT;
     constexpr int TVS = sizeof(CT) == 2 ? 32 : 16;
@@ -945,12 +946,12 @@ static hipError_t launch_bwd_forward_t(const BwdArgs& a, unsigned char* fws, uns
     if ((err = set_lds(chain_kernel<E, DK, DV, DV, TVS, CM_STATES>, LX::LDS)) != hipSuccess) return err;
     hipLaunchKernelGGL((chain_kernel<E, DK, DV, DV, TVS, CM_STATES>), dim3((DV / TVS) * nchain), dim3(256), LX::LDS,
                        st, (E*)nullptr, a.s0, (float*)nullptr, a.T, a.H, NC, NC, nchain, (const unsigned char*)fws,
-                       states, (CT*)vn);
+                       (CT*)states, (CT*)vn);
     return hipGetLastError();
 }
 
 template <class E>
-static hipError_t launch_bwd_forward_e(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+static hipError_t launch_bwd_forward_e(const BwdArgs& a, unsigned char* fws, unsigned char* bws, void* states,
                                        void* vn) {
     if (a.dk_dim == 128 && a.dv_dim == 128) return launch_bwd_forward_t<E, 128, 128>(a, fws, bws, states, vn);
     if (a.dk_dim == 128 && a.dv_dim == 64) return launch_bwd_forward_t<E, 128, 64>(a, fws, bws, states, vn);
@@ -958,7 +959,7 @@ static hipError_t launch_bwd_forward_e(const BwdArgs& a, unsigned char* fws, uns
     return launch_bwd_forward_t<E, 64, 64>(a, fws, bws, states, vn);
 }
 
-hipError_t launch_chunk_bwd_forward(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+hipError_t launch_chunk_bwd_forward(const BwdArgs& a, unsigned char* fws, unsigned char* bws, void* states,
                                     void* vn) {
     return a.bf16 ? launch_bwd_forward_e<bf16>(a, fws, bws, states, vn)
                   : launch_bwd_forward_e<float>(a, fws, bws, states, vn);

@@ -125,7 +125,7 @@ hipError_t launch_bwd(const BwdArgs& a);
 // per-chunk operands of both directions, then each chunk's entering state and
 // V_new), the reverse chunk recurrence and the per-chunk gradients in
 // bwd_chunk.hip.  g_min below CHUNK_G_MIN_LIMIT and T == 0 run launch_bwd.
-hipError_t launch_chunk_bwd_forward(const BwdArgs& a, unsigned char* fws, unsigned char* bws, float* states,
+hipError_t launch_chunk_bwd_forward(const BwdArgs& a, unsigned char* fws, unsigned char* bws, void* states,
                                     void* vn);
 size_t chunk_bwd_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
 hipError_t launch_chunk_bwd(const BwdArgs& a);
