@@ -121,10 +121,34 @@ struct DChain {
     static constexpr size_t OFF_DSR = OFF_DST + align16((size_t)DV * LDK * sizeof(CT));  // [DK][LDV] dS
     static constexpr size_t OFF_DVT = OFF_DSR + align16((size_t)DK * LDV * sizeof(CT));  // [DV][LC]  -dVn^T
     static constexpr size_t OFF_DVR = OFF_DVT + align16((size_t)DV * LC * sizeof(CT));   // [C][LDV]  -dVn
-    static constexpr size_t LDS = OFF_DVR + align16((size_t)C * LDV * sizeof(CT));
+    // bf16: the chunk's entering state S, staged by asynchronous global->LDS
+    // loads one chunk ahead; rows of DV elements in 16-byte groups, group g of
+    // row r at position g ^ (r mod DV/8), so a fragment read (16 rows, one
+    // group) touches 16 distinct positions
+    static constexpr bool SL = std::is_same<CT, bf16>::value;
+    static constexpr size_t OFF_S = OFF_DVR + align16((size_t)C * LDV * sizeof(CT));     // [DK][DV]  S
+    static constexpr size_t LDS = OFF_S + (SL ? (size_t)DK * DV * 2 : 0);
     static_assert(LDS <= 160 * 1024, "reverse chain LDS budget");
+    static_assert(!SL || ((size_t)DK * DV * 2) % (1024 * NW) == 0, "whole 1 KB loads per wave");
     static_assert(NW % 4 == 0 && NT % NCG == 0 && (DK / 16) % NCG == 0 && (C / 16) % NCG == 0, "wave split");
 };
+
+// One chunk's entering state S (DK x DV bf16) into LDS by asynchronous
+// global->LDS loads: wave instruction i fills bytes 1024 i .. 1024 i + 1023;
+// group g of row r lands at position g ^ (r mod DV/8) of its row.
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void stage_state(const bf16* __restrict__ src, unsigned char* lds) {
+    constexpr int SG = DV / 8, PER_WAVE = DK * DV * 2 / 1024 / NW;
+    const int w = wave_id(), l = lane_id();
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int ins = w * PER_WAVE + i, byte = ins * 1024 + 16 * l;
+        const int r = byte / (DV * 2), p = (byte % (DV * 2)) / 16, g = p ^ (r & (SG - 1));
+        __builtin_amdgcn_global_load_lds(src + (size_t)r * DV + g * 8, lds + ins * 1024, 16, 0, 0);
+    }
+}
+template <int DK, int DV, int NW>
+__device__ __forceinline__ void stage_state(const float*, unsigned char*) {}   // fp32: S is read from memory
 
 template <class E, int DK, int DV>
 __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ dout, const float* __restrict__ ds_final,
@@ -150,10 +174,22 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
     CT* dSR = reinterpret_cast<CT*>(smem + L::OFF_DSR);
     CT* dVT = reinterpret_cast<CT*>(smem + L::OFF_DVT);
     CT* dVR = reinterpret_cast<CT*>(smem + L::OFF_DVR);
+    CT* Ss = reinterpret_cast<CT*>(smem + L::OFF_S);
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int X = w & 3, cg = w >> 2;         // token-row block and column group of this wave
     const size_t bh = blockIdx.x;
+    constexpr int SG = DV / 8;                // 16-byte groups per row of S
+    auto issue_s = [&](int m) { stage_state<DK, DV, L::NW>(states + (bh * NC + m) * DK * DV, smem + L::OFF_S); };
+    // fragment (rows row0 + l%16, columns k0 + 8(l/16) ..) and element reads of the staged S
+    auto s_frag = [&](int row0, int k0) -> typename MF::frag {
+        const int r = row0 + (l & 15), g = k0 / 8 + (l >> 4);
+        return *reinterpret_cast<const typename MF::frag*>(Ss + r * DV + ((g ^ (r & (SG - 1))) << 3));
+    };
+    auto s_elem = [&](int r, int c) -> float {
+        return to_f32(Ss[r * DV + ((((c >> 3) ^ (r & (SG - 1))) << 3) | (c & 7))]);
+    };
+    if constexpr (L::SL) issue_s(NC - 1);
     const int bb = (int)(bh / H), hh = (int)(bh % H);
     const int srow = w * 16 + 4 * (l >> 4);   // first dS row of this lane
 
@@ -234,6 +270,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
 #pragma unroll
             for (int e = 0; e < 4; ++e) dVR[(row + e) * LDV + col] = from_f32<CT>(-accV[ct][e]);
         }
+        if constexpr (L::SL) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's S loads have landed
         __syncthreads();
 
         // dO rows 16X.. (zero past the end) and Vn rows 16X.. as A operands
@@ -260,7 +297,11 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             f32x4 accQ = zero4(), accW = zero4(), accK = zero4();
 #pragma unroll
             for (int kk = 0; kk < DV / KS; ++kk) {
-                const typename MF::frag fs = load_frag<CT>(Sn, DV, cb * 16, kk * KS);
+                typename MF::frag fs;
+                if constexpr (L::SL)
+                    fs = s_frag(cb * 16, kk * KS);
+                else
+                    fs = load_frag<CT>(Sn, DV, cb * 16, kk * KS);
                 accW = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fs, accW);
                 if constexpr (H16) {   // (channel, token) orientation: rows of dO S^T and Vn dS'^T
                     accQ = MF::mma(fs, dof[kk], accQ);
@@ -323,7 +364,12 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int e = 0; e < 4; ++e) {
             float sacc = 0.f;
 #pragma unroll
-            for (int ct = 0; ct < NT; ++ct) sacc += accD[ct][e] * to_f32(Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)]);
+            for (int ct = 0; ct < NT; ++ct) {
+                if constexpr (L::SL)
+                    sacc += accD[ct][e] * s_elem(srow + e, ct * 16 + (l & 15));
+                else
+                    sacc += accD[ct][e] * to_f32(Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)]);
+            }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) sacc += __shfl_xor(sacc, off);
             if ((l & 15) == 0) {
@@ -346,7 +392,10 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                 accD[ct] = MF::mma(aw, load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[ct]);
             }
         }
-        __syncthreads();   // this chunk's reads of dO^T, dS, dVn in LDS are done
+        __syncthreads();   // this chunk's reads of dO^T, dS, dVn and S in LDS are done
+        if constexpr (L::SL) {
+            if (n > 0) issue_s(n - 1);   // lands before the next chunk's products (the barrier after its dVn waits)
+        }
         store_ds();
     }
     if (ds0) {
