@@ -179,6 +179,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int X = w & 3, cg = w >> 2;         // token-row block and column group of this wave
     const size_t bh = blockIdx.x;
+    const int bb = (int)(bh / H), hh = (int)(bh % H);
     constexpr int SG = DV / 8;                // 16-byte groups per row of S
     auto issue_s = [&](int m) { stage_state<DK, DV, L::NW>(states + (bh * NC + m) * DK * DV, smem + L::OFF_S); };
     // fragment (rows row0 + l%16, columns k0 + 8(l/16) ..) and element reads of the staged S
@@ -190,7 +191,22 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         return to_f32(Ss[r * DV + ((((c >> 3) ^ (r & (SG - 1))) << 3) | (c & 7))]);
     };
     if constexpr (L::SL) issue_s(NC - 1);
-    const int bb = (int)(bh / H), hh = (int)(bh % H);
+    // dO rows of chunk m into registers, zero past the end of the sequence
+    constexpr int NU = C * DV / VE / NTH;
+    static_assert(NU * VE * NTH == C * DV, "whole dO rows per thread");
+    // (raw 16-byte vectors: rows past the end are zeroed when staged, so the
+    // loads are not waited for here)
+    u32x4 dov[NU];
+    auto load_do = [&](int m) {
+        const int valid_m = min(C, T - m * C);
+        const E* dob_m = dout + (((size_t)bb * T + (size_t)m * C) * H + hh) * DV;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NTH, r = u % C, j0 = (u / C) * VE;   // consecutive lanes: consecutive tokens
+            dov[i] = *reinterpret_cast<const u32x4*>(dob_m + (size_t)min(r, valid_m - 1) * H * DV + j0);
+        }
+    };
+    load_do(NC - 1);
     const int srow = w * 16 + 4 * (l >> 4);   // first dS row of this lane
 
     f32x4 accD[NT];
@@ -223,20 +239,22 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         const E* dob = dout + (((size_t)bb * T + (size_t)n * C) * H + hh) * DV;   // row r at r * H * DV
         const size_t rs = (size_t)H * DV;
 
-        // dO^T into LDS, zero past the end of the sequence
-        for (int u = tid; u < C * DV / VE; u += NTH) {
-            const int r = u / (DV / VE), j0 = (u % (DV / VE)) * VE;
+        // this wave's M^T and Kc rows (token block X) for dVn, loaded first so
+        // that they arrive while dO^T is staged
+        typename MF::frag mtf[C / KS], kcf[DK / KS];
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk) mtf[kk] = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS);
+#pragma unroll
+        for (int kk = 0; kk < DK / KS; ++kk) kcf[kk] = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS);
+
+        // dO^T into LDS (rows loaded into registers during the previous chunk)
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = tid + i * NTH, r = u % C, j0 = (u / C) * VE;
             CT vals[VE];
-            if (r < valid) {
-                const CT* src = reinterpret_cast<const CT*>(dob + r * rs + j0);
+            __builtin_memcpy(vals, &dov[i], 16);
 #pragma unroll
-                for (int x = 0; x < VE; ++x) vals[x] = src[x];
-            } else {
-#pragma unroll
-                for (int x = 0; x < VE; ++x) vals[x] = from_f32<CT>(0.f);
-            }
-#pragma unroll
-            for (int x = 0; x < VE; ++x) dOT[(j0 + x) * LC + r] = vals[x];
+            for (int x = 0; x < VE; ++x) dOT[(j0 + x) * LC + r] = r < valid ? vals[x] : from_f32<CT>(0.f);
         }
         __syncthreads();
 
@@ -247,17 +265,15 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int ct = 0; ct < NTG; ++ct) accV[ct] = zero4();
 #pragma unroll
         for (int kk = 0; kk < C / KS; ++kk) {
-            const typename MF::frag a = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS);
 #pragma unroll
             for (int ct = 0; ct < NTG; ++ct)
-                accV[ct] = MF::mma(a, load_frag<CT>(dOT, LC, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
+                accV[ct] = MF::mma(mtf[kk], load_frag<CT>(dOT, LC, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
         }
 #pragma unroll
         for (int kk = 0; kk < DK / KS; ++kk) {
-            const typename MF::frag a = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS);
 #pragma unroll
             for (int ct = 0; ct < NTG; ++ct)
-                accV[ct] = MF::mma(a, load_frag<CT>(dST, LDK, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
+                accV[ct] = MF::mma(kcf[kk], load_frag<CT>(dST, LDK, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
         }
 #pragma unroll
         for (int ct = 0; ct < NTG; ++ct) {
@@ -357,6 +373,14 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                 *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
             }
         }
+        // (Q e^G)^T and W^T rows of this wave for the dS update, loaded here
+        // so that they arrive during the row sums
+        typename MF::frag aqf[C / KS], awf[C / KS];
+#pragma unroll
+        for (int kk = 0; kk < C / KS; ++kk) {
+            aqf[kk] = load_frag<CT>(bk + WB::QGT, C, w * 16, kk * KS);
+            awf[kk] = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS);
+        }
         // e^{G_C} rowsum(S dS'), rows of this wave
         const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
         const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + srow);
@@ -384,18 +408,17 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int ct = 0; ct < NT; ++ct) accD[ct] *= eg;
 #pragma unroll
         for (int kk = 0; kk < C / KS; ++kk) {
-            const typename MF::frag aq = load_frag<CT>(bk + WB::QGT, C, w * 16, kk * KS);
-            const typename MF::frag aw = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS);
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                accD[ct] = MF::mma(aq, load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[ct]);
-                accD[ct] = MF::mma(aw, load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[ct]);
+                accD[ct] = MF::mma(aqf[kk], load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[ct]);
+                accD[ct] = MF::mma(awf[kk], load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[ct]);
             }
         }
         __syncthreads();   // this chunk's reads of dO^T, dS, dVn and S in LDS are done
         if constexpr (L::SL) {
             if (n > 0) issue_s(n - 1);   // lands before the next chunk's products (the barrier after its dVn waits)
         }
+        if (n > 0) load_do(n - 1);
         store_ds();
     }
     if (ds0) {
