@@ -931,7 +931,9 @@ template <class E, int DK, int DV>
 static hipError_t launch_bwd_forward_t(const BwdArgs& a, unsigned char* fws, unsigned char* bws, void* states,
                                        void* vn) {
     typedef typename Compute<E>::type CT;
-    constexpr int TVS = sizeof(CT) == 2 ? 32 : 16;
+    // bf16: one workgroup per chain over all value columns, so each chunk's W and
+    // (K e^{G_C-G})^T are read once (8.3 against 9.1 ms for 32-column tiles at 8x8192x32)
+    constexpr int TVS = sizeof(CT) == 2 ? (DV < 128 ? DV : 128) : 16;
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
