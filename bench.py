@@ -22,10 +22,12 @@ Also measured in the same run:
     kda_out_gate) -- the training-shape layer with its projection
     (kda_chunk_layer_fwd, likewise), and the scalar-gate (Gated DeltaNet)
     prefill at the 32k shape;
-  * backward: kda_recurrent_bwd (the recurrence's gradients, token-sequential)
-    on the 8 x 8192 training shape;
-  * ceilings: what this GPU reaches on plain torch kernels -- an in-place
-    fp32 scale (read-modify-write), a device copy and a large bf16 matmul --
+  * backward: kda_chunk_bwd (the recurrence's gradients by 64-token chunks)
+    on the 8 x 8192 training shape, beside kda_recurrent_bwd (token-sequential);
+  * dplr: KDA against the general diagonal-plus-low-rank recurrence at the
+    32k shape, and one decode step of each;
+  * ceilings: what this GPU reaches -- libkda's streaming read-modify-write
+    kernel, an in-place torch scale, a device copy and a large bf16 matmul --
     so that each kernel's rate can be read against them as well as against
     the published peaks.
 
@@ -101,6 +103,7 @@ def parse():
     p.add_argument("--no-long", action="store_true", help="skip the 1M-token shape")
     p.add_argument("--no-ceilings", action="store_true")
     p.add_argument("--no-dplr", action="store_true", help="skip the KDA vs general DPLR comparison")
+    p.add_argument("--no-backward", action="store_true", help="skip the 8x8192 backward")
     p.add_argument("--copy-only", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     p.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -387,7 +390,7 @@ def bench_backward(torch, kda, ki, calls=2):
     return {"workload": "train_8x8k backward", "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "dtype": "bf16",
             "calls": 5, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1), "unit": "tokens/s",
             "kernels": "kda_chunk_bwd (chunk_intra_kernel, chain_kernel storing states, dchain_kernel, "
-                       "dintra_kernel)",
+                       "dintra16_kernel)",
             "workspace_bytes": ws_bytes,
             "token_sequential_us_per_call": round(per_seq * 1e6, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -716,7 +719,7 @@ def main():
         if not args.no_long:
             wl.append(bench_workload(torch, kda, ki, "long_1m", 4, 2))
         line["workloads"] = wl
-    if not args.no_workloads:
+    if not args.no_backward:
         line["backward"] = bench_backward(torch, kda, ki)
     if not args.no_dplr:
         line["dplr"] = bench_dplr(torch, kda, ki)
