@@ -971,27 +971,41 @@ struct DIntraH {
     static constexpr int NTH = 512, NW = 8;
     static constexpr int CP = DK / 2, NPART = NTH / CP, RP = C / NPART;   // gate scan: channel pairs x row parts
     static constexpr int NCTH = DK / 32, NVTH = DV / 32;                  // 16-wide tiles per half
-    static constexpr int DKP = DK + 4, LA = C + 4, LY = C + 8, LT = C + 8;
+    static constexpr int DKP = DK + 4, LY = C + 8, LT = C + 8;
     static constexpr int NCAR = NPART > 4 ? NPART : 4;
     static constexpr size_t OFF_G = 0;                                   // [C][DKP] fp32 G (log2), then dG
     static constexpr size_t OFF_KR = OFF_G + (size_t)C * DKP * 4;        // [DK][LY] bf16 Kr^T
     static constexpr size_t OFF_KC = OFF_KR + (size_t)DK * LY * 2;       // [DK][LY] bf16 Kc^T
     static constexpr size_t OFF_QC = OFF_KC + (size_t)DK * LY * 2;       // [DK][LY] bf16 Qc^T
-    static constexpr size_t OFF_A = OFF_QC + (size_t)DK * LY * 2;        // [C][LA] fp32 Ab, then (beta dA)^T bf16
-    static constexpr size_t OFF_T = OFF_A + (size_t)C * LA * 4;          // [C][LA] fp32 T, then beta dA bf16
-    static constexpr size_t OFF_TT = OFF_T + (size_t)C * LA * 4;         // [C][LT] bf16 T^T
-    static constexpr size_t OFF_X = OFF_TT + (size_t)C * LT * 2;         // [3][16][16] fp32 (solve)
-    static constexpr size_t OFF_GM = OFF_X + 3 * SUB * SUB * 4;          // [5][DK] G_m(0..3), G_C
+    static constexpr size_t OFF_TT = OFF_QC + (size_t)DK * LY * 2;       // [C][C] bf16 T^T (swizzled)
+    static constexpr size_t OFF_AB = OFF_TT + (size_t)C * C * 2;         // [C][C] bf16 Ab (swizzled)
+    static constexpr size_t OFF_DA = OFF_AB + (size_t)C * C * 2;         // [C][LT] bf16 beta dA
+    static constexpr size_t OFF_DAT = OFF_DA + (size_t)C * LT * 2;       // [C][LT] bf16 (beta dA)^T
+    static constexpr size_t OFF_GM = OFF_DAT + (size_t)C * LT * 2;       // [5][DK] G_m(0..3), G_C
     static constexpr size_t OFF_RHO = OFF_GM + 5 * DK * 4;               // [3][DK] e^{G_m(Y+1) - G_m(Y)}
-    static constexpr size_t OFF_XP = OFF_RHO + 3 * DK * 4;               // [6][DK] e^{G_m(R) - G_m(I)}, I < R
-    static constexpr size_t OFF_CAR = OFF_XP + 6 * DK * 4;               // [NCAR][DK]
+    static constexpr size_t OFF_CAR = OFF_RHO + 3 * DK * 4;              // [NCAR][DK]
     static constexpr size_t OFF_BET = OFF_CAR + (size_t)NCAR * DK * 4;   // [C]
     static constexpr size_t OFF_DB = OFF_BET + C * 4;                    // [6][C] dbeta partials
     static constexpr size_t LDS = OFF_DB + 6 * C * 4;
     static_assert(LDS <= 160 * 1024, "per-chunk gradient LDS budget");
-    static_assert((size_t)C * LT * 2 <= (size_t)C * LA * 4, "bf16 64x64 tiles over fp32 ones");
     static_assert(RP % 2 == 0 && 16 % RP == 0 && DK % 32 == 0 && DV % 32 == 0, "tiling");
+    static_assert(2 * C * C * 2 == 2 * 1024 * NW, "T^T and Ab: two 1 KB loads per wave");
 };
+
+// T^T and Ab (64 x 64 bf16 each) into LDS by asynchronous global->LDS loads,
+// two 1 KB wave instructions per wave of an 8-wave workgroup; group g (8
+// elements) of row r lands at position g ^ (r mod 8) of its 128-byte row.
+__device__ __forceinline__ void stage_tt_ab(const bf16* __restrict__ tt, const bf16* __restrict__ ab,
+                                            unsigned char* lds_tt, unsigned char* lds_ab) {
+    const int w = wave_id(), l = lane_id();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int ins = w * 2 + i, mat = ins >> 3, byte = (ins & 7) * 1024 + 16 * l;
+        const int r = byte / (C * 2), g = ((byte % (C * 2)) / 16) ^ (r & 7);
+        __builtin_amdgcn_global_load_lds((mat ? ab : tt) + r * C + g * 8, (mat ? lds_ab : lds_tt) + (ins & 7) * 1024,
+                                         16, 0, 0);
+    }
+}
 
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -1012,13 +1026,14 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
                                                        const bf16* __restrict__ v, const bf16* __restrict__ z,
                                                        const bf16* __restrict__ beta, float g_min, int T, int H,
                                                        int NC, const unsigned char* __restrict__ obuf,
+                                                       const unsigned char* __restrict__ bws,
                                                        float* __restrict__ dq, float* __restrict__ dk,
                                                        float* __restrict__ dvo, float* __restrict__ dz,
                                                        float* __restrict__ dbeta) {
     typedef DIntraH<DK, DV> L;
     typedef ObH<DK, DV> OH;
     typedef Mfma<bf16> MF;
-    constexpr int NTH = L::NTH, RP = L::RP, DKP = L::DKP, LA = L::LA, LY = L::LY, LT = L::LT;
+    constexpr int NTH = L::NTH, RP = L::RP, DKP = L::DKP, LY = L::LY, LT = L::LT;
     constexpr int NCTH = L::NCTH, NVTH = L::NVTH;
     constexpr float LOG2E = 1.4426950408889634f;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1026,15 +1041,12 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
     bf16* KRt = reinterpret_cast<bf16*>(smem + L::OFF_KR);
     bf16* KCt = reinterpret_cast<bf16*>(smem + L::OFF_KC);
     bf16* QCt = reinterpret_cast<bf16*>(smem + L::OFF_QC);
-    float* As = reinterpret_cast<float*>(smem + L::OFF_A);
-    float* Ts = reinterpret_cast<float*>(smem + L::OFF_T);
-    bf16* DAT = reinterpret_cast<bf16*>(smem + L::OFF_A);   // (beta dA)^T, once Ab is dead
-    bf16* DA = reinterpret_cast<bf16*>(smem + L::OFF_T);    // beta dA, once T is dead
-    bf16* TT = reinterpret_cast<bf16*>(smem + L::OFF_TT);
-    float* Xs = reinterpret_cast<float*>(smem + L::OFF_X);
+    const bf16* TT = reinterpret_cast<const bf16*>(smem + L::OFF_TT);
+    const bf16* AB = reinterpret_cast<const bf16*>(smem + L::OFF_AB);
+    bf16* DA = reinterpret_cast<bf16*>(smem + L::OFF_DA);
+    bf16* DAT = reinterpret_cast<bf16*>(smem + L::OFF_DAT);
     float* gm = reinterpret_cast<float*>(smem + L::OFF_GM);
     float* rho = reinterpret_cast<float*>(smem + L::OFF_RHO);
-    float* xp = reinterpret_cast<float*>(smem + L::OFF_XP);
     float* car = reinterpret_cast<float*>(smem + L::OFF_CAR);
     float* bet = reinterpret_cast<float*>(smem + L::OFF_BET);
     float* dbp = reinterpret_cast<float*>(smem + L::OFF_DB);
@@ -1049,6 +1061,40 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
     const int lr = l & 15, lg = l >> 4;
     const int X = w & 3, hf = w >> 2;   // token block and channel half of this wave
     const int rX = X * 16 + lr;         // token (accumulator column) of this lane
+    const bf16* wb = reinterpret_cast<const bf16*>(bws + (((size_t)bb * H + hh) * NC + n) * WsB<bf16, DK, DV>::BYTES);
+
+    // T^T and Ab (written by the forward half's intra-chunk kernel) into LDS
+    // by asynchronous loads: rows of 64 bf16 in 16-byte groups, group g of row
+    // r at position g ^ (r mod 8); they land before the barrier that ends the
+    // operand families
+    stage_tt_ab(wb + WsB<bf16, DK, DV>::TT, wb + WsB<bf16, DK, DV>::AB, smem + L::OFF_TT, smem + L::OFF_AB);
+    // fragment (rows row0 + l%16, token columns k0 + 8(l/16) ..) of T^T, and an element of Ab
+    auto tt_frag = [&](int row0, int k0) -> MF::frag {
+        const int r = row0 + lr, g = k0 / 8 + lg;
+        return *reinterpret_cast<const MF::frag*>(TT + r * C + ((g ^ (r & 7)) << 3));
+    };
+    auto ab_elem = [&](int r, int i) -> float {
+        return to_f32(AB[r * C + ((((i >> 3) ^ (r & 7)) << 3) | (i & 7))]);
+    };
+    // this wave's block pairs (R, I), and the reverse chain's operands of the
+    // dA phase and the decayed products: NP^T of the pairs, dM and dM^T rows
+    // of this lane's token (every block); issued here to be in flight during
+    // the gate scan and the operand families
+    const int R0 = kPairsB[w][0][0], I0 = kPairsB[w][0][1], R1 = kPairsB[w][1][0], I1 = kPairsB[w][1][1];
+    const bool two = R1 >= 0;
+    bf16x8 npf[2][C / 32];
+#pragma unroll
+    for (int kb = 0; kb < C / 32; ++kb) {
+        npf[0][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I0 * 16 + lr) * C + kb * 32 + lg * 8);
+        npf[1][kb] = two ? *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I1 * 16 + lr) * C + kb * 32 + lg * 8)
+                         : bf16x8{};
+    }
+    bf16x4 dmr[4], dmc[4];
+#pragma unroll
+    for (int Y = 0; Y < 4; ++Y) {
+        dmr[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
+        dmc[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
+    }
 
     // the operand families' token loads (two tokens x eight channels per
     // thread) are issued first, to be in flight during the gate scan
@@ -1115,15 +1161,10 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         }
         __syncthreads();
     }
-    // reference ratios e^{G_m(Y+1) - G_m(Y)} and cross-block factors e^{G_m(R) - G_m(I)}
-    for (int idx = tid; idx < 9 * DK; idx += NTH) {
+    // reference ratios e^{G_m(Y+1) - G_m(Y)}
+    for (int idx = tid; idx < 3 * DK; idx += NTH) {
         const int p = idx / DK, cc = idx % DK;
-        if (p < 3) {
-            rho[idx] = dexp2<bf16>(gm[(p + 1) * DK + cc] - gm[p * DK + cc]);
-        } else {
-            const int pp = p - 3, R = pp < 1 ? 1 : (pp < 3 ? 2 : 3), I = pp - R * (R - 1) / 2;
-            xp[pp * DK + cc] = dexp2<bf16>(gm[R * DK + cc] - gm[I * DK + cc]);
-        }
+        rho[idx] = dexp2<bf16>(gm[(p + 1) * DK + cc] - gm[p * DK + cc]);
     }
     // operand families, channel-major
     if (fam) {
@@ -1155,114 +1196,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         }
     }
     const size_t trow = row0 + (size_t)min(rX, last) * H;   // token row of rX, clamped in bounds
-    __syncthreads();
-
-    // block pairs (R, I) of this wave
-    const int R0 = kPairsB[w][0][0], I0 = kPairsB[w][0][1], R1 = kPairsB[w][1][0], I1 = kPairsB[w][1][1];
-    const bool two = R1 >= 0;
-    // ---- Ab = tril_-1(Kg Kt^T) per block pair (R, I): (Kc rows of R) e^{G_m(R) - G_m(I)}
-    //      against (Kr rows of I), bf16 MFMA; the fragments gather eight
-    //      channels of one token from the channel-major families
-#pragma unroll
-    for (int jp = 0; jp < 2; ++jp) {
-        const int R = jp ? R1 : R0, I = jp ? I1 : I0;
-        if (jp && !two) break;
-        const float* cx = xp + (I < R ? pair_index(R, I) : 0) * DK;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            const int c0 = kb * 32 + lg * 8;
-            MF::frag fa, fb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = to_f32(KCt[(c0 + j) * LY + R * 16 + lr]);
-                fa[j] = (bf16)(I < R ? x * cx[c0 + j] : x);
-                fb[j] = KRt[(c0 + j) * LY + I * 16 + lr];
-            }
-            acc = MF::mma(fa, fb, acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
-            As[r * LA + i] = i < r ? acc[e] : 0.f;
-        }
-    }
-    for (int idx = tid; idx < 6 * SUB * SUB; idx += NTH) {
-        int R, I;
-        upper_block(idx / (SUB * SUB), R, I);
-        const int e = idx % (SUB * SUB);
-        As[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
-        Ts[(R * SUB + e / SUB) * LA + I * SUB + e % SUB] = 0.f;
-    }
-    __syncthreads();
-
-    // ---- T = (I + diag(beta) Ab)^{-1}, blocked forward substitution (fp32)
-    if (w == 0) {
-        const int base = lg * SUB, col = lr;
-        float x[SUB];
-#pragma unroll
-        for (int r = 0; r < SUB; ++r) {
-            float acc = (r == col) ? 1.f : 0.f;
-            const float br = bet[base + r];
-#pragma unroll
-            for (int i = 0; i < r; ++i) acc -= br * As[(base + r) * LA + base + i] * x[i];
-            x[r] = acc;
-        }
-#pragma unroll
-        for (int r = 0; r < SUB; ++r) Ts[(base + r) * LA + base + col] = x[r];
-    }
-    __syncthreads();
-    for (int R = 1; R < 4; ++R) {
-        if (w < R) {
-            const int I = w;
-            f32x4 x = zero4();
-            const float br = bet[R * SUB + lr];
-            for (int J = I; J < R; ++J)
-#pragma unroll
-                for (int kk = 0; kk < SUB; kk += 4) {
-                    const float a = br * As[(R * SUB + lr) * LA + J * SUB + kk + lg];
-                    const float b = Ts[(J * SUB + kk + lg) * LA + I * SUB + lr];
-                    x = mma4(a, b, x);
-                }
-            float* xs = Xs + I * SUB * SUB;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) xs[(4 * lg + e) * SUB + lr] = x[e];
-            f32x4 y = zero4();
-#pragma unroll
-            for (int kk = 0; kk < SUB; kk += 4) {
-                const float a = Ts[(R * SUB + lr) * LA + R * SUB + kk + lg];
-                const float b = xs[(kk + lg) * SUB + lr];
-                y = mma4(a, b, y);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) Ts[(R * SUB + 4 * lg + e) * LA + I * SUB + lr] = -y[e];
-        }
-        __syncthreads();
-    }
-    // the later phases' reverse-chain operands, issued here to be in flight
-    // during the transpose of T: NP^T of this wave's pairs, dM and dM^T rows
-    // of its tokens (every block)
-    bf16x8 npf[2][C / 32];
-#pragma unroll
-    for (int kb = 0; kb < C / 32; ++kb) {
-        npf[0][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I0 * 16 + lr) * C + kb * 32 + lg * 8);
-        npf[1][kb] = two ? *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I1 * 16 + lr) * C + kb * 32 + lg * 8)
-                         : bf16x8{};
-    }
-    bf16x4 dmr[4], dmc[4];
-#pragma unroll
-    for (int Y = 0; Y < 4; ++Y) {
-        dmr[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
-        dmc[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
-    }
-    // T^T in bf16, token index contiguous
-    for (int idx = tid; idx < C * (C / 8); idx += NTH) {
-        const int r = idx % C, a8 = (idx / C) * 8;
-        float t[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t[j] = Ts[(a8 + j) * LA + r];
-        store8<bf16>(TT + r * LT + a8, t);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's T^T / Ab loads have landed
     __syncthreads();
 
     // ---- dA = tril_-1(T^T NP) per block pair, in both orientations; the
@@ -1275,7 +1209,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         if (R < 0) continue;
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb) {
-            const MF::frag ft = load_frag<bf16>(TT, LT, R * 16, kb * 32);
+            const MF::frag ft = tt_frag(R * 16, kb * 32);
             d1[jp] = MF::mma(ft, npf[jp][kb], d1[jp]);   // (row r, column i)
             d2[jp] = MF::mma(npf[jp][kb], ft, d2[jp]);   // (row i, column r)
         }
@@ -1283,12 +1217,11 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         for (int e = 0; e < 4; ++e) {
             const int r = R * 16 + 4 * lg + e, i = I * 16 + lr;
             d1[jp][e] = i < r ? d1[jp][e] : 0.f;
-            const float t = sum16(d1[jp][e] * As[r * LA + i]);
+            const float t = sum16(d1[jp][e] * ab_elem(r, i));
             if (lr == 0) dbp[I * C + r] = t;
             d2[jp][e] = (I * 16 + 4 * lg + e < R * 16 + lr) ? d2[jp][e] : 0.f;
         }
     }
-    __syncthreads();   // every read of Ab and T (fp32) is done
 #pragma unroll
     for (int jp = 0; jp < 2; ++jp) {
         const int R = kPairsB[w][jp][0], I = kPairsB[w][jp][1];
@@ -1355,7 +1288,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
         f32x4 accK = zero4();
 #pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) accK = MF::mma(cur.w[kb], load_frag<bf16>(TT, LT, X * 16, kb * 32), accK);
+        for (int kb = 0; kb < C / 32; ++kb) accK = MF::mma(cur.w[kb], tt_frag(X * 16, kb * 32), accK);
         // the token blocks Y accumulate by Horner's scheme, branch-free: the
         // accumulator is scaled by e^{G_m(Y) - G_m(Y-1)} (row side, upward) or
         // e^{G_m(Y+1) - G_m(Y)} (column side, downward) inside the triangle and
@@ -1433,7 +1366,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         const int jb = hf * (DV / 2) + jt * 16, j4 = jb + 4 * lg;
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < C / 32; ++kb) acc = MF::mma(dvf[jt][kb], load_frag<bf16>(TT, LT, X * 16, kb * 32), acc);
+        for (int kb = 0; kb < C / 32; ++kb) acc = MF::mma(dvf[jt][kb], tt_frag(X * 16, kb * 32), acc);
         const f32x4 v4 = okX ? widen4(vr[jt]) : zero4();
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb += acc[e] * v4[e];
@@ -1529,8 +1462,8 @@ hipError_t launch_t(const BwdArgs& a) {
             return err;
         hipLaunchKernelGGL((dintra16_kernel<DK, DV>), dim3(NC, a.H, a.B), dim3(LI::NTH), LI::LDS, st,
                            (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, (const bf16*)a.z,
-                           (const bf16*)a.beta, a.g_min, a.T, a.H, NC, (const unsigned char*)(ws + lo.ob), a.dq,
-                           a.dk, a.dv, a.dz, a.dbeta);
+                           (const bf16*)a.beta, a.g_min, a.T, a.H, NC, (const unsigned char*)(ws + lo.ob),
+                           (const unsigned char*)(ws + lo.bws), a.dq, a.dk, a.dv, a.dz, a.dbeta);
     } else {
         typedef DIntra<E, DK, DV> LI;
         if ((err = hipFuncSetAttribute((const void*)dintra_kernel<E, DK, DV>,

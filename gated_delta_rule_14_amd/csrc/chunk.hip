@@ -124,6 +124,9 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
     CT* gKC = reinterpret_cast<CT*>(bblk) + WB::KC;
     CT* gQGT = reinterpret_cast<CT*>(bblk) + WB::QGT;
     CT* gWT = reinterpret_cast<CT*>(bblk) + WB::WT;
+    CT* gTT = reinterpret_cast<CT*>(bblk) + WB::TT;
+    CT* gAB = reinterpret_cast<CT*>(bblk) + WB::AB;
+    constexpr bool BT = BWD && sizeof(CT) == 2;   // T^T and Ab for the bf16 per-chunk gradients
 
     const int tid = threadIdx.x, l = lane_id(), w = wave_id();
     const int last = valid - 1;
@@ -271,12 +274,14 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
         }
         const int r = R * SUB + (l & 15);
         const int i0 = I * SUB + 4 * (l >> 4);
-        f32x4 mv;
+        f32x4 mv, abv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            av[j][e] = (i0 + e < r) ? bet[r] * accA[e] : 0.f;
+            abv[e] = (i0 + e < r) ? accA[e] : 0.f;
+            av[j][e] = bet[r] * abv[e];
             mv[e] = (i0 + e <= r) ? accM[e] : 0.f;
         }
+        if constexpr (BT) store4<CT>(gAB + r * C + i0, abv);
         if constexpr (!BWD) store4<CT>(gM + r * C + i0, mv);
         if constexpr (BWD) {
 #pragma unroll
@@ -291,6 +296,7 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             const int I = p < 3 ? p + 1 : (p < 5 ? p - 1 : 3);
             if constexpr (!BWD) store4<CT>(gM + (R * SUB + (l & 15)) * C + I * SUB + 4 * (l >> 4), zero4());
             if constexpr (BWD) store4<CT>(gMT + (I * SUB + (l & 15)) * C + R * SUB + 4 * (l >> 4), zero4());
+            if constexpr (BT) store4<CT>(gAB + (R * SUB + (l & 15)) * C + I * SUB + 4 * (l >> 4), zero4());
         }
     }
     __syncthreads();   // KL / QL / KR are dead from here on; As, Ts and R_V^T alias them
@@ -369,6 +375,16 @@ __device__ __forceinline__ void intra_chunk(const E* __restrict__ q, const E* __
             for (int e = 0; e < 4; ++e) Ts[(R * SUB + 4 * (l >> 4) + e) * LT + I * SUB + (l & 15)] = -y[e];
         }
         __syncthreads();
+    }
+
+    if constexpr (BT) {   // T^T, token index contiguous
+        for (int idx = tid; idx < C * (C / 8); idx += 256) {
+            const int r = idx % C, a8 = (idx / C) * 8;
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = Ts[(a8 + j) * LT + r];
+            store8<CT>(gTT + r * C + a8, t);
+        }
     }
 
     // ---- phase 5: W = T R_K (computed as W^T = R_K^T T^T) and U = T R_V;

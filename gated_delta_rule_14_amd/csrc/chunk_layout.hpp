@@ -37,14 +37,18 @@ struct Ws {
 
 // The same chunk's operands as the backward's reverse chunk recurrence
 // contracts them (kda_chunk_bwd): M^T, K e^{G_C - G} row-major, (Q e^G)^T and
-// W^T.  Written by the intra-chunk kernel only when it runs for the backward.
+// W^T; with bf16 tokens also T^T (T = (I + diag(beta) Ab)^{-1}) and Ab =
+// tril_-1(Kg Kt^T) for the per-chunk gradients.  Written by the intra-chunk
+// kernel only when it runs for the backward.
 template <class CT, int DK, int DV>
 struct WsB {
     static constexpr size_t MT = 0;                     // (C, C)   M^T
     static constexpr size_t KC = MT + (size_t)C * C;    // (C, DK)  k * e^{G_C - G}
     static constexpr size_t QGT = KC + (size_t)C * DK;  // (DK, C)  (q * e^G)^T
     static constexpr size_t WT = QGT + (size_t)DK * C;  // (DK, C)  W^T
-    static constexpr size_t END = WT + (size_t)DK * C;
+    static constexpr size_t TT = WT + (size_t)DK * C;   // (C, C)   T^T      (bf16 tokens)
+    static constexpr size_t AB = TT + (size_t)C * C;    // (C, C)   Ab       (bf16 tokens)
+    static constexpr size_t END = AB + (size_t)C * C;
     static constexpr size_t BYTES = END * sizeof(CT);
 };
 
