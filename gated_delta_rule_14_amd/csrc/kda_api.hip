@@ -214,10 +214,17 @@ kda_status kda_gdn_chunk_fwd(const void* q, const void* k, const void* v, const 
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     const size_t esz = dt == KDA_BF16 ? 2 : 4;
     const size_t zbytes = (size_t)B * T * H * dk * esz;
+    const size_t base = need - zbytes;
+    if (kda::chunk_scalar_gate_native(T, dk, dv, dt == KDA_BF16, g_min)) {
+        // the pipelined kernels read the logit per (token, head) directly
+        kda::ChunkArgs a{q, k, v, z, beta, g_min, s0, o, s_final, B, T, H, dk, dv, true,
+                         base ? workspace : nullptr, stream};
+        a.scalar_z = true;
+        return finish(kda::launch_chunk(a), stream);
+    }
     void* zfull = zbytes ? (unsigned char*)workspace + (need - zbytes) : nullptr;
     hipError_t err = kda::launch_broadcast_gate(z, zfull, (size_t)B * T * H, dk, dt == KDA_BF16, stream);
     if (err != hipSuccess) return finish(err, stream);
-    const size_t base = need - zbytes;
     kda::ChunkArgs a{q, k, v, zfull, beta, g_min, s0, o, s_final, B, T, H, dk, dv, dt == KDA_BF16,
                      base ? workspace : nullptr, stream};
     return finish(kda::launch_chunk(a), stream);

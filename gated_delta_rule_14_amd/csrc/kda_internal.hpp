@@ -67,12 +67,19 @@ struct ChunkArgs {
     const void* gate = nullptr;
     float eps = 0.f;
     void* y = nullptr;
+    // z holds one logit per (token, head), shape (B, T, H): the scalar gate,
+    // read directly by the pipelined kernels (only where
+    // chunk_scalar_gate_native())
+    bool scalar_z = false;
 };
 size_t chunk_workspace_bytes(int B, int T, int H, int dk, int dv, bool bf16);
 // whether the prefill kernels for these sizes run the output epilogue in
 // their own launches (bf16 tokens, d_k = d_v = 128, the pipelined kernels on
 // a segmented plan, whose light expand has LDS to stage the outputs)
 bool chunk_gate_fused(int B, int T, int H, int dk, int dv, bool bf16);
+// whether the prefill kernels for these sizes read a scalar gate directly
+// (bf16 tokens, d_k = d_v = 128, the pipelined kernels, chunkwise g_min)
+bool chunk_scalar_gate_native(int T, int dk, int dv, bool bf16, float g_min);
 hipError_t launch_chunk(const ChunkArgs& a);
 // token-sequential prefill (any g_min; with gate != NULL also the epilogue,
 // y in the token dtype)

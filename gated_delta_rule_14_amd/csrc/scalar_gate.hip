@@ -5,7 +5,9 @@
 // channel-wise one; "Diagonal-Plus-Low-Rank Matrices and Kimi Delta
 // Attention": a uniform alpha is the scalar-decay case).
 //
-// The prefill runs through the same kernels as the channel-wise operator:
+// The prefill runs through the same kernels as the channel-wise operator.
+// The pipelined bf16 kernels (d_k = d_v = 128) read the scalar logit directly
+// and form each row's decay factors once (seg.hip, SG); elsewhere
 // broadcast_gate_kernel writes each scalar logit across the d_k channels of
 // a workspace buffer, which then serves as z.  Decode reads the scalar
 // directly (decode.hip).

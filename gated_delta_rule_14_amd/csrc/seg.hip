@@ -1047,11 +1047,19 @@ struct PV {
     bf16x2 v[SUB];
 };
 
-template <bool HASQ>
+// The scalar gate (SG, one logit per token and head, z of shape (B, T, H)):
+// lane l holds the logit of row 16R + l%16 (in both halves of z[0]).
+__device__ __forceinline__ bf16x2 pfetch_zs(const bf16* __restrict__ z, size_t row0, int valid, int H, int R) {
+    const bf16 x = z[row0 + (size_t)min(SUB * R + (lane_id() & 15), valid - 1) * H];
+    return bf16x2{x, x};
+}
+
+template <bool HASQ, bool SG = false>
 __device__ __forceinline__ void pfetch_zkq(PIn<HASQ>& r, const bf16* __restrict__ q, const bf16* __restrict__ k,
                                            const bf16* __restrict__ z, const bf16* __restrict__ beta, size_t row0,
                                            int valid, int H, int R) {
     const int l = lane_id(), last = valid - 1;
+    if constexpr (SG) r.z[0] = pfetch_zs(z, row0, valid, H, R);
     // wave-uniform chunk bases and 32-bit byte offsets (row, clamped to the
     // last token, then the lane's two channels): scalar-base addressing
     const char* zb = reinterpret_cast<const char*>(z + row0 * 128);
@@ -1061,7 +1069,7 @@ __device__ __forceinline__ void pfetch_zkq(PIn<HASQ>& r, const bf16* __restrict_
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
         const unsigned off = (unsigned)min(SUB * R + i, last) * rstride + lo;
-        r.z[i] = *reinterpret_cast<const bf16x2*>(zb + off);
+        if constexpr (!SG) r.z[i] = *reinterpret_cast<const bf16x2*>(zb + off);
         r.k[i] = *reinterpret_cast<const bf16x2*>(kb + off);
         if constexpr (HASQ) r.q[i] = *reinterpret_cast<const bf16x2*>(qb + off);
     }
@@ -1069,9 +1077,13 @@ __device__ __forceinline__ void pfetch_zkq(PIn<HASQ>& r, const bf16* __restrict_
 }
 
 // The same loads in two parts: z alone, then k, q and beta.
-template <bool HASQ>
+template <bool HASQ, bool SG = false>
 __device__ __forceinline__ void pfetch_z(PIn<HASQ>& r, const bf16* __restrict__ z, size_t row0, int valid, int H,
                                          int R) {
+    if constexpr (SG) {
+        r.z[0] = pfetch_zs(z, row0, valid, H, R);
+        return;
+    }
     const int last = valid - 1;
     const char* zb = reinterpret_cast<const char*>(z + row0 * 128);
     const unsigned lo = 4u * (unsigned)lane_id(), rstride = (unsigned)H * 256u;
@@ -1099,12 +1111,17 @@ __device__ __forceinline__ void pfetch_kq(PIn<HASQ>& r, const bf16* __restrict__
 // Rows at or past `valid` of a ragged last chunk become identity tokens:
 // z = -inf (a zero gate, alpha = 1) and k = q = 0 (no write, no read); beta
 // is set to 0 where it is stored.
-template <bool HASQ>
+template <bool HASQ, bool SG = false>
 __device__ __forceinline__ void pmask(PIn<HASQ>& r, int valid, int R) {
+    if constexpr (SG) {   // the lane's own row
+        const unsigned keep = SUB * R + (lane_id() & 15) < valid ? 0xffffffffu : 0u;
+        r.z[0] = __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, r.z[0]) & keep) | (0xff80ff80u & ~keep));
+    }
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
         const unsigned keep = SUB * R + i < valid ? 0xffffffffu : 0u;
-        r.z[i] = __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, r.z[i]) & keep) | (0xff80ff80u & ~keep));
+        if constexpr (!SG)
+            r.z[i] = __builtin_bit_cast(bf16x2, (__builtin_bit_cast(unsigned, r.z[i]) & keep) | (0xff80ff80u & ~keep));
         r.k[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.k[i]) & keep);
         if constexpr (HASQ) r.q[i] = __builtin_bit_cast(bf16x2, __builtin_bit_cast(unsigned, r.q[i]) & keep);
     }
@@ -1121,8 +1138,30 @@ __device__ __forceinline__ void pfetch_v(PV& r, const bf16* __restrict__ v, size
 
 // S[i] = running sum of sigmoid(z) over the block's rows (registers only);
 // the log2 decay is G = kg2 S.
-template <bool HASQ>
-__device__ __forceinline__ void gate_sums(const PIn<HASQ>& in, float (&S)[SUB][2]) {
+// With the scalar gate the block's 16 rows are spread over the lanes of each
+// DPP row (lane l: row l%16): sigmoid once per lane, then the running sum
+// passed down the lanes one at a time, so that every partial sum is formed
+// in the same order, with the same roundings, as the per-channel loop below;
+// `own` keeps the lane's own row's sum, S[i] every row's (wave-uniform).
+template <bool HASQ, bool SG = false>
+__device__ __forceinline__ void gate_sums(const PIn<HASQ>& in, float (&S)[SUB][2], float& own) {
+    if constexpr (SG) {
+        const int lr = lane_id() & 15;
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-LOG2E * (float)in.z[0][0]));
+        float x = 0.f + sg;
+#pragma unroll
+        for (int t = 1; t < SUB; ++t) {   // row_shr:1 -- lane t takes lane t-1's finished sum
+            const float prev =
+                __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, false));
+            x = lr == t ? prev + sg : x;
+        }
+        own = x;
+#pragma unroll
+        for (int i = 0; i < SUB; ++i)
+            S[i][0] = S[i][1] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), i));
+        return;
+    }
+    (void)own;
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
@@ -1136,10 +1175,11 @@ __device__ __forceinline__ void gate_sums(const PIn<HASQ>& in, float (&S)[SUB][2
 // The rest of S1: block sums and references, beta, the block-local factors
 // e^{+-(G_r - G_m(R))} and the operands k e^{G-G_m} (not needed without the
 // solve), k e^{G_m-G}, q e^{G-G_m}.
-template <int MODE>
+template <int MODE, bool SG = false>
 __device__ __forceinline__ void gate_rest(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
-                                          unsigned char* smem, const float (&S)[SUB][2], float (&kl)[SUB][2],
-                                          float (&kr)[SUB][2], float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
+                                          unsigned char* smem, const float (&S)[SUB][2], float own,
+                                          float (&kl)[SUB][2], float (&kr)[SUB][2],
+                                          float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
     typedef PLay<MODE> L;
     constexpr bool EXP = L::EXP;
     constexpr int LDK = L::LDK;
@@ -1154,13 +1194,34 @@ __device__ __forceinline__ void gate_rest(const PIn<MODE != COMPOSE>& in, int R,
     *reinterpret_cast<float2*>(tot + R * 128 + c0) = float2{kg2 * S[SUB - 1][0], kg2 * S[SUB - 1][1]};
     *reinterpret_cast<float2*>(mloc + R * 128 + c0) = float2{m0, m1};
     if ((l >> 4) == R) bet[l] = l < valid ? (float)in.beta : 0.f;
+    // scalar gate: each lane forms its own row's factors, which every lane
+    // then reads (wave-uniform)
+    float lf = 0.f, rf = 0.f;
+    if constexpr (SG) {
+        const float el = __builtin_fmaf(kg2, own, -m0);
+        lf = __builtin_amdgcn_exp2f(el);
+        rf = __builtin_amdgcn_exp2f(-el);
+    }
+    (void)own;
 #pragma unroll
     for (int i = 0; i < SUB; ++i) {
         const int r = SUB * R + i;
+        float lsg = 0.f, rsg = 0.f;
+        if constexpr (SG) {
+            lsg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lf), i));
+            rsg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rf), i));
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const float el = __builtin_fmaf(kg2, S[i][j], -(j ? m1 : m0));   // G_r - G_m(R)
-            const float left = __builtin_amdgcn_exp2f(el), right = __builtin_amdgcn_exp2f(-el);
+            float left, right;
+            if constexpr (SG) {
+                left = lsg;
+                right = rsg;
+            } else {
+                const float el = __builtin_fmaf(kg2, S[i][j], -(j ? m1 : m0));   // G_r - G_m(R)
+                left = __builtin_amdgcn_exp2f(el);
+                right = __builtin_amdgcn_exp2f(-el);
+            }
             const float kv = (float)in.k[i][j];
             kl[i][j] = kv * left;
             kr[i][j] = kv * right;
@@ -1174,13 +1235,13 @@ __device__ __forceinline__ void gate_rest(const PIn<MODE != COMPOSE>& in, int R,
 
 // S1 of gate wave R (rows past the end have been made identity tokens).  On
 // return kl, kr, ql hold the block's decay-scaled k and q (fp32).
-template <int MODE>
+template <int MODE, bool SG = false>
 __device__ __forceinline__ void pipe_gate(const PIn<MODE != COMPOSE>& in, int R, int valid, float kg2,
                                           unsigned char* smem, float (&kl)[SUB][2], float (&kr)[SUB][2],
                                           float (&ql)[MODE != COMPOSE ? SUB : 1][2]) {
-    float S[SUB][2];
-    gate_sums<MODE != COMPOSE>(in, S);
-    gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
+    float S[SUB][2], own;
+    gate_sums<MODE != COMPOSE, SG>(in, S, own);
+    gate_rest<MODE, SG>(in, R, valid, kg2, smem, S, own, kl, kr, ql);
 }
 
 // S2 of gate wave R: A_RR (and M_RR) from the block's own rows of KL, KR,
@@ -1441,7 +1502,8 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
 // laid out like o; o is written only when not NULL.  Chunk m's outputs are
 // staged in LDS in S1 and its epilogue runs in S2, on the state waves (rows
 // 0-15 on waves 0-1, whose M pairs are the longer, rows 16-63 on waves 2-3).
-template <int MODE, bool GATED = false>
+// SG: the scalar gate (z holds one logit per token and head, shape (B, T, H)).
+template <int MODE, bool GATED = false, bool SG = false>
 __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                    const bf16* __restrict__ v, const bf16* __restrict__ z,
                                                    const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
@@ -1633,13 +1695,13 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         const float kg2 = g_min * LOG2E;
         PIn<true> in;
         PV pv;
-        float S[SUB][2];
+        float S[SUB][2], own;
         {
             const int valid = min(C, T - n0 * C);
-            pfetch_zkq<true>(in, q, k, z, beta, row_of(n0), valid, H, R);
+            pfetch_zkq<true, SG>(in, q, k, z, beta, row_of(n0), valid, H, R);
             if constexpr (LITE) pfetch_v(pv, v, row_of(n0), valid, H, R);
-            if (valid < C) pmask<true>(in, valid, R);
-            gate_sums<true>(in, S);
+            if (valid < C) pmask<true, SG>(in, valid, R);
+            gate_sums<true, SG>(in, S, own);
         }
         float kl[SUB][2], kr[SUB][2], ql[SUB][2];
         for (int i = 0; i < nL; ++i) {
@@ -1647,8 +1709,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             const int valid = min(C, T - m * C);
             const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
             const int valid_n = min(C, T - mn * C);
-            pfetch_z<true>(in, z, row_of(mn), valid_n, H, R);   // this chunk's z is consumed
-            gate_rest<MODE>(in, R, valid, kg2, smem, S, kl, kr, ql);
+            pfetch_z<true, SG>(in, z, row_of(mn), valid_n, H, R);   // this chunk's z is consumed
+            gate_rest<MODE, SG>(in, R, valid, kg2, smem, S, own, kl, kr, ql);
             pfetch_kq<true>(in, q, k, beta, row_of(mn), valid_n, H, R);
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
@@ -1661,8 +1723,8 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             } else {
                 __syncthreads();   // S2 | S3
             }
-            if (valid_n < C) pmask<true>(in, valid_n, R);
-            gate_sums<true>(in, S);
+            if (valid_n < C) pmask<true, SG>(in, valid_n, R);
+            gate_sums<true, SG>(in, S, own);
             __syncthreads();   // S2 (S3 for EXPAND) | next S1
         }
         if constexpr (GATED) __syncthreads();   // the state waves' last epilogue
@@ -1674,7 +1736,7 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
         PV pv;
         {
             const int valid = min(C, T - n0 * C);
-            pfetch_zkq<false>(in, q, k, z, beta, row_of(n0), valid, H, R);
+            pfetch_zkq<false, SG>(in, q, k, z, beta, row_of(n0), valid, H, R);
             pfetch_v(pv, v, row_of(n0), valid, H, R);
         }
         float kl[SUB][2], kr[SUB][2], ql[1][2];
@@ -1683,9 +1745,9 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
             const int valid = min(C, T - m * C);
             const int mn = min(m + 1, n1 - 1);   // prefetch target, clamped (unconditional)
             const int valid_n = min(C, T - mn * C);
-            if (valid < C) pmask<false>(in, valid, R);
-            pipe_gate<MODE>(in, R, valid, kg2, smem, kl, kr, ql);
-            pfetch_zkq<false>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
+            if (valid < C) pmask<false, SG>(in, valid, R);
+            pipe_gate<MODE, SG>(in, R, valid, kg2, smem, kl, kr, ql);
+            pfetch_zkq<false, SG>(in, q, k, z, beta, row_of(mn), valid_n, H, R);
             __syncthreads();   // S1 | S2
             f32x4 accA, accM;
             pipe_abs<MODE>(R, smem, kl, kr, ql, m & 1);
@@ -1889,7 +1951,7 @@ static hipError_t launch_scan(const ChunkArgs& a, const Plan& p, float* Pb, floa
 
 // d_k = d_v = 128: compose (writing every chunk's T'), scan, and the light
 // expand; one full expand pass when one segment per chain suffices.
-template <bool GATED>
+template <bool GATED, bool SG>
 static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
@@ -1901,8 +1963,8 @@ static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     if (p.nseg == 1) {
         // the epilogue is fused into the light expand only (segmented plans)
         if (GATED) return hipErrorInvalidValue;
-        if ((err = set_lds(pipe_kernel<EXPAND>, PLay<EXPAND>::LDS)) != hipSuccess) return err;
-        hipLaunchKernelGGL((pipe_kernel<EXPAND>), dim3(nchain), dim3(NTH), PLay<EXPAND>::LDS, st, q, k, v, z, beta,
+        if ((err = set_lds(pipe_kernel<EXPAND, false, SG>, PLay<EXPAND>::LDS)) != hipSuccess) return err;
+        hipLaunchKernelGGL((pipe_kernel<EXPAND, false, SG>), dim3(nchain), dim3(NTH), PLay<EXPAND>::LDS, st, q, k, v, z, beta,
                            a.g_min, a.T, a.H, NC, NC, nchain, a.s0, a.s_final, (float*)nullptr, (bf16*)a.o,
                            (bf16*)nullptr, (const bf16*)nullptr, 0.f, (bf16*)nullptr);
         return hipGetLastError();
@@ -1912,20 +1974,21 @@ static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     float* Rb = reinterpret_cast<float*>(ws + p.r_off);
     float* Eb = reinterpret_cast<float*>(ws + p.e_off);
     bf16* TM = reinterpret_cast<bf16*>(ws + p.tm_off);
-    if ((err = set_lds(pipe_kernel<COMPOSE>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
-    hipLaunchKernelGGL(pipe_kernel<COMPOSE>, dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
+    if ((err = set_lds(pipe_kernel<COMPOSE, false, SG>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((pipe_kernel<COMPOSE, false, SG>), dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
                        beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr, TM,
                        (const bf16*)nullptr, 0.f, (bf16*)nullptr);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if ((err = launch_scan<128, 128>(a, p, Pb, Rb, Eb)) != hipSuccess) return err;
-    if ((err = set_lds(pipe_kernel<EXPAND_LITE, GATED>, PLay<EXPAND_LITE>::LDS)) != hipSuccess) return err;
-    hipLaunchKernelGGL((pipe_kernel<EXPAND_LITE, GATED>), dim3(p.nseg * nchain), dim3(NTH), PLay<EXPAND_LITE>::LDS,
+    if ((err = set_lds(pipe_kernel<EXPAND_LITE, GATED, SG>, PLay<EXPAND_LITE>::LDS)) != hipSuccess) return err;
+    hipLaunchKernelGGL((pipe_kernel<EXPAND_LITE, GATED, SG>), dim3(p.nseg * nchain), dim3(NTH), PLay<EXPAND_LITE>::LDS,
                        st, q, k, v, z, beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)Eb, (float*)nullptr,
                        (float*)nullptr, (bf16*)a.o, TM, gate, a.eps, y);
     return hipGetLastError();
 }
 static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
-    return a.gate ? launch_pipe_t<true>(a, p) : launch_pipe_t<false>(a, p);
+    if (a.scalar_z) return a.gate ? hipErrorInvalidValue : launch_pipe_t<false, true>(a, p);
+    return a.gate ? launch_pipe_t<true, false>(a, p) : launch_pipe_t<false, false>(a, p);
 }
 
 template <int DK, int DV>
@@ -1933,6 +1996,7 @@ static hipError_t launch_t(const ChunkArgs& a) {
     const Plan p = plan(a.B, a.T, a.H, DK, DV);
     if constexpr (DK == 128 && DV == 128)
         if (use_pipe()) return launch_pipe(a, p);
+    if (a.scalar_z) return hipErrorInvalidValue;   // only the pipelined kernels read a scalar gate
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
     hipStream_t st = (hipStream_t)a.stream;
@@ -1965,6 +2029,10 @@ static hipError_t launch_t(const ChunkArgs& a) {
 }  // namespace segk
 
 size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) { return segk::plan(B, T, H, dk, dv).total; }
+
+bool chunk_scalar_gate_native(int T, int dk, int dv, bool bf16, float g_min) {
+    return bf16 && dk == 128 && dv == 128 && T > 0 && g_min >= CHUNK_G_MIN_LIMIT && segk::use_pipe();
+}
 
 bool chunk_gate_fused(int B, int T, int H, int dk, int dv, bool bf16) {
     return bf16 && dk == 128 && dv == 128 && segk::use_pipe() && segk::plan(B, T, H, dk, dv).nseg > 1;

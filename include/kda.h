@@ -275,12 +275,15 @@ kda_status kda_chunk_layer_fwd(const void* q, const void* k, const void* v, cons
  *   z   (B, T, H) for kda_gdn_chunk_fwd, (B, H) for kda_gdn_recurrent_step,
  *       dtype dt
  *
- * The prefill runs on the channel-wise kernels: the logits are first
- * written across the d_k channels of the workspace, whose size
- * kda_gdn_chunk_fwd_workspace_bytes() returns (that of kda_chunk_fwd,
- * rounded up to 256 bytes, plus B*T*H*dk elements).  Decode reads the
- * scalar directly and needs no workspace.  The results equal those of the
- * channel-wise calls given z repeated over the channels, bit for bit.
+ * The prefill runs on the channel-wise kernels.  With bf16 tokens, d_k =
+ * d_v = 128 and g_min >= KDA_CHUNK_G_MIN_LIMIT they read the logit of each
+ * (token, head) directly and form its decay factors once per token instead
+ * of once per channel; otherwise the logits are first written across the
+ * d_k channels of the workspace.  The workspace size
+ * kda_gdn_chunk_fwd_workspace_bytes() returns covers both (that of
+ * kda_chunk_fwd, rounded up to 256 bytes, plus B*T*H*dk elements).  Decode
+ * reads the scalar directly and needs no workspace.  The results equal those
+ * of the channel-wise calls given z repeated over the channels, bit for bit.
  */
 size_t kda_gdn_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
                                          kda_dtype dt);
