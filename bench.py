@@ -399,9 +399,9 @@ def bench_backward(torch, kda, ki, calls=2):
 
 def bench_gdn_prefill(torch, kda, ki, calls=10):
     """The scalar-gate (Gated DeltaNet) prefill at the 32k shape: z is one
-    logit per (token, head), broadcast over the channels into the workspace,
-    then the channel-wise kernels.  Algorithmic bytes count z at 2 B per
-    token-head."""
+    logit per (token, head), which the pipelined prefill kernels read
+    directly (decay factors once per token).  Algorithmic bytes count z at
+    2 B per token-head."""
     cfg = ki.WORKLOADS["prefill_32k"]
     B, T, H, dk, dv = cfg["B"], cfg["T"], cfg["H"], cfg["dk"], cfg["dv"]
     dev = torch.device("cuda:0")
@@ -420,7 +420,7 @@ def bench_gdn_prefill(torch, kda, ki, calls=10):
     torch.cuda.empty_cache()
     return {"workload": "prefill_32k scalar gate (Gated DeltaNet)", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
             "dtype": "bf16", "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1),
-            "unit": "tokens/s", "kernels": "kda_gdn_chunk_fwd (broadcast_gate_kernel + the kda_chunk_fwd kernels)",
+            "unit": "tokens/s", "kernels": "kda_gdn_chunk_fwd (pipe_kernel compose + scan_x3_kernel + pipe_kernel expand, scalar logit)",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
 
@@ -568,7 +568,8 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
                                              if "pipe_kernel" in k or "seg_kernel" in k or "scan_x3" in k
                                              or "seg_scan" in k or "chunk_intra" in k or "chain_kernel" in k),
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --no-cpu --steps 2 "
-                      "--warmup 1 --decode-steps 8 --no-epilogue --no-workloads --no-ceilings; same with --copy-only for the "
+                      "--warmup 1 --decode-steps 8 --no-epilogue --no-workloads --no-ceilings --no-dplr --no-backward; same with "
+                      "--copy-only for the "
                       "scale factors"}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     json.dump(out, open(TRAFFIC_FILE, "w"), indent=1)

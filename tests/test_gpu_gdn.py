@@ -93,3 +93,14 @@ def test_gdn_decode_steps(dk, dv, dtype, tag):
     print(f"gdn decode {tag} dk={dk} dv={dv}: o {eo:.2e} state {es:.2e}")
     to, ts = TOL[tag]
     assert eo < to and es < ts
+
+
+def test_gdn_prefill_one_pass_equals_channelwise_call():
+    """256 chains (the one-pass plan: every chain in one workgroup, no
+    segments) with a ragged last chunk: the scalar-gate call gives the
+    channel-wise call's bits, and sampled heads match the oracle."""
+    x = scalar_gate_inputs(8, 300, 32, 128, 128, torch.bfloat16, 41)
+    o1, s1 = check_prefill(x, "bf16", heads=[0, 17, 31], label="one pass, 8 x 300 x 32")
+    o2, s2 = kda.chunk_fwd(x["q"], x["k"], x["v"], x["z"], x["beta"], ki.G_MIN, x["s0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
