@@ -420,7 +420,7 @@ def bench_gdn_prefill(torch, kda, ki, calls=10):
     torch.cuda.empty_cache()
     return {"workload": "prefill_32k scalar gate (Gated DeltaNet)", "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
             "dtype": "bf16", "calls": calls, "us_per_call": round(per * 1e6, 1), "value": round(B * T / per, 1),
-            "unit": "tokens/s", "kernels": "kda_gdn_chunk_fwd (pipe_kernel compose + scan_x3_kernel + pipe_kernel expand, scalar logit)",
+            "unit": "tokens/s", "kernels": "kda_gdn_chunk_fwd (pipe_first_kernel + scan_x3_kernel + pipe_last_kernel, scalar logit)",
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "algorithmic_bytes": nbytes}}
 
@@ -484,7 +484,7 @@ def bench_dplr(torch, kda, ki, calls=5):
         "dplr_chunk_mfma_frac": round(tokens * H * DPLR_FLOP_PER_TOKEN_HEAD / chunk_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         "dplr_chunk_workspace_bytes": ws_bytes,
         "decode_step_us": {"kda": round(kda_step * 1e6, 1), "dplr": round(dplr_step * 1e6, 1)},
-        "kernels": "kda_chunk_fwd (pipe_kernel x2 + scan); kda_dplr_chunk_fwd (dplr_intra_kernel, "
+        "kernels": "kda_chunk_fwd (pipe_first_kernel, scan_x3_kernel, pipe_last_kernel); kda_dplr_chunk_fwd (dplr_intra_kernel, "
                    "dplr_chain_kernel x3, seg_scan_kernel); kda_dplr_fwd (dplr_seq_kernel); "
                    "decode_step_kernel vs dplr_step_kernel",
     }
@@ -565,7 +565,7 @@ def pmc_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
     out = {"source_hash": kernel_source_hash(), "copy_fetch_scale": round(sf, 4), "copy_write_scale": round(sw, 4),
            "copy_kernel": copy_k, "kernels": kernels,
            "prefill_hbm_bytes_per_call": sum(v["hbm_bytes"] for k, v in kernels.items()
-                                             if "pipe_kernel" in k or "seg_kernel" in k or "scan_x3" in k
+                                             if "pipe_" in k or "seg_kernel" in k or "scan_x3" in k
                                              or "seg_scan" in k or "chunk_intra" in k or "chain_kernel" in k),
            "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -f csv -- python bench.py --no-cpu --steps 2 "
                       "--warmup 1 --decode-steps 8 --no-epilogue --no-workloads --no-ceilings --no-dplr --no-backward; same with "
@@ -705,7 +705,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill"),
                      "algorithmic_bytes": r["bytes"],
-                     "kernel": "kda_chunk_fwd: pipe_kernel (compose) + scan_x3_kernel + pipe_kernel (expand)",
+                     "kernel": "kda_chunk_fwd: pipe_first_kernel (segment 0 expand + compose) + scan_x3_kernel + pipe_last_kernel (light expands + last segment expand)",
                      "mfma_frac": round(r["flop"] / r["mean"] / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_decode:

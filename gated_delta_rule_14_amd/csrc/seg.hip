@@ -17,6 +17,12 @@
 //            from S_start = 0.  A scan over segments then gives every
 //            segment's entry state, and EXPAND runs all segments in parallel.
 //
+// The first segment of a chain starts from s0 and the last one's transition
+// only matters for the final state, so the split plan (pipe_first_kernel,
+// pipe_last_kernel) expands those two directly, each beside the compose or
+// the light expand of the middle segments: a fifth of the chunks at the 32k
+// prefill shape then run once instead of twice.
+//
 // State in registers.  Each chain wave owns 16-column tiles of the state.  A
 // 16x16x32 bf16 MFMA reads operand B as (column l%16, contraction indices
 // 8(l/16)..+7) and leaves its result as (column l%16, rows 4(l/16)+e).  Two
@@ -1503,14 +1509,15 @@ __device__ __forceinline__ void pipe_tsolve(int wT, unsigned char* smem) {
 // staged in LDS in S1 and its epilogue runs in S2, on the state waves (rows
 // 0-15 on waves 0-1, whose M pairs are the longer, rows 16-63 on waves 2-3).
 // SG: the scalar gate (z holds one logit per token and head, shape (B, T, H)).
+// The body of one workgroup: segment `seg` of chain `bh`.
 template <int MODE, bool GATED = false, bool SG = false>
-__global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                   const bf16* __restrict__ v, const bf16* __restrict__ z,
-                                                   const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
-                                                   int L, int nchain, const float* __restrict__ xin,
-                                                   float* __restrict__ xo0, float* __restrict__ xo1,
-                                                   bf16* __restrict__ o, bf16* __restrict__ tm,
-                                                   const bf16* __restrict__ gate, float eps, bf16* __restrict__ y) {
+__device__ __forceinline__ void pipe_run(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                         const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                         const bf16* __restrict__ beta, float g_min, int T, int H, int NC, int L,
+                                         int nchain, const float* __restrict__ xin, float* __restrict__ xo0,
+                                         float* __restrict__ xo1, bf16* __restrict__ o, bf16* __restrict__ tm,
+                                         const bf16* __restrict__ gate, float eps, bf16* __restrict__ y, const int seg,
+                                         const size_t bh) {
     static_assert(!GATED || MODE == EXPAND_LITE, "the epilogue is fused into the light expand only");
     typedef PLay<MODE> LY;
     constexpr int DK = 128, DV = 128;
@@ -1518,8 +1525,6 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
     // v^T is written by the state waves in EXPAND, by the gate waves otherwise
     constexpr bool VSTATE = MODE == EXPAND;
     extern __shared__ __align__(16) unsigned char smem[];
-    const int seg = blockIdx.x / nchain;
-    const size_t bh = blockIdx.x % nchain;
     const int b = (int)(bh / H), h = (int)(bh % H);
     const int l = lane_id(), w = wave_id();
     __builtin_assume(w >= 0 && w < NTH / 64);
@@ -1764,6 +1769,62 @@ __global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, c
     }
 }
 
+template <int MODE, bool GATED = false, bool SG = false>
+__global__ __launch_bounds__(NTH) void pipe_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                   const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                   const bf16* __restrict__ beta, float g_min, int T, int H, int NC,
+                                                   int L, int nchain, const float* __restrict__ xin,
+                                                   float* __restrict__ xo0, float* __restrict__ xo1,
+                                                   bf16* __restrict__ o, bf16* __restrict__ tm,
+                                                   const bf16* __restrict__ gate, float eps, bf16* __restrict__ y) {
+    pipe_run<MODE, GATED, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, xin, xo0, xo1, o, tm, gate, eps, y,
+                              (int)(blockIdx.x / nchain), blockIdx.x % nchain);
+}
+
+// The split plan.  Segment 0 starts from s0, so it needs no transition: the
+// first pass runs it as a full expand (outputs, and its end state as the
+// entry state of segment 1) beside the compose of segments 1 .. nseg-2.  The
+// last segment's transition is not needed either: the second pass runs it as
+// a full expand from its entry state (outputs and s_final) beside the light
+// expands of segments 1 .. nseg-2.  Segment `seg` of chain `bh` is workgroup
+// (seg - first) * nchain + bh of its pass; P, R and the entry states E are
+// indexed by segment as in the uniform plan (slots 0 and nseg-1 of P and R
+// and slot 0 of E are not used).
+template <bool SG>
+__global__ __launch_bounds__(NTH) void pipe_first_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                         const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                         const bf16* __restrict__ beta, float g_min, int T, int H,
+                                                         int NC, int L, int nchain, const float* __restrict__ s0,
+                                                         float* __restrict__ e1, float* __restrict__ P,
+                                                         float* __restrict__ R, bf16* __restrict__ o,
+                                                         bf16* __restrict__ tm) {
+    const int seg = (int)(blockIdx.x / nchain);
+    const size_t bh = blockIdx.x % nchain;
+    if (seg == 0)
+        pipe_run<EXPAND, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, s0, e1, nullptr, o, nullptr,
+                                    nullptr, 0.f, nullptr, 0, bh);
+    else
+        pipe_run<COMPOSE, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, nullptr, P, R, nullptr, tm,
+                                     nullptr, 0.f, nullptr, seg, bh);
+}
+
+template <bool SG>
+__global__ __launch_bounds__(NTH) void pipe_last_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                        const bf16* __restrict__ v, const bf16* __restrict__ z,
+                                                        const bf16* __restrict__ beta, float g_min, int T, int H,
+                                                        int NC, int L, int nchain, int nseg,
+                                                        const float* __restrict__ E, float* __restrict__ s_final,
+                                                        bf16* __restrict__ o, bf16* __restrict__ tm) {
+    const int seg = (int)(blockIdx.x / nchain) + 1;
+    const size_t bh = blockIdx.x % nchain;
+    if (seg == nseg - 1)
+        pipe_run<EXPAND, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, s_final, nullptr, o, nullptr,
+                                    nullptr, 0.f, nullptr, seg, bh);
+    else
+        pipe_run<EXPAND_LITE, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, nullptr, nullptr, o, tm,
+                                         nullptr, 0.f, nullptr, seg, bh);
+}
+
 // ---------------------------------------------------------------------------
 // Scan over segments for one chain and 16 state columns:
 //   Sent[j] = S_j,  S_{j+1} = P_j S_j + R_j,  s_final = S_nseg.
@@ -1845,9 +1906,11 @@ __device__ __forceinline__ void scan_apply(f32x4 (&acc)[2], const ScanIn<DK, DV>
 }
 
 template <int DK, int DV>
+// (s0 may be Sent itself: each element is read, then written with the same
+// value, by one thread.)
 __global__ __launch_bounds__(256) void scan_x3_kernel(const float* __restrict__ P, const float* __restrict__ R,
-                                                      const float* __restrict__ s0, float* __restrict__ Sent,
-                                                      float* __restrict__ s_final, int nseg, int nchain) {
+                                                      const float* s0, float* Sent, float* __restrict__ s_final,
+                                                      int nseg, int nchain) {
     static_assert(DK == 128, "four waves of 32 state rows");
     constexpr int LS = DK + 4;
     __shared__ __align__(16) float St[16 * LS];
@@ -1894,6 +1957,7 @@ constexpr int FILL_CHAINS = 256;
 
 struct Plan {
     int nseg, L;
+    bool split;   // the first and last segments run as full expands (pipe_first_kernel, pipe_last_kernel)
     size_t p_off, r_off, e_off, tm_off, total;
 };
 
@@ -1907,7 +1971,15 @@ static bool use_pipe() {
     return on;
 }
 
-static Plan plan(int B, int T, int H, int DK, int DV) {
+// Uniform plan: nseg segments of L chunks (the last one shorter), composed,
+// scanned and expanded.  With `split` (the pipelined kernels without the
+// fused epilogue), a segmented plan of nseg segments becomes nseg + 1 of
+// them, the first and last ones expanded directly (pipe_first_kernel,
+// pipe_last_kernel), so each pass still runs nseg workgroups per chain.  The
+// last segment, a full expand beside light expands, is made shorter: a full
+// expand costs about 1.2x a light one per chunk, so L = NC / (nseg + 5/6)
+// balances the second pass.
+static Plan plan(int B, int T, int H, int DK, int DV, bool split = false) {
     Plan p{};
     const int NC = (T + C - 1) / C;
     const long nchain = (long)B * H;
@@ -1919,6 +1991,16 @@ static Plan plan(int B, int T, int H, int DK, int DV) {
     }
     p.L = (NC + nseg - 1) / nseg;
     p.nseg = nseg > 1 ? (NC + p.L - 1) / p.L : 1;
+    p.split = false;
+    if (split && p.nseg > 1) {
+        const int L = (int)((6L * NC + 6L * nseg + 4) / (6L * nseg + 5));   // ceil(NC / (nseg + 5/6))
+        const int n = (NC + L - 1) / L;
+        if (n >= 3) {
+            p.L = L;
+            p.nseg = n;
+            p.split = true;
+        }
+    }
     p.p_off = p.r_off = p.e_off = p.tm_off = p.total = 0;
     if (p.nseg > 1) {
         p.r_off = (size_t)p.nseg * nchain * DK * DK * 4;
@@ -1974,6 +2056,26 @@ static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     float* Rb = reinterpret_cast<float*>(ws + p.r_off);
     float* Eb = reinterpret_cast<float*>(ws + p.e_off);
     bf16* TM = reinterpret_cast<bf16*>(ws + p.tm_off);
+    if (p.split) {
+        if (GATED) return hipErrorInvalidValue;
+        const size_t pslot = (size_t)nchain * 128 * 128;   // one segment's P, R or E (fp32)
+        constexpr size_t LDS1 = PLay<EXPAND>::LDS > PLay<COMPOSE>::LDS ? PLay<EXPAND>::LDS : PLay<COMPOSE>::LDS;
+        constexpr size_t LDS2 = PLay<EXPAND>::LDS > PLay<EXPAND_LITE>::LDS ? PLay<EXPAND>::LDS : PLay<EXPAND_LITE>::LDS;
+        if ((err = set_lds(pipe_first_kernel<SG>, LDS1)) != hipSuccess) return err;
+        hipLaunchKernelGGL((pipe_first_kernel<SG>), dim3((p.nseg - 1) * nchain), dim3(NTH), LDS1, st, q, k, v, z, beta,
+                           a.g_min, a.T, a.H, NC, p.L, nchain, a.s0, Eb + pslot, Pb, Rb, (bf16*)a.o, TM);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        // entry states of segments 2 .. nseg-1 from that of segment 1 over
+        // the transitions of segments 1 .. nseg-2
+        hipLaunchKernelGGL((scan_x3_kernel<128, 128>), dim3(8 * nchain), dim3(256), 0, st, (const float*)(Pb + pslot),
+                           (const float*)(Rb + pslot), (const float*)(Eb + pslot), Eb + pslot,
+                           Eb + (size_t)(p.nseg - 1) * pslot, p.nseg - 2, nchain);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if ((err = set_lds(pipe_last_kernel<SG>, LDS2)) != hipSuccess) return err;
+        hipLaunchKernelGGL((pipe_last_kernel<SG>), dim3((p.nseg - 1) * nchain), dim3(NTH), LDS2, st, q, k, v, z, beta,
+                           a.g_min, a.T, a.H, NC, p.L, nchain, p.nseg, (const float*)Eb, a.s_final, (bf16*)a.o, TM);
+        return hipGetLastError();
+    }
     if ((err = set_lds(pipe_kernel<COMPOSE, false, SG>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
     hipLaunchKernelGGL((pipe_kernel<COMPOSE, false, SG>), dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
                        beta, a.g_min, a.T, a.H, NC, p.L, nchain, (const float*)nullptr, Pb, Rb, (bf16*)nullptr, TM,
@@ -1993,9 +2095,9 @@ static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
 
 template <int DK, int DV>
 static hipError_t launch_t(const ChunkArgs& a) {
-    const Plan p = plan(a.B, a.T, a.H, DK, DV);
     if constexpr (DK == 128 && DV == 128)
-        if (use_pipe()) return launch_pipe(a, p);
+        if (use_pipe()) return launch_pipe(a, plan(a.B, a.T, a.H, DK, DV, a.gate == nullptr));
+    const Plan p = plan(a.B, a.T, a.H, DK, DV);
     if (a.scalar_z) return hipErrorInvalidValue;   // only the pipelined kernels read a scalar gate
     const int NC = (a.T + C - 1) / C;
     const int nchain = a.B * a.H;
@@ -2028,7 +2130,13 @@ static hipError_t launch_t(const ChunkArgs& a) {
 
 }  // namespace segk
 
-size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) { return segk::plan(B, T, H, dk, dv).total; }
+size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) {
+    // room for either plan: the layer call with the fused epilogue runs the
+    // uniform one
+    const size_t u = segk::plan(B, T, H, dk, dv).total;
+    const size_t s = dk == 128 && dv == 128 ? segk::plan(B, T, H, dk, dv, true).total : 0;
+    return u > s ? u : s;
+}
 
 bool chunk_scalar_gate_native(int T, int dk, int dv, bool bf16, float g_min) {
     return bf16 && dk == 128 && dv == 128 && T > 0 && g_min >= CHUNK_G_MIN_LIMIT && segk::use_pipe();

@@ -59,12 +59,15 @@ def test_workspace_sizes(lib):
     # transition P (d_k x d_k), the input term R and the entry state
     # (d_k x d_v), fp32; with d_k = d_v = 128, also every chunk's
     # T' = (I + A)^-1 diag(beta) (64 x 64 bf16) handed from the compose pass
-    # to the expand pass
-    seg = 8 * 32 * (128 * 128 + 2 * 128 * 128) * 4
+    # to the expand pass.  With d_k = d_v = 128 the workspace also holds the
+    # split plan, one segment more: ceil(512 / (8 + 5/6)) = 58 chunks per
+    # segment, 9 segments.
+    seg = 9 * 32 * (128 * 128 + 2 * 128 * 128) * 4
     tm = 64 * 64 * 2
     assert lib.kda_chunk_fwd_workspace_bytes(1, 32768, 32, 128, 128, 64, BF16) == seg + 32 * 512 * tm
-    # one chain of 31 chunks: 3 segments of at least 8 chunks
-    assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 3 * 3 * 128 * 128 * 4 + 31 * tm
+    # one chain of 31 chunks: 3 segments of at least 8 chunks, split into
+    # ceil(31 / 9) = 4 of ceil(31 / (3 + 5/6)) = 9 chunks
+    assert lib.kda_chunk_fwd_workspace_bytes(1, 31 * 64, 1, 128, 128, 64, BF16) == 4 * 3 * 128 * 128 * 4 + 31 * tm
     # below 16 chunks, or with 256 chains or more, a single segment: no workspace
     assert lib.kda_chunk_fwd_workspace_bytes(1, 15 * 64, 1, 128, 128, 64, BF16) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(8, 8192, 32, 128, 128, 64, BF16) == 0
