@@ -103,6 +103,11 @@ struct GateArgs {
 };
 size_t gate_workspace_bytes(int B, int T, int H, int dv, int d_model, bool bf16, bool proj);
 hipError_t launch_out_gate(const GateArgs& a);
+// The epilogue (bf16, d_v = 128) on tokens [0, t_a) and [t_b, T) of each
+// sequence, o -> y (o may be y): the rows the split prefill plan's full
+// expands leave to it.
+hipError_t launch_gate_ends(const void* o, const void* gate, float eps, void* y, int B, int T, int H, int t_a, int t_b,
+                            void* stream);
 // out (M x N, bf16) = y (M x K, bf16) . w (N x K, bf16)^T (gemm.hip); N a
 // multiple of 16, K of 64; scratch holds projection_scratch_bytes(M, N, K)
 // bytes (fp32 partial tiles of a split K range for small M, else none)

@@ -1808,21 +1808,25 @@ __global__ __launch_bounds__(NTH) void pipe_first_kernel(const bf16* __restrict_
                                      nullptr, 0.f, nullptr, seg, bh);
 }
 
-template <bool SG>
+// GATED: the light expands apply the output epilogue (y, and o when not
+// NULL); the last segment's outputs go to o_end, for the epilogue kernel.
+template <bool GATED, bool SG>
 __global__ __launch_bounds__(NTH) void pipe_last_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         const bf16* __restrict__ v, const bf16* __restrict__ z,
                                                         const bf16* __restrict__ beta, float g_min, int T, int H,
                                                         int NC, int L, int nchain, int nseg,
                                                         const float* __restrict__ E, float* __restrict__ s_final,
-                                                        bf16* __restrict__ o, bf16* __restrict__ tm) {
+                                                        bf16* __restrict__ o, bf16* __restrict__ o_end,
+                                                        bf16* __restrict__ tm, const bf16* __restrict__ gate,
+                                                        float eps, bf16* __restrict__ y) {
     const int seg = (int)(blockIdx.x / nchain) + 1;
     const size_t bh = blockIdx.x % nchain;
     if (seg == nseg - 1)
-        pipe_run<EXPAND, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, s_final, nullptr, o, nullptr,
-                                    nullptr, 0.f, nullptr, seg, bh);
+        pipe_run<EXPAND, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, s_final, nullptr, o_end,
+                                    nullptr, nullptr, 0.f, nullptr, seg, bh);
     else
-        pipe_run<EXPAND_LITE, false, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, nullptr, nullptr, o, tm,
-                                         nullptr, 0.f, nullptr, seg, bh);
+        pipe_run<EXPAND_LITE, GATED, SG>(q, k, v, z, beta, g_min, T, H, NC, L, nchain, E, nullptr, nullptr, o, tm,
+                                         gate, eps, y, seg, bh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1972,9 +1976,8 @@ static bool use_pipe() {
 }
 
 // Uniform plan: nseg segments of L chunks (the last one shorter), composed,
-// scanned and expanded.  With `split` (the pipelined kernels without the
-// fused epilogue), a segmented plan of nseg segments becomes nseg + 1 of
-// them, the first and last ones expanded directly (pipe_first_kernel,
+// scanned and expanded.  With `split` (the pipelined kernels), a segmented
+// plan of nseg segments becomes nseg + 1 of them, the first and last ones expanded directly (pipe_first_kernel,
 // pipe_last_kernel), so each pass still runs nseg workgroups per chain.  The
 // last segment, a full expand beside light expands, is made shorter: a full
 // expand costs about 1.2x a light one per chunk, so L = NC / (nseg + 5/6)
@@ -2057,13 +2060,15 @@ static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
     float* Eb = reinterpret_cast<float*>(ws + p.e_off);
     bf16* TM = reinterpret_cast<bf16*>(ws + p.tm_off);
     if (p.split) {
-        if (GATED) return hipErrorInvalidValue;
+        // GATED: the first and last segments' outputs go to o, or else to
+        // y's rows (same layout), and the epilogue kernel gates them there
+        bf16* o_end = GATED && !a.o ? y : (bf16*)a.o;
         const size_t pslot = (size_t)nchain * 128 * 128;   // one segment's P, R or E (fp32)
         constexpr size_t LDS1 = PLay<EXPAND>::LDS > PLay<COMPOSE>::LDS ? PLay<EXPAND>::LDS : PLay<COMPOSE>::LDS;
         constexpr size_t LDS2 = PLay<EXPAND>::LDS > PLay<EXPAND_LITE>::LDS ? PLay<EXPAND>::LDS : PLay<EXPAND_LITE>::LDS;
         if ((err = set_lds(pipe_first_kernel<SG>, LDS1)) != hipSuccess) return err;
         hipLaunchKernelGGL((pipe_first_kernel<SG>), dim3((p.nseg - 1) * nchain), dim3(NTH), LDS1, st, q, k, v, z, beta,
-                           a.g_min, a.T, a.H, NC, p.L, nchain, a.s0, Eb + pslot, Pb, Rb, (bf16*)a.o, TM);
+                           a.g_min, a.T, a.H, NC, p.L, nchain, a.s0, Eb + pslot, Pb, Rb, o_end, TM);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         // entry states of segments 2 .. nseg-1 from that of segment 1 over
         // the transitions of segments 1 .. nseg-2
@@ -2071,10 +2076,17 @@ static hipError_t launch_pipe_t(const ChunkArgs& a, const Plan& p) {
                            (const float*)(Rb + pslot), (const float*)(Eb + pslot), Eb + pslot,
                            Eb + (size_t)(p.nseg - 1) * pslot, p.nseg - 2, nchain);
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        if ((err = set_lds(pipe_last_kernel<SG>, LDS2)) != hipSuccess) return err;
-        hipLaunchKernelGGL((pipe_last_kernel<SG>), dim3((p.nseg - 1) * nchain), dim3(NTH), LDS2, st, q, k, v, z, beta,
-                           a.g_min, a.T, a.H, NC, p.L, nchain, p.nseg, (const float*)Eb, a.s_final, (bf16*)a.o, TM);
-        return hipGetLastError();
+        if ((err = set_lds(pipe_last_kernel<GATED, SG>, LDS2)) != hipSuccess) return err;
+        hipLaunchKernelGGL((pipe_last_kernel<GATED, SG>), dim3((p.nseg - 1) * nchain), dim3(NTH), LDS2, st, q, k, v, z,
+                           beta, a.g_min, a.T, a.H, NC, p.L, nchain, p.nseg, (const float*)Eb, a.s_final, (bf16*)a.o,
+                           o_end, TM, gate, a.eps, y);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+        if constexpr (GATED) {
+            // tokens [0, L C) and [(nseg - 1) L C, T) of every sequence
+            const int t_a = min(a.T, p.L * C), t_b = (p.nseg - 1) * p.L * C;
+            return launch_gate_ends(o_end, gate, a.eps, y, a.B, a.T, a.H, t_a, t_b, a.stream);
+        }
+        return hipSuccess;
     }
     if ((err = set_lds(pipe_kernel<COMPOSE, false, SG>, PLay<COMPOSE>::LDS)) != hipSuccess) return err;
     hipLaunchKernelGGL((pipe_kernel<COMPOSE, false, SG>), dim3(p.nseg * nchain), dim3(NTH), PLay<COMPOSE>::LDS, st, q, k, v, z,
@@ -2096,7 +2108,7 @@ static hipError_t launch_pipe(const ChunkArgs& a, const Plan& p) {
 template <int DK, int DV>
 static hipError_t launch_t(const ChunkArgs& a) {
     if constexpr (DK == 128 && DV == 128)
-        if (use_pipe()) return launch_pipe(a, plan(a.B, a.T, a.H, DK, DV, a.gate == nullptr));
+        if (use_pipe()) return launch_pipe(a, plan(a.B, a.T, a.H, DK, DV, true));
     const Plan p = plan(a.B, a.T, a.H, DK, DV);
     if (a.scalar_z) return hipErrorInvalidValue;   // only the pipelined kernels read a scalar gate
     const int NC = (a.T + C - 1) / C;
@@ -2131,8 +2143,7 @@ static hipError_t launch_t(const ChunkArgs& a) {
 }  // namespace segk
 
 size_t seg_workspace_bytes(int B, int T, int H, int dk, int dv) {
-    // room for either plan: the layer call with the fused epilogue runs the
-    // uniform one
+    // room for either plan (KDA_PIPELINE=0 selects the uniform one)
     const size_t u = segk::plan(B, T, H, dk, dv).total;
     const size_t s = dk == 128 && dv == 128 ? segk::plan(B, T, H, dk, dv, true).total : 0;
     return u > s ? u : s;
