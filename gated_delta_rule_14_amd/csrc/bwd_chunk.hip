@@ -62,9 +62,10 @@ struct Ob {
 };
 
 // Per chunk, bf16 tokens: bf16 products, each stored in the orientation the
-// per-chunk kernel contracts it in (offsets in bf16 elements), then the fp32
-// e^{G_C} rowsum(S dS').  NP = -tril_-1(dVn Vn^T), which with
-// dT T^T = dVn Vn^T (I + A)^T T^T = dVn Vn^T gives dA = tril_-1(T^T NP).
+// per-chunk kernel contracts it in (offsets in bf16 elements; each matrix in
+// 16 x 16 tiles, see tix), then the fp32 e^{G_C} rowsum(S dS').
+// NP = -tril_-1(dVn Vn^T), which with dT T^T = dVn Vn^T (I + A)^T T^T =
+// dVn Vn^T gives dA = tril_-1(T^T NP).
 template <int DK, int DV>
 struct ObH {
     static constexpr size_t DVNT = 0;                      // (DV, C)  dVn^T
@@ -79,6 +80,15 @@ struct ObH {
     static constexpr size_t BYTES = DGC_BYTE + DK * 4;
     static_assert(BYTES % 16 == 0, "16-byte aligned chunk blocks");
 };
+
+// Element (r, c) of an ObH matrix with ncol columns: 16 x 16 tiles in
+// row-major tile order, each tile row-major, so that a wave's 16 x 16 MFMA
+// result (4 consecutive columns per lane) is one contiguous 512-byte store
+// and a fragment read (4 or 8 consecutive columns of 16 rows) stays inside a
+// tile's rows.
+__device__ __forceinline__ size_t tix(int r, int c, int ncol) {
+    return ((size_t)(r >> 4) * (ncol >> 4) + (c >> 4)) * 256 + (r & 15) * 16 + (c & 15);
+}
 
 template <class CT, int DK, int DV>
 constexpr size_t ob_bytes() {
@@ -101,6 +111,16 @@ Lay lay_t(int B, int T, int H) {
     lo.ob = lo.vn + a256(nchunk * C * DV * sizeof(CT));
     lo.total = lo.ob + nchunk * ob_bytes<CT, DK, DV>();
     return lo;
+}
+
+// Sum over the 16 lanes of a DPP row, in every lane: quad swaps, then the
+// half-row and row mirrors.
+__device__ __forceinline__ float sum16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+    return x;
 }
 
 // ---------------------------------------------------------------------------
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
     constexpr int SG = DV / 8;                // 16-byte groups per row of S
     auto issue_s = [&](int m) { stage_state<DK, DV, L::NW>(states + (bh * NC + m) * DK * DV, smem + L::OFF_S); };
     // fragment (rows row0 + l%16, columns k0 + 8(l/16) ..) and element reads of the staged S
-    auto s_frag = [&](int row0, int k0) -> typename MF::frag {
+    auto s_frag = [&](int row0, int k0, int l) -> typename MF::frag {
         const int r = row0 + (l & 15), g = k0 / 8 + (l >> 4);
         return *reinterpret_cast<const typename MF::frag*>(Ss + r * DV + ((g ^ (r & (SG - 1))) << 3));
     };
@@ -197,7 +217,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
     // (raw 16-byte vectors: rows past the end are zeroed when staged, so the
     // loads are not waited for here)
     u32x4 dov[NU];
-    auto load_do = [&](int m) {
+    auto load_do = [&](int m, int tid) {
         const int valid_m = min(C, T - m * C);
         const E* dob_m = dout + (((size_t)bb * T + (size_t)m * C) * H + hh) * DV;
 #pragma unroll
@@ -206,7 +226,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             dov[i] = *reinterpret_cast<const u32x4*>(dob_m + (size_t)min(r, valid_m - 1) * H * DV + j0);
         }
     };
-    load_do(NC - 1);
+    load_do(NC - 1, tid);
     const int srow = w * 16 + 4 * (l >> 4);   // first dS row of this lane
 
     f32x4 accD[NT];
@@ -216,7 +236,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
 #pragma unroll
         for (int e = 0; e < 4; ++e) accD[ct][e] = ds_final ? ds_final[(bh * DK + srow + e) * DV + col] : 0.f;
     }
-    auto store_ds = [&]() {
+    auto store_ds = [&](int l, int srow) {
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
             const int col = ct * 16 + (l & 15);
@@ -225,9 +245,13 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             for (int e = 0; e < 4; ++e) dSR[(srow + e) * LDV + col] = from_f32<CT>(accD[ct][e]);
         }
     };
-    store_ds();
+    store_ds(l, srow);
 
     for (int n = NC - 1; n >= 0; --n) {
+        // lane-derived addresses are recomputed in every chunk instead of
+        // being held in registers across the loop
+        const int l = opaque(lane_id()), tid = opaque((int)threadIdx.x);
+        const int srow = w * 16 + 4 * (l >> 4);
         const int valid = min(C, T - n * C);
         const size_t cid = bh * NC + n;
         const unsigned char* fb = fws + cid * WL::BYTES;
@@ -239,13 +263,32 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         const E* dob = dout + (((size_t)bb * T + (size_t)n * C) * H + hh) * DV;   // row r at r * H * DV
         const size_t rs = (size_t)H * DV;
 
-        // this wave's M^T and Kc rows (token block X) for dVn, loaded first so
-        // that they arrive while dO^T is staged
+        // this wave's M^T and Kc rows (token block X) for dVn; then, for the
+        // products after dVn, dO rows 16X.. (zero past the end) and Vn rows
+        // 16X.. as A operands, and the Vn rows of this wave's dM blocks: all
+        // issued first, so that they arrive while dO^T is staged and dVn runs
         typename MF::frag mtf[C / KS], kcf[DK / KS];
 #pragma unroll
-        for (int kk = 0; kk < C / KS; ++kk) mtf[kk] = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS);
+        for (int kk = 0; kk < C / KS; ++kk) mtf[kk] = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS, l);
 #pragma unroll
-        for (int kk = 0; kk < DK / KS; ++kk) kcf[kk] = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS);
+        for (int kk = 0; kk < DK / KS; ++kk) kcf[kk] = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS, l);
+        constexpr int NKK = DV / KS, NIB = C / 16 / NCG;
+        typename MF::frag dof[NKK], vf[NKK], fvm[NIB][NKK];
+        {
+            const int r = X * 16 + (l & 15);
+            const bool ok = r < valid;
+            // the row address is clamped to the last token (in bounds); rows
+            // past the end are zeroed
+            const CT* drow = reinterpret_cast<const CT*>(dob + (size_t)min(r, valid - 1) * rs) + (l >> 4) * MF::KPL;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                dof[kk] = *reinterpret_cast<const typename MF::frag*>(drow + kk * KS);
+                if (!ok) dof[kk] = typename MF::frag{};
+                vf[kk] = load_frag<CT>(Vn, DV, X * 16, kk * KS, l);
+#pragma unroll
+                for (int u = 0; u < NIB; ++u) fvm[u][kk] = load_frag<CT>(Vn, DV, (cg * NIB + u) * 16, kk * KS, l);
+            }
+        }
 
         // dO^T into LDS (rows loaded into registers during the previous chunk)
 #pragma unroll
@@ -267,19 +310,19 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int kk = 0; kk < C / KS; ++kk) {
 #pragma unroll
             for (int ct = 0; ct < NTG; ++ct)
-                accV[ct] = MF::mma(mtf[kk], load_frag<CT>(dOT, LC, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
+                accV[ct] = MF::mma(mtf[kk], load_frag<CT>(dOT, LC, (cg * NTG + ct) * 16, kk * KS, l), accV[ct]);
         }
 #pragma unroll
         for (int kk = 0; kk < DK / KS; ++kk) {
 #pragma unroll
             for (int ct = 0; ct < NTG; ++ct)
-                accV[ct] = MF::mma(kcf[kk], load_frag<CT>(dST, LDK, (cg * NTG + ct) * 16, kk * KS), accV[ct]);
+                accV[ct] = MF::mma(kcf[kk], load_frag<CT>(dST, LDK, (cg * NTG + ct) * 16, kk * KS, l), accV[ct]);
         }
 #pragma unroll
         for (int ct = 0; ct < NTG; ++ct) {
             const int col = (cg * NTG + ct) * 16 + (l & 15), row = X * 16 + 4 * (l >> 4);
             if constexpr (H16)
-                store4<bf16>(obh + OH::DVNT + (size_t)col * C + row, accV[ct]);
+                store4<bf16>(obh + OH::DVNT + tix(col, row, C), accV[ct]);
             else
                 *reinterpret_cast<f32x4*>(ob + OL::DVNT + (size_t)col * C + row) = accV[ct];
             store4<CT>(dVT + col * LC + row, -accV[ct]);
@@ -289,64 +332,63 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         if constexpr (L::SL) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's S loads have landed
         __syncthreads();
 
-        // dO rows 16X.. (zero past the end) and Vn rows 16X.. as A operands
-        typename MF::frag dof[DV / KS], vf[DV / KS];
-        {
-            const int r = X * 16 + (l & 15);
-            const bool ok = r < valid;
-            // the row address is clamped to the last token (in bounds); rows
-            // past the end are zeroed
-            const CT* drow = reinterpret_cast<const CT*>(dob + (size_t)min(r, valid - 1) * rs) + (l >> 4) * MF::KPL;
-#pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) {
-                dof[kk] = *reinterpret_cast<const typename MF::frag*>(drow + kk * KS);
-                if (!ok) dof[kk] = typename MF::frag{};
-                vf[kk] = load_frag<CT>(Vn, DV, X * 16, kk * KS);
-            }
-        }
         // dQg = dO S^T, dW = -dVn S^T and dKc = Vn dS'^T (rows 16X.., this
         // wave's group of d_k column tiles)
         constexpr int NCB = DK / 16 / NCG;
-#pragma unroll 2
+        // operand fragments from LDS, issued one column block ahead of their
+        // MFMAs (double-buffered); -dVn's rows are the same for every block
+        typename MF::frag fvr[NKK], fsb[2][NKK], fdb[2][NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) fvr[kk] = load_frag<CT>(dVR, LDV, X * 16, kk * KS, l);
+        auto load_cb = [&](int u, typename MF::frag (&fs)[NKK], typename MF::frag (&fd)[NKK]) {
+            const int cb = cg * NCB + u;
+#pragma unroll
+            for (int kk = 0; kk < NKK; ++kk) {
+                if constexpr (L::SL)
+                    fs[kk] = s_frag(cb * 16, kk * KS, l);
+                else
+                    fs[kk] = load_frag<CT>(Sn, DV, cb * 16, kk * KS, l);
+                fd[kk] = load_frag<CT>(dSR, LDV, cb * 16, kk * KS, l);
+            }
+        };
+        load_cb(0, fsb[0], fdb[0]);
+#pragma unroll
         for (int u = 0; u < NCB; ++u) {
             const int cb = cg * NCB + u;
+            if (u + 1 < NCB) load_cb(u + 1, fsb[(u + 1) & 1], fdb[(u + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);   // the next block's reads stay ahead of these MFMAs
+            const typename MF::frag(&fs)[NKK] = fsb[u & 1];
+            const typename MF::frag(&fd)[NKK] = fdb[u & 1];
             f32x4 accQ = zero4(), accW = zero4(), accK = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) {
-                typename MF::frag fs;
-                if constexpr (L::SL)
-                    fs = s_frag(cb * 16, kk * KS);
-                else
-                    fs = load_frag<CT>(Sn, DV, cb * 16, kk * KS);
-                accW = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fs, accW);
+            for (int kk = 0; kk < NKK; ++kk) {
+                accW = MF::mma(fvr[kk], fs[kk], accW);
                 if constexpr (H16) {   // (channel, token) orientation: rows of dO S^T and Vn dS'^T
-                    accQ = MF::mma(fs, dof[kk], accQ);
-                    accK = MF::mma(load_frag<CT>(dSR, LDV, cb * 16, kk * KS), vf[kk], accK);
+                    accQ = MF::mma(fs[kk], dof[kk], accQ);
+                    accK = MF::mma(fd[kk], vf[kk], accK);
                 } else {
-                    accQ = MF::mma(dof[kk], fs, accQ);
-                    accK = MF::mma(vf[kk], load_frag<CT>(dSR, LDV, cb * 16, kk * KS), accK);
+                    accQ = MF::mma(dof[kk], fs[kk], accQ);
+                    accK = MF::mma(vf[kk], fd[kk], accK);
                 }
             }
-            const size_t off = (size_t)(cb * 16 + (l & 15)) * C + X * 16 + 4 * (l >> 4);
             if constexpr (H16) {
-                const size_t offr = (size_t)(X * 16 + (l & 15)) * DK + cb * 16 + 4 * (l >> 4);
-                store4<bf16>(obh + OH::DQG + offr, accQ);
-                store4<bf16>(obh + OH::DWT + off, accW);
-                store4<bf16>(obh + OH::DKC + offr, accK);
+                store4<bf16>(obh + OH::DQG + tix(X * 16 + (l & 15), cb * 16 + 4 * (l >> 4), DK), accQ);
+                store4<bf16>(obh + OH::DWT + tix(cb * 16 + (l & 15), X * 16 + 4 * (l >> 4), C), accW);
+                store4<bf16>(obh + OH::DKC + tix(X * 16 + (l & 15), cb * 16 + 4 * (l >> 4), DK), accK);
             } else {
+                const size_t off = (size_t)(cb * 16 + (l & 15)) * C + X * 16 + 4 * (l >> 4);
                 *reinterpret_cast<f32x4*>(ob + OL::DQGT + off) = accQ;
                 *reinterpret_cast<f32x4*>(ob + OL::DWT + off) = accW;
                 *reinterpret_cast<f32x4*>(ob + OL::DKCT + off) = accK;
             }
         }
         // dM = tril(dO Vn^T) (rows r, columns i), stored transposed
-        constexpr int NIB = C / 16 / NCG;
 #pragma unroll
         for (int u = 0; u < NIB; ++u) {
             const int ib = cg * NIB + u;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kk = 0; kk < DV / KS; ++kk) acc = MF::mma(dof[kk], load_frag<CT>(Vn, DV, ib * 16, kk * KS), acc);
+            for (int kk = 0; kk < NKK; ++kk) acc = MF::mma(dof[kk], fvm[u][kk], acc);
             const int i = ib * 16 + (l & 15), r0 = X * 16 + 4 * (l >> 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = (i <= r0 + e) ? acc[e] : 0.f;
@@ -355,10 +397,9 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                 // NP = -tril_-1(dVn Vn^T), stored transposed
                 f32x4 accR = zero4(), accP = zero4();
 #pragma unroll
-                for (int kk = 0; kk < DV / KS; ++kk) {
-                    const typename MF::frag fv = load_frag<CT>(Vn, DV, ib * 16, kk * KS);
-                    accR = MF::mma(fv, dof[kk], accR);
-                    accP = MF::mma(load_frag<CT>(dVR, LDV, X * 16, kk * KS), fv, accP);
+                for (int kk = 0; kk < NKK; ++kk) {
+                    accR = MF::mma(fvm[u][kk], dof[kk], accR);
+                    accP = MF::mma(fvr[kk], fvm[u][kk], accP);
                 }
                 const int r = X * 16 + (l & 15), i0 = ib * 16 + 4 * (l >> 4);
 #pragma unroll
@@ -366,9 +407,9 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                     accR[e] = (i0 + e <= r) ? accR[e] : 0.f;
                     accP[e] = (i < r0 + e) ? accP[e] : 0.f;
                 }
-                store4<bf16>(obh + OH::DMT + (size_t)i * C + r0, acc);
-                store4<bf16>(obh + OH::DM + (size_t)r * C + i0, accR);
-                store4<bf16>(obh + OH::NPT + (size_t)i * C + r0, accP);
+                store4<bf16>(obh + OH::DMT + tix(i, r0, C), acc);
+                store4<bf16>(obh + OH::DM + tix(r, i0, C), accR);
+                store4<bf16>(obh + OH::NPT + tix(i, r0, C), accP);
             } else {
                 *reinterpret_cast<f32x4*>(ob + OL::DMT + (size_t)i * C + r0) = acc;
             }
@@ -378,8 +419,8 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         typename MF::frag aqf[C / KS], awf[C / KS];
 #pragma unroll
         for (int kk = 0; kk < C / KS; ++kk) {
-            aqf[kk] = load_frag<CT>(bk + WB::QGT, C, w * 16, kk * KS);
-            awf[kk] = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS);
+            aqf[kk] = load_frag<CT>(bk + WB::QGT, C, w * 16, kk * KS, l);
+            awf[kk] = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS, l);
         }
         // e^{G_C} rowsum(S dS'), rows of this wave
         const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
@@ -394,8 +435,7 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                 else
                     sacc += accD[ct][e] * to_f32(Sn[(size_t)(srow + e) * DV + ct * 16 + (l & 15)]);
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) sacc += __shfl_xor(sacc, off);
+            sacc = sum16(sacc);
             if ((l & 15) == 0) {
                 if constexpr (H16)
                     reinterpret_cast<float*>(obuf + cid * OH::BYTES + OH::DGC_BYTE)[srow + e] = sacc * eg[e];
@@ -410,16 +450,16 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         for (int kk = 0; kk < C / KS; ++kk) {
 #pragma unroll
             for (int ct = 0; ct < NT; ++ct) {
-                accD[ct] = MF::mma(aqf[kk], load_frag<CT>(dOT, LC, ct * 16, kk * KS), accD[ct]);
-                accD[ct] = MF::mma(awf[kk], load_frag<CT>(dVT, LC, ct * 16, kk * KS), accD[ct]);
+                accD[ct] = MF::mma(aqf[kk], load_frag<CT>(dOT, LC, ct * 16, kk * KS, l), accD[ct]);
+                accD[ct] = MF::mma(awf[kk], load_frag<CT>(dVT, LC, ct * 16, kk * KS, l), accD[ct]);
             }
         }
         __syncthreads();   // this chunk's reads of dO^T, dS, dVn and S in LDS are done
         if constexpr (L::SL) {
             if (n > 0) issue_s(n - 1);   // lands before the next chunk's products (the barrier after its dVn waits)
         }
-        if (n > 0) load_do(n - 1);
-        store_ds();
+        if (n > 0) load_do(n - 1, tid);
+        store_ds(l, srow);
     }
     if (ds0) {
 #pragma unroll
@@ -1011,16 +1051,6 @@ __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
-// Sum over the 16 lanes of a DPP row, in every lane: quad swaps, then the
-// half-row and row mirrors.
-__device__ __forceinline__ float sum16(float x) {
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
-    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
-    return x;
-}
-
 template <int DK, int DV>
 __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                        const bf16* __restrict__ v, const bf16* __restrict__ z,
@@ -1080,20 +1110,20 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
     // dA phase and the decayed products: NP^T of the pairs, dM and dM^T rows
     // of this lane's token (every block); issued here to be in flight during
     // the gate scan and the operand families
-    const int R0 = kPairsB[w][0][0], I0 = kPairsB[w][0][1], R1 = kPairsB[w][1][0], I1 = kPairsB[w][1][1];
-    const bool two = R1 >= 0;
+    const int I0 = kPairsB[w][0][1], I1 = kPairsB[w][1][1];
+    const bool two = kPairsB[w][1][0] >= 0;
     bf16x8 npf[2][C / 32];
 #pragma unroll
     for (int kb = 0; kb < C / 32; ++kb) {
-        npf[0][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I0 * 16 + lr) * C + kb * 32 + lg * 8);
-        npf[1][kb] = two ? *reinterpret_cast<const bf16x8*>(ob + OH::NPT + (size_t)(I1 * 16 + lr) * C + kb * 32 + lg * 8)
+        npf[0][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::NPT + tix(I0 * 16 + lr, kb * 32 + lg * 8, C));
+        npf[1][kb] = two ? *reinterpret_cast<const bf16x8*>(ob + OH::NPT + tix(I1 * 16 + lr, kb * 32 + lg * 8, C))
                          : bf16x8{};
     }
     bf16x4 dmr[4], dmc[4];
 #pragma unroll
     for (int Y = 0; Y < 4; ++Y) {
-        dmr[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DM + (size_t)rX * C + Y * 16 + 4 * lg);
-        dmc[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + (size_t)rX * C + Y * 16 + 4 * lg);
+        dmr[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DM + tix(rX, Y * 16 + 4 * lg, C));
+        dmc[Y] = *reinterpret_cast<const bf16x4*>(ob + OH::DMT + tix(rX, Y * 16 + 4 * lg, C));
     }
 
     // the operand families' token loads (two tokens x eight channels per
@@ -1258,11 +1288,11 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
 #pragma unroll
         for (int kb = 0; kb < C / 32; ++kb)
-            t.w[kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DWT + (size_t)(cb + lr) * C + kb * 32 + lg * 8);
+            t.w[kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DWT + tix(cb + lr, kb * 32 + lg * 8, C));
         t.k4 = load_raw4<bf16>(k + trow * DK + c4);
         t.q4 = load_raw4<bf16>(q + trow * DK + c4);
-        t.dqg = load_raw4<bf16>(ob + OH::DQG + (size_t)rX * DK + c4);
-        t.dkc = load_raw4<bf16>(ob + OH::DKC + (size_t)rX * DK + c4);
+        t.dqg = load_raw4<bf16>(ob + OH::DQG + tix(rX, c4, DK));
+        t.dkc = load_raw4<bf16>(ob + OH::DKC + tix(rX, c4, DK));
     };
     f32x4 fG[NCTH];   // dq and dk are final within their tile and stored there
     float sb = 0.f;   // dbeta partial of token rX
@@ -1281,7 +1311,7 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
                 const int jb = hf * (DV / 2) + jt * 16;
 #pragma unroll
                 for (int kb = 0; kb < C / 32; ++kb)
-                    dvf[jt][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + (size_t)(jb + lr) * C + kb * 32 + lg * 8);
+                    dvf[jt][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + tix(jb + lr, kb * 32 + lg * 8, C));
                 vr[jt] = load_raw4<bf16>(v + trow * DV + jb + 4 * lg);
             }
         }

@@ -77,10 +77,20 @@ template <> struct Mfma<float> {
 // `ld` is the row stride in elements; for bf16 the address must be 16-byte
 // aligned (ld and k0 multiples of 8).
 template <class CT>
-__device__ __forceinline__ typename Mfma<CT>::frag load_frag(const CT* base, int ld, int row0, int k0) {
-    const int l = lane_id();
+__device__ __forceinline__ typename Mfma<CT>::frag load_frag(const CT* base, int ld, int row0, int k0, int l) {
     const CT* p = base + (size_t)(row0 + (l & 15)) * ld + k0 + (l >> 4) * Mfma<CT>::KPL;
     return *reinterpret_cast<const typename Mfma<CT>::frag*>(p);
+}
+template <class CT>
+__device__ __forceinline__ typename Mfma<CT>::frag load_frag(const CT* base, int ld, int row0, int k0) {
+    return load_frag<CT>(base, ld, row0, k0, lane_id());
+}
+
+// An opaque copy of x: values computed from it inside a loop are not hoisted
+// into the preheader, where they would hold registers across the whole loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
 }
 
 // Same addressing, from an fp32 tile, converted to the operand type.
