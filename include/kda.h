@@ -119,8 +119,9 @@ const char* kda_version(void);
  * 256 (batch, head) chains (the per-segment transition P, input term R and
  * entry state, fp32; with dk = dv = 128 also every chunk's
  * T' = (I + A)^-1 diag(beta), 64 x 64 bf16, which the pass that composes
- * the segments hands to the pass that writes the outputs); a single segment
- * needs no workspace.  fp32 sequences also stage the per-chunk products
+ * the segments hands to the pass that writes the outputs; there the first
+ * and last segments of each sequence are expanded directly, without a
+ * transition); a single segment needs no workspace.  fp32 sequences also stage the per-chunk products
  * (W, U^T, M, q e^G, (k e^{G_C-G})^T, e^{G_C}).
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
@@ -253,8 +254,10 @@ kda_status kda_recurrent_layer_step(const void* q, const void* k, const void* v,
  * (fewer than 256 (batch, head) chains and at least 16 chunks), the
  * normalisation and gate run inside the prefill's last kernel, on the
  * outputs rounded to bf16 (the values kda_out_gate would read back), so o
- * need not be written; the projection, when asked for, is a launch of its
- * own.  Other sizes run kda_chunk_fwd's kernels and then kda_out_gate's.
+ * need not be written (the first and last segments' outputs, which that
+ * kernel does not gate, go to o, or else to the rows the epilogue writes: y,
+ * or with a projection the workspace's gated rows; one more launch gates
+ * them); the projection, when asked for, is a launch of its own.  Other sizes run kda_chunk_fwd's kernels and then kda_out_gate's.
  * Every other rule is that of kda_chunk_fwd and kda_out_gate.
  */
 size_t kda_chunk_layer_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int chunk,
