@@ -270,6 +270,8 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
         typename MF::frag mtf[C / KS], kcf[DK / KS];
 #pragma unroll
         for (int kk = 0; kk < C / KS; ++kk) mtf[kk] = load_frag<CT>(bk + WB::MT, C, X * 16, kk * KS, l);
+        // e^{G_C} of this wave's rows, for the row sums and the dS update
+        const f32x4 eg = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(fb + WL::END * sizeof(CT)) + srow);
 #pragma unroll
         for (int kk = 0; kk < DK / KS; ++kk) kcf[kk] = load_frag<CT>(bk + WB::KC, DK, X * 16, kk * KS, l);
         constexpr int NKK = DV / KS, NIB = C / 16 / NCG;
@@ -423,8 +425,6 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
             awf[kk] = load_frag<CT>(bk + WB::WT, C, w * 16, kk * KS, l);
         }
         // e^{G_C} rowsum(S dS'), rows of this wave
-        const float* egc = reinterpret_cast<const float*>(fb + WL::END * sizeof(CT));
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(egc + srow);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sacc = 0.f;
