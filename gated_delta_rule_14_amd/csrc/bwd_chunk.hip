@@ -1430,6 +1430,11 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         const bf16* zl = z;
         asm volatile("" : "+s"(zl));
         const int c0 = 2 * (tid % L::CP), part = tid / L::CP, r0 = part * RP;
+        // this thread's logits, issued before the sums they wait for
+        bf16x2 zz[RP];
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            zz[i] = load2<bf16>(zl + (row0 + (size_t)min(r0 + i, valid - 1) * H) * DK + c0);
         float suf[RP][2];
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -1453,10 +1458,9 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
             const int r = r0 + i;
             if (r < valid) {
                 const size_t off = (row0 + (size_t)r * H) * DK + c0;
-                const bf16x2 zz = load2<bf16>(zl + off);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + dexp2<bf16>(-LOG2E * to_f32(zz[j])));
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + dexp2<bf16>(-LOG2E * to_f32(zz[i][j])));
                     dz[off + j] = (suf[i][j] + cr[j]) * g_min * sg * (1.0f - sg);
                 }
             }
