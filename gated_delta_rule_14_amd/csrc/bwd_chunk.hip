@@ -123,6 +123,30 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// Two adjacent 16-channel tiles P (channels c .. c + 15) and Q (c + 16 ..
+// c + 31) in the layout of a 16x16 MFMA result (lane lr + 16 lg: row lr,
+// channels 4 lg .. 4 lg + 3 of its tile), rearranged for row-contiguous
+// stores: lane 8 r + j of lo holds row r and of hi row r + 8, channels
+// c + 4 j .. c + 4 j + 3, so that one store instruction covers 8 rows of 128
+// contiguous bytes rather than 16 rows of 64.  A rotate by 8 lanes within
+// each 16-lane DPP row first brings row r + 8 of one tile beside row r of
+// the other; ds_bpermute then gathers.
+__device__ __forceinline__ void pair_rows(const f32x4& P, const f32x4& Q, f32x4& lo, f32x4& hi) {
+    const int l = lane_id(), lr = l & 15, r = l >> 3, j = l & 7;
+    const int src = ((j & 3) * 16 + r + 8 * (j >> 2)) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // the element into a scalar first: clang bit-casts a subscripted vector
+        // element as element 0
+        const float pe = P[e], qe = Q[e];
+        const int p = __builtin_bit_cast(int, pe), q = __builtin_bit_cast(int, qe);
+        const int pr = __builtin_amdgcn_mov_dpp(p, 0x128, 0xF, 0xF, false);
+        const int qr = __builtin_amdgcn_mov_dpp(q, 0x128, 0xF, 0xF, false);
+        lo[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, lr < 8 ? p : qr));
+        hi[e] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, lr < 8 ? pr : q));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Reverse chunk recurrence of one chain (b, h), all d_v columns: one wave per
 // 16 rows of dS (d_k / 16 waves).  dS rows of wave w: 16w + 4(l/16) + e,
@@ -1029,6 +1053,7 @@ struct DIntraH {
     static constexpr size_t LDS = OFF_DB + 6 * C * 4;
     static_assert(LDS <= 160 * 1024, "per-chunk gradient LDS budget");
     static_assert(RP % 2 == 0 && 16 % RP == 0 && DK % 32 == 0 && DV % 32 == 0, "tiling");
+    static_assert(NCTH % 2 == 0 && NVTH % 2 == 0, "result tiles are stored in pairs");
     static_assert(2 * C * C * 2 == 2 * 1024 * NW, "T^T and Ab: two 1 KB loads per wave");
 };
 
@@ -1298,23 +1323,16 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
     float sb = 0.f;   // dbeta partial of token rX
     bf16x8 dvf[NVTH][C / 32];   // dVn^T tiles of this wave's value half, and v
     bf16x4 vr[NVTH];
-    Tile cur;
-    load_tile(0, cur);
-#pragma unroll 1
-    for (int ct = 0; ct < NCTH; ++ct) {
-        Tile nxt;
-        if (ct + 1 < NCTH) {
-            load_tile(ct + 1, nxt);
-        } else {
-#pragma unroll
-            for (int jt = 0; jt < NVTH; ++jt) {
-                const int jb = hf * (DV / 2) + jt * 16;
-#pragma unroll
-                for (int kb = 0; kb < C / 32; ++kb)
-                    dvf[jt][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + tix(jb + lr, kb * 32 + lg * 8, C));
-                vr[jt] = load_raw4<bf16>(v + trow * DV + jb + 4 * lg);
-            }
-        }
+    // results of rows X*16 + (l >> 3) (+ 8), 16 bytes at channel 4 (l & 7) of a tile pair
+    const int prow = X * 16 + (l >> 3), pj = 4 * (l & 7);
+    auto put_pair = [&](float* dst, int ld, int c0, const f32x4& P, const f32x4& Q) {
+        f32x4 lo, hi;
+        pair_rows(P, Q, lo, hi);
+        if (prow < valid) *reinterpret_cast<f32x4*>(dst + (row0 + (size_t)prow * H) * ld + c0 + pj) = lo;
+        if (prow + 8 < valid) *reinterpret_cast<f32x4*>(dst + (row0 + (size_t)(prow + 8) * H) * ld + c0 + pj) = hi;
+    };
+    f32x4 pQ, pK;   // the even tile of a pair, stored with the odd one
+    auto tile_step = [&](const int ct, const Tile& cur) {
         const int cb = hf * (DK / 2) + ct * 16, c4 = cb + 4 * lg;
         f32x4 accK = zero4();
 #pragma unroll
@@ -1384,13 +1402,37 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) cs[e] = sum16(cs[e]);
         if (lr == 0) *reinterpret_cast<f32x4*>(car + X * DK + c4) = cs;
-        if (okX) {
-            *reinterpret_cast<f32x4*>(dq + trow * DK + c4) = fQ;
-            *reinterpret_cast<f32x4*>(dk + trow * DK + c4) = fK;
+        if (ct & 1) {
+            put_pair(dq, DK, cb - 16, pQ, fQ);
+            put_pair(dk, DK, cb - 16, pK, fK);
+        } else {
+            pQ = fQ;
+            pK = fK;
         }
+    };
+    // straight-line prefetch (no branch in the loop, so the waits before
+    // a tile's first use count only the loads issued after its own)
+    Tile cur;
+    load_tile(0, cur);
+#pragma unroll 1
+    for (int ct = 0; ct < NCTH - 1; ++ct) {
+        Tile nxt;
+        load_tile(ct + 1, nxt);
+        tile_step(ct, cur);
         cur = nxt;
     }
+    // the last tile, with the dBv operands loaded ahead
+#pragma unroll
+    for (int jt = 0; jt < NVTH; ++jt) {
+        const int jb = hf * (DV / 2) + jt * 16;
+#pragma unroll
+        for (int kb = 0; kb < C / 32; ++kb)
+            dvf[jt][kb] = *reinterpret_cast<const bf16x8*>(ob + OH::DVNT + tix(jb + lr, kb * 32 + lg * 8, C));
+        vr[jt] = load_raw4<bf16>(v + trow * DV + jb + 4 * lg);
+    }
+    tile_step(NCTH - 1, cur);
     // ---- dBv = T^T dVn: dV and the dBv . V part of dbeta
+    f32x4 pV;
 #pragma unroll
     for (int jt = 0; jt < NVTH; ++jt) {
         const int jb = hf * (DV / 2) + jt * 16, j4 = jb + 4 * lg;
@@ -1400,7 +1442,10 @@ __global__ __launch_bounds__(512) void dintra16_kernel(const bf16* __restrict__ 
         const f32x4 v4 = okX ? widen4(vr[jt]) : zero4();
 #pragma unroll
         for (int e = 0; e < 4; ++e) sb += acc[e] * v4[e];
-        if (okX) *reinterpret_cast<f32x4*>(dvo + trow * DV + j4) = acc * brX;
+        if (jt & 1)
+            put_pair(dvo, DV, jb - 16, pV, acc * brX);
+        else
+            pV = acc * brX;
     }
     sb += __shfl_xor(sb, 16);
     sb += __shfl_xor(sb, 32);
