@@ -123,6 +123,17 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// A workgroup barrier for LDS hand-offs that leaves global loads in flight
+// (__syncthreads would wait for every one of them): lgkmcnt(0) completes
+// this wave's LDS accesses, and the wavefront-scope fences keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Two adjacent 16-channel tiles P (channels c .. c + 15) and Q (c + 16 ..
 // c + 31) in the layout of a 16x16 MFMA result (lane lr + 16 lg: row lr,
 // channels 4 lg .. 4 lg + 3 of its tile), rearranged for row-contiguous
@@ -325,7 +336,9 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
 #pragma unroll
             for (int x = 0; x < VE; ++x) dOT[(j0 + x) * LC + r] = r < valid ? vals[x] : from_f32<CT>(0.f);
         }
-        __syncthreads();
+        lds_barrier();
+        // the next chunk's dO rows, a whole chunk ahead of their staging
+        if (n > 0) load_do(n - 1, tid);
 
         // dVn = M^T dO + Kc dS' (token rows 16X.., this wave's column group)
         constexpr int NTG = NT / NCG;
@@ -478,11 +491,10 @@ __global__ __launch_bounds__(DK * 4) void dchain_kernel(const E* __restrict__ do
                 accD[ct] = MF::mma(awf[kk], load_frag<CT>(dVT, LC, ct * 16, kk * KS, l), accD[ct]);
             }
         }
-        __syncthreads();   // this chunk's reads of dO^T, dS, dVn and S in LDS are done
+        lds_barrier();   // this chunk's reads of dO^T, dS, dVn and S in LDS are done
         if constexpr (L::SL) {
             if (n > 0) issue_s(n - 1);   // lands before the next chunk's products (the barrier after its dVn waits)
         }
-        if (n > 0) load_do(n - 1, tid);
         store_ds(l, srow);
     }
     if (ds0) {
