@@ -77,6 +77,35 @@ def test_decode_state_in_place_and_deterministic():
         assert torch.equal(t, before[n]), n
 
 
+@pytest.mark.parametrize("dtype,tag", [(torch.float32, "f32"), (torch.bfloat16, "bf16")])
+def test_decode_heads_dealt_over_workgroups(dtype, tag):
+    """1000 heads of d = 128: more heads than one launch has workgroups (two
+    per compute unit) and not a multiple of them, so a workgroup takes one or
+    more heads in turn, loading the next head's state meanwhile.  Every head
+    is checked against the oracle on its own, and every head is bit-equal to
+    the same sequences stepped in a call so small that each workgroup takes
+    one head."""
+    B, H, d = 125, 8, 128
+    go, gs, ro, rs = run_steps(B, H, d, d, dtype, steps=6, seed=31)
+    to, ts = TOL[tag]
+    eo = max(rel(go[i], ro[i]) for i in range(B * H))
+    es = max(rel(gs[i], rs[i]) for i in range(B * H))
+    print(f"decode {tag} 1000 heads: worst head o {eo:.2e} state {es:.2e}")
+    assert eo < to and es < ts
+
+    d_in = ki.decode_step_inputs(B, H, d, d, dtype, 77, 0, DEV)
+    s_full = ki.initial_state(B, H, d, d, 0.01, 77, DEV)
+    for lo, hi in ((0, 3), (120, 125)):
+        s_part = s_full[lo:hi].clone()
+        o_part = kda.recurrent_step(*(d_in[n][lo:hi].contiguous() for n in ("q", "k", "v", "z", "beta")),
+                                    ki.G_MIN, s_part)
+        if lo == 0:
+            s_ref = s_full.clone()
+            o_full = kda.recurrent_step(d_in["q"], d_in["k"], d_in["v"], d_in["z"], d_in["beta"], ki.G_MIN, s_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(o_full[lo:hi], o_part) and torch.equal(s_ref[lo:hi], s_part), (lo, hi)
+
+
 def test_decode_full_size_sampled():
     """B=256 sequences, H=32, d=128, fp32 state, bf16 tokens: the full decode
     workload, all 1024 steps with all 8192 heads launched; 64 heads checked
