@@ -20,7 +20,7 @@
 //    assigned so that consecutive workgroups on one XCD share an A row tile
 //    (and walk the B tiles together), which keeps both in that XCD's L2.
 //  * Results leave through LDS so that every global store is 16 bytes.
-//  * Small M (a decode batch): the K range is split over four workgroups
+//  * Small M (a decode batch): the K range is split over eight workgroups
 //    per tile (proj_gemm_kernel with KSPLIT > 1 writes fp32 partial tiles to
 //    the caller's scratch) and split_sum_kernel adds the partials in a fixed
 //    order, so the result is deterministic.
@@ -243,15 +243,21 @@ static hipError_t launch_t(const bf16* a, const bf16* b, bf16* out, float* part,
 }  // namespace gemmk
 
 // Shapes: N a multiple of 16 and K a multiple of 64 (d_model % 16 == 0,
-// K = H * d_v with d_v in {64, 128}).  Large M: 256 x 256 tiles of 2 x 2
+// K = H * d_v with d_v in {64, 128}).  Large M: 256 x 256 tiles of 4 x 4
 // waves (N a multiple of 256) or 128 x 128 tiles; small M (a decode batch):
-// 64 x 128 tiles of 1 x 4 waves with the K range split in four (N a multiple
-// of 128 and K of 128).  Other shapes: 64 x 16 tiles of one wave.
+// 256 x 128 tiles of 4 x 2 waves with the K range split in eight (N a
+// multiple of 128 and K of 256).  Other shapes: 64 x 16 tiles of one wave.
 bool gemm_small_m(int M) { return M <= 1024; }
 
-static bool split4(int M, int N, int K) { return gemm_small_m(M) && N % 128 == 0 && (K / gemmk::BK) % 4 == 0; }
+// Small M: a decode batch of up to 256 rows in one 256-row tile of 4 x 2
+// waves (up to four tiles for M <= 1024), 128 columns, the K range split in eight (measured at M = 256,
+// K = 4096, N = 2304 against 64 x 128 tiles split in four, 128 x 128 split
+// in four or eight and 256 x 128 split in sixteen: fewer re-reads of W and y
+// through L2 outweigh the larger fp32 partial tiles).
+constexpr int SM_BM = 256, SM_BN = 128, SM_KS = 8;
+static bool split_k(int M, int N, int K) { return gemm_small_m(M) && N % SM_BN == 0 && (K / gemmk::BK) % SM_KS == 0; }
 
-size_t projection_scratch_bytes(int M, int N, int K) { return split4(M, N, K) ? (size_t)4 * M * N * 4 : 0; }
+size_t projection_scratch_bytes(int M, int N, int K) { return split_k(M, N, K) ? (size_t)SM_KS * M * N * 4 : 0; }
 
 hipError_t launch_projection(const void* y, const void* w, void* out, int M, int N, int K, void* scratch,
                              void* stream) {
@@ -259,17 +265,17 @@ hipError_t launch_projection(const void* y, const void* w, void* out, int M, int
     if (M == 0) return hipSuccess;
     const bf16 *a = (const bf16*)y, *b = (const bf16*)w;
     bf16* o = (bf16*)out;
-    if (split4(M, N, K)) {
+    if (split_k(M, N, K)) {
         float* part = (float*)scratch;
-        hipError_t err = gemmk::launch_t<64, 128, 1, 4, 4>(a, b, o, part, M, N, K, st);
+        hipError_t err = gemmk::launch_t<SM_BM, SM_BN, 4, 2, SM_KS>(a, b, o, part, M, N, K, st);
         if (err != hipSuccess) return err;
         const size_t mn = (size_t)M * N;
         const size_t blocks = (mn / 4 + 255) / 256;
         hipLaunchKernelGGL(gemmk::split_sum_kernel, dim3((unsigned)(blocks < 65535 ? blocks : 65535)), dim3(256), 0,
-                           st, (const float*)part, o, mn, 4);
+                           st, (const float*)part, o, mn, SM_KS);
         return hipGetLastError();
     }
-    if (!gemm_small_m(M) && N % 256 == 0) return gemmk::launch_t<256, 256, 2, 4, 1>(a, b, o, nullptr, M, N, K, st);
+    if (!gemm_small_m(M) && N % 256 == 0) return gemmk::launch_t<256, 256, 4, 4, 1>(a, b, o, nullptr, M, N, K, st);
     if (!gemm_small_m(M) && N % 128 == 0) return gemmk::launch_t<128, 128, 2, 2, 1>(a, b, o, nullptr, M, N, K, st);
     return gemmk::launch_t<64, 16, 1, 1, 1>(a, b, o, nullptr, M, N, K, st);
 }

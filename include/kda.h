@@ -192,9 +192,9 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
  *             gated activations y and the projection GEMM's scratch
  * With a projection, dt must be KDA_BF16 and d_model a multiple of 16.  The
  * projection is libkda's own GEMM (bf16 MFMA, fp32 accumulation, output
- * rounded to bf16); for up to 1024 rows with d_model a multiple of 128 it
- * splits the K range in four and adds the fp32 partials in a fixed order,
- * using M * d_model * 16 bytes of the workspace.
+ * rounded to bf16); for up to 1024 rows with d_model a multiple of 128 and
+ * H * dv a multiple of 256 it splits the K range in eight and adds the fp32
+ * partials in a fixed order, using M * d_model * 32 bytes of the workspace.
  */
 size_t kda_out_gate_workspace_bytes(int B, int T, int H, int dv, int d_model, kda_dtype dt,
                                     int with_projection);

@@ -84,7 +84,7 @@ def test_workspace_sizes(lib):
     # gated activations y (bf16); a large M needs no GEMM scratch
     assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 2304, BF16, 1) == 8 * 8192 * 4096 * 2
     # a small M splits K in four: fp32 partial tiles after the rows
-    assert lib.kda_out_gate_workspace_bytes(1, 256, 32, 128, 2304, BF16, 1) == 256 * 4096 * 2 + 4 * 256 * 2304 * 4
+    assert lib.kda_out_gate_workspace_bytes(1, 256, 32, 128, 2304, BF16, 1) == 256 * 4096 * 2 + 8 * 256 * 2304 * 4
     assert lib.kda_out_gate_workspace_bytes(8, 8192, 32, 128, 0, BF16, 0) == 0
 
 
@@ -166,9 +166,9 @@ def lstep(lib, q=P, k=P, v=P, z=P, beta=P, g_min=-5.0, state=P, g=P, eps=1e-6, w
 
 def test_recurrent_layer_step_workspace_and_bad_arguments(lib):
     # the gated row in bf16 (256-byte aligned), then the GEMM's fp32 partial
-    # tiles of its four K splits (d_model a multiple of 128; none otherwise)
+    # tiles of its eight K splits (d_model a multiple of 128; none otherwise)
     assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 2304, BF16, 1) == \
-        256 * 32 * 128 * 2 + 4 * 256 * 2304 * 4
+        256 * 32 * 128 * 2 + 8 * 256 * 2304 * 4
     assert lib.kda_recurrent_layer_step_workspace_bytes(3, 1, 64, 16, BF16, 1) == 512
     assert lib.kda_recurrent_layer_step_workspace_bytes(256, 32, 128, 0, BF16, 0) == 0
     assert lstep(lib, g=None) == NULL

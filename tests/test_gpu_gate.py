@@ -131,7 +131,7 @@ def _gemm_case(B, T, H, dv, dm, seed, rows=None):
     (1, 1000, 8, 128, 512),      # 256 x 256 tiles, ragged last M tile
     (1, 1283, 4, 128, 384),      # 128 x 128 tiles (N a multiple of 128 only), ragged M
     (2, 1500, 2, 64, 272),       # 64 x 16 tiles (N = 17 * 16), ragged M
-    (1, 256, 32, 128, 2304),     # decode batch: K split in four, fp32 partials summed in order
+    (1, 256, 32, 128, 2304),     # decode batch: K split in eight, fp32 partials summed in order
     (1, 1024, 32, 128, 2304),    # the largest split-K M
     (1, 1025, 32, 128, 2304),    # the smallest whole-K M with ragged tiles
     (1, 3, 1, 64, 16),           # K = 64 (one stage), tiny M and N
