@@ -207,7 +207,7 @@ def bench_decode_layer(torch, kda, ki, state, steps, B, H, dv, d_model=2304):
     t_u = _time_calls(torch, unfused, 1) / n
     return {"d_model": d_model, "steps": n, "us_per_step_fused": round(t_f * 1e6, 1),
             "us_per_step_unfused": round(t_u * 1e6, 1),
-            "kernels": "fused: decode_step_kernel with the gate epilogue + split-K proj_gemm_kernel<64,128> "
+            "kernels": "fused: decode_step_kernel with the gate epilogue + split-K proj_gemm_kernel<256,128> "
                        "+ split_sum_kernel; unfused: decode_step_kernel + gate_kernel + the same GEMM"}
 
 
