@@ -24,8 +24,10 @@ __device__ __forceinline__ void gate_row(const E* o, const E* gate, float eps, E
     const size_t base = row * DV + sub * 8;
     float x[8], g[8];
     if constexpr (sizeof(E) == 2) {
-        const bf16x8 xv = *reinterpret_cast<const bf16x8*>(o + base);
-        const bf16x8 gv = *reinterpret_cast<const bf16x8*>(gate + base);
+        // non-temporal: every byte is touched once (279 -> 256 us on the
+        // 8 x 8192 x 32-head rows, one box)
+        const bf16x8 xv = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(o + base));
+        const bf16x8 gv = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(gate + base));
 #pragma unroll
         for (int j = 0; j < 8; ++j) { x[j] = (float)xv[j]; g[j] = (float)gv[j]; }
     } else {
@@ -45,7 +47,7 @@ __device__ __forceinline__ void gate_row(const E* o, const E* gate, float eps, E
         bf16x8 out;
 #pragma unroll
         for (int j = 0; j < 8; ++j) out[j] = (bf16)(x[j] * inv * sigmoidf_(g[j]));
-        *reinterpret_cast<bf16x8*>(y + base) = out;
+        __builtin_nontemporal_store(out, reinterpret_cast<bf16x8*>(y + base));
     } else {
         f32x4 y0, y1;
 #pragma unroll
